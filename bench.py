@@ -1,0 +1,282 @@
+#!/usr/bin/env python3
+"""Benchmark of the OSCAR INT2 KV-cache hot path on one MI355X.
+
+A step is one serving decode step of one attention layer for the whole batch:
+oscar_quant_append of each request's new token (rotate, clip, INT2-quantise,
+pack, route) followed by oscar_decode_attn over the three-region cache.  The
+default workload is 32 requests at 100,000 cached tokens, 32 query / 8 KV
+heads, head_dim 128 (Qwen3-4B-shaped), on synthetic seeded data with every
+input resident in HBM before timing starts.
+
+Printed: one JSON line with KV tokens/s (sum of context lengths / step time),
+the split-K kernel's achieved bandwidth against the HBM roofline (timed live
+with HIP events on the launch stream), the quant-append throughput of the
+131,072-token append workload, and the fp64 CPU oracle's rate on a bounded
+sample of the same decode workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "INT2 decode-attn KV tokens/s & % HBM roofline @100K ctx bs32; quant tok/s"
+HBM_PEAK_GBS = 8000.0
+HISTORY_BYTES_PER_TOKEN_HEAD = 96      # K codes 32 + V codes 32 + K (s,z) 16 + V (s,z) 16
+SLOT_BYTES_PER_TOKEN = 4
+BF16_BYTES_PER_TOKEN_HEAD = 512        # K and V, 128 bf16 each
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_kernel_bytes(lens, hkv, sink=64, recent=256):
+    """Algorithmic bytes read by the split-K kernel for one decode step."""
+    total = 0
+    for L in lens:
+        bf16 = min(L, sink + recent)
+        hist = L - bf16
+        total += hist * (hkv * HISTORY_BYTES_PER_TOKEN_HEAD + SLOT_BYTES_PER_TOKEN)
+        total += bf16 * hkv * BF16_BYTES_PER_TOKEN_HEAD
+    return total
+
+
+def append_bytes(n_tokens, hkv, sink=64, recent=256):
+    """Algorithmic bytes of appending n bf16 tokens of one request (positions 0..n-1)."""
+    read = n_tokens * hkv * 2 * 128 * 2 + n_tokens * 12         # K, V, req/pos/slot
+    n_int2 = max(0, n_tokens - sink)
+    n_ring = min(recent, n_int2)
+    write = n_int2 * hkv * HISTORY_BYTES_PER_TOKEN_HEAD + (min(sink, n_tokens) + n_ring) * hkv * 512
+    return read + write
+
+
+def build_rotations(B, w):
+    from rotated_int2_kv_amd import workloads
+    cov = workloads.covariances(w)
+    rk = np.stack([B.oscar_build_rotation(cov.sigma_q[h])[0] for h in range(w.num_kv_heads)])
+    rv = np.stack([B.oscar_build_rotation(cov.sigma_s[h])[0] for h in range(w.num_kv_heads)])
+    return rk.astype(np.float32), rv.astype(np.float32)
+
+
+def run_decode(args, torch, B, workloads):
+    w = workloads.workload(args.workload)
+    lens = np.asarray(w.seq_lens, np.int32)
+    bsz, hkv = w.batch, w.num_kv_heads
+    lay = B.Layout(128, 32, hkv, w.num_q_heads, w.sink, w.recent, num_slots=w.num_slots,
+                   max_requests=bsz)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    rk, rv = build_rotations(B, w)
+    rk_d, rv_d = dev(rk), dev(rv)
+    slots = workloads.slot_table(w)
+    table = dev(workloads.req_to_slot_matrix(w, slots, fill=0))
+    pool = B.new_pool(lay)
+
+    # cache fill: positions 0 .. L-2 of every request (the step appends L-1)
+    t0 = time.time()
+    after = dev(lens - 1)
+    chunk = 131072
+    for b in range(bsz):
+        n = int(lens[b]) - 1
+        for c0 in range(0, n, chunk):
+            c1 = min(n, c0 + chunk)
+            k, v = workloads.raw_kv_device(w, c1 - c0, stream=b * 1000 + c0 // chunk, device="cuda")
+            B.oscar_quant_append(lay, pool, k.to(torch.bfloat16), v.to(torch.bfloat16),
+                                 dev(np.full(c1 - c0, b, np.int32)),
+                                 dev(np.arange(c0, c1, dtype=np.int32)), dev(slots[b][c0:c1]),
+                                 after, rk_d, rv_d)
+            del k, v
+    torch.cuda.synchronize()
+    log(f"[bench] cache filled: {bsz} x {int(lens.max())} tokens in {time.time() - t0:.1f}s")
+
+    # step inputs
+    q = dev(workloads.queries(w, n_rows=bsz, stream=7)).to(torch.bfloat16)
+    kn, vn = workloads.raw_kv_device(w, bsz, stream=999_999, device="cuda")
+    kn, vn = kn.to(torch.bfloat16), vn.to(torch.bfloat16)
+    req_ids = dev(np.arange(bsz, dtype=np.int32))
+    pos = dev(lens - 1)
+    new_slots = dev(np.array([slots[b][lens[b] - 1] for b in range(bsz)], np.int32))
+    lens_d = dev(lens)
+    ws = torch.empty(B.oscar_decode_workspace_size(lay, lens, args.history_chunk), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty((bsz, w.num_q_heads, 128), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        B.oscar_quant_append(lay, pool, kn, vn, req_ids, pos, new_slots, lens_d, rk_d, rv_d,
+                             stream=stream)
+        B.oscar_decode_attn(lay, pool, q, req_ids, lens_d, lens, table, rk_d, rv_d, 128 ** -0.5,
+                            out, ws, stream=stream, kernel_begin=None if ev is None else ev[0],
+                            kernel_end=None if ev is None else ev[1],
+                            history_chunk=args.history_chunk)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(args.steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)   # create the underlying HIP events
+        b.record(stream)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    chunk_sz, items = B.oscar_decode_plan(lay, lens, args.history_chunk)
+    kbytes = decode_kernel_bytes(lens.tolist(), hkv, w.sink, w.recent)
+    return dict(w=w, lens=lens, ms=ms, kern_ms=kern_ms, kbytes=kbytes, chunk=chunk_sz, items=items,
+                o_finite=bool(torch.isfinite(out.float()).all().item()))
+
+
+def run_append(args, torch, B, workloads):
+    w = workloads.workload("append_131k")
+    n = w.seq_lens[0]
+    hkv = w.num_kv_heads
+    lay = B.Layout(128, 32, hkv, w.num_q_heads, w.sink, w.recent, num_slots=w.num_slots,
+                   max_requests=1)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    rk, rv = build_rotations(B, w)
+    rk_d, rv_d = dev(rk), dev(rv)
+    k, v = workloads.raw_kv_device(w, n, stream=0, device="cuda")
+    k, v = k.to(torch.bfloat16), v.to(torch.bfloat16)
+    torch.cuda.synchronize()
+    pool = B.new_pool(lay)
+    req = dev(np.zeros(n, np.int32))
+    pos = dev(np.arange(n, dtype=np.int32))
+    slots = dev(workloads.slot_table(w)[0])
+    after = dev(np.array([n], np.int32))
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        B.oscar_quant_append(lay, pool, k, v, req, pos, slots, after, rk_d, rv_d, stream=stream)
+    reps = max(5, args.steps // 2)
+    evs = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        b.record(stream)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    for i in range(reps):
+        B.oscar_quant_append(lay, pool, k, v, req, pos, slots, after, rk_d, rv_d, stream=stream,
+                             kernel_begin=evs[i][0], kernel_end=evs[i][1])
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    nbytes = append_bytes(n, hkv, w.sink, w.recent)
+    flops = 2 * n * hkv * 2 * 128 * 128
+    return dict(workload="append_131k", tokens=n, kv_heads=hkv, ms=ms,
+                tokens_per_s=n / (ms * 1e-3), head_vectors_per_s=n * hkv * 2 / (ms * 1e-3),
+                algorithmic_bytes=nbytes, gb_per_s=nbytes / (ms * 1e-3) / 1e9,
+                frac_hbm=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                rotation_tflops=flops / (ms * 1e-3) / 1e12)
+
+
+def cpu_baseline(workloads):
+    """The oracle, as it stands, on one request of the decode workload."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention, cache, quant, rotation
+    w = workloads.workload("decode_b32")
+    L = w.seq_lens[0]
+    with threadpool_limits(limits=1):
+        k, v = workloads.raw_kv_host(w, L)
+        k, v = quant.bf16_round(k), quant.bf16_round(v)
+        cov = workloads.covariances(w)
+        rk = np.stack([rotation.composite_rotation(cov.sigma_q[h]) for h in range(w.num_kv_heads)])
+        rv = np.stack([rotation.composite_rotation(cov.sigma_s[h]) for h in range(w.num_kv_heads)])
+        rk, rv = rk.astype(np.float32), rv.astype(np.float32)
+        lay = cache.Layout(128, 32, w.num_kv_heads, w.num_q_heads, w.sink, w.recent, L, 1)
+        pool = cache.new_pool(lay)
+        slots = np.arange(L)
+        cache.append(pool, lay, k, v, np.zeros(L, int), np.arange(L), slots, [L], rk, rv)
+        del k, v
+        q = quant.bf16_round(workloads.queries(w, n_rows=1, stream=7))
+        reps = 2
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            attention.decode(pool, lay, q, [0], [L], slots[None, :], rk, rv, 128 ** -0.5)
+        dt = time.perf_counter() - t0
+    return {"value": reps * L / dt, "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} decode steps of one request of the decode_b32 workload (L = {L}, "
+                      f"32 q / 8 KV heads, all heads), fp64 NumPy oracle, 1 thread, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_b32")
+    ap.add_argument("--history-chunk", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-append", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU: the hot path (per-request, per-KV-head "
+                                   "decode and append) is measured on one MI355X; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+
+    from rotated_int2_kv_amd import binding as B
+    from rotated_int2_kv_amd import workloads
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    d = run_decode(args, torch, B, workloads)
+    w = d["w"]
+    ms = d["ms"]
+    kv_tokens = int(d["lens"].sum())
+    achieved = d["kbytes"] / (d["kern_ms"] * 1e-3) / 1e9
+    log(f"[bench] step {ms:.3f} ms, split-K kernel {d['kern_ms']:.3f} ms, {achieved:.0f} GB/s")
+    app = None if args.no_append else run_append(args, torch, B, workloads)
+    if app:
+        log(f"[bench] append {app['ms']:.3f} ms, {app['tokens_per_s']:.3e} tok/s, {app['gb_per_s']:.0f} GB/s")
+    base = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle ...")
+        base = cpu_baseline(workloads)
+    res = {
+        "metric": METRIC,
+        "value": kv_tokens / (ms * 1e-3),
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": int(d["lens"].max()),
+                   "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": 128,
+                   "group_size": 32, "sink": w.sink, "recent": w.recent,
+                   "step": "oscar_quant_append(1 new token per request) + oscar_decode_attn",
+                   "history_chunk": d["chunk"], "items_per_request": d["items"]},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "partial_kernel (split-K)", "kernel_ms": d["kern_ms"],
+                     "algorithmic_bytes": d["kbytes"]},
+        "decode_steps_per_s": 1e3 / ms,
+        "quant_append": app,
+        "cpu_baseline": base,
+        "output_finite": d["o_finite"],
+    }
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

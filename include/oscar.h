@@ -1,0 +1,231 @@
+/*
+ * oscar.h - C ABI of the OSCAR INT2 KV-cache hot path for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The method (Together AI's OSCAR announcement, sections "What OSCAR does
+ * differently" and "Serving system: mixed-precision cache layout"):
+ *   - every new key head-vector k is rotated by R_K = U_Q H P_br and every
+ *     value head-vector v by R_V = U_S H P_br, then clipped, quantised to INT2
+ *     with a scale and zero per group of channels, and packed;
+ *   - each request's cache has three regions: the first 64 tokens (sink) and
+ *     the last 256 tokens (recent) stay in BF16, every token between them
+ *     (history) is kept in INT2;
+ *   - decode attention rotates the query by R_K, computes the logits in the
+ *     rotated basis against the dequantised cache, and brings the output back
+ *     with R_V^T.
+ *
+ * Conventions of this ABI
+ *   - Vectors are rows: x' = x R.  Matrices are row-major.
+ *   - Every pointer argument of a device-side call is a device pointer on the
+ *     current HIP device unless it is marked "host".  The caller owns all
+ *     memory; the library never allocates device memory.
+ *   - All arguments are validated on the host before any HIP call; invalid
+ *     arguments return a status and launch nothing.  Device work is
+ *     asynchronous on `stream`; execution faults surface at the caller's
+ *     synchronisation.  No call aborts or throws across the ABI.
+ *   - Calls are re-entrant.  The only global state is a thread-local error
+ *     message (oscar_last_error).  Two calls that write the same pool bytes
+ *     concurrently race; serialise them on one stream.
+ *   - Supported shapes: head_dim 128, group_size 32, 1 <= num_kv_heads <= 16,
+ *     num_q_heads = g * num_kv_heads with 1 <= g <= 8.  Other shapes return
+ *     OSCAR_ERR_UNSUPPORTED.
+ */
+#ifndef OSCAR_H
+#define OSCAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    OSCAR_OK = 0,
+    OSCAR_ERR_INVALID_ARG = 1,  /* null pointer, negative size, inconsistent layout */
+    OSCAR_ERR_UNSUPPORTED = 2,  /* shape outside the supported set above */
+    OSCAR_ERR_WORKSPACE = 3,    /* workspace smaller than oscar_decode_workspace_size */
+    OSCAR_ERR_HIP = 4,          /* a HIP launch or query failed */
+    OSCAR_ERR_NUMERIC = 5       /* eigensolver did not converge */
+} oscar_status;
+
+typedef enum { OSCAR_F32 = 0, OSCAR_BF16 = 1, OSCAR_F16 = 2 } oscar_dtype;
+
+/* Shape of one attention layer's cache. */
+typedef struct {
+    int32_t head_dim;       /* d; must be 128 */
+    int32_t group_size;     /* G, channels per scale/zero group; must be 32 */
+    int32_t num_kv_heads;   /* Hkv, 1..16 */
+    int32_t num_q_heads;    /* Hq = g * Hkv, 1 <= g <= 8 */
+    int32_t sink_tokens;    /* S, BF16 sink window (the pages use 64); 0..4096 */
+    int32_t recent_tokens;  /* W, BF16 recent window (the pages use 256); 1..4096 */
+    int64_t num_slots;      /* INT2 pool capacity in tokens (page_size = 1) */
+    int32_t max_requests;   /* rows of the sink/recent stores */
+} oscar_layout;
+
+/*
+ * Cache storage.  Byte formats (little endian):
+ *
+ * records: [num_slots][Hkv * 96] bytes.  The record of a slot holds one
+ *   96-byte head record per KV head, head h at byte 96 h:
+ *     [0, 32)   K codes      [32, 64)  V codes
+ *     [64, 80)  K (s, z)     [80, 96)  V (s, z)
+ *   Codes: the 128 rotated channels, 2 bits each, four per byte, least
+ *   significant bits first: byte j holds channels 4j .. 4j+3 at bit offsets
+ *   0, 2, 4, 6.  (s, z): for each of the 4 groups of 32 contiguous rotated
+ *   channels, fp16 scale s then fp16 zero z.  Element value = s * code + z.
+ * sink:    [max_requests][S][Hkv][2][128] bf16 (2 = K, V), rotated basis,
+ *          position p < S at index p.
+ * recent:  [max_requests][W][Hkv][2][128] bf16 ring, rotated basis,
+ *          position p at index p mod W.
+ */
+typedef struct {
+    uint8_t *records;
+    uint16_t *sink;
+    uint16_t *recent;
+} oscar_pool;
+
+/* Optional launch controls (pass NULL for defaults). */
+typedef struct {
+    /* If non-null, recorded on `stream` immediately before and after the
+       dominant kernel of the call (decode: the split-K partial kernel;
+       append: the rotate/quantise kernel), for live per-kernel timing. */
+    hipEvent_t kernel_begin;
+    hipEvent_t kernel_end;
+    /* Decode only: history tokens per split-K work item (multiple of 32,
+       32..65536); 0 = chosen from the sequence lengths. */
+    int32_t history_chunk;
+    /* Append only: tokens per workgroup (multiple of 16); 0 = automatic. */
+    int32_t append_chunk;
+} oscar_launch_opts;
+
+/* Returns OSCAR_OK if `layout` is valid and supported, else the status and
+   a message in oscar_last_error(). */
+oscar_status oscar_layout_check(const oscar_layout *layout);
+
+/* Bytes of one part of the storage: part 0 = records, 1 = sink, 2 = recent.
+   Returns 0 for an invalid layout or part. */
+size_t oscar_pool_bytes(const oscar_layout *layout, int32_t part);
+
+/*
+ * oscar_build_rotation (host only, fp64).
+ *
+ * R = U H P for a symmetric d x d covariance `cov` (host, row-major), where
+ *   U: eigenvectors of cov (Together AI OSCAR page, "What OSCAR does
+ *      differently": U_Q from C_Q = (1/N) sum q_n^T q_n for keys, U_S from
+ *      C_S = (1/N) V^T S^T S V for values), eigenvalues in descending order,
+ *      each column signed so that its largest-magnitude entry is positive
+ *      (first index on ties);
+ *   H: Sylvester Hadamard matrix / sqrt(d) (Qiita article, "Fix 3");
+ *   P: bit-reversal permutation of the channel index, (x P)[rev(i)] = x[i],
+ *      which gives every contiguous group one channel of every importance tier.
+ * flags select the factors: OSCAR_ROT_EIG | OSCAR_ROT_HAD | OSCAR_ROT_PBR is
+ * OSCAR; OSCAR_ROT_HAD alone a data-independent Hadamard rotation; 0 the
+ * identity.  cov is read only if OSCAR_ROT_EIG is set.  d: power of two,
+ * 1..1024.  R_out: host, d*d doubles.  eigvals_out: host, d doubles or NULL
+ * (descending eigenvalues; zeros if OSCAR_ROT_EIG is not set).
+ * Eigenvectors come from the cyclic Jacobi method; it stops when a sweep finds
+ * every off-diagonal entry negligible next to its diagonal pair or the
+ * off-diagonal norm is below 1e-15 of the matrix norm (at most 100 sweeps,
+ * else OSCAR_ERR_NUMERIC).  A non-finite or non-symmetric (beyond 1e-12
+ * relative) cov returns OSCAR_ERR_INVALID_ARG.
+ */
+#define OSCAR_ROT_EIG 1u
+#define OSCAR_ROT_HAD 2u
+#define OSCAR_ROT_PBR 4u
+#define OSCAR_ROT_OSCAR 7u
+oscar_status oscar_build_rotation(const double *cov, int32_t d, uint32_t flags,
+                                  double *R_out, double *eigvals_out);
+
+/*
+ * oscar_quant_append: rotate, clip, quantise and route n new tokens
+ * (Together AI OSCAR page, "Serving system": INT2 after rotation and
+ * clipping; BF16 sink and recent windows).
+ *
+ * k, v:          [n_tokens][Hkv][128] of in_dtype (F32, BF16 or F16).
+ * req_ids:       [n_tokens] int32, row of the sink/recent stores, < max_requests.
+ * positions:     [n_tokens] int32 >= 0, position of the token in its request.
+ * slots:         [n_tokens] int32, INT2 pool slot, < num_slots (ignored for
+ *                positions < S).
+ * seq_len_after: [max_requests] int32, cache length of each request once this
+ *                call's tokens are in (decides the recent window).
+ * R_K, R_V:      [Hkv][128][128] fp32 rotations.
+ * clip_ratio:    alpha in (0, 1]; 1 disables clipping.
+ * rotated_out:   NULL or [n_tokens][Hkv][2][128] fp32: the rotated values
+ *                x' = fl32(x R) (for testing).
+ * Per token and tensor: x' = x R in fp32; then per group of 32 channels
+ *   lo, hi = min, max of x'; lo_c = fl32(alpha lo) if lo < 0 else lo;
+ *   hi_c = fl32(alpha hi) if hi > 0 else hi; x_c = min(max(x', lo_c), hi_c);
+ *   s = fp16_rn(fl32((hi_c - lo_c) / 3)); z = fp16_rn(lo_c);
+ *   code = #{k in 0,1,2 : x_c >= z + (k + 1/2) s} (exact), 0 if s == 0.
+ * Routing: p < S -> sink[req][p] = bf16_rn(x'); p >= S -> the slot's record;
+ *   p >= S and p >= seq_len_after[req] - W -> also recent[req][p mod W].
+ * Tokens whose req_id, position or (for p >= S) slot is out of range are
+ * skipped.  Tokens of one call must not share a slot or a (req, position).
+ */
+oscar_status oscar_quant_append(hipStream_t stream, const oscar_layout *layout,
+                                const oscar_pool *pool, const void *k, const void *v,
+                                oscar_dtype in_dtype, int32_t n_tokens,
+                                const int32_t *req_ids, const int32_t *positions,
+                                const int32_t *slots, const int32_t *seq_len_after,
+                                const float *R_K, const float *R_V, float clip_ratio,
+                                float *rotated_out, const oscar_launch_opts *opts);
+
+/*
+ * Workspace bytes that oscar_decode_attn needs for this batch.
+ * seq_lens_host: host, [batch] int32 >= 1.  opts may be NULL.
+ */
+oscar_status oscar_decode_workspace_size(const oscar_layout *layout, int32_t batch,
+                                         const int32_t *seq_lens_host,
+                                         const oscar_launch_opts *opts, size_t *bytes);
+
+/*
+ * oscar_decode_attn: one decode step of attention for `batch` requests.
+ *
+ * q:             [batch][Hq][128] of q_dtype (F32, BF16 or F16).
+ * req_ids:       [batch] int32, rows of the stores and of req_to_slot.
+ * seq_lens:      [batch] int32, cache length L of each request (device copy).
+ * seq_lens_host: host, [batch] int32, the same lengths (used for planning;
+ *                if they differ from seq_lens the output is undefined but all
+ *                accesses stay in bounds).
+ * req_to_slot:   [max_requests][req_to_slot_stride] int32 slot ids per
+ *                position (page_size = 1); entries for history positions
+ *                [S, L - W) are read, out-of-range slot ids are skipped.
+ * R_K, R_V:      [Hkv][128][128] fp32.
+ * sm_scale:      logit scale (1/sqrt(128) is the usual choice).
+ * out:           [batch][Hq][128] of out_dtype (F32, BF16 or F16).
+ * workspace:     >= oscar_decode_workspace_size bytes, 256-byte aligned.
+ * Computes, for q head h reading KV head h / g (Qiita article, "Fix 4"):
+ *   q' = q R_K; logits over sink [0, min(S, L)), history [S, max(S, L - W))
+ *   (dequantised INT2) and recent [max(S, L - W), L) (BF16); softmax;
+ *   o' = sum_p softmax_p v'_p; out = o' R_V^T.
+ */
+oscar_status oscar_decode_attn(hipStream_t stream, const oscar_layout *layout,
+                               const oscar_pool *pool, const void *q, oscar_dtype q_dtype,
+                               int32_t batch, const int32_t *req_ids,
+                               const int32_t *seq_lens, const int32_t *seq_lens_host,
+                               const int32_t *req_to_slot, int64_t req_to_slot_stride,
+                               const float *R_K, const float *R_V, float sm_scale,
+                               void *out, oscar_dtype out_dtype, void *workspace,
+                               size_t workspace_bytes, const oscar_launch_opts *opts);
+
+/* Split-K plan that oscar_decode_attn uses: history tokens per work item and
+   work items per request (sink + recent + history chunks). */
+oscar_status oscar_decode_plan(const oscar_layout *layout, int32_t batch,
+                               const int32_t *seq_lens_host,
+                               const oscar_launch_opts *opts, int32_t *history_chunk,
+                               int32_t *items_per_request);
+
+/* Thread-local message of the last non-OK status of this thread. */
+const char *oscar_last_error(void);
+
+/* Library version string. */
+const char *oscar_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OSCAR_H */

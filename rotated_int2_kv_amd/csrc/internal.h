@@ -1,0 +1,48 @@
+// Internal declarations shared by the host code and the kernel launchers of
+// liboscar.  Not part of the ABI.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "../../include/oscar.h"
+
+namespace oscar {
+
+constexpr int kHeadDim = 128;
+constexpr int kGroup = 32;
+constexpr int kGroups = kHeadDim / kGroup;          // 4
+constexpr int kCodeBytes = kHeadDim / 4;            // 32 bytes of codes per head-vector
+constexpr int kSzBytes = 4 * kGroups;               // 16 bytes of (s, z) per head-vector
+constexpr int kHeadRecord = 2 * kCodeBytes + 2 * kSzBytes;  // 96
+constexpr int kMaxKvHeads = 16;
+constexpr int kMaxGroup = 8;                        // query heads per KV head
+
+oscar_status fail(oscar_status st, const std::string &msg);
+oscar_status ok();
+
+// Full validation of a layout (shape support included).
+oscar_status check_layout(const oscar_layout *lay);
+
+inline int64_t record_bytes(const oscar_layout &lay) {
+    return static_cast<int64_t>(lay.num_kv_heads) * kHeadRecord;
+}
+
+// Split-K plan of one decode call (pure function of the host lengths).
+struct DecodePlan {
+    int32_t chunk = 0;           // history tokens per work item
+    int32_t items = 0;           // work items per request: sink, recent, chunks
+    int32_t max_len = 0;
+    size_t ws_qrot = 0;          // byte offsets into the workspace
+    size_t ws_qsum = 0;
+    size_t ws_part_o = 0;
+    size_t ws_part_ml = 0;
+    size_t ws_bytes = 0;
+};
+
+oscar_status make_decode_plan(const oscar_layout &lay, int32_t batch,
+                              const int32_t *seq_lens_host, const oscar_launch_opts *opts,
+                              DecodePlan *plan);
+
+}  // namespace oscar

@@ -1,0 +1,350 @@
+// oscar_quant_append: rotate, clip, INT2-quantise, pack and route new K/V
+// tokens (Together AI OSCAR page, "Serving system"; group-wise INT2 with
+// per-group scale and zero, "Why is INT2 KV-cache quantization hard?").
+//
+// One workgroup = one (token chunk, KV head, tensor K or V); its four waves
+// own the four groups of 32 rotated output channels.  Each wave keeps the
+// transposed rotation columns of its group in registers as MFMA A operands:
+// the fp32 rotation is split exactly into three bf16 terms r1 + r2 + r3, so
+// with bf16 inputs the product x R is formed without approximation and
+// accumulated in fp32 on the matrix cores.  Tiles of 16 tokens are staged
+// through LDS as the B operand (x^T), and each lane ends up with 8 contiguous
+// rotated channels of one token, which it quantises, packs into 16 bits and
+// stores.  Group min/max need two cross-lane steps (the 4 lanes of a token).
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+#include <algorithm>
+
+#include "common.cuh"
+#include "internal.h"
+
+namespace oscar {
+namespace {
+
+constexpr int kTile = 16;             // tokens per MFMA tile
+constexpr int kWaves = 4;             // one per output group
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowBytes = 2 * kHeadDim + 16;   // padded LDS row of one token (bf16 plane)
+constexpr int kPlaneBytes = kTile * kRowBytes;
+
+struct AppendArgs {
+    const void *k;
+    const void *v;
+    const int32_t *req_ids;
+    const int32_t *positions;
+    const int32_t *slots;
+    const int32_t *seq_len_after;
+    const float *r_k;
+    const float *r_v;
+    float *rotated_out;
+    uint8_t *records;
+    uint16_t *sink;
+    uint16_t *recent;
+    int64_t num_slots;
+    int32_t n_tokens;
+    int32_t hkv;
+    int32_t sink_tokens;
+    int32_t recent_tokens;
+    int32_t max_requests;
+    int32_t chunk;
+    int32_t n_chunks;
+    int32_t in_dtype;
+    float alpha;
+};
+
+// Split an fp32 value into three bf16 terms whose sum is the value.
+__device__ __forceinline__ void split3(float x, uint16_t &a, uint16_t &b, uint16_t &c) {
+    a = bf16_bits_rn(x);
+    const float r1 = x - bf16_bits_to_f32(a);
+    b = bf16_bits_rn(r1);
+    const float r2 = r1 - bf16_bits_to_f32(b);
+    c = bf16_bits_rn(r2);
+}
+
+template <int XT>
+__global__ __launch_bounds__(kThreads) void quant_append_kernel(AppendArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[XT * kPlaneBytes];
+
+    // XCD-aware block order: blocks are dealt round-robin to the 8 XCDs, so
+    // all 2*Hkv workgroups of one token chunk land on the same XCD and its L2
+    // assembles the slot records of that chunk.
+    const int id = blockIdx.x;
+    const int xcd = id & 7;
+    const int li = id >> 3;
+    const int ht = li % (2 * a.hkv);
+    const int chunk_id = xcd + 8 * (li / (2 * a.hkv));
+    if (chunk_id >= a.n_chunks) return;
+    const int h = ht >> 1;
+    const int t = ht & 1;
+    const int tok_begin = chunk_id * a.chunk;
+    const int tok_end = min(a.n_tokens, tok_begin + a.chunk);
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;          // output group
+    const int lane = tid & 63;
+    const int n = lane & 15;
+    const int kb = lane >> 4;
+
+    // A operands: transposed rotation rows of this wave's 32 output channels.
+    // Row r of M-tile mt is output channel 32 w + 8 (r / 4) + 4 mt + r % 4, so
+    // that output lane (n, kb) receives channels 32 w + 8 kb + 0..7.
+    const float *R = (t == 0 ? a.r_k : a.r_v) + size_t(h) * kHeadDim * kHeadDim;
+    bf16x8 rf[2][4][3];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+        const int oc = 32 * w + 8 * (n >> 2) + 4 * mt + (n & 3);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int ic = 32 * ks + 8 * kb + j;
+                uint16_t x0, x1, x2;
+                split3(R[size_t(ic) * kHeadDim + oc], x0, x1, x2);
+                rf[mt][ks][0][j] = bits_to_bf16(x0);
+                rf[mt][ks][1][j] = bits_to_bf16(x1);
+                rf[mt][ks][2][j] = bits_to_bf16(x2);
+            }
+        }
+    }
+
+    // staging: thread -> (token row, 8-channel chunk)
+    const int st_row = tid >> 4;
+    const int st_col = tid & 15;
+    const void *X = (t == 0 ? a.k : a.v);
+
+    auto load_tile = [&](int tb, u32x4 &r0, u32x4 &r1) {
+        const int tok = tb + st_row;
+        r0 = u32x4{0, 0, 0, 0};
+        r1 = u32x4{0, 0, 0, 0};
+        if (tok < tok_end) {
+            const size_t elem = (size_t(tok) * a.hkv + h) * kHeadDim + 8 * st_col;
+            if (a.in_dtype == OSCAR_F32) {
+                const u32x4 *p = reinterpret_cast<const u32x4 *>(static_cast<const float *>(X) + elem);
+                r0 = p[0];
+                r1 = p[1];
+            } else {
+                r0 = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(X) + elem);
+            }
+        }
+    };
+    auto store_tile = [&](const u32x4 &r0, const u32x4 &r1) {
+        uint8_t *dst = lds + st_row * kRowBytes + 16 * st_col;
+        if constexpr (XT == 1) {
+            *reinterpret_cast<u32x4 *>(dst) = r0;
+        } else {
+            float f[8];
+            if (a.in_dtype == OSCAR_F32) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    f[j] = __uint_as_float(r0[j]);
+                    f[4 + j] = __uint_as_float(r1[j]);
+                }
+            } else {  // fp16 input, converted exactly to fp32
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    f[2 * j] = __half2float(__ushort_as_half(uint16_t(r0[j] & 0xFFFFu)));
+                    f[2 * j + 1] = __half2float(__ushort_as_half(uint16_t(r0[j] >> 16)));
+                }
+            }
+            uint16_t p0[8], p1[8], p2[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) split3(f[j], p0[j], p1[j], p2[j]);
+            u32x4 w0, w1, w2;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                w0[j] = uint32_t(p0[2 * j]) | (uint32_t(p0[2 * j + 1]) << 16);
+                w1[j] = uint32_t(p1[2 * j]) | (uint32_t(p1[2 * j + 1]) << 16);
+                w2[j] = uint32_t(p2[2 * j]) | (uint32_t(p2[2 * j + 1]) << 16);
+            }
+            *reinterpret_cast<u32x4 *>(dst) = w0;
+            *reinterpret_cast<u32x4 *>(dst + kPlaneBytes) = w1;
+            *reinterpret_cast<u32x4 *>(dst + 2 * kPlaneBytes) = w2;
+        }
+    };
+
+    const int64_t rec_bytes = int64_t(a.hkv) * kHeadRecord;
+    u32x4 pr0, pr1;
+    load_tile(tok_begin, pr0, pr1);
+
+    for (int tb = tok_begin; tb < tok_end; tb += kTile) {
+        __syncthreads();
+        store_tile(pr0, pr1);
+        __syncthreads();
+        if (tb + kTile < tok_end) load_tile(tb + kTile, pr0, pr1);
+
+        // x'^T (16 out channels x 16 tokens) per M-tile
+        f32x4 acc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+            for (int xa = 0; xa < XT; ++xa) {
+                const bf16x8 b = *reinterpret_cast<const bf16x8 *>(
+                    lds + xa * kPlaneBytes + n * kRowBytes + ks * 64 + kb * 16);
+#pragma unroll
+                for (int tr = 0; tr + xa < 3; ++tr) {
+                    acc[0] = mfma_bf16(rf[0][ks][tr], b, acc[0]);
+                    acc[1] = mfma_bf16(rf[1][ks][tr], b, acc[1]);
+                }
+            }
+        }
+
+        // lane (n, kb): token tb + n, rotated channels 32 w + 8 kb + j
+        float vals[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            vals[i] = acc[0][i];
+            vals[4 + i] = acc[1][i];
+        }
+        float lo = vals[0], hi = vals[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) {
+            lo = fminf(lo, vals[j]);
+            hi = fmaxf(hi, vals[j]);
+        }
+        lo = fminf(lo, __shfl_xor(lo, 16));
+        hi = fmaxf(hi, __shfl_xor(hi, 16));
+        lo = fminf(lo, __shfl_xor(lo, 32));
+        hi = fmaxf(hi, __shfl_xor(hi, 32));
+
+        const int tok = tb + n;
+        if (tok >= tok_end) continue;
+        const int req = a.req_ids[tok];
+        const int pos = a.positions[tok];
+        if (req < 0 || req >= a.max_requests || pos < 0) continue;
+        const int slot = a.slots[tok];
+        const bool to_sink = pos < a.sink_tokens;
+        if (!to_sink && (slot < 0 || int64_t(slot) >= a.num_slots)) continue;
+
+        const int c0 = 32 * w + 8 * kb;
+        if (a.rotated_out) {
+            float *ro = a.rotated_out + ((size_t(tok) * a.hkv + h) * 2 + t) * kHeadDim + c0;
+            *reinterpret_cast<f32x4 *>(ro) = f32x4{vals[0], vals[1], vals[2], vals[3]};
+            *reinterpret_cast<f32x4 *>(ro + 4) = f32x4{vals[4], vals[5], vals[6], vals[7]};
+        }
+        u32x4 bf;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            bf[j] = uint32_t(bf16_bits_rn(vals[2 * j])) | (uint32_t(bf16_bits_rn(vals[2 * j + 1])) << 16);
+        if (to_sink) {
+            uint16_t *dst = a.sink + ((size_t(req) * a.sink_tokens + pos) * a.hkv + h) * 2 * kHeadDim +
+                            t * kHeadDim + c0;
+            *reinterpret_cast<u32x4 *>(dst) = bf;
+            continue;
+        }
+
+        // clip bounds, scale and zero (fp32 ops, each rounded once)
+        const float lo_c = lo < 0.0f ? __fmul_rn(a.alpha, lo) : lo;
+        const float hi_c = hi > 0.0f ? __fmul_rn(a.alpha, hi) : hi;
+        const float range = __fsub_rn(hi_c, lo_c);
+        const __half s = __float2half_rn(__fdiv_rn(range, 3.0f));
+        const __half z = __float2half_rn(lo_c);
+        const double sd = double(__half2float(s)), zd = double(__half2float(z));
+        // thresholds z + (k + 1/2) s are exact in fp64; rounding them up to fp32
+        // keeps "x >= T" exact for fp32 x
+        const float t0 = __double2float_ru(zd + 0.5 * sd);
+        const float t1 = __double2float_ru(zd + 1.5 * sd);
+        const float t2 = __double2float_ru(zd + 2.5 * sd);
+        const bool zero_scale = __half2float(s) == 0.0f;
+        uint32_t packed = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float xc = fminf(fmaxf(vals[j], lo_c), hi_c);
+            const uint32_t c = zero_scale ? 0u : uint32_t(xc >= t0) + uint32_t(xc >= t1) + uint32_t(xc >= t2);
+            packed |= c << (2 * j);
+        }
+        uint8_t *rec = a.records + int64_t(slot) * rec_bytes + h * kHeadRecord;
+        *reinterpret_cast<uint16_t *>(rec + t * kCodeBytes + 8 * w + 2 * kb) = uint16_t(packed);
+        if (kb == 0) {
+            const uint32_t sz = uint32_t(__half_as_ushort(s)) | (uint32_t(__half_as_ushort(z)) << 16);
+            *reinterpret_cast<uint32_t *>(rec + 2 * kCodeBytes + t * kSzBytes + 4 * w) = sz;
+        }
+        const int L = a.seq_len_after[req];
+        if (pos >= L - a.recent_tokens) {
+            uint16_t *dst = a.recent +
+                            ((size_t(req) * a.recent_tokens + pos % a.recent_tokens) * a.hkv + h) * 2 * kHeadDim +
+                            t * kHeadDim + c0;
+            *reinterpret_cast<u32x4 *>(dst) = bf;
+        }
+    }
+}
+
+}  // namespace
+}  // namespace oscar
+
+using namespace oscar;
+
+extern "C" oscar_status oscar_quant_append(hipStream_t stream, const oscar_layout *layout,
+                                           const oscar_pool *pool, const void *k, const void *v,
+                                           oscar_dtype in_dtype, int32_t n_tokens,
+                                           const int32_t *req_ids, const int32_t *positions,
+                                           const int32_t *slots, const int32_t *seq_len_after,
+                                           const float *R_K, const float *R_V, float clip_ratio,
+                                           float *rotated_out, const oscar_launch_opts *opts) {
+    oscar_status st = check_layout(layout);
+    if (st != OSCAR_OK) return st;
+    if (!pool) return fail(OSCAR_ERR_INVALID_ARG, "pool is null");
+    if (n_tokens < 0) return fail(OSCAR_ERR_INVALID_ARG, "n_tokens must be >= 0");
+    if (in_dtype != OSCAR_F32 && in_dtype != OSCAR_BF16 && in_dtype != OSCAR_F16)
+        return fail(OSCAR_ERR_INVALID_ARG, "in_dtype must be F32, BF16 or F16");
+    if (!(clip_ratio > 0.0f && clip_ratio <= 1.0f))
+        return fail(OSCAR_ERR_INVALID_ARG, "clip_ratio must be in (0, 1]");
+    if (n_tokens == 0) return OSCAR_OK;
+    if (!k || !v || !req_ids || !positions || !slots || !seq_len_after || !R_K || !R_V)
+        return fail(OSCAR_ERR_INVALID_ARG, "a required pointer is null");
+    if (!pool->records || (layout->sink_tokens > 0 && !pool->sink) || !pool->recent)
+        return fail(OSCAR_ERR_INVALID_ARG, "a pool pointer is null");
+    int chunk = 0;
+    if (opts && opts->append_chunk) {
+        chunk = opts->append_chunk;
+        if (chunk < 16 || chunk % 16)
+            return fail(OSCAR_ERR_INVALID_ARG, "append_chunk must be a positive multiple of 16");
+    } else {
+        // about 768 workgroups (three per compute unit)
+        const int per = std::max(1, (768 + 2 * layout->num_kv_heads - 1) / (2 * layout->num_kv_heads));
+        chunk = (n_tokens + per - 1) / per;
+        chunk = std::max(16, (chunk + 15) / 16 * 16);
+    }
+    const int n_chunks = (n_tokens + chunk - 1) / chunk;
+
+    AppendArgs args;
+    args.k = k;
+    args.v = v;
+    args.req_ids = req_ids;
+    args.positions = positions;
+    args.slots = slots;
+    args.seq_len_after = seq_len_after;
+    args.r_k = R_K;
+    args.r_v = R_V;
+    args.rotated_out = rotated_out;
+    args.records = pool->records;
+    args.sink = pool->sink;
+    args.recent = pool->recent;
+    args.num_slots = layout->num_slots;
+    args.n_tokens = n_tokens;
+    args.hkv = layout->num_kv_heads;
+    args.sink_tokens = layout->sink_tokens;
+    args.recent_tokens = layout->recent_tokens;
+    args.max_requests = layout->max_requests;
+    args.chunk = chunk;
+    args.n_chunks = n_chunks;
+    args.in_dtype = in_dtype;
+    args.alpha = clip_ratio;
+
+    const int blocks = 8 * ((n_chunks + 7) / 8) * 2 * layout->num_kv_heads;
+    if (opts && opts->kernel_begin) {
+        if (hipEventRecord(opts->kernel_begin, stream) != hipSuccess)
+            return fail(OSCAR_ERR_HIP, "hipEventRecord failed");
+    }
+    if (in_dtype == OSCAR_BF16)
+        hipLaunchKernelGGL(quant_append_kernel<1>, dim3(blocks), dim3(kThreads), 0, stream, args);
+    else
+        hipLaunchKernelGGL(quant_append_kernel<3>, dim3(blocks), dim3(kThreads), 0, stream, args);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(OSCAR_ERR_HIP, std::string("quant_append launch: ") + hipGetErrorString(e));
+    if (opts && opts->kernel_end) {
+        if (hipEventRecord(opts->kernel_end, stream) != hipSuccess)
+            return fail(OSCAR_ERR_HIP, "hipEventRecord failed");
+    }
+    return OSCAR_OK;
+}

@@ -18,3 +18,10 @@ def golden():
     import json
     with open(os.path.join(ROOT, "tests", "golden", "pages_constants.json")) as f:
         return json.load(f)
+
+
+def pytest_runtest_setup(item):
+    if "gpu" in item.keywords:
+        import torch
+        if not torch.cuda.is_available():
+            pytest.skip("needs a GPU")

@@ -1,0 +1,203 @@
+"""Host-side tests of liboscar: exports, argument validation, host compute.
+
+Nothing here launches a kernel: every invalid call must return its status
+before any HIP call, and oscar_build_rotation runs on the host.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from oracle import rotation
+from rotated_int2_kv_amd import binding as B
+from rotated_int2_kv_amd import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "oscar.h")
+FAKE = ctypes.c_void_p(0x1000)     # never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(oscar_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (oscar_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(B._lib, n)
+
+
+def test_library_is_built_for_gfx950():
+    blob = open(B.LIB_PATH, "rb").read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in blob
+
+
+def L(**kw):
+    base = dict(head_dim=128, group_size=32, num_kv_heads=8, num_q_heads=32, sink_tokens=64,
+                recent_tokens=256, num_slots=1000, max_requests=4)
+    base.update(kw)
+    return B.Layout(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=64), B.OSCAR_ERR_UNSUPPORTED),
+    (dict(head_dim=0), B.OSCAR_ERR_INVALID_ARG),
+    (dict(group_size=64), B.OSCAR_ERR_UNSUPPORTED),
+    (dict(group_size=48), B.OSCAR_ERR_INVALID_ARG),
+    (dict(num_q_heads=30), B.OSCAR_ERR_INVALID_ARG),
+    (dict(num_q_heads=72), B.OSCAR_ERR_UNSUPPORTED),
+    (dict(num_kv_heads=32, num_q_heads=64), B.OSCAR_ERR_UNSUPPORTED),
+    (dict(sink_tokens=-1), B.OSCAR_ERR_INVALID_ARG),
+    (dict(recent_tokens=0), B.OSCAR_ERR_INVALID_ARG),
+    (dict(num_slots=-5), B.OSCAR_ERR_INVALID_ARG),
+    (dict(max_requests=0), B.OSCAR_ERR_INVALID_ARG),
+])
+def test_layout_errors(kw, status):
+    with pytest.raises(B.OscarError) as e:
+        B.oscar_layout_check(L(**kw))
+    assert e.value.status == status
+    assert B.oscar_last_error()
+
+
+def test_layout_ok_and_pool_bytes():
+    lay = L(num_kv_heads=4, num_q_heads=24, num_slots=123)
+    B.oscar_layout_check(lay)
+    assert B.oscar_pool_bytes(lay, 0) == 123 * 4 * 96
+    assert B.oscar_pool_bytes(lay, 1) == 4 * 64 * 4 * 2 * 128 * 2
+    assert B.oscar_pool_bytes(lay, 2) == 4 * 256 * 4 * 2 * 128 * 2
+    assert B.oscar_pool_bytes(lay, 3) == 0
+    assert B.oscar_pool_bytes(L(head_dim=64), 0) == 0
+
+
+def _append(lay, **over):
+    args = dict(stream=None, layout=ctypes.byref(lay.c()), pool=ctypes.byref(B.CPool(FAKE.value, FAKE.value, FAKE.value)),
+                k=FAKE, v=FAKE, dtype=B.OSCAR_BF16, n=16, req=FAKE, pos=FAKE, slots=FAKE, lens=FAKE,
+                rk=FAKE, rv=FAKE, clip=1.0, rot=None, opts=None)
+    args.update(over)
+    return B._lib.oscar_quant_append(*args.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(k=None), B.OSCAR_ERR_INVALID_ARG),
+    (dict(rv=None), B.OSCAR_ERR_INVALID_ARG),
+    (dict(lens=None), B.OSCAR_ERR_INVALID_ARG),
+    (dict(n=-1), B.OSCAR_ERR_INVALID_ARG),
+    (dict(dtype=7), B.OSCAR_ERR_INVALID_ARG),
+    (dict(clip=0.0), B.OSCAR_ERR_INVALID_ARG),
+    (dict(clip=1.5), B.OSCAR_ERR_INVALID_ARG),
+    (dict(clip=float("nan")), B.OSCAR_ERR_INVALID_ARG),
+    (dict(pool=None), B.OSCAR_ERR_INVALID_ARG),
+    (dict(layout=None), B.OSCAR_ERR_INVALID_ARG),
+])
+def test_quant_append_rejects_before_launch(over, status):
+    assert _append(L(), **over) == status
+
+
+def test_quant_append_rejects_unsupported_shape_and_zero_tokens_is_noop():
+    assert _append(L(head_dim=96)) == B.OSCAR_ERR_UNSUPPORTED
+    assert _append(L(), n=0, k=None, v=None) == B.OSCAR_OK
+
+
+def _decode(lay, lens, **over):
+    lens = np.asarray(lens, np.int32)
+    args = dict(stream=None, layout=ctypes.byref(lay.c()),
+                pool=ctypes.byref(B.CPool(FAKE.value, FAKE.value, FAKE.value)), q=FAKE,
+                qd=B.OSCAR_BF16, batch=len(lens), req=FAKE, lens=FAKE, lens_host=lens.ctypes.data,
+                r2s=FAKE, stride=int(lens.max()), rk=FAKE, rv=FAKE, sm=0.088, out=FAKE,
+                od=B.OSCAR_F32, ws=ctypes.c_void_p(0x100000), ws_bytes=1 << 40, opts=None)
+    args.update(over)
+    return B._lib.oscar_decode_attn(*args.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), B.OSCAR_ERR_INVALID_ARG),
+    (dict(r2s=None), B.OSCAR_ERR_INVALID_ARG),
+    (dict(out=None), B.OSCAR_ERR_INVALID_ARG),
+    (dict(qd=9), B.OSCAR_ERR_INVALID_ARG),
+    (dict(od=9), B.OSCAR_ERR_INVALID_ARG),
+    (dict(sm=float("inf")), B.OSCAR_ERR_INVALID_ARG),
+    (dict(batch=0), B.OSCAR_ERR_INVALID_ARG),
+    (dict(lens_host=None), B.OSCAR_ERR_INVALID_ARG),
+    (dict(stride=10), B.OSCAR_ERR_INVALID_ARG),
+    (dict(ws_bytes=100), B.OSCAR_ERR_WORKSPACE),
+    (dict(ws=None), B.OSCAR_ERR_WORKSPACE),
+    (dict(ws=ctypes.c_void_p(0x100010)), B.OSCAR_ERR_INVALID_ARG),
+])
+def test_decode_rejects_before_launch(over, status):
+    assert _decode(L(), [1000, 50000], **over) == status
+
+
+def test_decode_rejects_empty_sequence():
+    assert _decode(L(), [1000, 0]) == B.OSCAR_ERR_INVALID_ARG
+
+
+def test_decode_plan_and_workspace():
+    lay = L()
+    lens = [100000] * 32
+    chunk, items = B.oscar_decode_plan(lay, lens)
+    hist = 100000 - 64 - 256
+    assert chunk % 32 == 0 and 256 <= chunk <= 8192
+    assert chunk == -(-(-(-32 * hist // 2048)) // 32) * 32
+    assert items == 2 + -(-hist // chunk)
+    ws = B.oscar_decode_workspace_size(lay, lens)
+    need = 32 * 32 * 128 * 4 + 32 * 32 * 4 * 4 + 32 * items * 32 * 128 * 4 + 32 * items * 32 * 8
+    assert need <= ws <= need + 4 * 256
+    c2, it2 = B.oscar_decode_plan(lay, [300], history_chunk=64)
+    assert (c2, it2) == (64, 2)
+    with pytest.raises(B.OscarError):
+        B.oscar_decode_plan(lay, [300], history_chunk=48)
+
+
+@pytest.mark.parametrize("name", ["tiny", "layer_small", "mixed_small"])
+def test_build_rotation_matches_oracle(name):
+    cov = workloads.covariances(workloads.workload(name))
+    for c, spec in ((cov.sigma_q[0], cov.q_spectrum), (cov.sigma_s[-1], cov.s_spectrum)):
+        r, ev = B.oscar_build_rotation(c)
+        ro = rotation.composite_rotation(c, rotation.ROT_OSCAR)
+        assert np.abs(r @ r.T - np.eye(128)).max() < 1e-12
+        assert np.abs(ev - spec).max() < 1e-12
+        assert np.abs(r - ro).max() < 1e-9
+
+
+@pytest.mark.parametrize("flags", [0, B.OSCAR_ROT_HAD, B.OSCAR_ROT_PBR, B.OSCAR_ROT_HAD | B.OSCAR_ROT_PBR,
+                                   B.OSCAR_ROT_EIG | B.OSCAR_ROT_HAD])
+def test_build_rotation_flag_combinations(flags):
+    c = workloads.covariances(workloads.workload("tiny")).sigma_q[0]
+    r, _ = B.oscar_build_rotation(c if flags & B.OSCAR_ROT_EIG else None, 128, flags)
+    assert np.abs(r - rotation.composite_rotation(c, flags)).max() < 1e-9
+
+
+def test_build_rotation_errors():
+    c = np.eye(128)
+    with pytest.raises(B.OscarError):
+        B.oscar_build_rotation(np.eye(96), 96)
+    bad = c.copy()
+    bad[0, 1] = 0.5
+    with pytest.raises(B.OscarError):
+        B.oscar_build_rotation(bad)
+    bad = c.copy()
+    bad[3, 3] = np.nan
+    with pytest.raises(B.OscarError):
+        B.oscar_build_rotation(bad)
+    with pytest.raises(B.OscarError):
+        B.oscar_build_rotation(None, 128, B.OSCAR_ROT_OSCAR)
+    with pytest.raises(B.OscarError):
+        B.oscar_build_rotation(c, 128, 8)
+
+
+def test_build_rotation_degenerate_and_small():
+    r, ev = B.oscar_build_rotation(np.zeros((4, 4)), 4)
+    assert np.abs(r @ r.T - np.eye(4)).max() < 1e-15
+    r, ev = B.oscar_build_rotation(np.array([[2.0]]), 1)
+    assert r[0, 0] == 1.0 and ev[0] == 2.0

@@ -1,0 +1,171 @@
+"""GPU parity of oscar_decode_attn against the fp64 oracle (through the C ABI).
+
+Tolerance: max over (request, q head) of ||o_gpu - o_ref||_inf / ||o_ref||_inf
+<= 2e-3, the attention-output bound of the method's parity target.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import attention, cache
+from rotated_int2_kv_amd import workloads
+
+import gpu_setup as gs
+import parity_tools as pt
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+def _oracle_pool_case(w, lens, seed=0, rots=None):
+    """Pool written by the oracle from seeded inputs; the GPU decodes the same bytes."""
+    total = int(sum(lens))
+    num_slots = int(np.ceil(1.25 * total)) + 3
+    lay_b, lay_o = gs.layouts(w, num_slots, len(lens))
+    req, pos, slots, table = gs.append_batch(lens, num_slots, seed)
+    k, v = workloads.raw_kv_host(w, total, stream=seed)
+    if w.kv_dtype == "bf16":
+        from oracle import quant
+        k, v = quant.bf16_round(k), quant.bf16_round(v)
+    r_k, r_v = gs.oracle_rotations(w) if rots is None else rots
+    opool = cache.new_pool(lay_o)
+    cache.append(opool, lay_o, k, v, req, pos, slots, np.asarray(lens), r_k, r_v)
+    return lay_b, lay_o, opool, table, r_k, r_v
+
+
+def _queries(w, batch, seed, dtype_name):
+    torch = gs.torch_gpu()
+    q = workloads.queries(w, n_rows=batch, stream=seed)
+    dt = torch.bfloat16 if dtype_name == "bf16" else torch.float32
+    qd = torch.from_numpy(q).to(dt).cuda()
+    return qd.float().cpu().numpy(), qd
+
+
+def _gpu_decode(lay_b, pool, qd, lens, table, r_k, r_v, out_dtype="f32", history_chunk=0,
+                req_ids=None):
+    torch = gs.torch_gpu()
+    from rotated_int2_kv_amd import binding as B
+    lens = np.asarray(lens, np.int32)
+    req_ids = np.arange(len(lens), dtype=np.int32) if req_ids is None else req_ids
+    ws_bytes = B.oscar_decode_workspace_size(lay_b, lens, history_chunk)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    odt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[out_dtype]
+    out = torch.empty((len(lens), lay_b.num_q_heads, lay_b.head_dim), dtype=odt, device="cuda")
+    B.oscar_decode_attn(lay_b, pool, qd, gs.dev(req_ids), gs.dev(lens), lens, gs.dev(table),
+                        gs.dev(r_k), gs.dev(r_v), lay_b.head_dim ** -0.5, out, ws,
+                        history_chunk=history_chunk)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy()
+
+
+def _compare(o_gpu, o_ref, label):
+    err = pt.normwise_rel(o_gpu, o_ref)
+    gs.say(f"  {label}: max normwise rel err {err.max():.3e} (median {np.median(err):.3e})")
+    assert np.all(np.isfinite(o_gpu))
+    assert err.max() <= TOL
+    return err
+
+
+@pytest.mark.parametrize("wname,lens,qdt,chunk", [
+    ("tiny", (1024,), "f32", 0),
+    ("tiny", (1024,), "f32", 64),
+    ("layer_small", (2413,), "bf16", 0),
+    ("decode_small", (1500, 777, 3001, 321), "bf16", 0),
+    ("decode_small", (1500, 777, 3001, 321), "bf16", 96),
+    ("mixed_small", workloads.workload("mixed_small").seq_lens, "bf16", 0),
+    ("mixed_small", (1, 63, 64, 65, 319, 320, 321, 352, 353, 385), "bf16", 32),
+])
+def test_decode_over_oracle_pool(wname, lens, qdt, chunk):
+    w = workloads.custom(wname, batch=len(lens), seq_lens=tuple(lens))
+    lay_b, lay_o, opool, table, r_k, r_v = _oracle_pool_case(w, lens)
+    qh, qd = _queries(w, len(lens), 1, qdt)
+    gs.say(f"decode {wname} lens={lens} chunk={chunk}")
+    o_gpu = _gpu_decode(lay_b, gs.upload_oracle_pool(opool), qd, lens, table, r_k, r_v,
+                        history_chunk=chunk)
+    o_ref = attention.decode(opool, lay_o, qh, np.arange(len(lens)), lens, table, r_k, r_v,
+                             w.head_dim ** -0.5)
+    _compare(o_gpu, o_ref, wname)
+
+
+@pytest.mark.parametrize("g", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_decode_gqa_group_sweep(g):
+    """Every query head must read its own KV head (the head-tiling failure of
+    the Qiita article's 'Fix 4' shows up here as a large error)."""
+    w = workloads.custom("layer_small", num_kv_heads=2, num_q_heads=2 * g, batch=2,
+                         seq_lens=(900, 1333), seed=20 + g)
+    lens = w.seq_lens
+    lay_b, lay_o, opool, table, r_k, r_v = _oracle_pool_case(w, lens, seed=g)
+    qh, qd = _queries(w, 2, g, "bf16")
+    gs.say(f"decode gqa g={g}")
+    o_gpu = _gpu_decode(lay_b, gs.upload_oracle_pool(opool), qd, lens, table, r_k, r_v)
+    o_ref = attention.decode(opool, lay_o, qh, np.arange(2), lens, table, r_k, r_v, 128 ** -0.5)
+    _compare(o_gpu, o_ref, f"g={g}")
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
+def test_decode_output_dtypes(out_dtype):
+    w = workloads.custom("decode_small", batch=2, seq_lens=(2000, 700))
+    lens = w.seq_lens
+    lay_b, lay_o, opool, table, r_k, r_v = _oracle_pool_case(w, lens)
+    qh, qd = _queries(w, 2, 5, "bf16")
+    o_gpu = _gpu_decode(lay_b, gs.upload_oracle_pool(opool), qd, lens, table, r_k, r_v, out_dtype)
+    o_ref = attention.decode(opool, lay_o, qh, np.arange(2), lens, table, r_k, r_v, 128 ** -0.5)
+    err = pt.normwise_rel(o_gpu, o_ref)
+    assert err.max() <= TOL + 2.0 ** -8
+
+
+def test_decode_request_indirection():
+    """req_ids select rows of the stores and of the index table."""
+    w = workloads.custom("decode_small", batch=3, seq_lens=(1200, 500, 2100))
+    lens = w.seq_lens
+    lay_b, lay_o, opool, table, r_k, r_v = _oracle_pool_case(w, lens)
+    order = np.array([2, 0], np.int32)
+    qh, qd = _queries(w, 2, 9, "bf16")
+    o_gpu = _gpu_decode(lay_b, gs.upload_oracle_pool(opool), qd, np.asarray(lens)[order], table,
+                        r_k, r_v, req_ids=order)
+    o_ref = attention.decode(opool, lay_o, qh, order, np.asarray(lens)[order], table, r_k, r_v,
+                             128 ** -0.5)
+    _compare(o_gpu, o_ref, "req_ids")
+
+
+def test_decode_is_deterministic():
+    w = workloads.custom("decode_small", batch=2, seq_lens=(3001, 1500))
+    lens = w.seq_lens
+    lay_b, lay_o, opool, table, r_k, r_v = _oracle_pool_case(w, lens)
+    qh, qd = _queries(w, 2, 3, "bf16")
+    pool = gs.upload_oracle_pool(opool)
+    a = _gpu_decode(lay_b, pool, qd, lens, table, r_k, r_v)
+    b = _gpu_decode(lay_b, pool, qd, lens, table, r_k, r_v)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("wname,lens", [
+    ("tiny", (1024,)),
+    ("layer_small", (2413,)),
+    ("mixed_small", workloads.workload("mixed_small").seq_lens),
+])
+def test_end_to_end_against_full_oracle(wname, lens):
+    """GPU append (library rotations) + GPU decode vs the oracle's own rotations,
+    quantisation and attention on the same seeded inputs."""
+    torch = gs.torch_gpu()
+    from rotated_int2_kv_amd import binding as B
+    w = workloads.custom(wname, batch=len(lens), seq_lens=tuple(lens))
+    total = int(sum(lens))
+    num_slots = int(np.ceil(1.25 * total)) + 3
+    lay_b, lay_o = gs.layouts(w, num_slots, len(lens))
+    req, pos, slots, table = gs.append_batch(lens, num_slots, 4)
+    kh, vh, kd, vd = gs.kv_values(w, total, stream=4)
+    r_k, r_v = gs.product_rotations(w)
+    pool = B.new_pool(lay_b)
+    gs.say(f"end-to-end {wname}")
+    B.oscar_quant_append(lay_b, pool, kd, vd, gs.dev(req), gs.dev(pos), gs.dev(slots),
+                         gs.dev(np.asarray(lens, np.int32)), gs.dev(r_k), gs.dev(r_v))
+    qh, qd = _queries(w, len(lens), 2, w.q_dtype)
+    o_gpu = _gpu_decode(lay_b, pool, qd, lens, table, r_k, r_v)
+    ork, orv = gs.oracle_rotations(w)
+    opool = cache.new_pool(lay_o)
+    cache.append(opool, lay_o, kh, vh, req, pos, slots, np.asarray(lens), ork, orv)
+    o_ref = attention.decode(opool, lay_o, qh, np.arange(len(lens)), lens, table, ork, orv,
+                             128 ** -0.5)
+    _compare(o_gpu, o_ref, f"end-to-end {wname}")
+    torch.cuda.synchronize()

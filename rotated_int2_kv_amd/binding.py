@@ -61,6 +61,10 @@ class CLaunchOpts(ctypes.Structure):
 
 
 def _load() -> ctypes.CDLL:
+    # torch ships its own HIP runtime; importing it first makes liboscar's
+    # libamdhip64.so.7 dependency resolve (by soname) to that same runtime, so
+    # one process never holds two HIP runtimes (the second sees no device).
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -m rotated_int2_kv_amd.build`")
     lib = ctypes.CDLL(LIB_PATH)

@@ -11,11 +11,14 @@
 //               KV head; the workgroup holds all KV heads of the item so that
 //               the slot-major records are read as whole cache lines.
 //               History tiles of 32 tokens run on f16 MFMA:
-//                 QK: A = fp16(s * code) (dequant in the operand, exact for
-//                     codes 0..2 and rounded once for 3), B = q' split into
-//                     fp16 hi + lo columns; one extra MFMA adds sum_g z_g Qbar_g.
-//                 PV: A = softmax weights split hi + lo rows, B = fp16(s * code)
-//                     of 8 tokens per lane; one extra MFMA adds sum_t p_t z_t.
+//                 QK: A = s * code, dequantised in the operand and exact: the
+//                     scale is split into s_hi (9 significant bits) and s_lo
+//                     (the 2 low bits), so c s_hi and c s_lo are exact fp16
+//                     values and both are accumulated; B = q' split into fp16
+//                     hi + lo columns; one extra MFMA adds sum_g z_g Qbar_g.
+//                 PV: A = softmax weights split hi + lo rows, B = s * code of 8
+//                     tokens per lane, split the same way; one extra MFMA adds
+//                     sum_t p_t z_t.
 //               BF16 windows run on fp32 VALU.  Each item writes (m, l, o')
 //               with m in log2 units.
 //   3. merge:   log-sum-exp merge of the items and o = o' R_V^T.
@@ -145,13 +148,32 @@ __device__ __forceinline__ uint32_t to_bit8(uint32_t v, int from) {
     return from <= 8 ? v << (8 - from) : v >> (from - 8);
 }
 
-// fp16(s * c) for the two codes at bits 8-9 and 24-25 of `x`: the code becomes
-// the low mantissa bits of 4.0 (ulp 2^-8 there, so each half reads 4 + c), and
-// (4 + c) s - 4 s is formed by one fused multiply-add, rounded once.  Exact
-// for c <= 2; no overflow while 7 s <= 65504.
-__device__ __forceinline__ uint32_t dq_pair(uint32_t x, f16x2 s2, f16x2 c2) {
-    const uint32_t e = (x & 0x03000300u) | 0x44004400u;
-    return as_u32(__builtin_elementwise_fma(as_h2(e), s2, c2));
+// 4 + c in each fp16 half for the two codes at bits 8-9 and 24-25 of `x`:
+// the code becomes the low mantissa bits of 4.0, whose ulp is 2^-8.
+__device__ __forceinline__ f16x2 code_pair(uint32_t x) {
+    return as_h2((x & 0x03000300u) | 0x44004400u);
+}
+
+// c * s for a code pair e = 4 + c: (4 + c) s - 4 s in one fused multiply-add
+// (c2 = -4 s), rounded once; exact whenever c * s fits in fp16, which holds
+// for s with at most 9 significant bits.
+__device__ __forceinline__ uint32_t dq(f16x2 e, f16x2 s2, f16x2 c2) {
+    return as_u32(__builtin_elementwise_fma(e, s2, c2));
+}
+
+// Split fp16 scales (two per word) into s_hi (low 2 mantissa bits cleared) and
+// s_lo = s - s_hi (exact); returns the four multipliers and offsets.
+struct ScaleSplit {
+    f16x2 s_hi, s_lo, c_hi, c_lo;
+};
+__device__ __forceinline__ ScaleSplit split_scale(uint32_t s_bits2) {
+    const f16x2 neg4 = as_h2(0xC400C400u);   // (-4, -4)
+    ScaleSplit r;
+    r.s_hi = as_h2(s_bits2 & 0xFFFCFFFCu);
+    r.s_lo = as_h2(s_bits2) - r.s_hi;
+    r.c_hi = r.s_hi * neg4;
+    r.c_lo = r.s_lo * neg4;
+    return r;
 }
 
 __device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
@@ -216,7 +238,6 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hk, in
         qBz = u4_as_h8(w[0], w[1], w[2], w[3]);
     }
     const int partner = col_hi ? lane + GQ : (col_lo ? lane - GQ : lane);
-    const f16x2 neg4 = as_h2(0xC400C400u);   // (-4, -4)
 
     float m_run = -INFINITY;
     float l_lane = 0.0f;
@@ -245,16 +266,21 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hk, in
                 ksz = *reinterpret_cast<const u32x4 *>(rec + 2 * kCodeBytes);
             }
             const uint32_t szk = kb == 0 ? ksz[0] : (kb == 1 ? ksz[1] : (kb == 2 ? ksz[2] : ksz[3]));
-            const f16x2 s2 = as_h2((szk & 0xFFFFu) | (szk << 16));
-            const f16x2 c2 = s2 * neg4;
+            const ScaleSplit sk = split_scale((szk & 0xFFFFu) | (szk << 16));
             f32x4 acc = f32x4{0, 0, 0, 0};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const uint32_t d = (r < 2) ? kc[0] : kc[1];
                 const int sh = 8 * (r & 1);
-                const f16x8 A = u4_as_h8(dq_pair(to_bit8(d, sh), s2, c2), dq_pair(to_bit8(d, sh + 2), s2, c2),
-                                         dq_pair(to_bit8(d, sh + 4), s2, c2), dq_pair(to_bit8(d, sh + 6), s2, c2));
-                acc = mfma_f16(A, qB[r], acc);
+                f16x2 e[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) e[p] = code_pair(to_bit8(d, sh + 2 * p));
+                const f16x8 Ahi = u4_as_h8(dq(e[0], sk.s_hi, sk.c_hi), dq(e[1], sk.s_hi, sk.c_hi),
+                                           dq(e[2], sk.s_hi, sk.c_hi), dq(e[3], sk.s_hi, sk.c_hi));
+                const f16x8 Alo = u4_as_h8(dq(e[0], sk.s_lo, sk.c_lo), dq(e[1], sk.s_lo, sk.c_lo),
+                                           dq(e[2], sk.s_lo, sk.c_lo), dq(e[3], sk.s_lo, sk.c_lo));
+                acc = mfma_f16(Ahi, qB[r], acc);
+                acc = mfma_f16(Alo, qB[r], acc);
             }
             {
                 uint32_t z01 = 0, z23 = 0;
@@ -349,19 +375,20 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hk, in
             zp[p] = (szv[0] >> 16) | (szv[1] & 0xFFFF0000u);
         }
         const f16x8 BZ = u4_as_h8(zp[0], zp[1], zp[2], zp[3]);
-        f16x2 sv[4], cv[4];
+        ScaleSplit sv[4];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            sv[p] = as_h2(sp[p]);
-            cv[p] = sv[p] * neg4;
-        }
+        for (int p = 0; p < 4; ++p) sv[p] = split_scale(sp[p]);
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
-            const f16x8 B = u4_as_h8(dq_pair(to_bit8(vw[0], 2 * jj), sv[0], cv[0]),
-                                     dq_pair(to_bit8(vw[1], 2 * jj), sv[1], cv[1]),
-                                     dq_pair(to_bit8(vw[2], 2 * jj), sv[2], cv[2]),
-                                     dq_pair(to_bit8(vw[3], 2 * jj), sv[3], cv[3]));
-            oacc[jj] = mfma_f16(AP, B, oacc[jj]);
+            f16x2 e[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) e[p] = code_pair(to_bit8(vw[p], 2 * jj));
+            const f16x8 Bhi = u4_as_h8(dq(e[0], sv[0].s_hi, sv[0].c_hi), dq(e[1], sv[1].s_hi, sv[1].c_hi),
+                                       dq(e[2], sv[2].s_hi, sv[2].c_hi), dq(e[3], sv[3].s_hi, sv[3].c_hi));
+            const f16x8 Blo = u4_as_h8(dq(e[0], sv[0].s_lo, sv[0].c_lo), dq(e[1], sv[1].s_lo, sv[1].c_lo),
+                                       dq(e[2], sv[2].s_lo, sv[2].c_lo), dq(e[3], sv[3].s_lo, sv[3].c_lo));
+            oacc[jj] = mfma_f16(AP, Bhi, oacc[jj]);
+            oacc[jj] = mfma_f16(AP, Blo, oacc[jj]);
         }
         zacc = mfma_f16(AP, BZ, zacc);
     }

@@ -69,6 +69,11 @@ def _check_general(out, w, rots_oracle, alpha):
                                        z[:, h, t], gpu_rot[pool_tok], alpha)
             for key, val in st.items():
                 stats[key] = stats.get(key, 0) + val
+            # disagreement with the oracle's own scale/zero (its fp32 x' is exact
+            # rounded once); the rigorous check above already passed
+            _, s_or, z_or = quant.quantize(exact[pool_tok].astype(np.float32), 32, alpha)
+            stats["sz_mismatch"] = stats.get("sz_mismatch", 0) + int(
+                ((s_or != s[:, h, t]) | (z_or != z[:, h, t])).sum())
             sk = ~pool_tok
             if sk.any():
                 bits = sink[out["req"][sk], out["pos"][sk], h, t, :]
@@ -82,7 +87,7 @@ def _check_general(out, w, rots_oracle, alpha):
                     pt.check_bf16(exact[rg], delta[rg], bits)
     gs.say(f"  stats {stats}")
     assert stats["ambiguous_codes"] <= 2e-3 * stats["elements"]
-    assert stats["ambiguous_scale"] + stats["ambiguous_zero"] <= 5e-3 * stats["groups"]
+    assert stats["sz_mismatch"] <= 1e-3 * stats["groups"]
     return stats
 
 

@@ -223,6 +223,8 @@ def main():
     ap.add_argument("--history-chunk", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-append", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU: the hot path (per-request, per-KV-head "
@@ -235,6 +237,13 @@ def main():
     from rotated_int2_kv_amd import workloads
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] calibration copy: 1 GiB read + 1 GiB written")
+        del src, dst
     d = run_decode(args, torch, B, workloads)
     w = d["w"]
     ms = d["ms"]

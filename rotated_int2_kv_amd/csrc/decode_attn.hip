@@ -186,14 +186,34 @@ __device__ __forceinline__ f16x8 u4_as_h8(uint32_t a, uint32_t b, uint32_t c, ui
 }
 
 // History item on the matrix cores.  GQ = query heads per KV head.
+//
+// The whole workgroup streams the tile's slot records (all of its KV heads:
+// whole cache lines of the slot-major pool) with 16-byte loads, three per
+// thread per 32-token tile, into a two-stage LDS ring; each wave then
+// computes its own KV head from LDS.  Loads of tile i + 2 are in flight while
+// tile i is computed.  Tokens past the item or with an out-of-range slot are
+// zero-filled in LDS and masked out of the softmax.
 template <int GQ>
-__device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hk, int p0, int p1) {
-    const int lane = threadIdx.x & 63;
+__device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, int p0, int p1,
+                          uint8_t *smem) {
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int lane = tid & 63;
     const int n = lane & 15;
     const int kb = lane >> 4;
+    const int nthreads = 64 * a.waves;
+    const int h0 = hc * a.waves;
+    const int nh = min(a.waves, a.hkv - h0);      // KV heads of this workgroup
+    const bool active = w < nh;
+    const int hk = h0 + (active ? w : 0);
+    const int ts = nh * kHeadRecord + 16;          // LDS bytes per token (padded)
+    const int stage_bytes = kTileTokens * ts;
+    const int chunks_tok = nh * (kHeadRecord / 16);
+    const int chunks_tile = kTileTokens * chunks_tok;
     const int64_t rec_bytes = int64_t(a.hkv) * kHeadRecord;
-    const uint8_t *rec_base = a.records + hk * kHeadRecord;
+    const uint8_t *gbase = a.records + h0 * kHeadRecord;
     const int32_t *r2s = a.req_to_slot + int64_t(req) * a.r2s_stride;
+    const int n_tiles = (p1 - p0 + kTileTokens - 1) / kTileTokens;
 
     // column n of the QK B operand: head n (hi part) or head n - GQ (lo part)
     const bool col_hi = n < GQ;
@@ -203,7 +223,7 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hk, in
     f16x8 qB[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        uint32_t w[4];
+        uint32_t wq[4];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             // k-slots (2p, 2p+1) of MFMA r hold channels base + p and base + 8 + p
@@ -217,13 +237,13 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hk, in
                     x1 -= __half2float(__float2half_rn(x1));
                 }
             }
-            w[p] = pack_h2(x0, x1);
+            wq[p] = pack_h2(x0, x1);
         }
-        qB[r] = u4_as_h8(w[0], w[1], w[2], w[3]);
+        qB[r] = u4_as_h8(wq[0], wq[1], wq[2], wq[3]);
     }
     f16x8 qBz;
     {
-        uint32_t w[4] = {0, 0, 0, 0};
+        uint32_t wq[4] = {0, 0, 0, 0};
         if ((col_hi || col_lo) && kb == 0) {
             const float *qsum = a.qsum + (size_t(b) * a.hq + hk * GQ + col_head) * kGroups;
             float x[4];
@@ -232,12 +252,65 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hk, in
                 x[grp] = qsum[grp];
                 if (col_lo) x[grp] -= __half2float(__float2half_rn(x[grp]));
             }
-            w[0] = pack_h2(x[0], x[1]);
-            w[1] = pack_h2(x[2], x[3]);
+            wq[0] = pack_h2(x[0], x[1]);
+            wq[1] = pack_h2(x[2], x[3]);
         }
-        qBz = u4_as_h8(w[0], w[1], w[2], w[3]);
+        qBz = u4_as_h8(wq[0], wq[1], wq[2], wq[3]);
     }
     const int partner = col_hi ? lane + GQ : (col_lo ? lane - GQ : lane);
+
+    // Every load below is unconditional (out-of-range positions and slots are
+    // clamped to a safe address and masked afterwards), so each iteration
+    // issues the same straight-line sequence of loads and the loads of the
+    // next tile stay outstanding through the current tile's compute.
+    //
+    // raw slot id of token `lane & 31` of tile t; in_tile(t) says which are real
+    auto tile_slot = [&](int t) -> int {
+        const int pos = p0 + t * kTileTokens + (lane & (kTileTokens - 1));
+        return r2s[pos < p1 ? pos : p0];
+    };
+    auto tile_mask = [&](int t) -> uint32_t {   // positions of tile t inside [p0, p1)
+        const int cnt = min(kTileTokens, p1 - (p0 + t * kTileTokens));
+        return cnt <= 0 ? 0u : (cnt >= 32 ? 0xFFFFFFFFu : ((1u << cnt) - 1u));
+    };
+    // this thread's three 16-byte pieces of a tile
+    u32x4 rr[3];
+    bool rr_ok[3];
+    auto issue = [&](int slot_reg, uint32_t in_tile) {
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            const int q = u * nthreads + tid;
+            const int qc = q < chunks_tile ? q : 0;
+            const int tok = qc / chunks_tok;
+            const int c = qc - tok * chunks_tok;
+            const int slot = __shfl(slot_reg, tok);
+            const bool ok = q < chunks_tile && ((in_tile >> tok) & 1u) && slot >= 0 &&
+                            int64_t(slot) < a.num_slots;
+            rr_ok[u] = ok;
+            rr[u] = *reinterpret_cast<const u32x4 *>(gbase + int64_t(ok ? slot : 0) * rec_bytes + 16 * c);
+        }
+    };
+    auto stash = [&](int stage) {
+        uint8_t *dst = smem + stage * stage_bytes;
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            const int q = u * nthreads + tid;
+            const int tok = q / chunks_tok;
+            const int c = q - tok * chunks_tok;
+            const u32x4 v = rr_ok[u] ? rr[u] : u32x4{0, 0, 0, 0};
+            if (q < chunks_tile) *reinterpret_cast<u32x4 *>(dst + tok * ts + 16 * c) = v;
+        }
+    };
+    // tokens of a tile with a real position and an in-range slot
+    auto valid_mask = [&](int slot_reg, uint32_t in_tile) -> uint32_t {
+        const bool ok = lane < kTileTokens && ((in_tile >> lane) & 1u) && slot_reg >= 0 &&
+                        int64_t(slot_reg) < a.num_slots;
+        return uint32_t(__ballot(ok));
+    };
+    auto barrier = []() {
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes are done
+        __builtin_amdgcn_s_barrier();
+    };
 
     float m_run = -INFINITY;
     float l_lane = 0.0f;
@@ -246,152 +319,159 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hk, in
     for (int jj = 0; jj < 8; ++jj) oacc[jj] = f32x4{0, 0, 0, 0};
     f32x4 zacc = f32x4{0, 0, 0, 0};
 
-    for (int tb = p0; tb < p1; tb += kTileTokens) {
-        // slot of tile token `lane` (lanes 0..31)
-        int my_slot = -1;
-        if (lane < kTileTokens && tb + lane < p1) {
-            const int s = r2s[tb + lane];
-            if (s >= 0 && int64_t(s) < a.num_slots) my_slot = s;
+    // prologue: tile 0 into stage 0, tile 1 in flight, slots of tile 2 loaded
+    const int s0 = tile_slot(0);
+    const int s1 = tile_slot(1);
+    issue(s0, tile_mask(0));
+    uint32_t mask_cur = valid_mask(s0, tile_mask(0));
+    stash(0);
+    barrier();
+    int s_far = tile_slot(2);
+    issue(s1, tile_mask(1));
+    uint32_t mask_next = valid_mask(s1, tile_mask(1));
+
+    for (int it = 0; it < n_tiles; ++it) {
+        if (it > 0) {
+            // tile it arrived in registers one iteration ago: put it in LDS,
+            // then start loading tile it + 1
+            stash(it & 1);
+            barrier();
+            // slot ids first, record loads last: the loads stay outstanding
+            // through the compute below and are waited for by the next stash
+            const int s_new = tile_slot(it + 2);
+            issue(s_far, tile_mask(it + 1));
+            mask_cur = mask_next;
+            mask_next = valid_mask(s_far, tile_mask(it + 1));
+            s_far = s_new;
         }
-        // ---- QK: rows = tokens (two halves of 16), cols = (hi|lo, head)
-        float lg[2][4];
+        if (active) {
+            const uint8_t *stage = smem + (it & 1) * stage_bytes + w * kHeadRecord;
+            // ---- QK: rows = tokens (two halves of 16), cols = (hi|lo, head)
+            float lg[2][4];
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            const int slot = __shfl(my_slot, 16 * hf + n);
-            u32x2 kc = u32x2{0, 0};
-            u32x4 ksz = u32x4{0, 0, 0, 0};
-            if (slot >= 0) {
-                const uint8_t *rec = rec_base + int64_t(slot) * rec_bytes;
-                kc = *reinterpret_cast<const u32x2 *>(rec + 8 * kb);
-                ksz = *reinterpret_cast<const u32x4 *>(rec + 2 * kCodeBytes);
+            for (int hf = 0; hf < 2; ++hf) {
+                const uint8_t *row = stage + (16 * hf + n) * ts;
+                const u32x2 kc = *reinterpret_cast<const u32x2 *>(row + 8 * kb);
+                const u32x4 ksz = *reinterpret_cast<const u32x4 *>(row + 2 * kCodeBytes);
+                const uint32_t szk = kb == 0 ? ksz[0] : (kb == 1 ? ksz[1] : (kb == 2 ? ksz[2] : ksz[3]));
+                const ScaleSplit sk = split_scale((szk & 0xFFFFu) | (szk << 16));
+                f32x4 acc = f32x4{0, 0, 0, 0};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const uint32_t d = (r < 2) ? kc[0] : kc[1];
+                    const int sh = 8 * (r & 1);
+                    f16x2 e[4];
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) e[p] = code_pair(to_bit8(d, sh + 2 * p));
+                    const f16x8 Ahi = u4_as_h8(dq(e[0], sk.s_hi, sk.c_hi), dq(e[1], sk.s_hi, sk.c_hi),
+                                               dq(e[2], sk.s_hi, sk.c_hi), dq(e[3], sk.s_hi, sk.c_hi));
+                    const f16x8 Alo = u4_as_h8(dq(e[0], sk.s_lo, sk.c_lo), dq(e[1], sk.s_lo, sk.c_lo),
+                                               dq(e[2], sk.s_lo, sk.c_lo), dq(e[3], sk.s_lo, sk.c_lo));
+                    acc = mfma_f16(Ahi, qB[r], acc);
+                    acc = mfma_f16(Alo, qB[r], acc);
+                }
+                {
+                    uint32_t z01 = 0, z23 = 0;
+                    if (kb == 0) {
+                        z01 = (ksz[0] >> 16) | (ksz[1] & 0xFFFF0000u);
+                        z23 = (ksz[2] >> 16) | (ksz[3] & 0xFFFF0000u);
+                    }
+                    acc = mfma_f16(u4_as_h8(z01, z23, 0, 0), qBz, acc);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool ok = (mask_cur >> (16 * hf + 4 * kb + i)) & 1u;
+                    const float part = __shfl(acc[i], partner);
+                    lg[hf][i] = ok ? acc[i] + part : -INFINITY;
+                }
             }
-            const uint32_t szk = kb == 0 ? ksz[0] : (kb == 1 ? ksz[1] : (kb == 2 ? ksz[2] : ksz[3]));
-            const ScaleSplit sk = split_scale((szk & 0xFFFFu) | (szk << 16));
-            f32x4 acc = f32x4{0, 0, 0, 0};
+
+            // ---- online softmax (per column; all 4 row groups agree after the reduction)
+            float mx = lg[0][0];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const uint32_t d = (r < 2) ? kc[0] : kc[1];
-                const int sh = 8 * (r & 1);
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, lg[hf][i]);
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = fmaxf(m_run, mx);
+            if (__any(m_new > m_run)) {
+                const float alpha = (m_new > m_run) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+                l_lane *= alpha;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float ar = __shfl(alpha, 4 * kb + i);   // alpha of PV row 4 kb + i
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj) oacc[jj][i] *= ar;
+                    zacc[i] *= ar;
+                }
+                m_run = m_new;
+            }
+            float pv[8];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float x = lg[hf][i];
+                    const float p = (x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x - m_run);
+                    pv[4 * hf + i] = p;
+                    l_lane += p;
+                }
+            // PV A operand: row n = (hi|lo, head), k-slots = tokens 4 kb + s (s < 4)
+            // and 16 + 4 kb + s - 4 (s >= 4)
+            uint32_t aw[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                float x0 = pv[2 * p], x1 = pv[2 * p + 1];
+                if (col_lo) {
+                    x0 -= __half2float(__float2half_rn(x0));
+                    x1 -= __half2float(__float2half_rn(x1));
+                } else if (!col_hi) {
+                    x0 = 0.0f;
+                    x1 = 0.0f;
+                }
+                aw[p] = pack_h2(x0, x1);
+            }
+            const f16x8 AP = u4_as_h8(aw[0], aw[1], aw[2], aw[3]);
+
+            // ---- PV B operands: lane (n, kb) reads word n (channels 8n .. 8n+7)
+            // of the V codes and the (s, z) of group n / 4 for its 8 tokens
+            uint32_t vw[4], sp[4], zp[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                uint32_t wv[2], szv[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int sidx = 2 * p + e;
+                    const int tt = sidx < 4 ? 4 * kb + sidx : 16 + 4 * kb + (sidx - 4);
+                    const uint8_t *row = stage + tt * ts;
+                    wv[e] = *reinterpret_cast<const uint16_t *>(row + kCodeBytes + 2 * n);
+                    szv[e] = *reinterpret_cast<const uint32_t *>(row + 2 * kCodeBytes + kSzBytes + 4 * (n >> 2));
+                }
+                vw[p] = wv[0] | (wv[1] << 16);
+                sp[p] = (szv[0] & 0xFFFFu) | (szv[1] << 16);
+                zp[p] = (szv[0] >> 16) | (szv[1] & 0xFFFF0000u);
+            }
+            const f16x8 BZ = u4_as_h8(zp[0], zp[1], zp[2], zp[3]);
+            ScaleSplit sv[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) sv[p] = split_scale(sp[p]);
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
                 f16x2 e[4];
 #pragma unroll
-                for (int p = 0; p < 4; ++p) e[p] = code_pair(to_bit8(d, sh + 2 * p));
-                const f16x8 Ahi = u4_as_h8(dq(e[0], sk.s_hi, sk.c_hi), dq(e[1], sk.s_hi, sk.c_hi),
-                                           dq(e[2], sk.s_hi, sk.c_hi), dq(e[3], sk.s_hi, sk.c_hi));
-                const f16x8 Alo = u4_as_h8(dq(e[0], sk.s_lo, sk.c_lo), dq(e[1], sk.s_lo, sk.c_lo),
-                                           dq(e[2], sk.s_lo, sk.c_lo), dq(e[3], sk.s_lo, sk.c_lo));
-                acc = mfma_f16(Ahi, qB[r], acc);
-                acc = mfma_f16(Alo, qB[r], acc);
+                for (int p = 0; p < 4; ++p) e[p] = code_pair(to_bit8(vw[p], 2 * jj));
+                const f16x8 Bhi = u4_as_h8(dq(e[0], sv[0].s_hi, sv[0].c_hi), dq(e[1], sv[1].s_hi, sv[1].c_hi),
+                                           dq(e[2], sv[2].s_hi, sv[2].c_hi), dq(e[3], sv[3].s_hi, sv[3].c_hi));
+                const f16x8 Blo = u4_as_h8(dq(e[0], sv[0].s_lo, sv[0].c_lo), dq(e[1], sv[1].s_lo, sv[1].c_lo),
+                                           dq(e[2], sv[2].s_lo, sv[2].c_lo), dq(e[3], sv[3].s_lo, sv[3].c_lo));
+                oacc[jj] = mfma_f16(AP, Bhi, oacc[jj]);
+                oacc[jj] = mfma_f16(AP, Blo, oacc[jj]);
             }
-            {
-                uint32_t z01 = 0, z23 = 0;
-                if (kb == 0) {
-                    z01 = (ksz[0] >> 16) | (ksz[1] & 0xFFFF0000u);
-                    z23 = (ksz[2] >> 16) | (ksz[3] & 0xFFFF0000u);
-                }
-                acc = mfma_f16(u4_as_h8(z01, z23, 0, 0), qBz, acc);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tok = tb + 16 * hf + 4 * kb + i;
-                const bool ok = tok < p1;
-                const float part = __shfl(acc[i], partner);
-                lg[hf][i] = ok ? acc[i] + part : -INFINITY;
-            }
+            zacc = mfma_f16(AP, BZ, zacc);
         }
-        // token validity also needs a valid slot
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (__shfl(my_slot, 16 * hf + 4 * kb + i) < 0) lg[hf][i] = -INFINITY;
-
-        // ---- online softmax (per column; all 4 row groups agree after the reduction)
-        float mx = lg[0][0];
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, lg[hf][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        if (__any(m_new > m_run)) {
-            const float alpha = (m_new > m_run) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-            l_lane *= alpha;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float ar = __shfl(alpha, 4 * kb + i);   // alpha of PV row 4 kb + i
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) oacc[jj][i] *= ar;
-                zacc[i] *= ar;
-            }
-            m_run = m_new;
-        }
-        float pv[8];
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float x = lg[hf][i];
-                const float p = (x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x - m_run);
-                pv[4 * hf + i] = p;
-                l_lane += p;
-            }
-        // PV A operand: row n = (hi|lo, head), k-slots = tokens 4 kb + s (s < 4)
-        // and 16 + 4 kb + s - 4 (s >= 4)
-        uint32_t aw[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            float x0 = pv[2 * p], x1 = pv[2 * p + 1];
-            if (col_lo) {
-                x0 -= __half2float(__float2half_rn(x0));
-                x1 -= __half2float(__float2half_rn(x1));
-            } else if (!col_hi) {
-                x0 = 0.0f;
-                x1 = 0.0f;
-            }
-            aw[p] = pack_h2(x0, x1);
-        }
-        const f16x8 AP = u4_as_h8(aw[0], aw[1], aw[2], aw[3]);
-
-        // ---- PV B operands: lane (n, kb) reads word n (channels 8n .. 8n+7)
-        // of the V codes and the (s, z) of group n / 4 for its 8 tokens
-        uint32_t vw[4], sp[4], zp[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            uint32_t wv[2] = {0, 0}, szv[2] = {0, 0};
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int s = 2 * p + e;
-                const int tt = s < 4 ? 4 * kb + s : 16 + 4 * kb + (s - 4);
-                const int slot = __shfl(my_slot, tt);
-                if (slot >= 0) {
-                    const uint8_t *rec = rec_base + int64_t(slot) * rec_bytes;
-                    wv[e] = *reinterpret_cast<const uint16_t *>(rec + kCodeBytes + 2 * n);
-                    szv[e] = *reinterpret_cast<const uint32_t *>(rec + 2 * kCodeBytes + kSzBytes + 4 * (n >> 2));
-                }
-            }
-            vw[p] = wv[0] | (wv[1] << 16);
-            sp[p] = (szv[0] & 0xFFFFu) | (szv[1] << 16);
-            zp[p] = (szv[0] >> 16) | (szv[1] & 0xFFFF0000u);
-        }
-        const f16x8 BZ = u4_as_h8(zp[0], zp[1], zp[2], zp[3]);
-        ScaleSplit sv[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) sv[p] = split_scale(sp[p]);
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-            f16x2 e[4];
-#pragma unroll
-            for (int p = 0; p < 4; ++p) e[p] = code_pair(to_bit8(vw[p], 2 * jj));
-            const f16x8 Bhi = u4_as_h8(dq(e[0], sv[0].s_hi, sv[0].c_hi), dq(e[1], sv[1].s_hi, sv[1].c_hi),
-                                       dq(e[2], sv[2].s_hi, sv[2].c_hi), dq(e[3], sv[3].s_hi, sv[3].c_hi));
-            const f16x8 Blo = u4_as_h8(dq(e[0], sv[0].s_lo, sv[0].c_lo), dq(e[1], sv[1].s_lo, sv[1].c_lo),
-                                       dq(e[2], sv[2].s_lo, sv[2].c_lo), dq(e[3], sv[3].s_lo, sv[3].c_lo));
-            oacc[jj] = mfma_f16(AP, Bhi, oacc[jj]);
-            oacc[jj] = mfma_f16(AP, Blo, oacc[jj]);
-        }
-        zacc = mfma_f16(AP, BZ, zacc);
     }
+    if (!active) return;
 
     // ---- write the partial (m, l, o') of the GQ heads
     float l_col = l_lane + __shfl_xor(l_lane, 16);
@@ -533,7 +613,7 @@ __device__ void bf16_item(const DecodeArgs &a, int b, int req, int j, int hk, in
 
 template <int GQ>
 __global__ __launch_bounds__(512) void partial_kernel(DecodeArgs a) {
-    __shared__ float pbuf[8][kMaxGroup * kBf16Chunk];
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int id = blockIdx.x;
     const int hc = id % a.head_chunks;
     const int rest = id / a.head_chunks;
@@ -548,9 +628,10 @@ __global__ __launch_bounds__(512) void partial_kernel(DecodeArgs a) {
     const int hk = hc * a.waves + w;
     const bool active = hk < a.hkv;
     if (j < 2) {
-        bf16_item(a, b, req, j, active ? hk : 0, p0, p1, active, pbuf[w]);
-    } else if (active) {
-        int2_item<GQ>(a, b, req, j, hk, p0, p1);
+        float *pbuf = reinterpret_cast<float *>(smem) + w * (kMaxGroup * kBf16Chunk);
+        bf16_item(a, b, req, j, active ? hk : 0, p0, p1, active, pbuf);
+    } else if (a.num_slots > 0) {
+        int2_item<GQ>(a, b, req, j, hc, p0, p1, smem);
     }
 }
 
@@ -618,9 +699,17 @@ __global__ __launch_bounds__(128) void merge_kernel(DecodeArgs a) {
     }
 }
 
+// Dynamic LDS of the partial kernel: two stages of 32 padded token records
+// for the INT2 items, or the per-wave softmax buffers of the BF16 items.
+size_t partial_lds_bytes(const DecodeArgs &a) {
+    const size_t stages = 2 * size_t(kTileTokens) * (size_t(a.waves) * kHeadRecord + 16);
+    const size_t pbuf = size_t(a.waves) * kMaxGroup * kBf16Chunk * sizeof(float);
+    return stages > pbuf ? stages : pbuf;
+}
+
 template <int GQ>
 hipError_t launch_partial(const DecodeArgs &a, int blocks, hipStream_t stream) {
-    hipLaunchKernelGGL(partial_kernel<GQ>, dim3(blocks), dim3(64 * a.waves), 0, stream, a);
+    hipLaunchKernelGGL(partial_kernel<GQ>, dim3(blocks), dim3(64 * a.waves), partial_lds_bytes(a), stream, a);
     return hipGetLastError();
 }
 

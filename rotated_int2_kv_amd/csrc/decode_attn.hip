@@ -10,15 +10,8 @@
 //               the recent window (j = 1) or history chunk j - 2.  One wave per
 //               KV head; the workgroup holds all KV heads of the item so that
 //               the slot-major records are read as whole cache lines.
-//               History tiles of 32 tokens run on f16 MFMA:
-//                 QK: A = s * code, dequantised in the operand and exact: the
-//                     scale is split into s_hi (9 significant bits) and s_lo
-//                     (the 2 low bits), so c s_hi and c s_lo are exact fp16
-//                     values and both are accumulated; B = q' split into fp16
-//                     hi + lo columns; one extra MFMA adds sum_g z_g Qbar_g.
-//                 PV: A = softmax weights split hi + lo rows, B = s * code of 8
-//                     tokens per lane, split the same way; one extra MFMA adds
-//                     sum_t p_t z_t.
+//               History tiles of 32 tokens run on f16 MFMA with the INT2 codes
+//               as exact fp16 denormal operands (see int2_item).
 //               BF16 windows run on fp32 VALU.  Each item writes (m, l, o')
 //               with m in log2 units.
 //   3. merge:   log-sum-exp merge of the items and o = o' R_V^T.
@@ -49,7 +42,7 @@ struct DecodeArgs {
     const uint16_t *recent;
     void *out;
     float *qrot;       // [B][Hq][128], log2-scaled rotated query
-    float *qsum;       // [B][Hq][4], group sums of qrot
+    float *qsum;       // [B][Hq][8]: group sums of qrot, then 2^K, 2^(24-K) (operand scaling)
     float *part_o;     // [B][items][Hq][128]
     float *part_ml;    // [B][items][Hq][2] (m, l)
     int64_t r2s_stride;
@@ -133,7 +126,19 @@ __global__ __launch_bounds__(128) void prep_kernel(DecodeArgs a) {
         const int h = c / kGroups, grp = c % kGroups;
         float s = 0.0f;
         for (int i = 0; i < kGroup; ++i) s += qr[h][grp * kGroup + i];
-        a.qsum[(size_t(b) * a.hq + hk * a.g + h) * kGroups + grp] = s;
+        a.qsum[(size_t(b) * a.hq + hk * a.g + h) * 8 + grp] = s;
+    }
+    if (c < a.g) {
+        // power-of-two operand scale 2^K with max|q'| 2^K < 2^15, so that
+        // q' 2^(K - e) (e = 0..8) fits fp16 and its low part stays normal
+        float mx = 0.0f;
+        for (int i = 0; i < kHeadDim; ++i) mx = fmaxf(mx, fabsf(qr[c][i]));
+        int e = 0;
+        frexpf(mx, &e);                          // mx < 2^e
+        const int K = mx > 0.0f ? max(-20, min(24, 15 - e)) : 24;
+        float *info = a.qsum + (size_t(b) * a.hq + hk * a.g + c) * 8;
+        info[4] = ldexpf(1.0f, K);
+        info[5] = ldexpf(1.0f, 24 - K);
     }
 }
 
@@ -142,39 +147,6 @@ __global__ __launch_bounds__(128) void prep_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ f16x2 as_h2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
 __device__ __forceinline__ uint32_t as_u32(f16x2 h) { return __builtin_bit_cast(uint32_t, h); }
-
-// Move bit `from` of v to bit 8 (from is a constant after unrolling).
-__device__ __forceinline__ uint32_t to_bit8(uint32_t v, int from) {
-    return from <= 8 ? v << (8 - from) : v >> (from - 8);
-}
-
-// 4 + c in each fp16 half for the two codes at bits 8-9 and 24-25 of `x`:
-// the code becomes the low mantissa bits of 4.0, whose ulp is 2^-8.
-__device__ __forceinline__ f16x2 code_pair(uint32_t x) {
-    return as_h2((x & 0x03000300u) | 0x44004400u);
-}
-
-// c * s for a code pair e = 4 + c: (4 + c) s - 4 s in one fused multiply-add
-// (c2 = -4 s), rounded once; exact whenever c * s fits in fp16, which holds
-// for s with at most 9 significant bits.
-__device__ __forceinline__ uint32_t dq(f16x2 e, f16x2 s2, f16x2 c2) {
-    return as_u32(__builtin_elementwise_fma(e, s2, c2));
-}
-
-// Split fp16 scales (two per word) into s_hi (low 2 mantissa bits cleared) and
-// s_lo = s - s_hi (exact); returns the four multipliers and offsets.
-struct ScaleSplit {
-    f16x2 s_hi, s_lo, c_hi, c_lo;
-};
-__device__ __forceinline__ ScaleSplit split_scale(uint32_t s_bits2) {
-    const f16x2 neg4 = as_h2(0xC400C400u);   // (-4, -4)
-    ScaleSplit r;
-    r.s_hi = as_h2(s_bits2 & 0xFFFCFFFCu);
-    r.s_lo = as_h2(s_bits2) - r.s_hi;
-    r.c_hi = r.s_hi * neg4;
-    r.c_lo = r.s_lo * neg4;
-    return r;
-}
 
 __device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
     return uint32_t(__half_as_ushort(__float2half_rn(lo))) |
@@ -185,28 +157,58 @@ __device__ __forceinline__ f16x8 u4_as_h8(uint32_t a, uint32_t b, uint32_t c, ui
     return __builtin_bit_cast(f16x8, u32x4{a, b, c, d});
 }
 
-// History item on the matrix cores.  GQ = query heads per KV head.
+// Exponent offset of code pair j inside a 32-bit word of 16 LSB-first codes:
+// pairs (j, j + 8) sit at bits 2j and 16 + 2j; j = 0..4 are masked in place,
+// j = 5..7 after a right shift by 6.  Masked, each 16-bit half is an fp16
+// denormal of value c 2^(e_j - 24).
+__host__ __device__ constexpr int pair_exp(int j) { return j <= 4 ? 2 * j : 2 * j - 6; }
+
+__device__ __forceinline__ uint32_t code_bits(uint32_t w, uint32_t w_sh6, int j) {
+    return j <= 4 ? (w & (0x00030003u << (2 * j))) : (w_sh6 & (0x00030003u << (2 * j - 6)));
+}
+
+__device__ __forceinline__ float dpp_ror4_add(float v) {
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_ror8_add(float v) {
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+}
+
+// History item on the matrix cores.  GQ = query heads per KV head, handled in
+// sets of 4.
 //
-// The whole workgroup streams the tile's slot records (all of its KV heads:
-// whole cache lines of the slot-major pool) with 16-byte loads, three per
-// thread per 32-token tile, into a two-stage LDS ring; each wave then
-// computes its own KV head from LDS.  Loads of tile i + 2 are in flight while
-// tile i is computed.  Tokens past the item or with an out-of-range slot are
-// zero-filled in LDS and masked out of the softmax.
+// Loads: the whole workgroup streams the tile's slot records (all of its KV
+// heads: whole cache lines of the slot-major pool) with 16-byte loads, three
+// per thread per 32-token tile, into a two-stage LDS ring; loads of tile i + 1
+// are in flight while tile i is computed.  Tokens past the item or with an
+// out-of-range slot are zero-filled in LDS and masked out of the softmax.
+//
+// QK (per half of 16 tokens): A = the token's K codes as exact fp16 denormals
+// (one AND per pair, no scale); B = q' (hi and lo fp16 parts, times 2^(K - e))
+// placed block-diagonally so that column (g, h) collects the dot product of
+// group g only.  Each lane then applies s and z of its (token, group) in fp32
+// and a DPP rotate-add sums the four groups: every step is exact except the
+// final fp32 additions.
+// PV: rows (g, h) of A hold p s_g (hi and lo parts), B holds the V codes of 8
+// tokens per lane as exact denormals; the output of column (channel) c is read
+// from the row whose group is c's group.  A second pair of MFMAs adds p z.
 template <int GQ>
 __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, int p0, int p1,
                           uint8_t *smem) {
+    constexpr int HS = (GQ + 3) / 4;          // sets of 4 query heads
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int lane = tid & 63;
     const int n = lane & 15;
     const int kb = lane >> 4;
+    const int cg = n >> 2;                    // group of QK column / PV row n
+    const int ch = n & 3;                     // head (within a set) of column / row n
     const int nthreads = 64 * a.waves;
     const int h0 = hc * a.waves;
-    const int nh = min(a.waves, a.hkv - h0);      // KV heads of this workgroup
+    const int nh = min(a.waves, a.hkv - h0);  // KV heads of this workgroup
     const bool active = w < nh;
     const int hk = h0 + (active ? w : 0);
-    const int ts = nh * kHeadRecord + 16;          // LDS bytes per token (padded)
+    const int ts = nh * kHeadRecord + 16;     // LDS bytes per token (padded)
     const int stage_bytes = kTileTokens * ts;
     const int chunks_tok = nh * (kHeadRecord / 16);
     const int chunks_tile = kTileTokens * chunks_tok;
@@ -215,56 +217,43 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, in
     const int32_t *r2s = a.req_to_slot + int64_t(req) * a.r2s_stride;
     const int n_tiles = (p1 - p0 + kTileTokens - 1) / kTileTokens;
 
-    // column n of the QK B operand: head n (hi part) or head n - GQ (lo part)
-    const bool col_hi = n < GQ;
-    const bool col_lo = n >= GQ && n < 2 * GQ;
-    const int col_head = col_hi ? n : (col_lo ? n - GQ : 0);
-    const float *qr = a.qrot + (size_t(b) * a.hq + hk * GQ + col_head) * kHeadDim;
-    f16x8 qB[4];
+    // ---- per-item operands
+    f16x8 qB[HS][4][2];
+    float qz[HS];       // Qbar[h][cg] 2^(K - 24): zero-point term in the MFMA's units
+    float qout[HS];     // 2^(24 - K): back to logit units
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        uint32_t wq[4];
+    for (int hs = 0; hs < HS; ++hs) {
+        const int h = 4 * hs + ch;
+        const bool hv = h < GQ;
+        const size_t row = size_t(b) * a.hq + hk * GQ + (hv ? h : 0);
+        const float *qr = a.qrot + row * kHeadDim;
+        const float *info = a.qsum + row * 8;
+        const float k2 = info[4];
+        qz[hs] = hv ? info[cg] / info[5] : 0.0f;
+        qout[hs] = info[5];
+        const bool nz = hv && cg == kb;       // block-diagonal: K-block kb is group kb
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            // k-slots (2p, 2p+1) of MFMA r hold channels base + p and base + 8 + p
-            const int base = 32 * kb + 16 * (r >> 1) + 4 * (r & 1);
-            float x0 = 0.0f, x1 = 0.0f;
-            if (col_hi || col_lo) {
-                x0 = qr[base + p];
-                x1 = qr[base + 8 + p];
-                if (col_lo) {
-                    x0 -= __half2float(__float2half_rn(x0));
-                    x1 -= __half2float(__float2half_rn(x1));
-                }
+        for (int r = 0; r < 4; ++r) {
+            uint32_t whi[4], wlo[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int jj = 4 * (r & 1) + p;
+                const int c0 = 32 * kb + 16 * (r >> 1) + jj;
+                const float sc = k2 * __builtin_ldexpf(1.0f, -pair_exp(jj));
+                const float x0 = nz ? qr[c0] * sc : 0.0f;
+                const float x1 = nz ? qr[c0 + 8] * sc : 0.0f;
+                whi[p] = pack_h2(x0, x1);
+                const float h0f = __half2float(__ushort_as_half(uint16_t(whi[p] & 0xFFFFu)));
+                const float h1f = __half2float(__ushort_as_half(uint16_t(whi[p] >> 16)));
+                wlo[p] = pack_h2(x0 - h0f, x1 - h1f);
             }
-            wq[p] = pack_h2(x0, x1);
+            qB[hs][r][0] = u4_as_h8(whi[0], whi[1], whi[2], whi[3]);
+            qB[hs][r][1] = u4_as_h8(wlo[0], wlo[1], wlo[2], wlo[3]);
         }
-        qB[r] = u4_as_h8(wq[0], wq[1], wq[2], wq[3]);
     }
-    f16x8 qBz;
-    {
-        uint32_t wq[4] = {0, 0, 0, 0};
-        if ((col_hi || col_lo) && kb == 0) {
-            const float *qsum = a.qsum + (size_t(b) * a.hq + hk * GQ + col_head) * kGroups;
-            float x[4];
-#pragma unroll
-            for (int grp = 0; grp < 4; ++grp) {
-                x[grp] = qsum[grp];
-                if (col_lo) x[grp] -= __half2float(__float2half_rn(x[grp]));
-            }
-            wq[0] = pack_h2(x[0], x[1]);
-            wq[1] = pack_h2(x[2], x[3]);
-        }
-        qBz = u4_as_h8(wq[0], wq[1], wq[2], wq[3]);
-    }
-    const int partner = col_hi ? lane + GQ : (col_lo ? lane - GQ : lane);
 
-    // Every load below is unconditional (out-of-range positions and slots are
-    // clamped to a safe address and masked afterwards), so each iteration
-    // issues the same straight-line sequence of loads and the loads of the
-    // next tile stay outstanding through the current tile's compute.
-    //
-    // raw slot id of token `lane & 31` of tile t; in_tile(t) says which are real
+    // ---- load pipeline (all loads unconditional: out-of-range positions and
+    // slots read a safe address and are zeroed when written to LDS)
     auto tile_slot = [&](int t) -> int {
         const int pos = p0 + t * kTileTokens + (lane & (kTileTokens - 1));
         return r2s[pos < p1 ? pos : p0];
@@ -273,7 +262,6 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, in
         const int cnt = min(kTileTokens, p1 - (p0 + t * kTileTokens));
         return cnt <= 0 ? 0u : (cnt >= 32 ? 0xFFFFFFFFu : ((1u << cnt) - 1u));
     };
-    // this thread's three 16-byte pieces of a tile
     u32x4 rr[3];
     bool rr_ok[3];
     auto issue = [&](int slot_reg, uint32_t in_tile) {
@@ -301,7 +289,6 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, in
             if (q < chunks_tile) *reinterpret_cast<u32x4 *>(dst + tok * ts + 16 * c) = v;
         }
     };
-    // tokens of a tile with a real position and an in-range slot
     auto valid_mask = [&](int slot_reg, uint32_t in_tile) -> uint32_t {
         const bool ok = lane < kTileTokens && ((in_tile >> lane) & 1u) && slot_reg >= 0 &&
                         int64_t(slot_reg) < a.num_slots;
@@ -312,12 +299,16 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, in
         __builtin_amdgcn_s_barrier();
     };
 
-    float m_run = -INFINITY;
-    float l_lane = 0.0f;
-    f32x4 oacc[8];
+    float m_run[HS], l_lane[HS];
+    f32x4 oacc[HS][8], zacc[HS];
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) oacc[jj] = f32x4{0, 0, 0, 0};
-    f32x4 zacc = f32x4{0, 0, 0, 0};
+    for (int hs = 0; hs < HS; ++hs) {
+        m_run[hs] = -INFINITY;
+        l_lane[hs] = 0.0f;
+        zacc[hs] = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) oacc[hs][jj] = f32x4{0, 0, 0, 0};
+    }
 
     // prologue: tile 0 into stage 0, tile 1 in flight, slots of tile 2 loaded
     const int s0 = tile_slot(0);
@@ -333,177 +324,171 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, in
     for (int it = 0; it < n_tiles; ++it) {
         if (it > 0) {
             // tile it arrived in registers one iteration ago: put it in LDS,
-            // then start loading tile it + 1
+            // then start loading tile it + 1 (slot ids first, record loads last,
+            // so that the record loads stay outstanding through the compute)
             stash(it & 1);
             barrier();
-            // slot ids first, record loads last: the loads stay outstanding
-            // through the compute below and are waited for by the next stash
             const int s_new = tile_slot(it + 2);
             issue(s_far, tile_mask(it + 1));
             mask_cur = mask_next;
             mask_next = valid_mask(s_far, tile_mask(it + 1));
             s_far = s_new;
         }
-        if (active) {
-            const uint8_t *stage = smem + (it & 1) * stage_bytes + w * kHeadRecord;
-            // ---- QK: rows = tokens (two halves of 16), cols = (hi|lo, head)
-            float lg[2][4];
+        if (!active) continue;
+        const uint8_t *stage = smem + (it & 1) * stage_bytes + w * kHeadRecord;
+
+        // ---- QK
+        float lg[HS][8];      // logits of tokens 4 kb + i (i < 4) and 16 + 4 kb + i
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const uint8_t *row = stage + (16 * hf + n) * ts;
-                const u32x2 kc = *reinterpret_cast<const u32x2 *>(row + 8 * kb);
-                const u32x4 ksz = *reinterpret_cast<const u32x4 *>(row + 2 * kCodeBytes);
-                const uint32_t szk = kb == 0 ? ksz[0] : (kb == 1 ? ksz[1] : (kb == 2 ? ksz[2] : ksz[3]));
-                const ScaleSplit sk = split_scale((szk & 0xFFFFu) | (szk << 16));
+        for (int hf = 0; hf < 2; ++hf) {
+            const u32x2 kc = *reinterpret_cast<const u32x2 *>(stage + (16 * hf + n) * ts + 8 * kb);
+            const uint32_t d0s = kc[0] >> 6, d1s = kc[1] >> 6;
+            f16x8 A[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t d = r < 2 ? kc[0] : kc[1];
+                const uint32_t ds = r < 2 ? d0s : d1s;
+                A[r] = u4_as_h8(code_bits(d, ds, 4 * (r & 1) + 0), code_bits(d, ds, 4 * (r & 1) + 1),
+                                code_bits(d, ds, 4 * (r & 1) + 2), code_bits(d, ds, 4 * (r & 1) + 3));
+            }
+            // (s, z) of the output lane's 4 tokens for group cg
+            uint32_t szk[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                szk[i] = *reinterpret_cast<const uint32_t *>(stage + (16 * hf + 4 * kb + i) * ts +
+                                                            2 * kCodeBytes + 4 * cg);
+#pragma unroll
+            for (int hs = 0; hs < HS; ++hs) {
                 f32x4 acc = f32x4{0, 0, 0, 0};
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const uint32_t d = (r < 2) ? kc[0] : kc[1];
-                    const int sh = 8 * (r & 1);
-                    f16x2 e[4];
-#pragma unroll
-                    for (int p = 0; p < 4; ++p) e[p] = code_pair(to_bit8(d, sh + 2 * p));
-                    const f16x8 Ahi = u4_as_h8(dq(e[0], sk.s_hi, sk.c_hi), dq(e[1], sk.s_hi, sk.c_hi),
-                                               dq(e[2], sk.s_hi, sk.c_hi), dq(e[3], sk.s_hi, sk.c_hi));
-                    const f16x8 Alo = u4_as_h8(dq(e[0], sk.s_lo, sk.c_lo), dq(e[1], sk.s_lo, sk.c_lo),
-                                               dq(e[2], sk.s_lo, sk.c_lo), dq(e[3], sk.s_lo, sk.c_lo));
-                    acc = mfma_f16(Ahi, qB[r], acc);
-                    acc = mfma_f16(Alo, qB[r], acc);
-                }
-                {
-                    uint32_t z01 = 0, z23 = 0;
-                    if (kb == 0) {
-                        z01 = (ksz[0] >> 16) | (ksz[1] & 0xFFFF0000u);
-                        z23 = (ksz[2] >> 16) | (ksz[3] & 0xFFFF0000u);
-                    }
-                    acc = mfma_f16(u4_as_h8(z01, z23, 0, 0), qBz, acc);
+                    acc = mfma_f16(A[r], qB[hs][r][0], acc);
+                    acc = mfma_f16(A[r], qB[hs][r][1], acc);
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
+                    const float sf = __half2float(__ushort_as_half(uint16_t(szk[i] & 0xFFFFu)));
+                    const float zf = __half2float(__ushort_as_half(uint16_t(szk[i] >> 16)));
+                    float x = fmaf(acc[i], sf, zf * qz[hs]);
+                    x = dpp_ror8_add(dpp_ror4_add(x));          // sum over the 4 groups
                     const bool ok = (mask_cur >> (16 * hf + 4 * kb + i)) & 1u;
-                    const float part = __shfl(acc[i], partner);
-                    lg[hf][i] = ok ? acc[i] + part : -INFINITY;
+                    lg[hs][4 * hf + i] = ok ? x * qout[hs] : -INFINITY;
                 }
             }
+        }
 
-            // ---- online softmax (per column; all 4 row groups agree after the reduction)
-            float mx = lg[0][0];
+        // ---- online softmax and PV A operands
+        // (s, z) of V for group cg and the 8 tokens of this lane
+        uint32_t szv[8], vw[8];
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
+        for (int sidx = 0; sidx < 8; ++sidx) {
+            const int tt = sidx < 4 ? 4 * kb + sidx : 16 + 4 * kb + (sidx - 4);
+            const uint8_t *row = stage + tt * ts;
+            szv[sidx] = *reinterpret_cast<const uint32_t *>(row + 2 * kCodeBytes + kSzBytes + 4 * cg);
+            vw[sidx] = *reinterpret_cast<const uint16_t *>(row + kCodeBytes + 2 * n);
+        }
+        f16x8 AS[HS][2], AZ[HS][2];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, lg[hf][i]);
+        for (int hs = 0; hs < HS; ++hs) {
+            float mx = lg[hs][0];
+#pragma unroll
+            for (int i = 1; i < 8; ++i) mx = fmaxf(mx, lg[hs][i]);
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run, mx);
-            if (__any(m_new > m_run)) {
-                const float alpha = (m_new > m_run) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-                l_lane *= alpha;
+            const float m_new = fmaxf(m_run[hs], mx);
+            if (__any(m_new > m_run[hs])) {
+                const float alpha = (m_new > m_run[hs]) ? __builtin_amdgcn_exp2f(m_run[hs] - m_new) : 1.0f;
+                l_lane[hs] *= alpha;
+                // PV output row (g, h) = (kb, i): alpha of head i lives in lane i
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float ar = __shfl(alpha, 4 * kb + i);   // alpha of PV row 4 kb + i
+                    const float ai = __builtin_bit_cast(
+                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), i));
 #pragma unroll
-                    for (int jj = 0; jj < 8; ++jj) oacc[jj][i] *= ar;
-                    zacc[i] *= ar;
+                    for (int jj = 0; jj < 8; ++jj) oacc[hs][jj][i] *= ai;
+                    zacc[hs][i] *= ai;
                 }
-                m_run = m_new;
+                m_run[hs] = m_new;
             }
-            float pv[8];
+            uint32_t wsh[4], wsl[4], wzh[4], wzl[4];
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float x = lg[hf][i];
-                    const float p = (x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x - m_run);
-                    pv[4 * hf + i] = p;
-                    l_lane += p;
-                }
-            // PV A operand: row n = (hi|lo, head), k-slots = tokens 4 kb + s (s < 4)
-            // and 16 + 4 kb + s - 4 (s >= 4)
-            uint32_t aw[4];
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                float x0 = pv[2 * p], x1 = pv[2 * p + 1];
-                if (col_lo) {
-                    x0 -= __half2float(__float2half_rn(x0));
-                    x1 -= __half2float(__float2half_rn(x1));
-                } else if (!col_hi) {
-                    x0 = 0.0f;
-                    x1 = 0.0f;
-                }
-                aw[p] = pack_h2(x0, x1);
-            }
-            const f16x8 AP = u4_as_h8(aw[0], aw[1], aw[2], aw[3]);
-
-            // ---- PV B operands: lane (n, kb) reads word n (channels 8n .. 8n+7)
-            // of the V codes and the (s, z) of group n / 4 for its 8 tokens
-            uint32_t vw[4], sp[4], zp[4];
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                uint32_t wv[2], szv[2];
+            for (int pp = 0; pp < 4; ++pp) {
+                float pr[2], ps[2];
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
-                    const int sidx = 2 * p + e;
-                    const int tt = sidx < 4 ? 4 * kb + sidx : 16 + 4 * kb + (sidx - 4);
-                    const uint8_t *row = stage + tt * ts;
-                    wv[e] = *reinterpret_cast<const uint16_t *>(row + kCodeBytes + 2 * n);
-                    szv[e] = *reinterpret_cast<const uint32_t *>(row + 2 * kCodeBytes + kSzBytes + 4 * (n >> 2));
+                    const float x = lg[hs][2 * pp + e];
+                    const float p = (x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x - m_run[hs]);
+                    l_lane[hs] += p;
+                    pr[e] = p;
+                    ps[e] = p * __half2float(__ushort_as_half(uint16_t(szv[2 * pp + e] & 0xFFFFu)));
                 }
-                vw[p] = wv[0] | (wv[1] << 16);
-                sp[p] = (szv[0] & 0xFFFFu) | (szv[1] << 16);
-                zp[p] = (szv[0] >> 16) | (szv[1] & 0xFFFF0000u);
+                wsh[pp] = pack_h2(ps[0], ps[1]);
+                wzh[pp] = pack_h2(pr[0], pr[1]);
+                const float sh0 = __half2float(__ushort_as_half(uint16_t(wsh[pp] & 0xFFFFu)));
+                const float sh1 = __half2float(__ushort_as_half(uint16_t(wsh[pp] >> 16)));
+                const float zh0 = __half2float(__ushort_as_half(uint16_t(wzh[pp] & 0xFFFFu)));
+                const float zh1 = __half2float(__ushort_as_half(uint16_t(wzh[pp] >> 16)));
+                wsl[pp] = pack_h2(ps[0] - sh0, ps[1] - sh1);
+                wzl[pp] = pack_h2(pr[0] - zh0, pr[1] - zh1);
             }
-            const f16x8 BZ = u4_as_h8(zp[0], zp[1], zp[2], zp[3]);
-            ScaleSplit sv[4];
+            AS[hs][0] = u4_as_h8(wsh[0], wsh[1], wsh[2], wsh[3]);
+            AS[hs][1] = u4_as_h8(wsl[0], wsl[1], wsl[2], wsl[3]);
+            AZ[hs][0] = u4_as_h8(wzh[0], wzh[1], wzh[2], wzh[3]);
+            AZ[hs][1] = u4_as_h8(wzl[0], wzl[1], wzl[2], wzl[3]);
+        }
+
+        // ---- PV: B = V codes of channel 8 n + jj for the lane's 8 tokens
+        uint32_t xw[4], xs[4];
 #pragma unroll
-            for (int p = 0; p < 4; ++p) sv[p] = split_scale(sp[p]);
+        for (int pp = 0; pp < 4; ++pp) {
+            xw[pp] = vw[2 * pp] | (vw[2 * pp + 1] << 16);
+            xs[pp] = xw[pp] >> 6;
+        }
+        const f16x8 BZ = u4_as_h8((szv[0] >> 16) | (szv[1] & 0xFFFF0000u), (szv[2] >> 16) | (szv[3] & 0xFFFF0000u),
+                                  (szv[4] >> 16) | (szv[5] & 0xFFFF0000u), (szv[6] >> 16) | (szv[7] & 0xFFFF0000u));
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                f16x2 e[4];
+        for (int jj = 0; jj < 8; ++jj) {
+            const f16x8 Bj = u4_as_h8(code_bits(xw[0], xs[0], jj), code_bits(xw[1], xs[1], jj),
+                                      code_bits(xw[2], xs[2], jj), code_bits(xw[3], xs[3], jj));
 #pragma unroll
-                for (int p = 0; p < 4; ++p) e[p] = code_pair(to_bit8(vw[p], 2 * jj));
-                const f16x8 Bhi = u4_as_h8(dq(e[0], sv[0].s_hi, sv[0].c_hi), dq(e[1], sv[1].s_hi, sv[1].c_hi),
-                                           dq(e[2], sv[2].s_hi, sv[2].c_hi), dq(e[3], sv[3].s_hi, sv[3].c_hi));
-                const f16x8 Blo = u4_as_h8(dq(e[0], sv[0].s_lo, sv[0].c_lo), dq(e[1], sv[1].s_lo, sv[1].c_lo),
-                                           dq(e[2], sv[2].s_lo, sv[2].c_lo), dq(e[3], sv[3].s_lo, sv[3].c_lo));
-                oacc[jj] = mfma_f16(AP, Bhi, oacc[jj]);
-                oacc[jj] = mfma_f16(AP, Blo, oacc[jj]);
+            for (int hs = 0; hs < HS; ++hs) {
+                oacc[hs][jj] = mfma_f16(AS[hs][0], Bj, oacc[hs][jj]);
+                oacc[hs][jj] = mfma_f16(AS[hs][1], Bj, oacc[hs][jj]);
             }
-            zacc = mfma_f16(AP, BZ, zacc);
+        }
+#pragma unroll
+        for (int hs = 0; hs < HS; ++hs) {
+            zacc[hs] = mfma_f16(AZ[hs][0], BZ, zacc[hs]);
+            zacc[hs] = mfma_f16(AZ[hs][1], BZ, zacc[hs]);
         }
     }
     if (!active) return;
 
     // ---- write the partial (m, l, o') of the GQ heads
-    float l_col = l_lane + __shfl_xor(l_lane, 16);
-    l_col += __shfl_xor(l_col, 32);
     const size_t row0 = (size_t(b) * a.items + j) * a.hq + hk * GQ;
-    if (kb == 0 && col_hi) {
-        a.part_ml[(row0 + n) * 2 + 0] = m_run;
-        a.part_ml[(row0 + n) * 2 + 1] = l_col;
-    }
-    // PV output: lane (n, kb) holds rows 4 kb + i, channels 8 n + jj; row h
-    // (hi) and row GQ + h (lo) add up to head h
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 4 * kb + i;
-        const int e = (GQ + i) & 3;
-        const int src = n + 16 * (kb + ((GQ + i) >> 2));
-        float o[8];
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-            float lo_part = 0.0f;
-            switch (e) {  // register index must be static
-                case 0: lo_part = __shfl(oacc[jj][0] + zacc[0], src); break;
-                case 1: lo_part = __shfl(oacc[jj][1] + zacc[1], src); break;
-                case 2: lo_part = __shfl(oacc[jj][2] + zacc[2], src); break;
-                default: lo_part = __shfl(oacc[jj][3] + zacc[3], src); break;
-            }
-            o[jj] = oacc[jj][i] + zacc[i] + lo_part;
+    for (int hs = 0; hs < HS; ++hs) {
+        float l_col = l_lane[hs] + __shfl_xor(l_lane[hs], 16);
+        l_col += __shfl_xor(l_col, 32);
+        const int h = 4 * hs + ch;
+        if (kb == 0 && cg == 0 && h < GQ) {
+            a.part_ml[(row0 + h) * 2 + 0] = m_run[hs];
+            a.part_ml[(row0 + h) * 2 + 1] = l_col;
         }
-        if (r < GQ) {
-            float *dst = a.part_o + (row0 + r) * kHeadDim + 8 * n;
-            *reinterpret_cast<f32x4 *>(dst) = f32x4{o[0], o[1], o[2], o[3]};
-            *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
+        // output lane (n, kb) holds rows (g = kb, h = i); the row whose group
+        // matches channel 8 n + jj (group n / 4) carries the result
+        if (kb == cg) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (4 * hs + i >= GQ) break;
+                float o[8];
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj)
+                    o[jj] = oacc[hs][jj][i] * __builtin_ldexpf(1.0f, 24 - pair_exp(jj)) + zacc[hs][i];
+                float *dst = a.part_o + (row0 + 4 * hs + i) * kHeadDim + 8 * n;
+                *reinterpret_cast<f32x4 *>(dst) = f32x4{o[0], o[1], o[2], o[3]};
+                *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
+            }
         }
     }
 }

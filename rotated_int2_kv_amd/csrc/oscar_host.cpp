@@ -86,7 +86,7 @@ oscar_status make_decode_plan(const oscar_layout &lay, int32_t batch,
     plan->ws_qrot = off;
     off += align(size_t(batch) * hq * kHeadDim * sizeof(float));
     plan->ws_qsum = off;
-    off += align(size_t(batch) * hq * kGroups * sizeof(float));
+    off += align(size_t(batch) * hq * 8 * sizeof(float));
     plan->ws_part_o = off;
     off += align(size_t(batch) * items * hq * kHeadDim * sizeof(float));
     plan->ws_part_ml = off;

@@ -27,6 +27,13 @@ COMMON_FLAGS = [
     "-ffp-contract=off",
     # packed fp32 arithmetic stays off (plain fp32 VALU only)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the kernels rescale and read them
+    # with VALU ops, which on accumulation registers costs a copy each way
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+    # NaN inputs are outside the contract (the quantiser and the softmax
+    # assume finite values); without it every fmax first quiets NaNs, which
+    # also keeps DPP lane moves from fusing into the max
+    "-fno-honor-nans",
     "-Wall", "-Wextra", "-Wno-unused-parameter",
     "-I", os.path.join(ROOT, "include"),
 ]

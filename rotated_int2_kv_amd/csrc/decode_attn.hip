@@ -29,6 +29,7 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kTileTokens = 32;      // history tokens per MFMA tile
 constexpr int kBf16Chunk = 64;       // BF16-window tokens per VALU step
+constexpr int kPartialWaves = 4;     // KV heads (waves) per split-K workgroup
 
 struct DecodeArgs {
     const void *q;
@@ -45,6 +46,7 @@ struct DecodeArgs {
     float *qsum;       // [B][Hq][8]: group sums of qrot, then 2^K, 2^(24-K) (operand scaling)
     float *part_o;     // [B][items][Hq][128]
     float *part_ml;    // [B][items][Hq][2] (m, l)
+    uint8_t *zero_rec; // 256 zero bytes (cleared by the prep kernel)
     int64_t r2s_stride;
     int64_t num_slots;
     float scale_log2;
@@ -97,46 +99,57 @@ __device__ __forceinline__ float load_as_f32(const void *p, int dtype, size_t id
 // ---------------------------------------------------------------------------
 // 1. query rotation
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(128) void prep_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(512) void prep_kernel(DecodeArgs a) {
     __shared__ float qs[kMaxGroup][kHeadDim];
-    __shared__ float qr[kMaxGroup][kHeadDim];
+    __shared__ float part[4][kMaxGroup][kHeadDim];
     const int b = blockIdx.x / a.hkv;
     const int hk = blockIdx.x % a.hkv;
-    const int c = threadIdx.x;
-    for (int h = 0; h < a.g; ++h)
-        qs[h][c] = load_as_f32(a.q, a.q_dtype, (size_t(b) * a.hq + hk * a.g + h) * kHeadDim + c);
+    const int t = threadIdx.x;
+    const int c = t & (kHeadDim - 1);        // output channel
+    const int quarter = t >> 7;               // input channels [32 quarter, 32 quarter + 32)
+    if (blockIdx.x == 0 && t < 64) reinterpret_cast<uint32_t *>(a.zero_rec)[t] = 0u;
+    for (int e = t; e < a.g * kHeadDim; e += 512) {
+        const int h = e / kHeadDim, i = e % kHeadDim;
+        qs[h][i] = load_as_f32(a.q, a.q_dtype, (size_t(b) * a.hq + hk * a.g + h) * kHeadDim + i);
+    }
     __syncthreads();
     const float *R = a.r_k + size_t(hk) * kHeadDim * kHeadDim;
     float acc[kMaxGroup];
 #pragma unroll
     for (int h = 0; h < kMaxGroup; ++h) acc[h] = 0.0f;
-    for (int i = 0; i < kHeadDim; ++i) {
+#pragma unroll 8
+    for (int ii = 0; ii < kHeadDim / 4; ++ii) {
+        const int i = quarter * (kHeadDim / 4) + ii;
         const float r = R[size_t(i) * kHeadDim + c];
 #pragma unroll
         for (int h = 0; h < kMaxGroup; ++h)
             if (h < a.g) acc[h] = fmaf(qs[h][i], r, acc[h]);
     }
-    for (int h = 0; h < a.g; ++h) {
-        const float v = acc[h] * a.scale_log2;
-        qr[h][c] = v;
-        a.qrot[(size_t(b) * a.hq + hk * a.g + h) * kHeadDim + c] = v;
+    for (int h = 0; h < a.g; ++h) part[quarter][h][c] = acc[h];
+    __syncthreads();
+    for (int e = t; e < a.g * kHeadDim; e += 512) {
+        const int h = e / kHeadDim, cc = e % kHeadDim;
+        const float v = (part[0][h][cc] + part[1][h][cc] + part[2][h][cc] + part[3][h][cc]) * a.scale_log2;
+        qs[h][cc] = v;
+        a.qrot[(size_t(b) * a.hq + hk * a.g + h) * kHeadDim + cc] = v;
     }
     __syncthreads();
-    if (c < a.g * kGroups) {
-        const int h = c / kGroups, grp = c % kGroups;
-        float s = 0.0f;
-        for (int i = 0; i < kGroup; ++i) s += qr[h][grp * kGroup + i];
-        a.qsum[(size_t(b) * a.hq + hk * a.g + h) * 8 + grp] = s;
+    if (t < a.g * kGroups) {
+        const int h = t / kGroups, grp = t % kGroups;
+        float sum = 0.0f;
+        for (int i = 0; i < kGroup; ++i) sum += qs[h][grp * kGroup + i];
+        a.qsum[(size_t(b) * a.hq + hk * a.g + h) * 8 + grp] = sum;
     }
-    if (c < a.g) {
+    if (t >= 64 && t < 64 + a.g) {
         // power-of-two operand scale 2^K with max|q'| 2^K < 2^15, so that
         // q' 2^(K - e) (e = 0..8) fits fp16 and its low part stays normal
+        const int h = t - 64;
         float mx = 0.0f;
-        for (int i = 0; i < kHeadDim; ++i) mx = fmaxf(mx, fabsf(qr[c][i]));
+        for (int i = 0; i < kHeadDim; ++i) mx = fmaxf(mx, fabsf(qs[h][i]));
         int e = 0;
         frexpf(mx, &e);                          // mx < 2^e
         const int K = mx > 0.0f ? max(-20, min(24, 15 - e)) : 24;
-        float *info = a.qsum + (size_t(b) * a.hq + hk * a.g + c) * 8;
+        float *info = a.qsum + (size_t(b) * a.hq + hk * a.g + h) * 8;
         info[4] = ldexpf(1.0f, K);
         info[5] = ldexpf(1.0f, 24 - K);
     }
@@ -145,12 +158,16 @@ __global__ __launch_bounds__(128) void prep_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // 2. split-K partials
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ f16x2 as_h2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
-__device__ __forceinline__ uint32_t as_u32(f16x2 h) { return __builtin_bit_cast(uint32_t, h); }
 
-__device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
-    return uint32_t(__half_as_ushort(__float2half_rn(lo))) |
-           (uint32_t(__half_as_ushort(__float2half_rn(hi))) << 16);
+// x ~ hi + lo with hi, lo fp16 pairs: hi rounded toward zero, lo the exact
+// fp32 residual rounded toward zero (relative error of hi + lo below 2^-20).
+struct HiLo2 {
+    uint32_t hi, lo;
+};
+__device__ __forceinline__ HiLo2 split_hilo(float x0, float x1) {
+    const auto h = __builtin_amdgcn_cvt_pkrtz(x0, x1);
+    const auto l = __builtin_amdgcn_cvt_pkrtz(x0 - float(h[0]), x1 - float(h[1]));
+    return {__builtin_bit_cast(uint32_t, h), __builtin_bit_cast(uint32_t, l)};
 }
 
 __device__ __forceinline__ f16x8 u4_as_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
@@ -167,285 +184,289 @@ __device__ __forceinline__ uint32_t code_bits(uint32_t w, uint32_t w_sh6, int j)
     return j <= 4 ? (w & (0x00030003u << (2 * j))) : (w_sh6 & (0x00030003u << (2 * j - 6)));
 }
 
-__device__ __forceinline__ float dpp_ror4_add(float v) {
-    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
+// reductions over the 16 lanes of a DPP row (every lane of the row gets the result)
+template <int K>
+__device__ __forceinline__ float row_ror(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x120 + K, 0xF, 0xF, false));
 }
-__device__ __forceinline__ float dpp_ror8_add(float v) {
-    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, row_ror<1>(v));
+    v = fmaxf(v, row_ror<2>(v));
+    v = fmaxf(v, row_ror<4>(v));
+    return fmaxf(v, row_ror<8>(v));
 }
+__device__ __forceinline__ float row16_sum(float v) {
+    v += row_ror<1>(v);
+    v += row_ror<2>(v);
+    v += row_ror<4>(v);
+    return v + row_ror<8>(v);
+}
+__device__ __forceinline__ float half_lo(uint32_t w) { return __half2float(__ushort_as_half(uint16_t(w))); }
+__device__ __forceinline__ float half_hi(uint32_t w) { return __half2float(__ushort_as_half(uint16_t(w >> 16))); }
 
 // History item on the matrix cores.  GQ = query heads per KV head, handled in
-// sets of 4.
+// sets of 4.  One wave per KV head; the waves of a workgroup run the same
+// positions for all KV heads of the slot-major records, so together they read
+// whole cache lines, but each wave runs its own pipeline without barriers.
 //
-// Loads: the whole workgroup streams the tile's slot records (all of its KV
-// heads: whole cache lines of the slot-major pool) with 16-byte loads, three
-// per thread per 32-token tile, into a two-stage LDS ring; loads of tile i + 1
-// are in flight while tile i is computed.  Tokens past the item or with an
-// out-of-range slot are zero-filled in LDS and masked out of the softmax.
+// Loads: per 32-token tile a wave reads its 96-byte head records with three
+// 16-byte loads per lane into registers and writes them into its own
+// two-stage LDS ring (112-byte token stride); two tiles are in flight while a
+// third is computed.  Tokens past the item or with an out-of-range slot are
+// zero-filled and masked out of the softmax.
 //
-// QK (per half of 16 tokens): A = the token's K codes as exact fp16 denormals
-// (one AND per pair, no scale); B = q' (hi and lo fp16 parts, times 2^(K - e))
-// placed block-diagonally so that column (g, h) collects the dot product of
-// group g only.  Each lane then applies s and z of its (token, group) in fp32
-// and a DPP rotate-add sums the four groups: every step is exact except the
-// final fp32 additions.
-// PV: rows (g, h) of A hold p s_g (hi and lo parts), B holds the V codes of 8
-// tokens per lane as exact denormals; the output of column (channel) c is read
-// from the row whose group is c's group.  A second pair of MFMAs adds p z.
+// QK (per half of 16 tokens): B = the tokens' K codes as exact fp16 denormals
+// (one AND per pair, no scale); A = q' (hi and lo fp16 parts, times
+// 2^(K - e)) in rows (h, g) that are block-diagonal over the K blocks, so
+// that output row (h, g) holds the dot product of group g only.  Lane
+// (token n, head h) thereby receives its four group sums and applies s and z
+// in fp32: one logit per lane, nothing repeated.
+// PV: the lane of (token, head) forms p s_g (hi and lo fp16 parts) for the
+// four groups and accumulates p z_g itself; the weights go through the
+// wave's LDS into rows (g, h) of A, B holds the V codes of 8 tokens per lane
+// as exact denormals, and the output of column (channel) c is read from the
+// row whose group is c's group.
+constexpr int kTokStride = kHeadRecord + 16;           // LDS bytes per token
+constexpr int kStageBytes = kTileTokens * kTokStride;  // one tile of one KV head
+constexpr int kWRow = 2 * kTileTokens * 2 + 16;        // weight row: hi and lo of 32 tokens, padded
+constexpr int kWSetBytes = 16 * kWRow;                 // rows (g, h) of one set of 4 heads
+__host__ __device__ constexpr int wave_lds_bytes(int gq) { return 2 * kStageBytes + ((gq + 3) / 4) * kWSetBytes; }
+
 template <int GQ>
-__device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, int p0, int p1,
-                          uint8_t *smem) {
+__device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hk, int p0, int p1,
+                          uint8_t *wlds) {
     constexpr int HS = (GQ + 3) / 4;          // sets of 4 query heads
-    const int tid = threadIdx.x;
-    const int w = tid >> 6;
-    const int lane = tid & 63;
+    const int lane = threadIdx.x & 63;
     const int n = lane & 15;
     const int kb = lane >> 4;
-    const int cg = n >> 2;                    // group of QK column / PV row n
-    const int ch = n & 3;                     // head (within a set) of column / row n
-    const int nthreads = 64 * a.waves;
-    const int h0 = hc * a.waves;
-    const int nh = min(a.waves, a.hkv - h0);  // KV heads of this workgroup
-    const bool active = w < nh;
-    const int hk = h0 + (active ? w : 0);
-    const int ts = nh * kHeadRecord + 16;     // LDS bytes per token (padded)
-    const int stage_bytes = kTileTokens * ts;
-    const int chunks_tok = nh * (kHeadRecord / 16);
-    const int chunks_tile = kTileTokens * chunks_tok;
-    const int64_t rec_bytes = int64_t(a.hkv) * kHeadRecord;
-    const uint8_t *gbase = a.records + h0 * kHeadRecord;
+    const uint32_t rec_bytes = uint32_t(a.hkv) * kHeadRecord;
+    const uint8_t *gbase = a.records + hk * kHeadRecord;
     const int32_t *r2s = a.req_to_slot + int64_t(req) * a.r2s_stride;
     const int n_tiles = (p1 - p0 + kTileTokens - 1) / kTileTokens;
+    uint8_t *wbuf = wlds + 2 * kStageBytes;
+    const size_t head0 = size_t(b) * a.hq + size_t(hk) * GQ;
 
     // ---- per-item operands
-    f16x8 qB[HS][4][2];
-    float qz[HS];       // Qbar[h][cg] 2^(K - 24): zero-point term in the MFMA's units
-    float qout[HS];     // 2^(24 - K): back to logit units
+    f16x8 qA[HS][4][2];   // QK A: row n = (h = n / 4, g = n % 4), nonzero in K block g
+    float qz[HS][4];      // Qbar[head kb][g] 2^(K - 24): zero-point term in the MFMA's units
+    float qout[HS];       // 2^(24 - K) of head kb: back to logit units
 #pragma unroll
     for (int hs = 0; hs < HS; ++hs) {
-        const int h = 4 * hs + ch;
-        const bool hv = h < GQ;
-        const size_t row = size_t(b) * a.hq + hk * GQ + (hv ? h : 0);
-        const float *qr = a.qrot + row * kHeadDim;
-        const float *info = a.qsum + row * 8;
-        const float k2 = info[4];
-        qz[hs] = hv ? info[cg] / info[5] : 0.0f;
-        qout[hs] = info[5];
-        const bool nz = hv && cg == kb;       // block-diagonal: K-block kb is group kb
+        {
+            const int h = 4 * hs + (n >> 2);
+            const bool hv = h < GQ;
+            const float *qr = a.qrot + (head0 + (hv ? h : 0)) * kHeadDim;
+            const float k2 = a.qsum[(head0 + (hv ? h : 0)) * 8 + 4];
+            const bool nz = hv && (n & 3) == kb;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            uint32_t whi[4], wlo[4];
+            for (int r = 0; r < 4; ++r) {
+                uint32_t whi[4], wlo[4];
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const int jj = 4 * (r & 1) + p;
-                const int c0 = 32 * kb + 16 * (r >> 1) + jj;
-                const float sc = k2 * __builtin_ldexpf(1.0f, -pair_exp(jj));
-                const float x0 = nz ? qr[c0] * sc : 0.0f;
-                const float x1 = nz ? qr[c0 + 8] * sc : 0.0f;
-                whi[p] = pack_h2(x0, x1);
-                const float h0f = __half2float(__ushort_as_half(uint16_t(whi[p] & 0xFFFFu)));
-                const float h1f = __half2float(__ushort_as_half(uint16_t(whi[p] >> 16)));
-                wlo[p] = pack_h2(x0 - h0f, x1 - h1f);
+                for (int p = 0; p < 4; ++p) {
+                    const int jj = 4 * (r & 1) + p;
+                    const int c0 = 32 * kb + 16 * (r >> 1) + jj;
+                    const float sc = k2 * __builtin_ldexpf(1.0f, -pair_exp(jj));
+                    const float x0 = nz ? qr[c0] * sc : 0.0f;
+                    const float x1 = nz ? qr[c0 + 8] * sc : 0.0f;
+                    const HiLo2 hl = split_hilo(x0, x1);
+                    whi[p] = hl.hi;
+                    wlo[p] = hl.lo;
+                }
+                qA[hs][r][0] = u4_as_h8(whi[0], whi[1], whi[2], whi[3]);
+                qA[hs][r][1] = u4_as_h8(wlo[0], wlo[1], wlo[2], wlo[3]);
             }
-            qB[hs][r][0] = u4_as_h8(whi[0], whi[1], whi[2], whi[3]);
-            qB[hs][r][1] = u4_as_h8(wlo[0], wlo[1], wlo[2], wlo[3]);
+        }
+        {
+            const int h = 4 * hs + kb;
+            const bool hv = h < GQ;
+            const float *info = a.qsum + (head0 + (hv ? h : 0)) * 8;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) qz[hs][g] = hv ? info[g] / info[5] : 0.0f;
+            qout[hs] = hv ? info[5] : 0.0f;
         }
     }
 
-    // ---- load pipeline (all loads unconditional: out-of-range positions and
-    // slots read a safe address and are zeroed when written to LDS)
-    auto tile_slot = [&](int t) -> int {
-        const int pos = p0 + t * kTileTokens + (lane & (kTileTokens - 1));
+    // ---- load pipeline.  Every load is unconditional (out-of-range
+    // positions and slots read a safe address and are zeroed at the stash), so
+    // each step issues a fixed sequence and the compiler's wait counts leave
+    // the younger tiles in flight.
+    int q_tok[3], q_off[3];                   // token and 16-byte piece of each load
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+        const int q = u * 64 + lane;          // 192 pieces = 32 tokens x 6
+        q_tok[u] = q / 6;
+        q_off[u] = 16 * (q - 6 * q_tok[u]);
+    }
+    auto pair_slots = [&](int t) -> int {      // slots of tiles t and t + 1, a position per lane
+        const int pos = p0 + t * kTileTokens + lane;
         return r2s[pos < p1 ? pos : p0];
     };
-    auto tile_mask = [&](int t) -> uint32_t {   // positions of tile t inside [p0, p1)
-        const int cnt = min(kTileTokens, p1 - (p0 + t * kTileTokens));
-        return cnt <= 0 ? 0u : (cnt >= 32 ? 0xFFFFFFFFu : ((1u << cnt) - 1u));
+    auto pair_valid = [&](int slot_reg, int t) -> uint64_t {   // usable positions of tiles t, t + 1
+        const int pos = p0 + t * kTileTokens + lane;
+        return __ballot(pos < p1 && slot_reg >= 0 && int64_t(slot_reg) < a.num_slots);
     };
-    u32x4 rr[3];
-    bool rr_ok[3];
-    auto issue = [&](int slot_reg, uint32_t in_tile) {
+    struct Tile {
+        u32x4 v[3];
+    };
+    // slots of the pieces a lane loads of tile `half` of a pair
+    auto piece_slots = [&](int slot_reg, int half, int (&sl)[3]) {
+#pragma unroll
+        for (int u = 0; u < 3; ++u) sl[u] = __shfl(slot_reg, q_tok[u] + kTileTokens * half);
+    };
+    // record loads of one tile; `valid` = its 32 usable positions.  Unusable
+    // tokens read the zero record, so they arrive as s = z = 0 and codes 0.
+    auto issue = [&](Tile &tl, const int (&sl)[3], uint32_t valid) {
 #pragma unroll
         for (int u = 0; u < 3; ++u) {
-            const int q = u * nthreads + tid;
-            const int qc = q < chunks_tile ? q : 0;
-            const int tok = qc / chunks_tok;
-            const int c = qc - tok * chunks_tok;
-            const int slot = __shfl(slot_reg, tok);
-            const bool ok = q < chunks_tile && ((in_tile >> tok) & 1u) && slot >= 0 &&
-                            int64_t(slot) < a.num_slots;
-            rr_ok[u] = ok;
-            rr[u] = *reinterpret_cast<const u32x4 *>(gbase + int64_t(ok ? slot : 0) * rec_bytes + 16 * c);
+            const bool ok = (valid >> q_tok[u]) & 1u;
+            const uint8_t *src = gbase + uint64_t(uint32_t(sl[u])) * rec_bytes;
+            asm volatile("" : "+v"(src));     // computed on every lane: a select, not a branch
+            src = ok ? src : a.zero_rec;
+            tl.v[u] = *reinterpret_cast<const u32x4 *>(src + q_off[u]);
         }
     };
-    auto stash = [&](int stage) {
-        uint8_t *dst = smem + stage * stage_bytes;
+    // LDS is used by this wave alone and runs a wave's operations in order;
+    // the fences keep the compiler from moving LDS accesses across them
+    auto lds_order = [] {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    auto stash = [&](const Tile &tl, int stage) {
+        uint8_t *dst = wlds + stage * kStageBytes;
+        lds_order();
 #pragma unroll
-        for (int u = 0; u < 3; ++u) {
-            const int q = u * nthreads + tid;
-            const int tok = q / chunks_tok;
-            const int c = q - tok * chunks_tok;
-            const u32x4 v = rr_ok[u] ? rr[u] : u32x4{0, 0, 0, 0};
-            if (q < chunks_tile) *reinterpret_cast<u32x4 *>(dst + tok * ts + 16 * c) = v;
-        }
-    };
-    auto valid_mask = [&](int slot_reg, uint32_t in_tile) -> uint32_t {
-        const bool ok = lane < kTileTokens && ((in_tile >> lane) & 1u) && slot_reg >= 0 &&
-                        int64_t(slot_reg) < a.num_slots;
-        return uint32_t(__ballot(ok));
-    };
-    auto barrier = []() {
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes are done
-        __builtin_amdgcn_s_barrier();
+        for (int u = 0; u < 3; ++u) *reinterpret_cast<u32x4 *>(dst + q_tok[u] * kTokStride + q_off[u]) = tl.v[u];
+        lds_order();
     };
 
-    float m_run[HS], l_lane[HS];
-    f32x4 oacc[HS][8], zacc[HS];
+    // running state, per lane = (token n, head kb of each set)
+    float m_run[HS], l_lane[HS], zl[HS][4];
+    f32x4 oacc[HS][8];    // PV output: lane (n, kb) rows (g = kb, h = i), channel 8 n + jj
 #pragma unroll
     for (int hs = 0; hs < HS; ++hs) {
         m_run[hs] = -INFINITY;
         l_lane[hs] = 0.0f;
-        zacc[hs] = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int g = 0; g < 4; ++g) zl[hs][g] = 0.0f;
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) oacc[hs][jj] = f32x4{0, 0, 0, 0};
     }
 
-    // prologue: tile 0 into stage 0, tile 1 in flight, slots of tile 2 loaded
-    const int s0 = tile_slot(0);
-    const int s1 = tile_slot(1);
-    issue(s0, tile_mask(0));
-    uint32_t mask_cur = valid_mask(s0, tile_mask(0));
-    stash(0);
-    barrier();
-    int s_far = tile_slot(2);
-    issue(s1, tile_mask(1));
-    uint32_t mask_next = valid_mask(s1, tile_mask(1));
-
-    for (int it = 0; it < n_tiles; ++it) {
-        if (it > 0) {
-            // tile it arrived in registers one iteration ago: put it in LDS,
-            // then start loading tile it + 1 (slot ids first, record loads last,
-            // so that the record loads stay outstanding through the compute)
-            stash(it & 1);
-            barrier();
-            const int s_new = tile_slot(it + 2);
-            issue(s_far, tile_mask(it + 1));
-            mask_cur = mask_next;
-            mask_next = valid_mask(s_far, tile_mask(it + 1));
-            s_far = s_new;
-        }
-        if (!active) continue;
-        const uint8_t *stage = smem + (it & 1) * stage_bytes + w * kHeadRecord;
-
-        // ---- QK
-        float lg[HS][8];      // logits of tokens 4 kb + i (i < 4) and 16 + 4 kb + i
+    // one tile: QK, online softmax, PV (reads LDS stage `stage`)
+    auto compute = [&](int stage, uint32_t mask) {
+        const uint8_t *st = wlds + stage * kStageBytes;
+        // ---- QK: logit of (token 16 hf + n, head 4 hs + kb)
+        float lg[HS][2];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-            const u32x2 kc = *reinterpret_cast<const u32x2 *>(stage + (16 * hf + n) * ts + 8 * kb);
+            const uint8_t *row = st + (16 * hf + n) * kTokStride;
+            const u32x2 kc = *reinterpret_cast<const u32x2 *>(row + 8 * kb);
+            const u32x4 szk = *reinterpret_cast<const u32x4 *>(row + 2 * kCodeBytes);
             const uint32_t d0s = kc[0] >> 6, d1s = kc[1] >> 6;
-            f16x8 A[4];
+            f16x8 B[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const uint32_t d = r < 2 ? kc[0] : kc[1];
                 const uint32_t ds = r < 2 ? d0s : d1s;
-                A[r] = u4_as_h8(code_bits(d, ds, 4 * (r & 1) + 0), code_bits(d, ds, 4 * (r & 1) + 1),
+                B[r] = u4_as_h8(code_bits(d, ds, 4 * (r & 1) + 0), code_bits(d, ds, 4 * (r & 1) + 1),
                                 code_bits(d, ds, 4 * (r & 1) + 2), code_bits(d, ds, 4 * (r & 1) + 3));
             }
-            // (s, z) of the output lane's 4 tokens for group cg
-            uint32_t szk[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                szk[i] = *reinterpret_cast<const uint32_t *>(stage + (16 * hf + 4 * kb + i) * ts +
-                                                            2 * kCodeBytes + 4 * cg);
+            const bool live = (mask >> (16 * hf + n)) & 1u;
 #pragma unroll
             for (int hs = 0; hs < HS; ++hs) {
                 f32x4 acc = f32x4{0, 0, 0, 0};
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    acc = mfma_f16(A[r], qB[hs][r][0], acc);
-                    acc = mfma_f16(A[r], qB[hs][r][1], acc);
+                    acc = mfma_f16(qA[hs][r][0], B[r], acc);
+                    acc = mfma_f16(qA[hs][r][1], B[r], acc);
                 }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float sf = __half2float(__ushort_as_half(uint16_t(szk[i] & 0xFFFFu)));
-                    const float zf = __half2float(__ushort_as_half(uint16_t(szk[i] >> 16)));
-                    float x = fmaf(acc[i], sf, zf * qz[hs]);
-                    x = dpp_ror8_add(dpp_ror4_add(x));          // sum over the 4 groups
-                    const bool ok = (mask_cur >> (16 * hf + 4 * kb + i)) & 1u;
-                    lg[hs][4 * hf + i] = ok ? x * qout[hs] : -INFINITY;
-                }
+                // acc[g] = group g's dot product; s_g, z_g are halves of szk[g]
+                float xa = fmaf(acc[0], half_lo(szk[0]), half_hi(szk[0]) * qz[hs][0]);
+                float xb = fmaf(acc[2], half_lo(szk[2]), half_hi(szk[2]) * qz[hs][2]);
+                xa = fmaf(half_hi(szk[1]), qz[hs][1], fmaf(acc[1], half_lo(szk[1]), xa));
+                xb = fmaf(half_hi(szk[3]), qz[hs][3], fmaf(acc[3], half_lo(szk[3]), xb));
+                lg[hs][hf] = fmaf(xa + xb, qout[hs], live ? 0.0f : -INFINITY);
             }
         }
-
-        // ---- online softmax and PV A operands
-        // (s, z) of V for group cg and the 8 tokens of this lane
-        uint32_t szv[8], vw[8];
+        // ---- online softmax; PV weights to LDS
+        bool grow[HS];
+        float alpha[HS];
+        u32x4 szv[2];
 #pragma unroll
-        for (int sidx = 0; sidx < 8; ++sidx) {
-            const int tt = sidx < 4 ? 4 * kb + sidx : 16 + 4 * kb + (sidx - 4);
-            const uint8_t *row = stage + tt * ts;
-            szv[sidx] = *reinterpret_cast<const uint32_t *>(row + 2 * kCodeBytes + kSzBytes + 4 * cg);
-            vw[sidx] = *reinterpret_cast<const uint16_t *>(row + kCodeBytes + 2 * n);
-        }
-        f16x8 AS[HS][2], AZ[HS][2];
+        for (int hf = 0; hf < 2; ++hf)
+            szv[hf] = *reinterpret_cast<const u32x4 *>(st + (16 * hf + n) * kTokStride + 2 * kCodeBytes + kSzBytes);
 #pragma unroll
         for (int hs = 0; hs < HS; ++hs) {
-            float mx = lg[hs][0];
-#pragma unroll
-            for (int i = 1; i < 8; ++i) mx = fmaxf(mx, lg[hs][i]);
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mx = row16_max(fmaxf(lg[hs][0], lg[hs][1]));
             const float m_new = fmaxf(m_run[hs], mx);
-            if (__any(m_new > m_run[hs])) {
-                const float alpha = (m_new > m_run[hs]) ? __builtin_amdgcn_exp2f(m_run[hs] - m_new) : 1.0f;
-                l_lane[hs] *= alpha;
-                // PV output row (g, h) = (kb, i): alpha of head i lives in lane i
+            grow[hs] = __any(m_new > m_run[hs]);
+            if (__builtin_expect(grow[hs], 0)) {
+                alpha[hs] = (m_new > m_run[hs]) ? __builtin_amdgcn_exp2f(m_run[hs] - m_new) : 1.0f;
+                l_lane[hs] *= alpha[hs];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float ai = __builtin_bit_cast(
-                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), i));
-#pragma unroll
-                    for (int jj = 0; jj < 8; ++jj) oacc[hs][jj][i] *= ai;
-                    zacc[hs][i] *= ai;
-                }
+                for (int g = 0; g < 4; ++g) zl[hs][g] *= alpha[hs];
                 m_run[hs] = m_new;
             }
-            uint32_t wsh[4], wsl[4], wzh[4], wzl[4];
+            // exponent reference: a finite stand-in while every token so far is masked
+            const float m_ref = m_run[hs] == -INFINITY ? 0.0f : m_run[hs];
+            uint8_t *wrow = wbuf + hs * kWSetBytes + kb * kWRow;   // row (g = 0, h = kb)
 #pragma unroll
-            for (int pp = 0; pp < 4; ++pp) {
-                float pr[2], ps[2];
+            for (int hf = 0; hf < 2; ++hf) {
+                const float p = __builtin_amdgcn_exp2f(lg[hs][hf] - m_ref);   // 0 for masked tokens
+                l_lane[hs] += p;
 #pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const float x = lg[hs][2 * pp + e];
-                    const float p = (x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x - m_run[hs]);
-                    l_lane[hs] += p;
-                    pr[e] = p;
-                    ps[e] = p * __half2float(__ushort_as_half(uint16_t(szv[2 * pp + e] & 0xFFFFu)));
+                for (int g = 0; g < 4; ++g) zl[hs][g] = fmaf(p, half_hi(szv[hf][g]), zl[hs][g]);
+                // w_g = p s_g as hi + lo fp16 parts; lo = w_g - hi exactly rounded
+                uint32_t hw[2], lw[2];
+#pragma unroll
+                for (int q2 = 0; q2 < 2; ++q2) {
+                    const float s0 = half_lo(szv[hf][2 * q2]), s1 = half_lo(szv[hf][2 * q2 + 1]);
+                    hw[q2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(fmaf(p, s0, 0.0f), fmaf(p, s1, 0.0f)));
+                    lw[q2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(fmaf(p, s0, -half_lo(hw[q2])),
+                                                                                     fmaf(p, s1, -half_hi(hw[q2]))));
                 }
-                wsh[pp] = pack_h2(ps[0], ps[1]);
-                wzh[pp] = pack_h2(pr[0], pr[1]);
-                const float sh0 = __half2float(__ushort_as_half(uint16_t(wsh[pp] & 0xFFFFu)));
-                const float sh1 = __half2float(__ushort_as_half(uint16_t(wsh[pp] >> 16)));
-                const float zh0 = __half2float(__ushort_as_half(uint16_t(wzh[pp] & 0xFFFFu)));
-                const float zh1 = __half2float(__ushort_as_half(uint16_t(wzh[pp] >> 16)));
-                wsl[pp] = pack_h2(ps[0] - sh0, ps[1] - sh1);
-                wzl[pp] = pack_h2(pr[0] - zh0, pr[1] - zh1);
+                const int tcol = 2 * (16 * hf + n);
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int sh = 16 * (g & 1);
+                    *reinterpret_cast<uint16_t *>(wrow + 4 * g * kWRow + tcol) = uint16_t(hw[g >> 1] >> sh);
+                    *reinterpret_cast<uint16_t *>(wrow + 4 * g * kWRow + 2 * kTileTokens + tcol) =
+                        uint16_t(lw[g >> 1] >> sh);
+                }
             }
-            AS[hs][0] = u4_as_h8(wsh[0], wsh[1], wsh[2], wsh[3]);
-            AS[hs][1] = u4_as_h8(wsl[0], wsl[1], wsl[2], wsl[3]);
-            AZ[hs][0] = u4_as_h8(wzh[0], wzh[1], wzh[2], wzh[3]);
-            AZ[hs][1] = u4_as_h8(wzl[0], wzl[1], wzl[2], wzl[3]);
         }
-
-        // ---- PV: B = V codes of channel 8 n + jj for the lane's 8 tokens
+        lds_order();
+        // ---- PV: A rows (g, h) = weights of tokens 8 kb .. 8 kb + 7; B = V codes
+        // of channel 8 n + jj for the same tokens
         uint32_t xw[4], xs[4];
 #pragma unroll
         for (int pp = 0; pp < 4; ++pp) {
-            xw[pp] = vw[2 * pp] | (vw[2 * pp + 1] << 16);
+            const uint8_t *r0 = st + (8 * kb + 2 * pp) * kTokStride + kCodeBytes + 2 * n;
+            xw[pp] = uint32_t(*reinterpret_cast<const uint16_t *>(r0)) |
+                     (uint32_t(*reinterpret_cast<const uint16_t *>(r0 + kTokStride)) << 16);
             xs[pp] = xw[pp] >> 6;
         }
-        const f16x8 BZ = u4_as_h8((szv[0] >> 16) | (szv[1] & 0xFFFF0000u), (szv[2] >> 16) | (szv[3] & 0xFFFF0000u),
-                                  (szv[4] >> 16) | (szv[5] & 0xFFFF0000u), (szv[6] >> 16) | (szv[7] & 0xFFFF0000u));
+        // rescale the output rows of heads whose running max grew; PV output
+        // row (g, h) = (kb, i): the factor of head i lives in row i of lanes
+#pragma unroll
+        for (int hs = 0; hs < HS; ++hs) {
+            if (__builtin_expect(grow[hs], 0)) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float ai = __builtin_bit_cast(
+                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha[hs]), 16 * i));
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj) oacc[hs][jj][i] *= ai;
+                }
+            }
+        }
+        f16x8 AS[HS][2];
+#pragma unroll
+        for (int hs = 0; hs < HS; ++hs) {
+            const uint8_t *arow = wbuf + hs * kWSetBytes + n * kWRow + 16 * kb;
+            AS[hs][0] = *reinterpret_cast<const f16x8 *>(arow);
+            AS[hs][1] = *reinterpret_cast<const f16x8 *>(arow + 2 * kTileTokens);
+        }
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
             const f16x8 Bj = u4_as_h8(code_bits(xw[0], xs[0], jj), code_bits(xw[1], xs[1], jj),
@@ -456,35 +477,85 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, in
                 oacc[hs][jj] = mfma_f16(AS[hs][1], Bj, oacc[hs][jj]);
             }
         }
-#pragma unroll
-        for (int hs = 0; hs < HS; ++hs) {
-            zacc[hs] = mfma_f16(AZ[hs][0], BZ, zacc[hs]);
-            zacc[hs] = mfma_f16(AZ[hs][1], BZ, zacc[hs]);
-        }
+        lds_order();
+    };
+
+    // ---- pipeline.  At the top of the loop body: LDS stage 0 holds tile t,
+    // tl[1] (tile t + 1) and tl[0] (tile t + 2) are in flight, v_cur holds
+    // the usable positions of tiles t + 2 and t + 3, sl_hi the slots of tile
+    // t + 3, and the slots of tiles t + 4 and t + 5 are loading into s_next.
+    // Each slot load is issued before the record loads of its step, and the
+    // pending slot register is dead before the next one is loaded, so every
+    // wait below leaves the younger tile in flight.  An odd tile count runs
+    // one more, fully masked tile: the loop body is straight-line code.
+    Tile tl[2];
+    int sl_lo[3], sl_hi[3];
+    uint32_t m0, m1;   // usable positions of tiles t and t + 1
+    int s_next;
+    uint64_t v_cur;
+    {
+        const int s01 = pair_slots(0);
+        const int s23 = pair_slots(2);
+        const uint64_t v01 = pair_valid(s01, 0);
+        m0 = uint32_t(v01);
+        m1 = uint32_t(v01 >> 32);
+        piece_slots(s01, 0, sl_lo);
+        issue(tl[0], sl_lo, m0);
+        piece_slots(s01, 1, sl_hi);
+        issue(tl[1], sl_hi, m1);
+        s_next = pair_slots(4);
+        v_cur = pair_valid(s23, 2);
+        piece_slots(s23, 0, sl_lo);
+        piece_slots(s23, 1, sl_hi);
     }
-    if (!active) return;
+    stash(tl[0], 0);
+    issue(tl[0], sl_lo, uint32_t(v_cur));
+    for (int t = 0; t < n_tiles; t += 2) {
+        compute(0, m0);
+        stash(tl[1], 1);
+        issue(tl[1], sl_hi, uint32_t(v_cur >> 32));                 // tile t + 3
+        compute(1, m1);
+        const uint64_t v_next = pair_valid(s_next, t + 4);
+        piece_slots(s_next, 0, sl_lo);
+        piece_slots(s_next, 1, sl_hi);
+        s_next = pair_slots(t + 6);
+        stash(tl[0], 0);
+        issue(tl[0], sl_lo, uint32_t(v_next));                      // tile t + 4
+        m0 = uint32_t(v_cur);
+        m1 = uint32_t(v_cur >> 32);
+        v_cur = v_next;
+    }
 
     // ---- write the partial (m, l, o') of the GQ heads
     const size_t row0 = (size_t(b) * a.items + j) * a.hq + hk * GQ;
+    const int cg = n >> 2;                    // group of output channels 8 n .. 8 n + 7
 #pragma unroll
     for (int hs = 0; hs < HS; ++hs) {
-        float l_col = l_lane[hs] + __shfl_xor(l_lane[hs], 16);
-        l_col += __shfl_xor(l_col, 32);
-        const int h = 4 * hs + ch;
-        if (kb == 0 && cg == 0 && h < GQ) {
-            a.part_ml[(row0 + h) * 2 + 0] = m_run[hs];
-            a.part_ml[(row0 + h) * 2 + 1] = l_col;
-        }
-        // output lane (n, kb) holds rows (g = kb, h = i); the row whose group
-        // matches channel 8 n + jj (group n / 4) carries the result
-        if (kb == cg) {
+        const float l_row = row16_sum(l_lane[hs]);
+        float zt[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (4 * hs + i >= GQ) break;
+        for (int g = 0; g < 4; ++g) zt[g] = row16_sum(zl[hs][g]);
+        if (n == 0 && 4 * hs + kb < GQ) {
+            a.part_ml[(row0 + 4 * hs + kb) * 2 + 0] = m_run[hs];
+            a.part_ml[(row0 + 4 * hs + kb) * 2 + 1] = l_row;
+        }
+        // lane (n, kb) holds rows (g = kb, h = i); the row whose group matches
+        // channel 8 n + jj (group n / 4) carries the result
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (4 * hs + i >= GQ) break;
+            // p z summed over the item for head i, group cg (held by row i of lanes)
+            float z = 0.0f;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float zi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, zt[g]), 16 * i));
+                z = g == cg ? zi : z;
+            }
+            if (kb == cg) {
                 float o[8];
 #pragma unroll
                 for (int jj = 0; jj < 8; ++jj)
-                    o[jj] = oacc[hs][jj][i] * __builtin_ldexpf(1.0f, 24 - pair_exp(jj)) + zacc[hs][i];
+                    o[jj] = oacc[hs][jj][i] * __builtin_ldexpf(1.0f, 24 - pair_exp(jj)) + z;
                 float *dst = a.part_o + (row0 + 4 * hs + i) * kHeadDim + 8 * n;
                 *reinterpret_cast<f32x4 *>(dst) = f32x4{o[0], o[1], o[2], o[3]};
                 *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
@@ -597,7 +668,7 @@ __device__ void bf16_item(const DecodeArgs &a, int b, int req, int j, int hk, in
 }
 
 template <int GQ>
-__global__ __launch_bounds__(512) void partial_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kPartialWaves) void partial_kernel(DecodeArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int id = blockIdx.x;
     const int hc = id % a.head_chunks;
@@ -615,40 +686,48 @@ __global__ __launch_bounds__(512) void partial_kernel(DecodeArgs a) {
     if (j < 2) {
         float *pbuf = reinterpret_cast<float *>(smem) + w * (kMaxGroup * kBf16Chunk);
         bf16_item(a, b, req, j, active ? hk : 0, p0, p1, active, pbuf);
-    } else if (a.num_slots > 0) {
-        int2_item<GQ>(a, b, req, j, hc, p0, p1, smem);
+    } else if (a.num_slots > 0 && active) {
+        int2_item<GQ>(a, b, req, j, hk, p0, p1, smem + w * wave_lds_bytes(GQ));
     }
 }
 
 // ---------------------------------------------------------------------------
 // 3. merge + un-rotation
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(128) void merge_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(512) void merge_kernel(DecodeArgs a) {
     __shared__ float ob[kMaxGroup][kHeadDim];
     const int b = blockIdx.x / a.hkv;
     const int hk = blockIdx.x % a.hkv;
-    const int c = threadIdx.x;
+    const int t = threadIdx.x;
+    const int c = t & (kHeadDim - 1);
     int req = 0;
     const int L = request_length(a, b, req);
-    for (int h = 0; h < a.g; ++h) {
+    // items that exist for this request (the same ranges as the partial kernel)
+    int n_items = 0;
+    for (int j = 0; j < a.items; ++j) {
+        int p0, p1;
+        item_range(a, L, j, p0, p1);
+        if (p0 < p1) n_items = j + 1;
+    }
+    for (int h = t >> 7; h < a.g; h += 4) {
         const size_t head = size_t(hk) * a.g + h;
+        const size_t base = size_t(b) * a.items * a.hq + head;   // row of item 0
         float M = -INFINITY;
-        for (int j = 0; j < a.items; ++j) {
+        for (int j = 0; j < n_items; ++j) {
             int p0, p1;
             item_range(a, L, j, p0, p1);
-            if (p0 >= p1) continue;
-            M = fmaxf(M, a.part_ml[((size_t(b) * a.items + j) * a.hq + head) * 2]);
+            if (p0 < p1) M = fmaxf(M, a.part_ml[(base + size_t(j) * a.hq) * 2]);
         }
         float acc = 0.0f, l = 0.0f;
         if (M != -INFINITY) {
-            for (int j = 0; j < a.items; ++j) {
+#pragma unroll 4
+            for (int j = 0; j < n_items; ++j) {
                 int p0, p1;
                 item_range(a, L, j, p0, p1);
                 if (p0 >= p1) continue;
-                const size_t row = (size_t(b) * a.items + j) * a.hq + head;
+                const size_t row = base + size_t(j) * a.hq;
                 const float m = a.part_ml[row * 2];
-                if (m == -INFINITY) continue;
-                const float wgt = __builtin_amdgcn_exp2f(m - M);
+                const float wgt = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
                 l = fmaf(wgt, a.part_ml[row * 2 + 1], l);
                 acc = fmaf(wgt, a.part_o[row * kHeadDim + c], acc);
             }
@@ -656,38 +735,33 @@ __global__ __launch_bounds__(128) void merge_kernel(DecodeArgs a) {
         ob[h][c] = l > 0.0f ? acc / l : 0.0f;
     }
     __syncthreads();
-    // o[c] = sum_i o'[i] R_V[c][i]
+    // o[h][c] = sum_i o'[h][i] R_V[c][i]
     const float *R = a.r_v + (size_t(hk) * kHeadDim + c) * kHeadDim;
-    float o[kMaxGroup];
-#pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h) o[h] = 0.0f;
-    for (int i = 0; i < kHeadDim; i += 4) {
-        const f32x4 r = *reinterpret_cast<const f32x4 *>(R + i);
-#pragma unroll
-        for (int h = 0; h < kMaxGroup; ++h) {
-            if (h < a.g) {
-                o[h] = fmaf(ob[h][i], r[0], o[h]);
-                o[h] = fmaf(ob[h][i + 1], r[1], o[h]);
-                o[h] = fmaf(ob[h][i + 2], r[2], o[h]);
-                o[h] = fmaf(ob[h][i + 3], r[3], o[h]);
-            }
+    for (int h = t >> 7; h < a.g; h += 4) {
+        float o = 0.0f;
+#pragma unroll 8
+        for (int i = 0; i < kHeadDim; i += 4) {
+            const f32x4 r = *reinterpret_cast<const f32x4 *>(R + i);
+            o = fmaf(ob[h][i], r[0], o);
+            o = fmaf(ob[h][i + 1], r[1], o);
+            o = fmaf(ob[h][i + 2], r[2], o);
+            o = fmaf(ob[h][i + 3], r[3], o);
         }
-    }
-    for (int h = 0; h < a.g; ++h) {
         const size_t idx = (size_t(b) * a.hq + hk * a.g + h) * kHeadDim + c;
         if (a.out_dtype == OSCAR_F32)
-            static_cast<float *>(a.out)[idx] = o[h];
+            static_cast<float *>(a.out)[idx] = o;
         else if (a.out_dtype == OSCAR_BF16)
-            static_cast<uint16_t *>(a.out)[idx] = bf16_bits_rn(o[h]);
+            static_cast<uint16_t *>(a.out)[idx] = bf16_bits_rn(o);
         else
-            static_cast<uint16_t *>(a.out)[idx] = __half_as_ushort(__float2half_rn(o[h]));
+            static_cast<uint16_t *>(a.out)[idx] = __half_as_ushort(__float2half_rn(o));
     }
 }
 
-// Dynamic LDS of the partial kernel: two stages of 32 padded token records
-// for the INT2 items, or the per-wave softmax buffers of the BF16 items.
+// Dynamic LDS of the partial kernel: each wave's two-stage ring of 32 padded
+// token records and PV weight rows for the INT2 items, or its softmax buffer
+// for the BF16 items.
 size_t partial_lds_bytes(const DecodeArgs &a) {
-    const size_t stages = 2 * size_t(kTileTokens) * (size_t(a.waves) * kHeadRecord + 16);
+    const size_t stages = size_t(a.waves) * wave_lds_bytes(a.g);
     const size_t pbuf = size_t(a.waves) * kMaxGroup * kBf16Chunk * sizeof(float);
     return stages > pbuf ? stages : pbuf;
 }
@@ -748,6 +822,7 @@ extern "C" oscar_status oscar_decode_attn(hipStream_t stream, const oscar_layout
     a.qsum = reinterpret_cast<float *>(ws + plan.ws_qsum);
     a.part_o = reinterpret_cast<float *>(ws + plan.ws_part_o);
     a.part_ml = reinterpret_cast<float *>(ws + plan.ws_part_ml);
+    a.zero_rec = ws + plan.ws_zero;
     a.r2s_stride = req_to_slot_stride;
     a.num_slots = layout->num_slots;
     a.scale_log2 = sm_scale * kLog2e;
@@ -762,10 +837,10 @@ extern "C" oscar_status oscar_decode_attn(hipStream_t stream, const oscar_layout
     a.max_requests = layout->max_requests;
     a.chunk = plan.chunk;
     a.items = plan.items;
-    a.waves = a.hkv < 8 ? a.hkv : 8;
+    a.waves = a.hkv < kPartialWaves ? a.hkv : kPartialWaves;
     a.head_chunks = (a.hkv + a.waves - 1) / a.waves;
 
-    hipLaunchKernelGGL(prep_kernel, dim3(batch * a.hkv), dim3(128), 0, stream, a);
+    hipLaunchKernelGGL(prep_kernel, dim3(batch * a.hkv), dim3(512), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(OSCAR_ERR_HIP, std::string("prep launch: ") + hipGetErrorString(e));
 
@@ -786,7 +861,7 @@ extern "C" oscar_status oscar_decode_attn(hipStream_t stream, const oscar_layout
     if (opts && opts->kernel_end && hipEventRecord(opts->kernel_end, stream) != hipSuccess)
         return fail(OSCAR_ERR_HIP, "hipEventRecord failed");
 
-    hipLaunchKernelGGL(merge_kernel, dim3(batch * a.hkv), dim3(128), 0, stream, a);
+    hipLaunchKernelGGL(merge_kernel, dim3(batch * a.hkv), dim3(512), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(OSCAR_ERR_HIP, std::string("merge launch: ") + hipGetErrorString(e));
     return OSCAR_OK;

@@ -38,6 +38,7 @@ struct DecodePlan {
     size_t ws_qsum = 0;
     size_t ws_part_o = 0;
     size_t ws_part_ml = 0;
+    size_t ws_zero = 0;          // 256 bytes the decode clears: stand-in record of unusable tokens
     size_t ws_bytes = 0;
 };
 

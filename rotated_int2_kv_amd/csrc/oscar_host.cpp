@@ -91,6 +91,8 @@ oscar_status make_decode_plan(const oscar_layout &lay, int32_t batch,
     off += align(size_t(batch) * items * hq * kHeadDim * sizeof(float));
     plan->ws_part_ml = off;
     off += align(size_t(batch) * items * hq * 2 * sizeof(float));
+    plan->ws_zero = off;
+    off += 256;
     plan->ws_bytes = off;
     return OSCAR_OK;
 }

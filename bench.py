@@ -18,8 +18,10 @@ sample of the same decode workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -33,10 +35,40 @@ HBM_PEAK_GBS = 8000.0
 HISTORY_BYTES_PER_TOKEN_HEAD = 96      # K codes 32 + V codes 32 + K (s,z) 16 + V (s,z) 16
 SLOT_BYTES_PER_TOKEN = 4
 BF16_BYTES_PER_TOKEN_HEAD = 512        # K and V, 128 bf16 each
+# HBM byte counters of the split-K kernel, taken with rocprofv3 on this workload
+# (FETCH_SIZE and WRITE_SIZE, scaled by a plain-copy calibration); valid only
+# while the kernel's sources hash to the value recorded with them
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "partial_kernel_decode_b32_hbm_bytes.md")
+KERNEL_SOURCES = ("rotated_int2_kv_amd/csrc/decode_attn.hip", "rotated_int2_kv_amd/csrc/common.cuh",
+                  "rotated_int2_kv_amd/csrc/internal.h", "rotated_int2_kv_amd/build.py")
+CPU_BASELINE_SECONDS = 10.0
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    """sha256 over the sources and build flags the split-K kernel is compiled from."""
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter summary, or None if the
+    kernel has changed since the counters were taken."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    sha = re.search(r"^source_sha256:\s*([0-9a-f]{64})", text, re.M)
+    val = re.search(r"^traffic_bytes_per_launch:\s*([0-9]+)", text, re.M)
+    if not sha or not val or sha.group(1) != kernel_source_hash():
+        return None
+    return int(val.group(1))
 
 
 def decode_kernel_bytes(lens, hkv, sink=64, recent=256):
@@ -204,10 +236,11 @@ def cpu_baseline(workloads):
         cache.append(pool, lay, k, v, np.zeros(L, int), np.arange(L), slots, [L], rk, rv)
         del k, v
         q = quant.bf16_round(workloads.queries(w, n_rows=1, stream=7))
-        reps = 2
+        reps = 0
         t0 = time.perf_counter()
-        for _ in range(reps):
+        while reps < 1 or time.perf_counter() - t0 < CPU_BASELINE_SECONDS:
             attention.decode(pool, lay, q, [0], [L], slots[None, :], rk, rv, 128 ** -0.5)
+            reps += 1
         dt = time.perf_counter() - t0
     return {"value": reps * L / dt, "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{reps} decode steps of one request of the decode_b32 workload (L = {L}, "
@@ -276,7 +309,7 @@ def main():
                    "step": "oscar_quant_append(1 new token per request) + oscar_decode_attn",
                    "history_chunk": d["chunk"], "items_per_request": d["items"]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": "partial_kernel (split-K)", "kernel_ms": d["kern_ms"],
                      "algorithmic_bytes": d["kbytes"]},
         "decode_steps_per_s": 1e3 / ms,

@@ -99,53 +99,63 @@ __device__ __forceinline__ float load_as_f32(const void *p, int dtype, size_t id
 // ---------------------------------------------------------------------------
 // 1. query rotation
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
 __global__ __launch_bounds__(512) void prep_kernel(DecodeArgs a) {
     __shared__ float qs[kMaxGroup][kHeadDim];
     __shared__ float part[4][kMaxGroup][kHeadDim];
+    __shared__ float half_max[kMaxGroup][2];
     const int b = blockIdx.x / a.hkv;
     const int hk = blockIdx.x % a.hkv;
     const int t = threadIdx.x;
     const int c = t & (kHeadDim - 1);        // output channel
     const int quarter = t >> 7;               // input channels [32 quarter, 32 quarter + 32)
     if (blockIdx.x == 0 && t < 64) reinterpret_cast<uint32_t *>(a.zero_rec)[t] = 0u;
+    // this thread's slice of column c of R_K, all loads in flight at once
+    const float *R = a.r_k + size_t(hk) * kHeadDim * kHeadDim;
+    float r[kHeadDim / 4];
+#pragma unroll
+    for (int ii = 0; ii < kHeadDim / 4; ++ii) r[ii] = R[size_t(quarter * (kHeadDim / 4) + ii) * kHeadDim + c];
     for (int e = t; e < a.g * kHeadDim; e += 512) {
         const int h = e / kHeadDim, i = e % kHeadDim;
         qs[h][i] = load_as_f32(a.q, a.q_dtype, (size_t(b) * a.hq + hk * a.g + h) * kHeadDim + i);
     }
     __syncthreads();
-    const float *R = a.r_k + size_t(hk) * kHeadDim * kHeadDim;
-    float acc[kMaxGroup];
+    for (int h = 0; h < a.g; ++h) {
+        float acc = 0.0f;
 #pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h) acc[h] = 0.0f;
-#pragma unroll 8
-    for (int ii = 0; ii < kHeadDim / 4; ++ii) {
-        const int i = quarter * (kHeadDim / 4) + ii;
-        const float r = R[size_t(i) * kHeadDim + c];
-#pragma unroll
-        for (int h = 0; h < kMaxGroup; ++h)
-            if (h < a.g) acc[h] = fmaf(qs[h][i], r, acc[h]);
-    }
-    for (int h = 0; h < a.g; ++h) part[quarter][h][c] = acc[h];
-    __syncthreads();
-    for (int e = t; e < a.g * kHeadDim; e += 512) {
-        const int h = e / kHeadDim, cc = e % kHeadDim;
-        const float v = (part[0][h][cc] + part[1][h][cc] + part[2][h][cc] + part[3][h][cc]) * a.scale_log2;
-        qs[h][cc] = v;
-        a.qrot[(size_t(b) * a.hq + hk * a.g + h) * kHeadDim + cc] = v;
+        for (int ii = 0; ii < kHeadDim / 4; ++ii) acc = fmaf(qs[h][quarter * (kHeadDim / 4) + ii], r[ii], acc);
+        part[quarter][h][c] = acc;
     }
     __syncthreads();
-    if (t < a.g * kGroups) {
-        const int h = t / kGroups, grp = t % kGroups;
-        float sum = 0.0f;
-        for (int i = 0; i < kGroup; ++i) sum += qs[h][grp * kGroup + i];
-        a.qsum[(size_t(b) * a.hq + hk * a.g + h) * 8 + grp] = sum;
+    // the head index is uniform over each wave: 128 threads per head
+    for (int h = t >> 7; h < a.g; h += 4) {
+        const float v = (part[0][h][c] + part[1][h][c] + part[2][h][c] + part[3][h][c]) * a.scale_log2;
+        const size_t row = size_t(b) * a.hq + hk * a.g + h;
+        a.qrot[row * kHeadDim + c] = v;
+        // sum over the 32 channels of c's group (32 aligned lanes of the wave)
+        float gsum = v;
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1) gsum += __shfl_xor(gsum, off);
+        if ((c & (kGroup - 1)) == 0) a.qsum[row * 8 + c / kGroup] = gsum;
+        const float mx = wave_max(fabsf(v));
+        if ((t & 63) == 0) half_max[h][c >> 6] = mx;
     }
-    if (t >= 64 && t < 64 + a.g) {
+    __syncthreads();
+    if (t < a.g) {
         // power-of-two operand scale 2^K with max|q'| 2^K < 2^15, so that
         // q' 2^(K - e) (e = 0..8) fits fp16 and its low part stays normal
-        const int h = t - 64;
-        float mx = 0.0f;
-        for (int i = 0; i < kHeadDim; ++i) mx = fmaxf(mx, fabsf(qs[h][i]));
+        const int h = t;
+        const float mx = fmaxf(half_max[h][0], half_max[h][1]);
         int e = 0;
         frexpf(mx, &e);                          // mx < 2^e
         const int K = mx > 0.0f ? max(-20, min(24, 15 - e)) : 24;
@@ -209,11 +219,14 @@ __device__ __forceinline__ float half_hi(uint32_t w) { return __half2float(__ush
 // positions for all KV heads of the slot-major records, so together they read
 // whole cache lines, but each wave runs its own pipeline without barriers.
 //
-// Loads: per 32-token tile a wave reads its 96-byte head records with three
-// 16-byte loads per lane into registers and writes them into its own
-// two-stage LDS ring (112-byte token stride); two tiles are in flight while a
-// third is computed.  Tokens past the item or with an out-of-range slot are
-// zero-filled and masked out of the softmax.
+// Loads go straight from HBM into the wave's LDS (global_load_lds, no
+// registers in between).  Per 32-token tile a wave first fetches the 32 slot
+// ids (each twice, so that lane l holds the slot of token l / 2), then its
+// 96-byte head record of every token as three 16-byte pieces per lane: K codes,
+// V codes, (s, z).  A stage of three such 1 KiB planes is one tile; three
+// stages let two tiles be in flight while a third is computed.  Tokens past
+// the item or with an out-of-range slot read a zero record, so they arrive as
+// s = z = 0 and codes 0, and are masked out of the softmax.
 //
 // QK (per half of 16 tokens): B = the tokens' K codes as exact fp16 denormals
 // (one AND per pair, no scale); A = q' (hi and lo fp16 parts, times
@@ -225,12 +238,28 @@ __device__ __forceinline__ float half_hi(uint32_t w) { return __half2float(__ush
 // four groups and accumulates p z_g itself; the weights go through the
 // wave's LDS into rows (g, h) of A, B holds the V codes of 8 tokens per lane
 // as exact denormals, and the output of column (channel) c is read from the
-// row whose group is c's group.
-constexpr int kTokStride = kHeadRecord + 16;           // LDS bytes per token
-constexpr int kStageBytes = kTileTokens * kTokStride;  // one tile of one KV head
+// row whose group is c's group.  K-slot k of the PV products is token
+// 4 (k % 8) + k / 8, so that the four lane groups read V-code rows in
+// different LDS banks.
+constexpr int kPlane = kTileTokens * 32;               // 32 tokens x 32 bytes
+constexpr int kStage = 3 * kPlane;                     // K codes | V codes | (s, z)
+constexpr int kStages = 3;
+constexpr int kSlotRing = 4;                           // slot-id buffers of 64 entries
 constexpr int kWRow = 2 * kTileTokens * 2 + 16;        // weight row: hi and lo of 32 tokens, padded
 constexpr int kWSetBytes = 16 * kWRow;                 // rows (g, h) of one set of 4 heads
-__host__ __device__ constexpr int wave_lds_bytes(int gq) { return 2 * kStageBytes + ((gq + 3) / 4) * kWSetBytes; }
+__host__ __device__ constexpr int wave_lds_bytes(int gq) {
+    return kStages * kStage + kSlotRing * 256 + ((gq + 3) / 4) * kWSetBytes;
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Wait until at most N vector-memory operations of this wave are pending.
+// The compiler does not track global_load_lds, so the pipeline below waits
+// by hand; the memory clobber keeps LDS accesses on their side of the wait.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 template <int GQ>
 __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hk, int p0, int p1,
@@ -243,7 +272,8 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hk, in
     const uint8_t *gbase = a.records + hk * kHeadRecord;
     const int32_t *r2s = a.req_to_slot + int64_t(req) * a.r2s_stride;
     const int n_tiles = (p1 - p0 + kTileTokens - 1) / kTileTokens;
-    uint8_t *wbuf = wlds + 2 * kStageBytes;
+    uint8_t *ring = wlds + kStages * kStage;
+    uint8_t *wbuf = ring + kSlotRing * 256;
     const size_t head0 = size_t(b) * a.hq + size_t(hk) * GQ;
 
     // ---- per-item operands
@@ -286,57 +316,36 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hk, in
         }
     }
 
-    // ---- load pipeline.  Every load is unconditional (out-of-range
-    // positions and slots read a safe address and are zeroed at the stash), so
-    // each step issues a fixed sequence and the compiler's wait counts leave
-    // the younger tiles in flight.
-    int q_tok[3], q_off[3];                   // token and 16-byte piece of each load
-#pragma unroll
-    for (int u = 0; u < 3; ++u) {
-        const int q = u * 64 + lane;          // 192 pieces = 32 tokens x 6
-        q_tok[u] = q / 6;
-        q_off[u] = 16 * (q - 6 * q_tok[u]);
-    }
-    auto pair_slots = [&](int t) -> int {      // slots of tiles t and t + 1, a position per lane
-        const int pos = p0 + t * kTileTokens + lane;
-        return r2s[pos < p1 ? pos : p0];
+    // ---- loads.  Every tile issues the same four operations (one slot-id
+    // load, three record loads), including the tiles past the end, which read
+    // position p0 and the zero record: the wait counts below are constants.
+    // Order: S(T+1) comes right before R(T), so the stream is
+    //   S0 S1 R0 S2 R1 S3 R2 ...  (R = three operations)
+    auto slot_load = [&](int T) {
+        const int pos = p0 + T * kTileTokens + (lane >> 1);
+        const int32_t *src = r2s + (pos < p1 ? pos : p0);
+        __builtin_amdgcn_global_load_lds(src, (lds_void *)(ring + (T & (kSlotRing - 1)) * 256), 4, 0, 0);
     };
-    auto pair_valid = [&](int slot_reg, int t) -> uint64_t {   // usable positions of tiles t, t + 1
-        const int pos = p0 + t * kTileTokens + lane;
-        return __ballot(pos < p1 && slot_reg >= 0 && int64_t(slot_reg) < a.num_slots);
-    };
-    struct Tile {
-        u32x4 v[3];
-    };
-    // slots of the pieces a lane loads of tile `half` of a pair
-    auto piece_slots = [&](int slot_reg, int half, int (&sl)[3]) {
-#pragma unroll
-        for (int u = 0; u < 3; ++u) sl[u] = __shfl(slot_reg, q_tok[u] + kTileTokens * half);
-    };
-    // record loads of one tile; `valid` = its 32 usable positions.  Unusable
-    // tokens read the zero record, so they arrive as s = z = 0 and codes 0.
-    auto issue = [&](Tile &tl, const int (&sl)[3], uint32_t valid) {
-#pragma unroll
-        for (int u = 0; u < 3; ++u) {
-            const bool ok = (valid >> q_tok[u]) & 1u;
-            const uint8_t *src = gbase + uint64_t(uint32_t(sl[u])) * rec_bytes;
-            asm volatile("" : "+v"(src));     // computed on every lane: a select, not a branch
-            src = ok ? src : a.zero_rec;
-            tl.v[u] = *reinterpret_cast<const u32x4 *>(src + q_off[u]);
-        }
+    // record loads of tile T into stage `stage`; returns the ballot of the
+    // usable tokens (bit 2 i for token i)
+    auto record_load = [&](int T, int stage) -> uint64_t {
+        const int slot = *reinterpret_cast<const int *>(ring + (T & (kSlotRing - 1)) * 256 + 4 * lane);
+        const int pos = p0 + T * kTileTokens + (lane >> 1);
+        const bool ok = pos < p1 && slot >= 0 && int64_t(slot) < a.num_slots;
+        const uint8_t *src = gbase + uint64_t(uint32_t(slot)) * rec_bytes;
+        asm volatile("" : "+v"(src));         // computed on every lane: a select, not a branch
+        src = (ok ? src : a.zero_rec) + 16 * (lane & 1);
+        uint8_t *st = wlds + stage * kStage;
+        __builtin_amdgcn_global_load_lds(src, (lds_void *)st, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(src + kCodeBytes, (lds_void *)(st + kPlane), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(src + 2 * kCodeBytes, (lds_void *)(st + 2 * kPlane), 16, 0, 0);
+        return __ballot(ok);
     };
     // LDS is used by this wave alone and runs a wave's operations in order;
     // the fences keep the compiler from moving LDS accesses across them
     auto lds_order = [] {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    };
-    auto stash = [&](const Tile &tl, int stage) {
-        uint8_t *dst = wlds + stage * kStageBytes;
-        lds_order();
-#pragma unroll
-        for (int u = 0; u < 3; ++u) *reinterpret_cast<u32x4 *>(dst + q_tok[u] * kTokStride + q_off[u]) = tl.v[u];
-        lds_order();
     };
 
     // running state, per lane = (token n, head kb of each set)
@@ -352,16 +361,21 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hk, in
         for (int jj = 0; jj < 8; ++jj) oacc[hs][jj] = f32x4{0, 0, 0, 0};
     }
 
-    // one tile: QK, online softmax, PV (reads LDS stage `stage`)
-    auto compute = [&](int stage, uint32_t mask) {
-        const uint8_t *st = wlds + stage * kStageBytes;
+    // K-slot of token i in the PV products, and of this lane's two QK tokens
+    const int kcol0 = 8 * (n & 3) + (n >> 2);             // token n      (half 0)
+    const int kcol1 = 8 * (n & 3) + 4 + (n >> 2);         // token 16 + n (half 1)
+
+    // one tile: QK, online softmax, PV (reads LDS stage `st`)
+    auto compute = [&](const uint8_t *st, uint64_t valid) {
         // ---- QK: logit of (token 16 hf + n, head 4 hs + kb)
         float lg[HS][2];
+        u32x4 szv[2];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-            const uint8_t *row = st + (16 * hf + n) * kTokStride;
-            const u32x2 kc = *reinterpret_cast<const u32x2 *>(row + 8 * kb);
-            const u32x4 szk = *reinterpret_cast<const u32x4 *>(row + 2 * kCodeBytes);
+            const int tk = 16 * hf + n;
+            const u32x2 kc = *reinterpret_cast<const u32x2 *>(st + 32 * tk + 8 * kb);
+            const u32x4 szk = *reinterpret_cast<const u32x4 *>(st + 2 * kPlane + 32 * tk);
+            szv[hf] = *reinterpret_cast<const u32x4 *>(st + 2 * kPlane + 32 * tk + kSzBytes);
             const uint32_t d0s = kc[0] >> 6, d1s = kc[1] >> 6;
             f16x8 B[4];
 #pragma unroll
@@ -371,7 +385,7 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hk, in
                 B[r] = u4_as_h8(code_bits(d, ds, 4 * (r & 1) + 0), code_bits(d, ds, 4 * (r & 1) + 1),
                                 code_bits(d, ds, 4 * (r & 1) + 2), code_bits(d, ds, 4 * (r & 1) + 3));
             }
-            const bool live = (mask >> (16 * hf + n)) & 1u;
+            const bool live = (valid >> (2 * tk)) & 1u;
 #pragma unroll
             for (int hs = 0; hs < HS; ++hs) {
                 f32x4 acc = f32x4{0, 0, 0, 0};
@@ -391,10 +405,6 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hk, in
         // ---- online softmax; PV weights to LDS
         bool grow[HS];
         float alpha[HS];
-        u32x4 szv[2];
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-            szv[hf] = *reinterpret_cast<const u32x4 *>(st + (16 * hf + n) * kTokStride + 2 * kCodeBytes + kSzBytes);
 #pragma unroll
         for (int hs = 0; hs < HS; ++hs) {
             const float mx = row16_max(fmaxf(lg[hs][0], lg[hs][1]));
@@ -425,7 +435,7 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hk, in
                     lw[q2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(fmaf(p, s0, -half_lo(hw[q2])),
                                                                                      fmaf(p, s1, -half_hi(hw[q2]))));
                 }
-                const int tcol = 2 * (16 * hf + n);
+                const int tcol = 2 * (hf ? kcol1 : kcol0);
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int sh = 16 * (g & 1);
@@ -436,14 +446,15 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hk, in
             }
         }
         lds_order();
-        // ---- PV: A rows (g, h) = weights of tokens 8 kb .. 8 kb + 7; B = V codes
-        // of channel 8 n + jj for the same tokens
+        // ---- PV: A rows (g, h) = weights of K-slots 8 kb .. 8 kb + 7, i.e.
+        // tokens 4 c + kb (c = 0..7); B = V codes of channel 8 n + jj for the
+        // same tokens, two tokens per 32-bit word
         uint32_t xw[4], xs[4];
 #pragma unroll
         for (int pp = 0; pp < 4; ++pp) {
-            const uint8_t *r0 = st + (8 * kb + 2 * pp) * kTokStride + kCodeBytes + 2 * n;
+            const uint8_t *r0 = st + kPlane + 32 * (8 * pp + kb) + 2 * n;
             xw[pp] = uint32_t(*reinterpret_cast<const uint16_t *>(r0)) |
-                     (uint32_t(*reinterpret_cast<const uint16_t *>(r0 + kTokStride)) << 16);
+                     (uint32_t(*reinterpret_cast<const uint16_t *>(r0 + 32 * 4)) << 16);
             xs[pp] = xw[pp] >> 6;
         }
         // rescale the output rows of heads whose running max grew; PV output
@@ -480,51 +491,30 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hk, in
         lds_order();
     };
 
-    // ---- pipeline.  At the top of the loop body: LDS stage 0 holds tile t,
-    // tl[1] (tile t + 1) and tl[0] (tile t + 2) are in flight, v_cur holds
-    // the usable positions of tiles t + 2 and t + 3, sl_hi the slots of tile
-    // t + 3, and the slots of tiles t + 4 and t + 5 are loading into s_next.
-    // Each slot load is issued before the record loads of its step, and the
-    // pending slot register is dead before the next one is loaded, so every
-    // wait below leaves the younger tile in flight.  An odd tile count runs
-    // one more, fully masked tile: the loop body is straight-line code.
-    Tile tl[2];
-    int sl_lo[3], sl_hi[3];
-    uint32_t m0, m1;   // usable positions of tiles t and t + 1
-    int s_next;
-    uint64_t v_cur;
-    {
-        const int s01 = pair_slots(0);
-        const int s23 = pair_slots(2);
-        const uint64_t v01 = pair_valid(s01, 0);
-        m0 = uint32_t(v01);
-        m1 = uint32_t(v01 >> 32);
-        piece_slots(s01, 0, sl_lo);
-        issue(tl[0], sl_lo, m0);
-        piece_slots(s01, 1, sl_hi);
-        issue(tl[1], sl_hi, m1);
-        s_next = pair_slots(4);
-        v_cur = pair_valid(s23, 2);
-        piece_slots(s23, 0, sl_lo);
-        piece_slots(s23, 1, sl_hi);
+    // ---- pipeline.  Iteration t computes stage t % 3 while tiles t + 1 and
+    // t + 2 are in flight.  Before R(t + 2) is issued, S(t + 2) must have
+    // arrived: four operations follow it (R(t + 1) and S(t + 3)), and since
+    // R(t) precedes S(t + 2) that same wait also completes tile t.
+    slot_load(0);
+    slot_load(1);
+    wait_vmem<1>();
+    uint64_t v0 = record_load(0, 0);
+    slot_load(2);
+    wait_vmem<4>();
+    uint64_t v1 = record_load(1, 1);
+    int st_c = 0;                             // stage of tile t
+    for (int t = 0; t < n_tiles; ++t) {
+        slot_load(t + 3);
+        wait_vmem<4>();
+        const int st_n = st_c == 0 ? 2 * kStage : st_c - kStage;   // stage of tile t + 2
+        const uint64_t v2 = record_load(t + 2, st_n / kStage);
+        compute(wlds + st_c, v0);
+        v0 = v1;
+        v1 = v2;
+        st_c = st_c == 2 * kStage ? 0 : st_c + kStage;
     }
-    stash(tl[0], 0);
-    issue(tl[0], sl_lo, uint32_t(v_cur));
-    for (int t = 0; t < n_tiles; t += 2) {
-        compute(0, m0);
-        stash(tl[1], 1);
-        issue(tl[1], sl_hi, uint32_t(v_cur >> 32));                 // tile t + 3
-        compute(1, m1);
-        const uint64_t v_next = pair_valid(s_next, t + 4);
-        piece_slots(s_next, 0, sl_lo);
-        piece_slots(s_next, 1, sl_hi);
-        s_next = pair_slots(t + 6);
-        stash(tl[0], 0);
-        issue(tl[0], sl_lo, uint32_t(v_next));                      // tile t + 4
-        m0 = uint32_t(v_cur);
-        m1 = uint32_t(v_cur >> 32);
-        v_cur = v_next;
-    }
+    // the trailing (unused) loads still write this wave's LDS: let them land
+    wait_vmem<0>();
 
     // ---- write the partial (m, l, o') of the GQ heads
     const size_t row0 = (size_t(b) * a.items + j) * a.hq + hk * GQ;
@@ -694,42 +684,71 @@ __global__ __launch_bounds__(64 * kPartialWaves) void partial_kernel(DecodeArgs 
 // ---------------------------------------------------------------------------
 // 3. merge + un-rotation
 // ---------------------------------------------------------------------------
+// One workgroup per (request, KV head).  Wave h first reduces the running
+// maxima and sums of query head h over the items; then thread (h, c)
+// accumulates channel c over the items with independent loads.
 __global__ __launch_bounds__(512) void merge_kernel(DecodeArgs a) {
     __shared__ float ob[kMaxGroup][kHeadDim];
+    __shared__ float m_head[kMaxGroup], l_head[kMaxGroup];
     const int b = blockIdx.x / a.hkv;
     const int hk = blockIdx.x % a.hkv;
     const int t = threadIdx.x;
+    const int lane = t & 63;
     const int c = t & (kHeadDim - 1);
     int req = 0;
     const int L = request_length(a, b, req);
-    // items that exist for this request (the same ranges as the partial kernel)
-    int n_items = 0;
-    for (int j = 0; j < a.items; ++j) {
-        int p0, p1;
-        item_range(a, L, j, p0, p1);
-        if (p0 < p1) n_items = j + 1;
-    }
-    for (int h = t >> 7; h < a.g; h += 4) {
-        const size_t head = size_t(hk) * a.g + h;
-        const size_t base = size_t(b) * a.items * a.hq + head;   // row of item 0
-        float M = -INFINITY;
-        for (int j = 0; j < n_items; ++j) {
-            int p0, p1;
-            item_range(a, L, j, p0, p1);
-            if (p0 < p1) M = fmaxf(M, a.part_ml[(base + size_t(j) * a.hq) * 2]);
+    // items that hold a partial: the two BF16 windows if non-empty, then every
+    // history chunk (written only when the INT2 pool exists)
+    int p0, p1;
+    item_range(a, L, 0, p0, p1);
+    const bool sink_ok = p0 < p1;
+    item_range(a, L, 1, p0, p1);
+    const bool recent_ok = p0 < p1;
+    const int hist = max(0, max(a.sink_tokens, L - a.recent_tokens) - a.sink_tokens);
+    const int n_items = a.num_slots > 0 ? 2 + (hist + a.chunk - 1) / a.chunk : 2;
+    const size_t row_b = size_t(b) * a.items * a.hq + size_t(hk) * a.g;   // item 0, head 0
+    auto item_ok = [&](int j) { return j >= 2 || (j == 0 ? sink_ok : recent_ok); };
+
+    const int wv = t >> 6;
+    if (wv < a.g) {
+        float mx = -INFINITY;
+        for (int j = lane; j < n_items; j += 64) {
+            const float m = a.part_ml[(row_b + size_t(j) * a.hq + wv) * 2];
+            mx = item_ok(j) ? fmaxf(mx, m) : mx;
         }
-        float acc = 0.0f, l = 0.0f;
-        if (M != -INFINITY) {
-#pragma unroll 4
-            for (int j = 0; j < n_items; ++j) {
-                int p0, p1;
-                item_range(a, L, j, p0, p1);
-                if (p0 >= p1) continue;
-                const size_t row = base + size_t(j) * a.hq;
-                const float m = a.part_ml[row * 2];
-                const float wgt = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
-                l = fmaf(wgt, a.part_ml[row * 2 + 1], l);
-                acc = fmaf(wgt, a.part_o[row * kHeadDim + c], acc);
+        mx = wave_max(mx);
+        float l = 0.0f;
+        if (mx != -INFINITY) {
+            for (int j = lane; j < n_items; j += 64) {
+                const size_t row = row_b + size_t(j) * a.hq + wv;
+                const float e = __builtin_amdgcn_exp2f(a.part_ml[row * 2] - mx);
+                l = item_ok(j) ? fmaf(e, a.part_ml[row * 2 + 1], l) : l;
+            }
+        }
+        l = wave_sum(l);
+        if (lane == 0) {
+            m_head[wv] = mx;
+            l_head[wv] = l;
+        }
+    }
+    __syncthreads();
+    for (int h = t >> 7; h < a.g; h += 4) {
+        const float M = m_head[h], l = l_head[h];
+        float acc = 0.0f;
+        if (M != -INFINITY && l > 0.0f) {
+            const size_t row_h = row_b + h;
+            // every item that exists wrote finite (m, l, o'); a fully masked
+            // one has m = -inf and weight exp2(-inf) = 0
+            if (sink_ok)
+                acc = fmaf(__builtin_amdgcn_exp2f(a.part_ml[row_h * 2] - M), a.part_o[row_h * kHeadDim + c], acc);
+            if (recent_ok) {
+                const size_t row = row_h + a.hq;
+                acc = fmaf(__builtin_amdgcn_exp2f(a.part_ml[row * 2] - M), a.part_o[row * kHeadDim + c], acc);
+            }
+#pragma unroll 8
+            for (int j = 2; j < n_items; ++j) {
+                const size_t row = row_h + size_t(j) * a.hq;
+                acc = fmaf(__builtin_amdgcn_exp2f(a.part_ml[row * 2] - M), a.part_o[row * kHeadDim + c], acc);
             }
         }
         ob[h][c] = l > 0.0f ? acc / l : 0.0f;

@@ -19,6 +19,7 @@
 #include <hip/hip_fp16.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "common.cuh"
 #include "internal.h"
@@ -215,17 +216,22 @@ __device__ __forceinline__ float half_lo(uint32_t w) { return __half2float(__ush
 __device__ __forceinline__ float half_hi(uint32_t w) { return __half2float(__ushort_as_half(uint16_t(w >> 16))); }
 
 // History item on the matrix cores.  GQ = query heads per KV head, handled in
-// sets of 4.  One wave per KV head; the waves of a workgroup run the same
-// positions for all KV heads of the slot-major records, so together they read
-// whole cache lines, but each wave runs its own pipeline without barriers.
+// sets of 4.  A workgroup holds four waves, one per KV head of the head chunk
+// (the 384 bytes of four 96-byte head records that follow each other in a
+// slot-major record); waves past the last KV head only help with the loads.
 //
-// Loads go straight from HBM into the wave's LDS (global_load_lds, no
-// registers in between).  Per 32-token tile a wave first fetches the 32 slot
-// ids (each twice, so that lane l holds the slot of token l / 2), then its
-// 96-byte head record of every token as three 16-byte pieces per lane: K codes,
-// V codes, (s, z).  A stage of three such 1 KiB planes is one tile; three
-// stages let two tiles be in flight while a third is computed.  Tokens past
-// the item or with an out-of-range slot read a zero record, so they arrive as
+// Loads go straight from HBM into LDS (global_load_lds, no registers in
+// between) and are shared by the workgroup: for each 32-token tile the four
+// waves together fetch the chunk's 384 bytes of every token as whole 128-byte
+// lines (wave w fetches tokens 8 w .. 8 w + 7), so that each request fills a
+// line.  Token t of a tile occupies 384 bytes of the stage; within each of
+// its three 128-byte lines the 16-byte units are permuted by XOR with
+// (t / 2) % 8, so that the same field of 16 consecutive tokens falls in 16
+// different LDS bank groups.  Three stages let two tiles be in flight while a
+// third is computed; one workgroup barrier per tile publishes a landed tile
+// and retires the stage that the next loads overwrite.  Each wave fetches its
+// own copy of the tile's slot ids one tile before the records.  Tokens past the
+// item or with an out-of-range slot read a zero record, so they arrive as
 // s = z = 0 and codes 0, and are masked out of the softmax.
 //
 // QK (per half of 16 tokens): B = the tokens' K codes as exact fp16 denormals
@@ -239,19 +245,27 @@ __device__ __forceinline__ float half_hi(uint32_t w) { return __half2float(__ush
 // wave's LDS into rows (g, h) of A, B holds the V codes of 8 tokens per lane
 // as exact denormals, and the output of column (channel) c is read from the
 // row whose group is c's group.  K-slot k of the PV products is token
-// 4 (k % 8) + k / 8, so that the four lane groups read V-code rows in
-// different LDS banks.
-constexpr int kPlane = kTileTokens * 32;               // 32 tokens x 32 bytes
-constexpr int kStage = 3 * kPlane;                     // K codes | V codes | (s, z)
-constexpr int kStages = 3;
-constexpr int kSlotRing = 4;                           // slot-id buffers of 64 entries
+// 4 (k % 8) + k / 8, so that the four lane groups read V codes of tokens in
+// different LDS bank groups.
+constexpr int kTokBytes = 4 * kHeadRecord;             // 384: one token of a head chunk
+constexpr int kStage = kTileTokens * kTokBytes;        // 12 KiB per tile
+constexpr int kDepth = 2;                              // record tiles in flight during a compute
+constexpr int kStages = kDepth + 1;
+constexpr int kSlotRing = kStages;                     // slot-id buffers of 64 entries (per wave)
 constexpr int kWRow = 2 * kTileTokens * 2 + 16;        // weight row: hi and lo of 32 tokens, padded
 constexpr int kWSetBytes = 16 * kWRow;                 // rows (g, h) of one set of 4 heads
 __host__ __device__ constexpr int wave_lds_bytes(int gq) {
-    return kStages * kStage + kSlotRing * 256 + ((gq + 3) / 4) * kWSetBytes;
+    return kSlotRing * 256 + ((gq + 3) / 4) * kWSetBytes;
+}
+__host__ __device__ constexpr int int2_lds_bytes(int gq) { return kStages * kStage + kPartialWaves * wave_lds_bytes(gq); }
+
+// byte offset of 16-byte unit q (0..23) of token t inside a stage
+__device__ __forceinline__ int unit_addr(int t, int q) {
+    return t * kTokBytes + 16 * ((q & ~7) | ((q & 7) ^ ((t >> 1) & 7)));
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 // Wait until at most N vector-memory operations of this wave are pending.
 // The compiler does not track global_load_lds, so the pipeline below waits
@@ -262,19 +276,22 @@ __device__ __forceinline__ void wait_vmem() {
 }
 
 template <int GQ>
-__device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hk, int p0, int p1,
-                          uint8_t *wlds) {
+__device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, int p0, int p1,
+                          uint8_t *smem) {
     constexpr int HS = (GQ + 3) / 4;          // sets of 4 query heads
+    const int w = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int n = lane & 15;
     const int kb = lane >> 4;
+    const int hk = hc * kPartialWaves + w;    // this wave's KV head
+    const bool active = hk < a.hkv;
+    const int nh = min(kPartialWaves, a.hkv - hc * kPartialWaves);   // KV heads of the chunk
     const uint32_t rec_bytes = uint32_t(a.hkv) * kHeadRecord;
-    const uint8_t *gbase = a.records + hk * kHeadRecord;
     const int32_t *r2s = a.req_to_slot + int64_t(req) * a.r2s_stride;
     const int n_tiles = (p1 - p0 + kTileTokens - 1) / kTileTokens;
-    uint8_t *ring = wlds + kStages * kStage;
+    uint8_t *ring = smem + kStages * kStage + w * wave_lds_bytes(GQ);
     uint8_t *wbuf = ring + kSlotRing * 256;
-    const size_t head0 = size_t(b) * a.hq + size_t(hk) * GQ;
+    const size_t head0 = size_t(b) * a.hq + size_t(active ? hk : 0) * GQ;
 
     // ---- per-item operands
     f16x8 qA[HS][4][2];   // QK A: row n = (h = n / 4, g = n % 4), nonzero in K block g
@@ -284,7 +301,7 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hk, in
     for (int hs = 0; hs < HS; ++hs) {
         {
             const int h = 4 * hs + (n >> 2);
-            const bool hv = h < GQ;
+            const bool hv = h < GQ && active;
             const float *qr = a.qrot + (head0 + (hv ? h : 0)) * kHeadDim;
             const float k2 = a.qsum[(head0 + (hv ? h : 0)) * 8 + 4];
             const bool nz = hv && (n & 3) == kb;
@@ -308,7 +325,7 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hk, in
         }
         {
             const int h = 4 * hs + kb;
-            const bool hv = h < GQ;
+            const bool hv = h < GQ && active;
             const float *info = a.qsum + (head0 + (hv ? h : 0)) * 8;
 #pragma unroll
             for (int g = 0; g < 4; ++g) qz[hs][g] = hv ? info[g] / info[5] : 0.0f;
@@ -316,30 +333,55 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hk, in
         }
     }
 
-    // ---- loads.  Every tile issues the same four operations (one slot-id
-    // load, three record loads), including the tiles past the end, which read
-    // position p0 and the zero record: the wait counts below are constants.
-    // Order: S(T+1) comes right before R(T), so the stream is
-    //   S0 S1 R0 S2 R1 S3 R2 ...  (R = three operations)
-    auto slot_load = [&](int T) {
-        const int pos = p0 + T * kTileTokens + (lane >> 1);
-        const int32_t *src = r2s + (pos < p1 ? pos : p0);
-        __builtin_amdgcn_global_load_lds(src, (lds_void *)(ring + (T & (kSlotRing - 1)) * 256), 4, 0, 0);
+    // ---- what this lane fetches: 16-byte unit P of the stage, for P =
+    // 64 (3 w + u) + lane (u = 0..2), holds logical unit q of token tq[u];
+    // units of KV heads past the chunk read the zero record
+    int tq[3];
+    uint32_t src_off[3];
+    bool real[3];
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+        const int P = 64 * (3 * w + u) + lane;
+        const int t = P / 24, U = P % 24;
+        const int q = (U & ~7) | ((U & 7) ^ ((t >> 1) & 7));
+        tq[u] = t;
+        src_off[u] = uint32_t(hc * kTokBytes + 16 * q);
+        real[u] = q / 6 < nh;
+    }
+
+    // ---- loads.  Iteration t issues S(t + 3), the slot ids of tile t + 3,
+    // and R(t + 2), this wave's three record loads of tile t + 2: two record
+    // tiles are in flight while tile t is computed.  Every iteration issues
+    // the same four operations, including tiles past the end (which read
+    // position p0 and the zero record), and so does the prologue, whose first
+    // record loads are dummies: the wait counts are constants.
+    const uint32_t span = uint32_t(p1 - p0);
+    auto slot_load = [&](int T, int ring_slot) {
+        const uint32_t off = uint32_t(T * kTileTokens + (lane & 31));
+        const int32_t *src = r2s + p0 + (off < span ? off : 0u);
+        __builtin_amdgcn_global_load_lds(src, (lds_void *)(ring + ring_slot * 256), 4, 0, 0);
     };
-    // record loads of tile T into stage `stage`; returns the ballot of the
-    // usable tokens (bit 2 i for token i)
-    auto record_load = [&](int T, int stage) -> uint64_t {
-        const int slot = *reinterpret_cast<const int *>(ring + (T & (kSlotRing - 1)) * 256 + 4 * lane);
-        const int pos = p0 + T * kTileTokens + (lane >> 1);
-        const bool ok = pos < p1 && slot >= 0 && int64_t(slot) < a.num_slots;
-        const uint8_t *src = gbase + uint64_t(uint32_t(slot)) * rec_bytes;
-        asm volatile("" : "+v"(src));         // computed on every lane: a select, not a branch
-        src = (ok ? src : a.zero_rec) + 16 * (lane & 1);
-        uint8_t *st = wlds + stage * kStage;
-        __builtin_amdgcn_global_load_lds(src, (lds_void *)st, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(src + kCodeBytes, (lds_void *)(st + kPlane), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(src + 2 * kCodeBytes, (lds_void *)(st + 2 * kPlane), 16, 0, 0);
-        return __ballot(ok);
+    // record loads of tile T into `st`; returns the usable tokens (bit t)
+    auto record_load = [&](int T, int ring_slot, uint8_t *st) -> uint32_t {
+        const int *slots = reinterpret_cast<const int *>(ring + ring_slot * 256);
+        const uint32_t left = span - uint32_t(T * kTileTokens);   // positions left in the item (may wrap: none)
+        const uint32_t n_ok = uint32_t(T * kTileTokens) < span ? left : 0u;
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            const int slot = slots[tq[u]];
+            const bool ok = real[u] & (uint32_t(tq[u]) < n_ok) & (uint32_t(slot) < uint32_t(a.num_slots));
+            const uint8_t *src = a.records + uint64_t(uint32_t(slot)) * rec_bytes + src_off[u];
+            src = ok ? src : a.zero_rec;
+            __builtin_amdgcn_global_load_lds(src, (lds_void *)(st + 1024 * (3 * w + u)), 16, 0, 0);
+        }
+        const int s_own = slots[lane & 31];
+        return uint32_t(__ballot((uint32_t(lane & 31) < n_ok) & (uint32_t(s_own) < uint32_t(a.num_slots))));
+    };
+    // stand-in for the record loads of the prologue's first iteration: the
+    // zero record into this wave's PV weight rows, which are written only later
+    auto dummy_load = [&]() {
+#pragma unroll
+        for (int u = 0; u < 3; ++u) __builtin_amdgcn_global_load_lds(a.zero_rec, (lds_void *)wbuf, 16, 0, 0);
     };
     // LDS is used by this wave alone and runs a wave's operations in order;
     // the fences keep the compiler from moving LDS accesses across them
@@ -361,21 +403,32 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hk, in
         for (int jj = 0; jj < 8; ++jj) oacc[hs][jj] = f32x4{0, 0, 0, 0};
     }
 
-    // K-slot of token i in the PV products, and of this lane's two QK tokens
+    // this lane's LDS reads inside a stage (head w of token t)
+    const int qk_off0 = unit_addr(n, 6 * w + (kb >> 1)) + 8 * (kb & 1);          // K codes, token n
+    const int qk_off1 = unit_addr(16 + n, 6 * w + (kb >> 1)) + 8 * (kb & 1);     // token 16 + n
+    const int szk_off0 = unit_addr(n, 6 * w + 4), szk_off1 = unit_addr(16 + n, 6 * w + 4);
+    const int szv_off0 = unit_addr(n, 6 * w + 5), szv_off1 = unit_addr(16 + n, 6 * w + 5);
+    int pv_off[8];        // V codes (channels 8 n .. 8 n + 7) of tokens 8 pp + kb and 8 pp + 4 + kb
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+        pv_off[2 * pp] = unit_addr(8 * pp + kb, 6 * w + 2 + (n >> 3)) + ((2 * n) & 15);
+        pv_off[2 * pp + 1] = unit_addr(8 * pp + 4 + kb, 6 * w + 2 + (n >> 3)) + ((2 * n) & 15);
+    }
+    // K-slot of this lane's two QK tokens in the PV products
     const int kcol0 = 8 * (n & 3) + (n >> 2);             // token n      (half 0)
     const int kcol1 = 8 * (n & 3) + 4 + (n >> 2);         // token 16 + n (half 1)
 
     // one tile: QK, online softmax, PV (reads LDS stage `st`)
-    auto compute = [&](const uint8_t *st, uint64_t valid) {
+    auto compute = [&](const uint8_t *st, uint32_t valid) {
         // ---- QK: logit of (token 16 hf + n, head 4 hs + kb)
         float lg[HS][2];
         u32x4 szv[2];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             const int tk = 16 * hf + n;
-            const u32x2 kc = *reinterpret_cast<const u32x2 *>(st + 32 * tk + 8 * kb);
-            const u32x4 szk = *reinterpret_cast<const u32x4 *>(st + 2 * kPlane + 32 * tk);
-            szv[hf] = *reinterpret_cast<const u32x4 *>(st + 2 * kPlane + 32 * tk + kSzBytes);
+            const u32x2 kc = *reinterpret_cast<const u32x2 *>(st + (hf ? qk_off1 : qk_off0));
+            const u32x4 szk = *reinterpret_cast<const u32x4 *>(st + (hf ? szk_off1 : szk_off0));
+            szv[hf] = *reinterpret_cast<const u32x4 *>(st + (hf ? szv_off1 : szv_off0));
             const uint32_t d0s = kc[0] >> 6, d1s = kc[1] >> 6;
             f16x8 B[4];
 #pragma unroll
@@ -385,7 +438,7 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hk, in
                 B[r] = u4_as_h8(code_bits(d, ds, 4 * (r & 1) + 0), code_bits(d, ds, 4 * (r & 1) + 1),
                                 code_bits(d, ds, 4 * (r & 1) + 2), code_bits(d, ds, 4 * (r & 1) + 3));
             }
-            const bool live = (valid >> (2 * tk)) & 1u;
+            const bool live = (valid >> tk) & 1u;
 #pragma unroll
             for (int hs = 0; hs < HS; ++hs) {
                 f32x4 acc = f32x4{0, 0, 0, 0};
@@ -452,9 +505,10 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hk, in
         uint32_t xw[4], xs[4];
 #pragma unroll
         for (int pp = 0; pp < 4; ++pp) {
-            const uint8_t *r0 = st + kPlane + 32 * (8 * pp + kb) + 2 * n;
-            xw[pp] = uint32_t(*reinterpret_cast<const uint16_t *>(r0)) |
-                     (uint32_t(*reinterpret_cast<const uint16_t *>(r0 + 32 * 4)) << 16);
+            u16x2 pr;
+            pr.x = *reinterpret_cast<const uint16_t *>(st + pv_off[2 * pp]);
+            pr.y = *reinterpret_cast<const uint16_t *>(st + pv_off[2 * pp + 1]);
+            xw[pp] = __builtin_bit_cast(uint32_t, pr);
             xs[pp] = xw[pp] >> 6;
         }
         // rescale the output rows of heads whose running max grew; PV output
@@ -491,30 +545,46 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hk, in
         lds_order();
     };
 
-    // ---- pipeline.  Iteration t computes stage t % 3 while tiles t + 1 and
-    // t + 2 are in flight.  Before R(t + 2) is issued, S(t + 2) must have
-    // arrived: four operations follow it (R(t + 1) and S(t + 3)), and since
-    // R(t) precedes S(t + 2) that same wait also completes tile t.
-    slot_load(0);
-    slot_load(1);
-    wait_vmem<1>();
-    uint64_t v0 = record_load(0, 0);
-    slot_load(2);
+    // ---- pipeline.  At the top of iteration t this wave's R(t) must have
+    // landed (four operations follow it: S(t + 2), R(t + 1)); the barrier
+    // then publishes tile t of every wave and guarantees that every wave is
+    // done with tile t - 1, whose stage R(t + 2) overwrites.  Before R(t + 2)
+    // is issued, S(t + 2) must have arrived (R(t + 1) and S(t + 3) follow
+    // it).  The loop is unrolled by three so that stage and ring offsets are
+    // constants; tiles past the end are computed fully masked.
+    static_assert(kDepth == 2 && kStages == 3, "the unrolled pipeline assumes three stages");
+    const bool run_compute = __builtin_amdgcn_readfirstlane(int(active)) != 0;
+    uint32_t vq0, vq1, vq2;                   // usable tokens of tiles t, t + 1, t + 2
+    slot_load(0, 0);
     wait_vmem<4>();
-    uint64_t v1 = record_load(1, 1);
-    int st_c = 0;                             // stage of tile t
-    for (int t = 0; t < n_tiles; ++t) {
-        slot_load(t + 3);
+    dummy_load();
+    slot_load(1, 1);
+    wait_vmem<4>();
+    vq0 = record_load(0, 0, smem);
+    slot_load(2, 2);
+    wait_vmem<4>();
+    vq1 = record_load(1, 1, smem + kStage);
+    auto step = [&](int t, auto K) {
+        constexpr int k = decltype(K)::value;             // t % 3
+        constexpr int k2 = (k + 2) % 3;
         wait_vmem<4>();
-        const int st_n = st_c == 0 ? 2 * kStage : st_c - kStage;   // stage of tile t + 2
-        const uint64_t v2 = record_load(t + 2, st_n / kStage);
-        compute(wlds + st_c, v0);
-        v0 = v1;
-        v1 = v2;
-        st_c = st_c == 2 * kStage ? 0 : st_c + kStage;
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        slot_load(t + 3, k);
+        wait_vmem<4>();
+        vq2 = record_load(t + 2, k2, smem + k2 * kStage);
+        if (run_compute) compute(smem + k * kStage, vq0);
+        vq0 = vq1;
+        vq1 = vq2;
+    };
+    for (int t = 0; t < n_tiles; t += 3) {
+        step(t, std::integral_constant<int, 0>{});
+        step(t + 1, std::integral_constant<int, 1>{});
+        step(t + 2, std::integral_constant<int, 2>{});
     }
-    // the trailing (unused) loads still write this wave's LDS: let them land
+    // the trailing (unused) loads still write the stages: let them land
     wait_vmem<0>();
+    if (!active) return;
 
     // ---- write the partial (m, l, o') of the GQ heads
     const size_t row0 = (size_t(b) * a.items + j) * a.hq + hk * GQ;
@@ -554,13 +624,24 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hk, in
     }
 }
 
-// BF16 window item on fp32 VALU: lanes over tokens for QK, over channel pairs
-// for PV.  `pbuf` is this wave's LDS scratch [kMaxGroup][64].
+// BF16 window item on fp32 VALU (the sink and recent windows: a few hundred
+// tokens per request).  Chunks of 64 tokens; every load of a chunk is issued
+// before its data is used, so a chunk costs a few memory latencies, not one
+// per token.  QK: lane = token, its K row (16 x 16 bytes) against q' staged
+// in this wave's LDS.  PV: lane = channel pair, V rows of 16 tokens at a time.
+// `pbuf` is this wave's LDS scratch: q' [kMaxGroup][128] then p [kMaxGroup][64].
+constexpr int kBf16WaveFloats = kMaxGroup * kHeadDim + kMaxGroup * kBf16Chunk;
+
 __device__ void bf16_item(const DecodeArgs &a, int b, int req, int j, int hk, int p0, int p1,
                           bool active, float *pbuf) {
     const int lane = threadIdx.x & 63;
     const int g = a.g;
+    float *qs = pbuf;
+    float *ps = pbuf + kMaxGroup * kHeadDim;
     const float *qr = a.qrot + (size_t(b) * a.hq + hk * g) * kHeadDim;
+    for (int e = lane; e < g * kHeadDim; e += 64) qs[e] = qr[e];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const bool is_sink = (j == 0);
     float m_run[kMaxGroup], l_lane[kMaxGroup], o0[kMaxGroup], o1[kMaxGroup];
 #pragma unroll
@@ -577,27 +658,37 @@ __device__ void bf16_item(const DecodeArgs &a, int b, int req, int j, int hk, in
                t * kHeadDim;
     };
     for (int cb = p0; cb < p1; cb += kBf16Chunk) {
-        const int pos = cb + lane;
-        const bool ok = active && pos < p1;
+        const int cnt = min(kBf16Chunk, p1 - cb);
+        const bool ok = active && lane < cnt;
+        // ---- QK: the whole K row of this lane's token in flight at once
+        const uint16_t *kr = row_ptr(cb + (lane < cnt ? lane : 0), 0);
+        u32x4 kw[kHeadDim / 8];
+#pragma unroll
+        for (int i = 0; i < kHeadDim / 8; ++i) kw[i] = *reinterpret_cast<const u32x4 *>(kr + 8 * i);
         float acc[kMaxGroup];
 #pragma unroll
         for (int h = 0; h < kMaxGroup; ++h) acc[h] = 0.0f;
-        if (ok) {
-            const uint16_t *kr = row_ptr(pos, 0);
-            for (int i = 0; i < kHeadDim; i += 8) {
-                const u32x4 kw = *reinterpret_cast<const u32x4 *>(kr + i);
-                float kf[8];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    kf[2 * u] = bf16_bits_to_f32(kw[u] & 0xFFFFu);
-                    kf[2 * u + 1] = bf16_bits_to_f32(kw[u] >> 16);
-                }
+        for (int i = 0; i < kHeadDim / 8; ++i) {
+            float kf[8];
 #pragma unroll
-                for (int h = 0; h < kMaxGroup; ++h) {
-                    if (h < g) {
+            for (int u = 0; u < 4; ++u) {
+                kf[2 * u] = bf16_bits_to_f32(kw[i][u] & 0xFFFFu);
+                kf[2 * u + 1] = bf16_bits_to_f32(kw[i][u] >> 16);
+            }
 #pragma unroll
-                        for (int u = 0; u < 8; ++u) acc[h] = fmaf(qr[h * kHeadDim + i + u], kf[u], acc[h]);
-                    }
+            for (int h = 0; h < kMaxGroup; ++h) {
+                if (h < g) {
+                    const f32x4 qa = *reinterpret_cast<const f32x4 *>(qs + h * kHeadDim + 8 * i);
+                    const f32x4 qb = *reinterpret_cast<const f32x4 *>(qs + h * kHeadDim + 8 * i + 4);
+                    acc[h] = fmaf(qa[0], kf[0], acc[h]);
+                    acc[h] = fmaf(qa[1], kf[1], acc[h]);
+                    acc[h] = fmaf(qa[2], kf[2], acc[h]);
+                    acc[h] = fmaf(qa[3], kf[3], acc[h]);
+                    acc[h] = fmaf(qb[0], kf[4], acc[h]);
+                    acc[h] = fmaf(qb[1], kf[5], acc[h]);
+                    acc[h] = fmaf(qb[2], kf[6], acc[h]);
+                    acc[h] = fmaf(qb[3], kf[7], acc[h]);
                 }
             }
         }
@@ -613,31 +704,41 @@ __device__ void bf16_item(const DecodeArgs &a, int b, int req, int j, int hk, in
             m_run[h] = m_new;
             const float p = (x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x - m_new);
             l_lane[h] = l_lane[h] * alpha[h] + p;
-            if (h < g) pbuf[h * kBf16Chunk + lane] = p;
+            if (h < g) ps[h * kBf16Chunk + lane] = p;
         }
-        __syncthreads();
-        // PV: lane holds channels 2 lane, 2 lane + 1
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // ---- PV: lane holds channels 2 lane, 2 lane + 1; 16 V rows in flight
 #pragma unroll
         for (int h = 0; h < kMaxGroup; ++h) {
             o0[h] *= alpha[h];
             o1[h] *= alpha[h];
         }
         if (active) {
-            const int cnt = min(kBf16Chunk, p1 - cb);
-            for (int tt = 0; tt < cnt; ++tt) {
-                const uint32_t vw = *reinterpret_cast<const uint32_t *>(row_ptr(cb + tt, 1) + 2 * lane);
-                const float v0 = bf16_bits_to_f32(vw & 0xFFFFu), v1 = bf16_bits_to_f32(vw >> 16);
+            for (int t0 = 0; t0 < cnt; t0 += 16) {
+                uint32_t vw[16];
 #pragma unroll
-                for (int h = 0; h < kMaxGroup; ++h) {
-                    if (h < g) {
-                        const float p = pbuf[h * kBf16Chunk + tt];
-                        o0[h] = fmaf(p, v0, o0[h]);
-                        o1[h] = fmaf(p, v1, o1[h]);
+                for (int u = 0; u < 16; ++u) {
+                    const int tt = min(t0 + u, cnt - 1);   // past the chunk: p = 0 below
+                    vw[u] = *reinterpret_cast<const uint32_t *>(row_ptr(cb + tt, 1) + 2 * lane);
+                }
+#pragma unroll
+                for (int u = 0; u < 16; ++u) {
+                    const float v0 = bf16_bits_to_f32(vw[u] & 0xFFFFu), v1 = bf16_bits_to_f32(vw[u] >> 16);
+                    const int tt = min(t0 + u, kBf16Chunk - 1);
+#pragma unroll
+                    for (int h = 0; h < kMaxGroup; ++h) {
+                        if (h < g) {
+                            const float p = t0 + u < cnt ? ps[h * kBf16Chunk + tt] : 0.0f;
+                            o0[h] = fmaf(p, v0, o0[h]);
+                            o1[h] = fmaf(p, v1, o1[h]);
+                        }
                     }
                 }
             }
         }
-        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
     if (!active) return;
     const size_t row0 = (size_t(b) * a.items + j) * a.hq + hk * g;
@@ -671,13 +772,13 @@ __global__ __launch_bounds__(64 * kPartialWaves) void partial_kernel(DecodeArgs 
     item_range(a, L, j, p0, p1);
     if (p0 >= p1) return;                       // uniform over the workgroup
     const int w = threadIdx.x >> 6;
-    const int hk = hc * a.waves + w;
+    const int hk = hc * kPartialWaves + w;
     const bool active = hk < a.hkv;
     if (j < 2) {
-        float *pbuf = reinterpret_cast<float *>(smem) + w * (kMaxGroup * kBf16Chunk);
+        float *pbuf = reinterpret_cast<float *>(smem) + w * kBf16WaveFloats;
         bf16_item(a, b, req, j, active ? hk : 0, p0, p1, active, pbuf);
-    } else if (a.num_slots > 0 && active) {
-        int2_item<GQ>(a, b, req, j, hk, p0, p1, smem + w * wave_lds_bytes(GQ));
+    } else if (a.num_slots > 0) {
+        int2_item<GQ>(a, b, req, j, hc, p0, p1, smem);   // every wave: the loads are shared
     }
 }
 
@@ -780,14 +881,14 @@ __global__ __launch_bounds__(512) void merge_kernel(DecodeArgs a) {
 // token records and PV weight rows for the INT2 items, or its softmax buffer
 // for the BF16 items.
 size_t partial_lds_bytes(const DecodeArgs &a) {
-    const size_t stages = size_t(a.waves) * wave_lds_bytes(a.g);
-    const size_t pbuf = size_t(a.waves) * kMaxGroup * kBf16Chunk * sizeof(float);
-    return stages > pbuf ? stages : pbuf;
+    const size_t int2 = int2_lds_bytes(a.g);
+    const size_t pbuf = size_t(kPartialWaves) * kBf16WaveFloats * sizeof(float);
+    return int2 > pbuf ? int2 : pbuf;
 }
 
 template <int GQ>
 hipError_t launch_partial(const DecodeArgs &a, int blocks, hipStream_t stream) {
-    hipLaunchKernelGGL(partial_kernel<GQ>, dim3(blocks), dim3(64 * a.waves), partial_lds_bytes(a), stream, a);
+    hipLaunchKernelGGL(partial_kernel<GQ>, dim3(blocks), dim3(64 * kPartialWaves), partial_lds_bytes(a), stream, a);
     return hipGetLastError();
 }
 
@@ -856,8 +957,8 @@ extern "C" oscar_status oscar_decode_attn(hipStream_t stream, const oscar_layout
     a.max_requests = layout->max_requests;
     a.chunk = plan.chunk;
     a.items = plan.items;
-    a.waves = a.hkv < kPartialWaves ? a.hkv : kPartialWaves;
-    a.head_chunks = (a.hkv + a.waves - 1) / a.waves;
+    a.waves = kPartialWaves;
+    a.head_chunks = (a.hkv + kPartialWaves - 1) / kPartialWaves;
 
     hipLaunchKernelGGL(prep_kernel, dim3(batch * a.hkv), dim3(512), 0, stream, a);
     hipError_t e = hipGetLastError();

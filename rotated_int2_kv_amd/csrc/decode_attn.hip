@@ -170,15 +170,27 @@ __global__ __launch_bounds__(512) void prep_kernel(DecodeArgs a) {
 // 2. split-K partials
 // ---------------------------------------------------------------------------
 
-// x ~ hi + lo with hi, lo fp16 pairs: hi rounded toward zero, lo the exact
-// fp32 residual rounded toward zero (relative error of hi + lo below 2^-20).
+__device__ __forceinline__ float half_lo_f(uint32_t w) { return __half2float(__ushort_as_half(uint16_t(w))); }
+__device__ __forceinline__ float half_hi_f(uint32_t w) { return __half2float(__ushort_as_half(uint16_t(w >> 16))); }
+
+// Two fp32 values as an fp16 pair, each rounded to nearest (ties to even):
+// one v_cvt_pk_f16_f32.
+__device__ __forceinline__ uint32_t pk_rn(float x0, float x1) {
+    const f16x2 h = {static_cast<_Float16>(x0), static_cast<_Float16>(x1)};
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// x ~ hi + lo with hi, lo fp16 pairs: hi rounded to nearest, lo the exact
+// fp32 residual rounded to nearest (relative error of hi + lo below 2^-21,
+// and unbiased, so that errors of many such products do not add up in one
+// direction).
 struct HiLo2 {
     uint32_t hi, lo;
 };
 __device__ __forceinline__ HiLo2 split_hilo(float x0, float x1) {
-    const auto h = __builtin_amdgcn_cvt_pkrtz(x0, x1);
-    const auto l = __builtin_amdgcn_cvt_pkrtz(x0 - float(h[0]), x1 - float(h[1]));
-    return {__builtin_bit_cast(uint32_t, h), __builtin_bit_cast(uint32_t, l)};
+    const uint32_t h = pk_rn(x0, x1);
+    const uint32_t l = pk_rn(x0 - half_lo_f(h), x1 - half_hi_f(h));
+    return {h, l};
 }
 
 __device__ __forceinline__ f16x8 u4_as_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
@@ -230,7 +242,7 @@ __device__ __forceinline__ float half_hi(uint32_t w) { return __half2float(__ush
 // different LDS bank groups.  Three stages let two tiles be in flight while a
 // third is computed; one workgroup barrier per tile publishes a landed tile
 // and retires the stage that the next loads overwrite.  Each wave fetches its
-// own copy of the tile's slot ids one tile before the records.  Tokens past the
+// own copy of the tile's slot ids kAhead tiles before the records.  Tokens past the
 // item or with an out-of-range slot read a zero record, so they arrive as
 // s = z = 0 and codes 0, and are masked out of the softmax.
 //
@@ -244,16 +256,20 @@ __device__ __forceinline__ float half_hi(uint32_t w) { return __half2float(__ush
 // four groups and accumulates p z_g itself; the weights go through the
 // wave's LDS into rows (g, h) of A, B holds the V codes of 8 tokens per lane
 // as exact denormals, and the output of column (channel) c is read from the
-// row whose group is c's group.  K-slot k of the PV products is token
-// 4 (k % 8) + k / 8, so that the four lane groups read V codes of tokens in
-// different LDS bank groups.
+// row whose group is c's group.  K-slot 8 kb + i of the PV products is token
+// 2 (i % 2) + 8 (i / 2) + (kb % 2) + 4 (kb / 2): the four lane groups read V
+// codes of tokens t, t + 1, t + 4, t + 5 at once, which the token swizzle
+// puts in disjoint LDS banks.  Weight rows are 64 bytes with their 16-byte
+// units permuted by XOR with row / 4, which keeps both the 16-bit weight
+// writes and the 128-bit operand reads free of bank conflicts.
 constexpr int kTokBytes = 4 * kHeadRecord;             // 384: one token of a head chunk
 constexpr int kStage = kTileTokens * kTokBytes;        // 12 KiB per tile
 constexpr int kDepth = 2;                              // record tiles in flight during a compute
 constexpr int kStages = kDepth + 1;
-constexpr int kSlotRing = kStages;                     // slot-id buffers of 64 entries (per wave)
-constexpr int kWRow = 2 * kTileTokens * 2 + 16;        // weight row: hi and lo of 32 tokens, padded
-constexpr int kWSetBytes = 16 * kWRow;                 // rows (g, h) of one set of 4 heads
+constexpr int kAhead = 1;                              // slot ids fetched this many tiles before their records
+constexpr int kSlotRing = kAhead + 2;                  // slot-id buffers of 64 entries (per wave)
+constexpr int kWPlane = 16 * kTileTokens * 2;          // 16 rows (g, h) x 32 fp16 weights: 1 KiB
+constexpr int kWSetBytes = 2 * kWPlane;                // hi and lo planes of one set of 4 heads
 __host__ __device__ constexpr int wave_lds_bytes(int gq) {
     return kSlotRing * 256 + ((gq + 3) / 4) * kWSetBytes;
 }
@@ -349,9 +365,10 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, in
         real[u] = q / 6 < nh;
     }
 
-    // ---- loads.  Iteration t issues S(t + 3), the slot ids of tile t + 3,
-    // and R(t + 2), this wave's three record loads of tile t + 2: two record
-    // tiles are in flight while tile t is computed.  Every iteration issues
+    // ---- loads.  Iteration t issues S(t + 2 + A), the slot ids of tile
+    // t + 2 + A (A = kAhead), and R(t + 2), this wave's three record loads of
+    // tile t + 2: two record tiles are in flight while tile t is computed, and
+    // a record load uses slot ids fetched A iterations earlier.  Every iteration issues
     // the same four operations, including tiles past the end (which read
     // position p0 and the zero record), and so does the prologue, whose first
     // record loads are dummies: the wait counts are constants.
@@ -408,15 +425,25 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, in
     const int qk_off1 = unit_addr(16 + n, 6 * w + (kb >> 1)) + 8 * (kb & 1);     // token 16 + n
     const int szk_off0 = unit_addr(n, 6 * w + 4), szk_off1 = unit_addr(16 + n, 6 * w + 4);
     const int szv_off0 = unit_addr(n, 6 * w + 5), szv_off1 = unit_addr(16 + n, 6 * w + 5);
-    int pv_off[8];        // V codes (channels 8 n .. 8 n + 7) of tokens 8 pp + kb and 8 pp + 4 + kb
+    int pv_off[8];        // V codes (channels 8 n .. 8 n + 7) of the tokens of K-slots 8 kb + i
+    const int kb_tok = (kb & 1) + 4 * (kb >> 1);
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
-        pv_off[2 * pp] = unit_addr(8 * pp + kb, 6 * w + 2 + (n >> 3)) + ((2 * n) & 15);
-        pv_off[2 * pp + 1] = unit_addr(8 * pp + 4 + kb, 6 * w + 2 + (n >> 3)) + ((2 * n) & 15);
-    }
-    // K-slot of this lane's two QK tokens in the PV products
-    const int kcol0 = 8 * (n & 3) + (n >> 2);             // token n      (half 0)
-    const int kcol1 = 8 * (n & 3) + 4 + (n >> 2);         // token 16 + n (half 1)
+    for (int i = 0; i < 8; ++i)
+        pv_off[i] = unit_addr(2 * (i & 1) + 8 * (i >> 1) + kb_tok, 6 * w + 2 + (n >> 3)) + ((2 * n) & 15);
+    // weight-plane byte offset (row and unit) of token t for this lane's rows (g, kb)
+    auto wslot = [&](int t, int g) {
+        const int unit = (t & 1) + 2 * ((t >> 2) & 1);              // K-slot / 8
+        const int i = ((t >> 1) & 1) + 2 * (t >> 3);                // K-slot % 8
+        const int row = 4 * g + kb;
+        return row * 64 + 16 * (unit ^ g) + 2 * i;
+    };
+    int woff[2][4];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) woff[hf][g] = wslot(16 * hf + n, g);
+    // A-operand read of row n, K-slots 8 kb .. 8 kb + 7
+    const int aoff = n * 64 + 16 * (kb ^ (n >> 2));
 
     // one tile: QK, online softmax, PV (reads LDS stage `st`)
     auto compute = [&](const uint8_t *st, uint32_t valid) {
@@ -472,36 +499,32 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, in
             }
             // exponent reference: a finite stand-in while every token so far is masked
             const float m_ref = m_run[hs] == -INFINITY ? 0.0f : m_run[hs];
-            uint8_t *wrow = wbuf + hs * kWSetBytes + kb * kWRow;   // row (g = 0, h = kb)
+            uint8_t *wset = wbuf + hs * kWSetBytes;
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
                 const float p = __builtin_amdgcn_exp2f(lg[hs][hf] - m_ref);   // 0 for masked tokens
                 l_lane[hs] += p;
 #pragma unroll
                 for (int g = 0; g < 4; ++g) zl[hs][g] = fmaf(p, half_hi(szv[hf][g]), zl[hs][g]);
-                // w_g = p s_g as hi + lo fp16 parts; lo = w_g - hi exactly rounded
+                // w_g = p s_g as hi + lo fp16 parts, both rounded to nearest; lo = w_g - hi
                 uint32_t hw[2], lw[2];
 #pragma unroll
                 for (int q2 = 0; q2 < 2; ++q2) {
                     const float s0 = half_lo(szv[hf][2 * q2]), s1 = half_lo(szv[hf][2 * q2 + 1]);
-                    hw[q2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(fmaf(p, s0, 0.0f), fmaf(p, s1, 0.0f)));
-                    lw[q2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(fmaf(p, s0, -half_lo(hw[q2])),
-                                                                                     fmaf(p, s1, -half_hi(hw[q2]))));
+                    hw[q2] = pk_rn(fmaf(p, s0, 0.0f), fmaf(p, s1, 0.0f));
+                    lw[q2] = pk_rn(fmaf(p, s0, -half_lo(hw[q2])), fmaf(p, s1, -half_hi(hw[q2])));
                 }
-                const int tcol = 2 * (hf ? kcol1 : kcol0);
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int sh = 16 * (g & 1);
-                    *reinterpret_cast<uint16_t *>(wrow + 4 * g * kWRow + tcol) = uint16_t(hw[g >> 1] >> sh);
-                    *reinterpret_cast<uint16_t *>(wrow + 4 * g * kWRow + 2 * kTileTokens + tcol) =
-                        uint16_t(lw[g >> 1] >> sh);
+                    *reinterpret_cast<uint16_t *>(wset + woff[hf][g]) = uint16_t(hw[g >> 1] >> sh);
+                    *reinterpret_cast<uint16_t *>(wset + kWPlane + woff[hf][g]) = uint16_t(lw[g >> 1] >> sh);
                 }
             }
         }
         lds_order();
-        // ---- PV: A rows (g, h) = weights of K-slots 8 kb .. 8 kb + 7, i.e.
-        // tokens 4 c + kb (c = 0..7); B = V codes of channel 8 n + jj for the
-        // same tokens, two tokens per 32-bit word
+        // ---- PV: A rows (g, h) = weights of K-slots 8 kb .. 8 kb + 7; B = V
+        // codes of channel 8 n + jj for the same tokens, two per 32-bit word
         uint32_t xw[4], xs[4];
 #pragma unroll
         for (int pp = 0; pp < 4; ++pp) {
@@ -528,9 +551,9 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, in
         f16x8 AS[HS][2];
 #pragma unroll
         for (int hs = 0; hs < HS; ++hs) {
-            const uint8_t *arow = wbuf + hs * kWSetBytes + n * kWRow + 16 * kb;
+            const uint8_t *arow = wbuf + hs * kWSetBytes + aoff;
             AS[hs][0] = *reinterpret_cast<const f16x8 *>(arow);
-            AS[hs][1] = *reinterpret_cast<const f16x8 *>(arow + 2 * kTileTokens);
+            AS[hs][1] = *reinterpret_cast<const f16x8 *>(arow + kWPlane);
         }
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
@@ -546,33 +569,45 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, in
     };
 
     // ---- pipeline.  At the top of iteration t this wave's R(t) must have
-    // landed (four operations follow it: S(t + 2), R(t + 1)); the barrier
-    // then publishes tile t of every wave and guarantees that every wave is
-    // done with tile t - 1, whose stage R(t + 2) overwrites.  Before R(t + 2)
-    // is issued, S(t + 2) must have arrived (R(t + 1) and S(t + 3) follow
-    // it).  The loop is unrolled by three so that stage and ring offsets are
+    // landed (four operations follow it: S(t + 1 + A), R(t + 1)); the
+    // barrier then publishes tile t of every wave and guarantees that every
+    // wave is done with tile t - 1, whose stage R(t + 2) overwrites.  Before
+    // R(t + 2) is issued, S(t + 2) must have arrived: it was issued A
+    // iterations earlier, and 4 A operations follow it.  The prologue issues
+    // the same operations (dummy record loads first), so the counts hold from
+    // the start.  The loop is unrolled by three so that stage offsets are
     // constants; tiles past the end are computed fully masked.
     static_assert(kDepth == 2 && kStages == 3, "the unrolled pipeline assumes three stages");
     const bool run_compute = __builtin_amdgcn_readfirstlane(int(active)) != 0;
-    uint32_t vq0, vq1, vq2;                   // usable tokens of tiles t, t + 1, t + 2
-    slot_load(0, 0);
-    wait_vmem<4>();
-    dummy_load();
-    slot_load(1, 1);
-    wait_vmem<4>();
-    vq0 = record_load(0, 0, smem);
-    slot_load(2, 2);
-    wait_vmem<4>();
-    vq1 = record_load(1, 1, smem + kStage);
+    uint32_t vq0 = 0, vq1 = 0, vq2;           // usable tokens of tiles t, t + 1, t + 2
+    int ring_w = 0, ring_r = 0;               // ring slots of S(t + 2 + A) and S(t + 2)
+    auto next_ring = [](int r) { return r == kSlotRing - 1 ? 0 : r + 1; };
+#pragma unroll
+    for (int i = -(kDepth + kAhead); i < 0; ++i) {
+        slot_load(i + kDepth + kAhead, ring_w);
+        ring_w = next_ring(ring_w);
+        wait_vmem<4 * kAhead>();
+        if (i + kDepth == 0) {
+            vq0 = record_load(0, ring_r, smem);
+            ring_r = next_ring(ring_r);
+        } else if (i + kDepth == 1) {
+            vq1 = record_load(1, ring_r, smem + kStage);
+            ring_r = next_ring(ring_r);
+        } else {
+            dummy_load();
+        }
+    }
     auto step = [&](int t, auto K) {
         constexpr int k = decltype(K)::value;             // t % 3
         constexpr int k2 = (k + 2) % 3;
         wait_vmem<4>();
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        slot_load(t + 3, k);
-        wait_vmem<4>();
-        vq2 = record_load(t + 2, k2, smem + k2 * kStage);
+        slot_load(t + kDepth + kAhead, ring_w);
+        ring_w = next_ring(ring_w);
+        wait_vmem<4 * kAhead>();
+        vq2 = record_load(t + 2, ring_r, smem + k2 * kStage);
+        ring_r = next_ring(ring_r);
         if (run_compute) compute(smem + k * kStage, vq0);
         vq0 = vq1;
         vq1 = vq2;

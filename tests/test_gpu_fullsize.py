@@ -1,0 +1,180 @@
+"""GPU parity at the full workload sizes, in the launch configuration bench.py times.
+
+The fp64 oracle cannot redo a whole step of these workloads, so:
+
+* decode: every request's cache is filled (by the library's append, from the
+  seeded generator's K/V), except for a few sampled requests whose pool bytes
+  the oracle writes itself from the same generator's values; the whole batch
+  is decoded on the GPU with the default split-K plan, and the sampled
+  requests' outputs are compared with the oracle's fp64 decode of those bytes
+  (max over q heads of ||o - o_ref||_inf / ||o_ref||_inf <= 2e-3);
+* append: one call appends all 131,072 tokens of the append workload; on a
+  seeded sample of tokens the rotated values are checked against the exact
+  product (normwise <= 1e-5 and inside the per-element bound of the matrix-core
+  accumulation) and the codes, (s, z) and BF16 stores must equal, bit for bit,
+  what the oracle's quantiser makes of the GPU's own rotated values.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import attention, cache, quant
+from rotated_int2_kv_amd import workloads
+
+import gpu_setup as gs
+import parity_tools as pt
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+CHUNK = 131072
+
+
+def _fill_and_sample(w, sampled, q_stream):
+    """Fill a full-size cache; return the GPU outputs and the oracle's for `sampled`."""
+    torch = gs.torch_gpu()
+    from rotated_int2_kv_amd import binding as B
+    lens = np.asarray(w.seq_lens, np.int32)
+    bsz = len(lens)
+    lay_b, _ = gs.layouts(w, w.num_slots, bsz)
+    r_k, r_v = gs.oracle_rotations(w)
+    rk_d, rv_d = gs.dev(r_k), gs.dev(r_v)
+    slots = workloads.slot_table(w)
+    pool = B.new_pool(lay_b)
+    after = gs.dev(lens)
+    rec_view = pool.records[: w.num_slots * lay_b.num_kv_heads * 96].view(w.num_slots, -1)
+    shp = (bsz, w.sink, w.num_kv_heads, 2, w.head_dim)
+    sink_view = pool.sink[: int(np.prod(shp))].view(shp)
+    shp_r = (bsz, w.recent, w.num_kv_heads, 2, w.head_dim)
+    recent_view = pool.recent[: int(np.prod(shp_r))].view(shp_r)
+    refs = {}
+    for b in range(bsz):
+        L = int(lens[b])
+        if b not in sampled:
+            for c0 in range(0, L, CHUNK):
+                c1 = min(L, c0 + CHUNK)
+                k, v = workloads.raw_kv_device(w, c1 - c0, stream=b * 1000 + c0 // CHUNK, device="cuda")
+                B.oscar_quant_append(lay_b, pool, k.to(torch.bfloat16), v.to(torch.bfloat16),
+                                     gs.dev(np.full(c1 - c0, b, np.int32)),
+                                     gs.dev(np.arange(c0, c1, dtype=np.int32)), gs.dev(slots[b][c0:c1]),
+                                     after, rk_d, rv_d)
+                del k, v
+            continue
+        # the oracle writes this request's bytes from the same generator's values
+        k, v = workloads.raw_kv_device(w, L, stream=b * 1000, device="cuda")
+        kh = k.to(torch.bfloat16).float().cpu().numpy()
+        vh = v.to(torch.bfloat16).float().cpu().numpy()
+        del k, v
+        lay_c = cache.Layout(w.head_dim, w.group_size, w.num_kv_heads, w.num_q_heads, w.sink,
+                             w.recent, L, 1)
+        opool = cache.new_pool(lay_c)
+        gs.say(f"  oracle append of request {b} (L = {L})")
+        cache.append(opool, lay_c, kh, vh, np.zeros(L, np.int64), np.arange(L), np.arange(L), [L],
+                     r_k, r_v)
+        del kh, vh
+        rec_view[torch.from_numpy(slots[b].astype(np.int64)).cuda()] = torch.from_numpy(opool.records).cuda()
+        sink_view[b] = torch.from_numpy(opool.sink[0].view(np.int16)).cuda()
+        recent_view[b] = torch.from_numpy(opool.recent[0].view(np.int16)).cuda()
+        refs[b] = (opool, lay_c)
+    torch.cuda.synchronize()
+
+    q = workloads.queries(w, n_rows=bsz, stream=q_stream)
+    qd = torch.from_numpy(q).to(torch.bfloat16).cuda()
+    qh = qd.float().cpu().numpy()
+    table = gs.dev(workloads.req_to_slot_matrix(w, slots, fill=0))
+    ws = torch.empty(B.oscar_decode_workspace_size(lay_b, lens), dtype=torch.uint8, device="cuda")
+    out = torch.empty((bsz, w.num_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    gs.say(f"  decode {w.name}: batch {bsz}, plan {B.oscar_decode_plan(lay_b, lens)}")
+    B.oscar_decode_attn(lay_b, pool, qd, gs.dev(np.arange(bsz, dtype=np.int32)), gs.dev(lens), lens,
+                        table, rk_d, rv_d, w.head_dim ** -0.5, out, ws)
+    torch.cuda.synchronize()
+    o_gpu = out.cpu().numpy()
+    assert np.all(np.isfinite(o_gpu))
+    errs = {}
+    for b, (opool, lay_c) in refs.items():
+        L = int(lens[b])
+        o_ref = attention.decode(opool, lay_c, qh[b:b + 1], [0], [L], np.arange(L)[None, :], r_k, r_v,
+                                 w.head_dim ** -0.5)
+        errs[b] = pt.normwise_rel(o_gpu[b:b + 1], o_ref)
+    return errs
+
+
+def _check(errs, label):
+    for b, e in errs.items():
+        gs.say(f"  {label} request {b}: max normwise rel err {e.max():.3e} (median {np.median(e):.3e})")
+        assert e.max() <= TOL
+
+
+def test_decode_b32_full_size_sampled():
+    """32 requests x 100,000 tokens, 32 q / 8 KV heads (the bench workload)."""
+    w = workloads.workload("decode_b32")
+    gs.say("decode_b32 full size")
+    _check(_fill_and_sample(w, sampled={13}, q_stream=7), "decode_b32")
+
+
+def test_layer_32k_full_size():
+    """One request of 32,768 tokens, 32 q / 8 KV heads: every output checked."""
+    w = workloads.workload("layer_32k")
+    gs.say("layer_32k full size")
+    _check(_fill_and_sample(w, sampled={0}, q_stream=3), "layer_32k")
+
+
+def test_mixed_b64_full_size_sampled():
+    """64 requests of 4,096..131,072 tokens, 24 q / 4 KV heads (g = 6),
+    fragmented slots: the shortest and the longest request are checked."""
+    w = workloads.workload("mixed_b64")
+    lens = np.asarray(w.seq_lens)
+    sampled = {int(lens.argmin()), int(lens.argmax())}
+    gs.say(f"mixed_b64 full size, sampled {sorted(sampled)} (L = {sorted(lens[sorted(sampled)])})")
+    _check(_fill_and_sample(w, sampled=sampled, q_stream=5), "mixed_b64")
+
+
+def test_append_131k_full_size_sampled():
+    """One call appends 131,072 tokens x 8 KV heads; a seeded sample is checked."""
+    torch = gs.torch_gpu()
+    from rotated_int2_kv_amd import binding as B
+    w = workloads.workload("append_131k")
+    n = w.seq_lens[0]
+    hkv = w.num_kv_heads
+    lay_b, lay_o = gs.layouts(w, w.num_slots, 1)
+    r_k, r_v = gs.oracle_rotations(w)
+    k, v = workloads.raw_kv_device(w, n, stream=0, device="cuda")
+    k, v = k.to(torch.bfloat16), v.to(torch.bfloat16)
+    slots = workloads.slot_table(w)[0]
+    pool = B.new_pool(lay_b)
+    rot = torch.empty((n, hkv, 2, w.head_dim), dtype=torch.float32, device="cuda")
+    gs.say("append_131k full size")
+    B.oscar_quant_append(lay_b, pool, k, v, gs.dev(np.zeros(n, np.int32)),
+                         gs.dev(np.arange(n, dtype=np.int32)), gs.dev(slots),
+                         gs.dev(np.array([n], np.int32)), gs.dev(r_k), gs.dev(r_v), 1.0, rot)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(31)
+    # sample: random tokens plus every sink and recent-window position
+    idx = np.unique(np.concatenate([rng.choice(n, 4096, replace=False), np.arange(w.sink),
+                                    np.arange(n - w.recent, n)]))
+    it = torch.from_numpy(idx).cuda()
+    gpu_rot = rot[it].cpu().numpy()
+    kh = k[it].float().cpu().numpy()
+    vh = v[it].float().cpu().numpy()
+    rec, sink, recent = gs.pool_host(pool, lay_o)
+    del rot
+    for t, (x, rr) in enumerate(((kh, r_k), (vh, r_v))):
+        for h in range(hkv):
+            delta, exact = pt.delta_bound(x[:, h, :], rr[h], 3 * w.head_dim)
+            g = gpu_rot[:, h, t, :]
+            assert np.all(np.abs(g - exact) <= delta)
+            assert pt.normwise_rel(g, exact).max() <= 1e-5
+    pooled = idx >= w.sink
+    codes, s, z = quant.quantize(gpu_rot[pooled], w.group_size)      # [m, hkv, 2, d] from the GPU's x'
+    want = np.zeros((int(pooled.sum()), hkv, 96), np.uint8)
+    for t in range(2):
+        want[:, :, 32 * t:32 * t + 32] = quant.pack(codes[:, :, t, :])
+        want[:, :, 64 + 16 * t:80 + 16 * t] = cache.sz_to_bytes(s[:, :, t, :], z[:, :, t, :])
+    got = rec[slots[idx[pooled]]].reshape(-1, hkv, 96)
+    mism = int((got != want).sum())
+    gs.say(f"  {pooled.sum()} pooled tokens: {mism} byte mismatches")
+    assert mism == 0
+    bits = quant.bf16_bits(gpu_rot)
+    sk = idx < w.sink
+    assert np.array_equal(sink[0, idx[sk]], bits[sk])
+    rg = idx >= n - w.recent
+    assert np.array_equal(recent[0, idx[rg] % w.recent], bits[rg])

@@ -53,6 +53,18 @@ struct AppendArgs {
     float alpha;
 };
 
+// The exact sum a + b of two fp32 values, rounded toward +infinity: the
+// round-to-nearest sum S and its exact error e (Knuth's TwoSum, no fused
+// operations), then one ulp up if e > 0.  S is never zero when e != 0.
+__device__ __forceinline__ float round_up_sum(float a, float b) {
+    const float s = __fadd_rn(a, b);
+    const float bb = __fsub_rn(s, a);
+    const float e = __fadd_rn(__fsub_rn(a, __fsub_rn(s, bb)), __fsub_rn(b, bb));
+    const int u = __float_as_int(s);
+    const float up = __int_as_float(u >= 0 ? u + 1 : u - 1);
+    return e > 0.0f ? up : s;
+}
+
 // Split an fp32 value into three bf16 terms whose sum is the value.
 __device__ __forceinline__ void split3(float x, uint16_t &a, uint16_t &b, uint16_t &c) {
     a = bf16_bits_rn(x);
@@ -64,7 +76,7 @@ __device__ __forceinline__ void split3(float x, uint16_t &a, uint16_t &b, uint16
 
 template <int XT>
 __global__ __launch_bounds__(kThreads) void quant_append_kernel(AppendArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[XT * kPlaneBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_buf[2][XT * kPlaneBytes];
 
     // XCD-aware block order: blocks are dealt round-robin to the 8 XCDs, so
     // all 2*Hkv workgroups of one token chunk land on the same XCD and its L2
@@ -128,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(AppendArgs a) {
             }
         }
     };
-    auto store_tile = [&](const u32x4 &r0, const u32x4 &r1) {
+    auto store_tile = [&](uint8_t *lds, const u32x4 &r0, const u32x4 &r1) {
         uint8_t *dst = lds + st_row * kRowBytes + 16 * st_col;
         if constexpr (XT == 1) {
             *reinterpret_cast<u32x4 *>(dst) = r0;
@@ -164,14 +176,44 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(AppendArgs a) {
     };
 
     const int64_t rec_bytes = int64_t(a.hkv) * kHeadRecord;
-    u32x4 pr0, pr1;
-    load_tile(tok_begin, pr0, pr1);
+    // kDepth tiles of input in flight in registers (the waits are the
+    // compiler's); the LDS tile is double-buffered, so one barrier per tile
+    // both publishes the new tile and retires the buffer it overwrites next
+    constexpr int kDepth = 2;
+    u32x4 pr0[kDepth], pr1[kDepth];
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) load_tile(tok_begin + d * kTile, pr0[d], pr1[d]);
 
-    for (int tb = tok_begin; tb < tok_end; tb += kTile) {
+    // per-token routing data of this lane's token (tb + n), fetched ahead:
+    // request, position and slot two tiles early, the request's length one
+    // tile early, so that no tile waits on a dependent global load
+    auto load_meta = [&](int tb, int &req, int &pos, int &slot) {
+        const int tok = tb + n;
+        const int tc = tok < tok_end ? tok : tok_begin;
+        req = a.req_ids[tc];
+        pos = a.positions[tc];
+        slot = a.slots[tc];
+    };
+    auto load_len = [&](int req) {
+        return a.seq_len_after[(req >= 0 && req < a.max_requests) ? req : 0];
+    };
+    int req0, pos0, slot0, req1, pos1, slot1;
+    load_meta(tok_begin, req0, pos0, slot0);
+    load_meta(tok_begin + kTile, req1, pos1, slot1);
+    int len0 = load_len(req0);
+
+    for (int tb0 = tok_begin; tb0 < tok_end; tb0 += kDepth * kTile) {
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+        const int tb = tb0 + d * kTile;
+        if (tb >= tok_end) break;
+        uint8_t *lds = lds_buf[d & 1];
+        store_tile(lds, pr0[d], pr1[d]);
         __syncthreads();
-        store_tile(pr0, pr1);
-        __syncthreads();
-        if (tb + kTile < tok_end) load_tile(tb + kTile, pr0, pr1);
+        load_tile(tb + kDepth * kTile, pr0[d], pr1[d]);
+        int req2, pos2, slot2;
+        load_meta(tb + 2 * kTile, req2, pos2, slot2);
+        const int len1 = load_len(req1);
 
         // x'^T (16 out channels x 16 tokens) per M-tile
         f32x4 acc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
@@ -208,11 +250,12 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(AppendArgs a) {
         hi = fmaxf(hi, __shfl_xor(hi, 32));
 
         const int tok = tb + n;
+        const int req = req0, pos = pos0, slot = slot0, L = len0;
+        // the next tile's routing data moves up (every lane, before any early exit)
+        req0 = req1; pos0 = pos1; slot0 = slot1; len0 = len1;
+        req1 = req2; pos1 = pos2; slot1 = slot2;
         if (tok >= tok_end) continue;
-        const int req = a.req_ids[tok];
-        const int pos = a.positions[tok];
         if (req < 0 || req >= a.max_requests || pos < 0) continue;
-        const int slot = a.slots[tok];
         const bool to_sink = pos < a.sink_tokens;
         if (!to_sink && (slot < 0 || int64_t(slot) >= a.num_slots)) continue;
 
@@ -239,18 +282,21 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(AppendArgs a) {
         const float range = __fsub_rn(hi_c, lo_c);
         const __half s = __float2half_rn(__fdiv_rn(range, 3.0f));
         const __half z = __float2half_rn(lo_c);
-        const double sd = double(__half2float(s)), zd = double(__half2float(z));
-        // thresholds z + (k + 1/2) s are exact in fp64; rounding them up to fp32
-        // keeps "x >= T" exact for fp32 x
-        const float t0 = __double2float_ru(zd + 0.5 * sd);
-        const float t1 = __double2float_ru(zd + 1.5 * sd);
-        const float t2 = __double2float_ru(zd + 2.5 * sd);
-        const bool zero_scale = __half2float(s) == 0.0f;
+        // thresholds z + (k + 1/2) s, rounded up to fp32, so that "x >= T" is
+        // exact for fp32 x; a scale of zero gives +inf thresholds (codes 0)
+        const float sf = __half2float(s), zf = __half2float(z);
+        const float t0 = round_up_sum(zf, 0.5f * sf);
+        const float t1 = round_up_sum(zf, 1.5f * sf);
+        const float t2 = round_up_sum(zf, 2.5f * sf);
+        const bool zero_scale = sf == 0.0f;
+        const float u0 = zero_scale ? INFINITY : t0;
+        const float u1 = zero_scale ? INFINITY : t1;
+        const float u2 = zero_scale ? INFINITY : t2;
         uint32_t packed = 0;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const float xc = fminf(fmaxf(vals[j], lo_c), hi_c);
-            const uint32_t c = zero_scale ? 0u : uint32_t(xc >= t0) + uint32_t(xc >= t1) + uint32_t(xc >= t2);
+            const float xc = __builtin_amdgcn_fmed3f(vals[j], lo_c, hi_c);   // lo_c <= hi_c
+            const uint32_t c = uint32_t(xc >= u0) + uint32_t(xc >= u1) + uint32_t(xc >= u2);
             packed |= c << (2 * j);
         }
         uint8_t *rec = a.records + int64_t(slot) * rec_bytes + h * kHeadRecord;
@@ -259,13 +305,13 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(AppendArgs a) {
             const uint32_t sz = uint32_t(__half_as_ushort(s)) | (uint32_t(__half_as_ushort(z)) << 16);
             *reinterpret_cast<uint32_t *>(rec + 2 * kCodeBytes + t * kSzBytes + 4 * w) = sz;
         }
-        const int L = a.seq_len_after[req];
         if (pos >= L - a.recent_tokens) {
             uint16_t *dst = a.recent +
                             ((size_t(req) * a.recent_tokens + pos % a.recent_tokens) * a.hkv + h) * 2 * kHeadDim +
                             t * kHeadDim + c0;
             *reinterpret_cast<u32x4 *>(dst) = bf;
         }
+    }
     }
 }
 
@@ -300,8 +346,18 @@ extern "C" oscar_status oscar_quant_append(hipStream_t stream, const oscar_layou
         if (chunk < 16 || chunk % 16)
             return fail(OSCAR_ERR_INVALID_ARG, "append_chunk must be a positive multiple of 16");
     } else {
-        // about 768 workgroups (three per compute unit)
-        const int per = std::max(1, (768 + 2 * layout->num_kv_heads - 1) / (2 * layout->num_kv_heads));
+        // one round of workgroups that are all resident at once: compute
+        // units x workgroups per compute unit (from the kernel's registers)
+        int dev = 0, cus = 0, per_cu = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return fail(OSCAR_ERR_HIP, "querying the device failed");
+        const void *kern = in_dtype == OSCAR_BF16 ? reinterpret_cast<const void *>(quant_append_kernel<1>)
+                                                  : reinterpret_cast<const void *>(quant_append_kernel<3>);
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, 0) != hipSuccess)
+            return fail(OSCAR_ERR_HIP, "occupancy query failed");
+        const int slots = std::max(1, cus * std::max(1, per_cu));
+        const int per = std::max(1, slots / (2 * layout->num_kv_heads));
         chunk = (n_tokens + per - 1) / per;
         chunk = std::max(16, (chunk + 15) / 16 * 16);
     }

@@ -239,12 +239,13 @@ __device__ __forceinline__ float half_hi(uint32_t w) { return __half2float(__ush
 // line.  Token t of a tile occupies 384 bytes of the stage; within each of
 // its three 128-byte lines the 16-byte units are permuted by XOR with
 // (t / 2) % 8, so that the same field of 16 consecutive tokens falls in 16
-// different LDS bank groups.  Three stages let two tiles be in flight while a
-// third is computed; one workgroup barrier per tile publishes a landed tile
-// and retires the stage that the next loads overwrite.  Each wave fetches its
-// own copy of the tile's slot ids kAhead tiles before the records.  Tokens past the
-// item or with an out-of-range slot read a zero record, so they arrive as
-// s = z = 0 and codes 0, and are masked out of the softmax.
+// different LDS bank groups.  Four stages let three tiles be in flight while
+// a fourth is computed; one workgroup barrier per tile publishes a landed
+// tile and retires the stage that the next loads overwrite.  The slot ids of
+// a tile go to a ring shared by the workgroup (each wave fetches 8 of them)
+// two tiles before its records.  Tokens past the item or with an
+// out-of-range slot read a zero record, so they arrive as s = z = 0 and
+// codes 0, and are masked out of the softmax.
 //
 // QK (per half of 16 tokens): B = the tokens' K codes as exact fp16 denormals
 // (one AND per pair, no scale); A = q' (hi and lo fp16 parts, times
@@ -261,27 +262,59 @@ __device__ __forceinline__ float half_hi(uint32_t w) { return __half2float(__ush
 // codes of tokens t, t + 1, t + 4, t + 5 at once, which the token swizzle
 // puts in disjoint LDS banks.  Weight rows are 64 bytes with their 16-byte
 // units permuted by XOR with row / 4, which keeps both the 16-bit weight
-// writes and the 128-bit operand reads free of bank conflicts.
+// writes and the 128-bit operand reads free of bank conflicts.  The weight
+// rows live in the stage itself: once a wave has read its K codes and both
+// (s, z) of the tile into registers, those 128 units of its head are dead,
+// and each 16-byte unit of the weight rows takes a dead unit at the same
+// address modulo 256 (so the same banks as a dense layout).
 constexpr int kTokBytes = 4 * kHeadRecord;             // 384: one token of a head chunk
 constexpr int kStage = kTileTokens * kTokBytes;        // 12 KiB per tile
-constexpr int kDepth = 2;                              // record tiles in flight during a compute
-constexpr int kStages = kDepth + 1;
-constexpr int kAhead = 1;                              // slot ids fetched this many tiles before their records
-constexpr int kSlotRing = kAhead + 2;                  // slot-id buffers of 64 entries (per wave)
-constexpr int kWPlane = 16 * kTileTokens * 2;          // 16 rows (g, h) x 32 fp16 weights: 1 KiB
-constexpr int kWSetBytes = 2 * kWPlane;                // hi and lo planes of one set of 4 heads
-__host__ __device__ constexpr int wave_lds_bytes(int gq) {
-    return kSlotRing * 256 + ((gq + 3) / 4) * kWSetBytes;
-}
-__host__ __device__ constexpr int int2_lds_bytes(int gq) { return kStages * kStage + kPartialWaves * wave_lds_bytes(gq); }
+constexpr int kStages = 4;                             // three tiles in flight while one is computed
+constexpr int kRingBytes = kTileTokens * 4;            // slot ids of one tile
+constexpr int kRing = 4;                               // slot-id ring of the workgroup
+constexpr int kHalfTok = 16 * kTokBytes;               // token 16 + t of a stage is this far after token t
+__host__ __device__ constexpr int int2_lds_bytes() { return kStages * kStage + kRing * kRingBytes; }
 
 // byte offset of 16-byte unit q (0..23) of token t inside a stage
 __device__ __forceinline__ int unit_addr(int t, int q) {
     return t * kTokBytes + 16 * ((q & ~7) | ((q & 7) ^ ((t >> 1) & 7)));
 }
 
+// Byte offset inside a stage of unit u (0..3) of row r (0..15) of wave w's
+// PV weight plane 0 (hi parts); plane 1 (lo parts) is kHalfTok further.
+// Row r's units go to K-code or (s, z) unit {0, 1, 4, 5}[r / 4] of w's head
+// record, of the token among 0..15 whose swizzle puts the unit at bank group
+// (4 r + u) % 16: the bank group of unit (r, u) in a dense 64-byte-row plane.
+__device__ __forceinline__ int wunit_addr(int w, int r, int u) {
+    const int q = 6 * w + ((r >> 2) & 1) + 4 * (r >> 3);
+    const int bg = 4 * (r & 3) + u;
+    const int t = 2 * ((bg & 7) ^ (q & 7)) + ((bg >> 3) ^ ((q >> 3) & 1));
+    return unit_addr(t, q);
+}
+
 typedef __attribute__((address_space(3))) void lds_void;
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+// LDS byte addresses as 32-bit integers.  Per-lane addresses are computed
+// once per item and hidden from the optimiser (`lds_pin`), so that inside the
+// tile loop every LDS access is one instruction: a pinned register plus a
+// constant offset (the stage), with no re-added base.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return uint32_t(reinterpret_cast<uintptr_t>((const lds_void *)p));
+}
+__device__ __forceinline__ uint32_t lds_pin(uint32_t x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+template <class T>
+__device__ __forceinline__ T lds_ld(uint32_t addr) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) T *>(uintptr_t(addr));
+}
+template <class T>
+__device__ __forceinline__ void lds_st(uint32_t addr, T v) {
+    *reinterpret_cast<__attribute__((address_space(3))) T *>(uintptr_t(addr)) = v;
+}
+__device__ __forceinline__ lds_void *lds_ptr(uint32_t addr) { return reinterpret_cast<lds_void *>(uintptr_t(addr)); }
 
 // Wait until at most N vector-memory operations of this wave are pending.
 // The compiler does not track global_load_lds, so the pipeline below waits
@@ -295,7 +328,7 @@ template <int GQ>
 __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, int p0, int p1,
                           uint8_t *smem) {
     constexpr int HS = (GQ + 3) / 4;          // sets of 4 query heads
-    const int w = threadIdx.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform over the wave
     const int lane = threadIdx.x & 63;
     const int n = lane & 15;
     const int kb = lane >> 4;
@@ -305,8 +338,8 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, in
     const uint32_t rec_bytes = uint32_t(a.hkv) * kHeadRecord;
     const int32_t *r2s = a.req_to_slot + int64_t(req) * a.r2s_stride;
     const int n_tiles = (p1 - p0 + kTileTokens - 1) / kTileTokens;
-    uint8_t *ring = smem + kStages * kStage + w * wave_lds_bytes(GQ);
-    uint8_t *wbuf = ring + kSlotRing * 256;
+    const uint32_t st0 = lds_addr(smem);                                // stage 0
+    const uint32_t ring = st0 + kStages * kStage;                         // slot-id ring of the workgroup
     const size_t head0 = size_t(b) * a.hq + size_t(active ? hk : 0) * GQ;
 
     // ---- per-item operands
@@ -365,40 +398,41 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, in
         real[u] = q / 6 < nh;
     }
 
-    // ---- loads.  Iteration t issues S(t + 2 + A), the slot ids of tile
-    // t + 2 + A (A = kAhead), and R(t + 2), this wave's three record loads of
-    // tile t + 2: two record tiles are in flight while tile t is computed, and
-    // a record load uses slot ids fetched A iterations earlier.  Every iteration issues
-    // the same four operations, including tiles past the end (which read
-    // position p0 and the zero record), and so does the prologue, whose first
-    // record loads are dummies: the wait counts are constants.
+    // ---- loads.  Iteration t issues S(t + 5), this wave's 8 of the slot ids
+    // of tile t + 5, and R(t + 3), this wave's three record loads of tile
+    // t + 3: three record tiles are in flight while tile t is computed.  Every
+    // iteration issues the same four operations, including tiles past the end
+    // (which read position p0 and the zero record), and so does the prologue:
+    // the wait counts are constants.  The slot ids of tile T go to ring slot
+    // T % 4 and its records to stage T % 4.
     const uint32_t span = uint32_t(p1 - p0);
-    auto slot_load = [&](int T, int ring_slot) {
-        const uint32_t off = uint32_t(T * kTileTokens + (lane & 31));
+    auto slot_load = [&](int T, int rs) {
+        const uint32_t off = uint32_t(T * kTileTokens + 8 * w + (lane & 7));
         const int32_t *src = r2s + p0 + (off < span ? off : 0u);
-        __builtin_amdgcn_global_load_lds(src, (lds_void *)(ring + ring_slot * 256), 4, 0, 0);
+        if (lane < 8) __builtin_amdgcn_global_load_lds(src, lds_ptr(ring + rs * kRingBytes + 32 * w), 4, 0, 0);
     };
-    // record loads of tile T into `st`; returns the usable tokens (bit t)
-    auto record_load = [&](int T, int ring_slot, uint8_t *st) -> uint32_t {
-        const int *slots = reinterpret_cast<const int *>(ring + ring_slot * 256);
+    uint32_t slot_at[3];                      // ring addresses of the slot ids of tokens tq[u]
+#pragma unroll
+    for (int u = 0; u < 3; ++u) slot_at[u] = lds_pin(ring + 4 * tq[u]);
+    const uint32_t slot_own = lds_pin(ring + 4 * (lane & 31));
+    // record loads of tile T into stage `k`; returns the usable tokens (bit t).
+    // All slot ids are read before the first load is issued (the loads write
+    // LDS, so later reads could not be moved above them).
+    auto record_load = [&](int T, int k) -> uint32_t {
+        int slot[3];
+#pragma unroll
+        for (int u = 0; u < 3; ++u) slot[u] = lds_ld<int>(slot_at[u] + k * kRingBytes);
+        const int s_own = lds_ld<int>(slot_own + k * kRingBytes);
         const uint32_t left = span - uint32_t(T * kTileTokens);   // positions left in the item (may wrap: none)
         const uint32_t n_ok = uint32_t(T * kTileTokens) < span ? left : 0u;
 #pragma unroll
         for (int u = 0; u < 3; ++u) {
-            const int slot = slots[tq[u]];
-            const bool ok = real[u] & (uint32_t(tq[u]) < n_ok) & (uint32_t(slot) < uint32_t(a.num_slots));
-            const uint8_t *src = a.records + uint64_t(uint32_t(slot)) * rec_bytes + src_off[u];
+            const bool ok = real[u] & (uint32_t(tq[u]) < n_ok) & (uint32_t(slot[u]) < uint32_t(a.num_slots));
+            const uint8_t *src = a.records + uint64_t(uint32_t(slot[u])) * rec_bytes + src_off[u];
             src = ok ? src : a.zero_rec;
-            __builtin_amdgcn_global_load_lds(src, (lds_void *)(st + 1024 * (3 * w + u)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(src, lds_ptr(st0 + k * kStage + 1024 * (3 * w + u)), 16, 0, 0);
         }
-        const int s_own = slots[lane & 31];
         return uint32_t(__ballot((uint32_t(lane & 31) < n_ok) & (uint32_t(s_own) < uint32_t(a.num_slots))));
-    };
-    // stand-in for the record loads of the prologue's first iteration: the
-    // zero record into this wave's PV weight rows, which are written only later
-    auto dummy_load = [&]() {
-#pragma unroll
-        for (int u = 0; u < 3; ++u) __builtin_amdgcn_global_load_lds(a.zero_rec, (lds_void *)wbuf, 16, 0, 0);
     };
     // LDS is used by this wave alone and runs a wave's operations in order;
     // the fences keep the compiler from moving LDS accesses across them
@@ -420,42 +454,42 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, in
         for (int jj = 0; jj < 8; ++jj) oacc[hs][jj] = f32x4{0, 0, 0, 0};
     }
 
-    // this lane's LDS reads inside a stage (head w of token t)
-    const int qk_off0 = unit_addr(n, 6 * w + (kb >> 1)) + 8 * (kb & 1);          // K codes, token n
-    const int qk_off1 = unit_addr(16 + n, 6 * w + (kb >> 1)) + 8 * (kb & 1);     // token 16 + n
-    const int szk_off0 = unit_addr(n, 6 * w + 4), szk_off1 = unit_addr(16 + n, 6 * w + 4);
-    const int szv_off0 = unit_addr(n, 6 * w + 5), szv_off1 = unit_addr(16 + n, 6 * w + 5);
-    int pv_off[8];        // V codes (channels 8 n .. 8 n + 7) of the tokens of K-slots 8 kb + i
+    // this lane's LDS addresses in stage 0 (head w of token t); token 16 + t
+    // of a stage is 6144 bytes after token t (same swizzle)
+    constexpr int kHalfTok = 16 * kTokBytes;
+    const uint32_t qk_at = lds_pin(st0 + unit_addr(n, 6 * w + (kb >> 1)) + 8 * (kb & 1));   // K codes
+    const uint32_t szk_at = lds_pin(st0 + unit_addr(n, 6 * w + 4));
+    const uint32_t szv_at = lds_pin(st0 + unit_addr(n, 6 * w + 5));
+    uint32_t pv_at[8];    // V codes (channels 8 n .. 8 n + 7) of the tokens of K-slots 8 kb + i
     const int kb_tok = (kb & 1) + 4 * (kb >> 1);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-        pv_off[i] = unit_addr(2 * (i & 1) + 8 * (i >> 1) + kb_tok, 6 * w + 2 + (n >> 3)) + ((2 * n) & 15);
-    // weight-plane byte offset (row and unit) of token t for this lane's rows (g, kb)
-    auto wslot = [&](int t, int g) {
-        const int unit = (t & 1) + 2 * ((t >> 2) & 1);              // K-slot / 8
-        const int i = ((t >> 1) & 1) + 2 * (t >> 3);                // K-slot % 8
-        const int row = 4 * g + kb;
-        return row * 64 + 16 * (unit ^ g) + 2 * i;
-    };
-    int woff[2][4];
+        pv_at[i] = lds_pin(st0 + unit_addr(2 * (i & 1) + 8 * (i >> 1) + kb_tok, 6 * w + 2 + (n >> 3)) + ((2 * n) & 15));
+    // PV weight of token t (0..15; token 16 + t sits 8 bytes further) for this
+    // lane's row (g, kb): K-slot 8 unit + i of the row, unit XOR-permuted by g
+    uint32_t w_at[4];
+    {
+        const int unit = (n & 1) + 2 * ((n >> 2) & 1);              // K-slot / 8
+        const int i = ((n >> 1) & 1) + 2 * (n >> 3);                // K-slot % 8
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) woff[hf][g] = wslot(16 * hf + n, g);
+        for (int g = 0; g < 4; ++g) w_at[g] = lds_pin(st0 + wunit_addr(w, 4 * g + kb, unit ^ g) + 2 * i);
+    }
     // A-operand read of row n, K-slots 8 kb .. 8 kb + 7
-    const int aoff = n * 64 + 16 * (kb ^ (n >> 2));
+    const uint32_t a_at = lds_pin(st0 + wunit_addr(w, n, kb ^ (n >> 2)));
 
-    // one tile: QK, online softmax, PV (reads LDS stage `st`)
-    auto compute = [&](const uint8_t *st, uint32_t valid) {
+    // one tile: QK, online softmax, PV (LDS stage K)
+    auto compute = [&](auto K, uint32_t valid) {
+        constexpr uint32_t so = decltype(K)::value * kStage;   // stage offset
         // ---- QK: logit of (token 16 hf + n, head 4 hs + kb)
         float lg[HS][2];
         u32x4 szv[2];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             const int tk = 16 * hf + n;
-            const u32x2 kc = *reinterpret_cast<const u32x2 *>(st + (hf ? qk_off1 : qk_off0));
-            const u32x4 szk = *reinterpret_cast<const u32x4 *>(st + (hf ? szk_off1 : szk_off0));
-            szv[hf] = *reinterpret_cast<const u32x4 *>(st + (hf ? szv_off1 : szv_off0));
+            const uint32_t ho = so + hf * kHalfTok;
+            const u32x2 kc = lds_ld<u32x2>(qk_at + ho);
+            const u32x4 szk = lds_ld<u32x4>(szk_at + ho);
+            szv[hf] = lds_ld<u32x4>(szv_at + ho);
             const uint32_t d0s = kc[0] >> 6, d1s = kc[1] >> 6;
             f16x8 B[4];
 #pragma unroll
@@ -482,9 +516,9 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, in
                 lg[hs][hf] = fmaf(xa + xb, qout[hs], live ? 0.0f : -INFINITY);
             }
         }
-        // ---- online softmax; PV weights to LDS
+        // ---- online softmax
         bool grow[HS];
-        float alpha[HS];
+        float alpha[HS], pw[HS][2];
 #pragma unroll
         for (int hs = 0; hs < HS; ++hs) {
             const float mx = row16_max(fmaxf(lg[hs][0], lg[hs][1]));
@@ -499,14 +533,33 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, in
             }
             // exponent reference: a finite stand-in while every token so far is masked
             const float m_ref = m_run[hs] == -INFINITY ? 0.0f : m_run[hs];
-            uint8_t *wset = wbuf + hs * kWSetBytes;
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
                 const float p = __builtin_amdgcn_exp2f(lg[hs][hf] - m_ref);   // 0 for masked tokens
+                pw[hs][hf] = p;
                 l_lane[hs] += p;
 #pragma unroll
                 for (int g = 0; g < 4; ++g) zl[hs][g] = fmaf(p, half_hi(szv[hf][g]), zl[hs][g]);
-                // w_g = p s_g as hi + lo fp16 parts, both rounded to nearest; lo = w_g - hi
+            }
+        }
+        // ---- PV: A rows (g, h) = weights of K-slots 8 kb .. 8 kb + 7; B = V
+        // codes of channel 8 n + jj for the same tokens, two per 32-bit word
+        uint32_t xw[4], xs[4];
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+            u16x2 pr;
+            pr.x = lds_ld<uint16_t>(pv_at[2 * pp] + so);
+            pr.y = lds_ld<uint16_t>(pv_at[2 * pp + 1] + so);
+            xw[pp] = __builtin_bit_cast(uint32_t, pr);
+            xs[pp] = xw[pp] >> 6;
+        }
+#pragma unroll
+        for (int hs = 0; hs < HS; ++hs) {
+            // w_g = p s_g as hi + lo fp16 parts, both rounded to nearest; lo = w_g - hi.
+            // They overwrite this head's K codes and (s, z) of the stage, read above.
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const float p = pw[hs][hf];
                 uint32_t hw[2], lw[2];
 #pragma unroll
                 for (int q2 = 0; q2 < 2; ++q2) {
@@ -517,27 +570,13 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, in
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int sh = 16 * (g & 1);
-                    *reinterpret_cast<uint16_t *>(wset + woff[hf][g]) = uint16_t(hw[g >> 1] >> sh);
-                    *reinterpret_cast<uint16_t *>(wset + kWPlane + woff[hf][g]) = uint16_t(lw[g >> 1] >> sh);
+                    lds_st<uint16_t>(w_at[g] + so + 8 * hf, uint16_t(hw[g >> 1] >> sh));
+                    lds_st<uint16_t>(w_at[g] + so + 8 * hf + kHalfTok, uint16_t(lw[g >> 1] >> sh));
                 }
             }
-        }
-        lds_order();
-        // ---- PV: A rows (g, h) = weights of K-slots 8 kb .. 8 kb + 7; B = V
-        // codes of channel 8 n + jj for the same tokens, two per 32-bit word
-        uint32_t xw[4], xs[4];
-#pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
-            u16x2 pr;
-            pr.x = *reinterpret_cast<const uint16_t *>(st + pv_off[2 * pp]);
-            pr.y = *reinterpret_cast<const uint16_t *>(st + pv_off[2 * pp + 1]);
-            xw[pp] = __builtin_bit_cast(uint32_t, pr);
-            xs[pp] = xw[pp] >> 6;
-        }
-        // rescale the output rows of heads whose running max grew; PV output
-        // row (g, h) = (kb, i): the factor of head i lives in row i of lanes
-#pragma unroll
-        for (int hs = 0; hs < HS; ++hs) {
+            lds_order();
+            // rescale the output rows of heads whose running max grew; PV output
+            // row (g, h) = (kb, i): the factor of head i lives in row i of lanes
             if (__builtin_expect(grow[hs], 0)) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -547,75 +586,63 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, in
                     for (int jj = 0; jj < 8; ++jj) oacc[hs][jj][i] *= ai;
                 }
             }
-        }
-        f16x8 AS[HS][2];
+            const f16x8 ahi = lds_ld<f16x8>(a_at + so);
+            const f16x8 alo = lds_ld<f16x8>(a_at + so + kHalfTok);
 #pragma unroll
-        for (int hs = 0; hs < HS; ++hs) {
-            const uint8_t *arow = wbuf + hs * kWSetBytes + aoff;
-            AS[hs][0] = *reinterpret_cast<const f16x8 *>(arow);
-            AS[hs][1] = *reinterpret_cast<const f16x8 *>(arow + kWPlane);
-        }
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-            const f16x8 Bj = u4_as_h8(code_bits(xw[0], xs[0], jj), code_bits(xw[1], xs[1], jj),
-                                      code_bits(xw[2], xs[2], jj), code_bits(xw[3], xs[3], jj));
-#pragma unroll
-            for (int hs = 0; hs < HS; ++hs) {
-                oacc[hs][jj] = mfma_f16(AS[hs][0], Bj, oacc[hs][jj]);
-                oacc[hs][jj] = mfma_f16(AS[hs][1], Bj, oacc[hs][jj]);
+            for (int jj = 0; jj < 8; ++jj) {
+                const f16x8 Bj = u4_as_h8(code_bits(xw[0], xs[0], jj), code_bits(xw[1], xs[1], jj),
+                                          code_bits(xw[2], xs[2], jj), code_bits(xw[3], xs[3], jj));
+                oacc[hs][jj] = mfma_f16(ahi, Bj, oacc[hs][jj]);
+                oacc[hs][jj] = mfma_f16(alo, Bj, oacc[hs][jj]);
             }
+            // the next set's weights go to the same units: the reads above come first
+            lds_order();
         }
-        lds_order();
     };
 
-    // ---- pipeline.  At the top of iteration t this wave's R(t) must have
-    // landed (four operations follow it: S(t + 1 + A), R(t + 1)); the
-    // barrier then publishes tile t of every wave and guarantees that every
-    // wave is done with tile t - 1, whose stage R(t + 2) overwrites.  Before
-    // R(t + 2) is issued, S(t + 2) must have arrived: it was issued A
-    // iterations earlier, and 4 A operations follow it.  The prologue issues
-    // the same operations (dummy record loads first), so the counts hold from
-    // the start.  The loop is unrolled by three so that stage offsets are
-    // constants; tiles past the end are computed fully masked.
-    static_assert(kDepth == 2 && kStages == 3, "the unrolled pipeline assumes three stages");
+    // ---- pipeline.  At the top of iteration t, R(t) and S(t + 3) must have
+    // landed: seven operations follow them (R(t + 1), S(t + 4), R(t + 2)).
+    // The barrier then publishes tile t and the slot ids of tile t + 3 of
+    // every wave, and guarantees that every wave is done with tile t - 1,
+    // whose stage R(t + 3) overwrites, and with the slot ids of tile t + 1,
+    // whose ring slot S(t + 5) overwrites.  The prologue issues the same
+    // operations for t = -3 .. -1, so the counts hold from the start.  The
+    // loop is unrolled by four so that stage and ring offsets are constants;
+    // tiles with no usable token (past the end) are not computed.
     const bool run_compute = __builtin_amdgcn_readfirstlane(int(active)) != 0;
-    uint32_t vq0 = 0, vq1 = 0, vq2;           // usable tokens of tiles t, t + 1, t + 2
-    int ring_w = 0, ring_r = 0;               // ring slots of S(t + 2 + A) and S(t + 2)
-    auto next_ring = [](int r) { return r == kSlotRing - 1 ? 0 : r + 1; };
-#pragma unroll
-    for (int i = -(kDepth + kAhead); i < 0; ++i) {
-        slot_load(i + kDepth + kAhead, ring_w);
-        ring_w = next_ring(ring_w);
-        wait_vmem<4 * kAhead>();
-        if (i + kDepth == 0) {
-            vq0 = record_load(0, ring_r, smem);
-            ring_r = next_ring(ring_r);
-        } else if (i + kDepth == 1) {
-            vq1 = record_load(1, ring_r, smem + kStage);
-            ring_r = next_ring(ring_r);
-        } else {
-            dummy_load();
-        }
-    }
-    auto step = [&](int t, auto K) {
-        constexpr int k = decltype(K)::value;             // t % 3
-        constexpr int k2 = (k + 2) % 3;
-        wait_vmem<4>();
+    auto sync = [] {
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        slot_load(t + kDepth + kAhead, ring_w);
-        ring_w = next_ring(ring_w);
-        wait_vmem<4 * kAhead>();
-        vq2 = record_load(t + 2, ring_r, smem + k2 * kStage);
-        ring_r = next_ring(ring_r);
-        if (run_compute) compute(smem + k * kStage, vq0);
+    };
+    uint32_t vq0, vq1, vq2, vq3;              // usable tokens of tiles t .. t + 3
+    slot_load(0, 0);
+    slot_load(1, 1);
+    wait_vmem<0>();
+    sync();
+    slot_load(2, 2);
+    vq0 = record_load(0, 0);
+    slot_load(3, 3);
+    vq1 = record_load(1, 1);
+    wait_vmem<7>();                           // S(2)
+    sync();
+    slot_load(4, 0);
+    vq2 = record_load(2, 2);
+    auto step = [&](int t, auto K) {
+        constexpr int k = decltype(K)::value;             // t % 4
+        wait_vmem<7>();
+        sync();
+        slot_load(t + 5, (k + 1) & 3);
+        vq3 = record_load(t + 3, (k + 3) & 3);
+        if (run_compute && vq0 != 0u) compute(K, vq0);
         vq0 = vq1;
         vq1 = vq2;
+        vq2 = vq3;
     };
-    for (int t = 0; t < n_tiles; t += 3) {
+    for (int t = 0; t < n_tiles; t += 4) {
         step(t, std::integral_constant<int, 0>{});
         step(t + 1, std::integral_constant<int, 1>{});
         step(t + 2, std::integral_constant<int, 2>{});
+        step(t + 3, std::integral_constant<int, 3>{});
     }
     // the trailing (unused) loads still write the stages: let them land
     wait_vmem<0>();
@@ -912,11 +939,10 @@ __global__ __launch_bounds__(512) void merge_kernel(DecodeArgs a) {
     }
 }
 
-// Dynamic LDS of the partial kernel: each wave's two-stage ring of 32 padded
-// token records and PV weight rows for the INT2 items, or its softmax buffer
-// for the BF16 items.
-size_t partial_lds_bytes(const DecodeArgs &a) {
-    const size_t int2 = int2_lds_bytes(a.g);
+// Dynamic LDS of the partial kernel: the four record stages and the slot-id
+// ring of the INT2 items, or each wave's softmax buffer for the BF16 items.
+size_t partial_lds_bytes(const DecodeArgs &) {
+    const size_t int2 = int2_lds_bytes();
     const size_t pbuf = size_t(kPartialWaves) * kBf16WaveFloats * sizeof(float);
     return int2 > pbuf ? int2 : pbuf;
 }

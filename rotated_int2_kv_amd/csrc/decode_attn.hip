@@ -384,55 +384,63 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, in
 
     // ---- what this lane fetches: 16-byte unit P of the stage, for P =
     // 64 (3 w + u) + lane (u = 0..2), holds logical unit q of token tq[u];
-    // units of KV heads past the chunk read the zero record
+    // units of KV heads past the chunk (never read) repeat the chunk's first head
     int tq[3];
-    uint32_t src_off[3];
-    bool real[3];
+    const uint8_t *src_base[3];
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
         const int P = 64 * (3 * w + u) + lane;
         const int t = P / 24, U = P % 24;
         const int q = (U & ~7) | ((U & 7) ^ ((t >> 1) & 7));
         tq[u] = t;
-        src_off[u] = uint32_t(hc * kTokBytes + 16 * q);
-        real[u] = q / 6 < nh;
+        src_base[u] = a.records + hc * kTokBytes + 16 * (q / 6 < nh ? q : q % 6);
     }
 
-    // ---- loads.  Iteration t issues S(t + 5), this wave's 8 of the slot ids
-    // of tile t + 5, and R(t + 3), this wave's three record loads of tile
-    // t + 3: three record tiles are in flight while tile t is computed.  Every
-    // iteration issues the same four operations, including tiles past the end
-    // (which read position p0 and the zero record), and so does the prologue:
-    // the wait counts are constants.  The slot ids of tile T go to ring slot
-    // T % 4 and its records to stage T % 4.
+    // ---- loads.  Iteration t issues S(t + 6), this wave's 8 of the slot ids
+    // of tile t + 6, and R(t + 3), this wave's three record loads of tile
+    // t + 3: three record tiles are in flight while tile t is computed.  The
+    // record addresses of tile t + 4 are formed at the end of iteration t,
+    // from slot ids that landed two iterations earlier, so that the record
+    // loads leave right after the barrier.  Every iteration issues the same
+    // four operations, including tiles past the end, and so does the
+    // prologue: the wait counts are constants.  The slot ids of tile T go to
+    // ring slot T % 4 and its records to stage T % 4.
     const uint32_t span = uint32_t(p1 - p0);
     auto slot_load = [&](int T, int rs) {
         const uint32_t off = uint32_t(T * kTileTokens + 8 * w + (lane & 7));
-        const int32_t *src = r2s + p0 + (off < span ? off : 0u);
+        const int32_t *src = r2s + p0 + (off < span ? off : 0u);   // past the item: position p0
         if (lane < 8) __builtin_amdgcn_global_load_lds(src, lds_ptr(ring + rs * kRingBytes + 32 * w), 4, 0, 0);
     };
     uint32_t slot_at[3];                      // ring addresses of the slot ids of tokens tq[u]
 #pragma unroll
     for (int u = 0; u < 3; ++u) slot_at[u] = lds_pin(ring + 4 * tq[u]);
     const uint32_t slot_own = lds_pin(ring + 4 * (lane & 31));
-    // record loads of tile T into stage `k`; returns the usable tokens (bit t).
-    // All slot ids are read before the first load is issued (the loads write
-    // LDS, so later reads could not be moved above them).
-    auto record_load = [&](int T, int k) -> uint32_t {
+    // record addresses of tile T (slot ids in ring slot rs) and its usable
+    // tokens (bit t); out-of-range slot ids read the zero record
+    struct Fetch {
+        const uint8_t *src[3];
+        uint32_t valid;
+    };
+    auto prep = [&](int T, int rs) -> Fetch {
+        Fetch f;
         int slot[3];
 #pragma unroll
-        for (int u = 0; u < 3; ++u) slot[u] = lds_ld<int>(slot_at[u] + k * kRingBytes);
-        const int s_own = lds_ld<int>(slot_own + k * kRingBytes);
-        const uint32_t left = span - uint32_t(T * kTileTokens);   // positions left in the item (may wrap: none)
-        const uint32_t n_ok = uint32_t(T * kTileTokens) < span ? left : 0u;
+        for (int u = 0; u < 3; ++u) slot[u] = lds_ld<int>(slot_at[u] + rs * kRingBytes);
+        const int s_own = lds_ld<int>(slot_own + rs * kRingBytes);
 #pragma unroll
         for (int u = 0; u < 3; ++u) {
-            const bool ok = real[u] & (uint32_t(tq[u]) < n_ok) & (uint32_t(slot[u]) < uint32_t(a.num_slots));
-            const uint8_t *src = a.records + uint64_t(uint32_t(slot[u])) * rec_bytes + src_off[u];
-            src = ok ? src : a.zero_rec;
-            __builtin_amdgcn_global_load_lds(src, lds_ptr(st0 + k * kStage + 1024 * (3 * w + u)), 16, 0, 0);
+            const bool ok = uint32_t(slot[u]) < uint32_t(a.num_slots);
+            f.src[u] = ok ? src_base[u] + uint64_t(uint32_t(slot[u])) * rec_bytes : a.zero_rec;
         }
-        return uint32_t(__ballot((uint32_t(lane & 31) < n_ok) & (uint32_t(s_own) < uint32_t(a.num_slots))));
+        const uint32_t left = span - uint32_t(T * kTileTokens);   // positions left in the item (may wrap: none)
+        const uint32_t n_ok = uint32_t(T * kTileTokens) < span ? left : 0u;
+        f.valid = uint32_t(__ballot((uint32_t(lane & 31) < n_ok) & (uint32_t(s_own) < uint32_t(a.num_slots))));
+        return f;
+    };
+    auto issue = [&](const Fetch &f, int k) {
+#pragma unroll
+        for (int u = 0; u < 3; ++u)
+            __builtin_amdgcn_global_load_lds(f.src[u], lds_ptr(st0 + k * kStage + 1024 * (3 * w + u)), 16, 0, 0);
     };
     // LDS is used by this wave alone and runs a wave's operations in order;
     // the fences keep the compiler from moving LDS accesses across them
@@ -600,43 +608,52 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, in
         }
     };
 
-    // ---- pipeline.  At the top of iteration t, R(t) and S(t + 3) must have
-    // landed: seven operations follow them (R(t + 1), S(t + 4), R(t + 2)).
-    // The barrier then publishes tile t and the slot ids of tile t + 3 of
+    // ---- pipeline.  At the top of iteration t, R(t) and S(t + 4) must have
+    // landed: seven operations follow them (R(t + 1), S(t + 5), R(t + 2)).
+    // The barrier then publishes tile t and the slot ids of tile t + 4 of
     // every wave, and guarantees that every wave is done with tile t - 1,
-    // whose stage R(t + 3) overwrites, and with the slot ids of tile t + 1,
-    // whose ring slot S(t + 5) overwrites.  The prologue issues the same
-    // operations for t = -3 .. -1, so the counts hold from the start.  The
-    // loop is unrolled by four so that stage and ring offsets are constants;
-    // tiles with no usable token (past the end) are not computed.
+    // whose stage R(t + 3) overwrites, and with the slot ids of tile t + 2,
+    // whose ring slot S(t + 6) overwrites.  The prologue leaves the same
+    // operations in flight, so the counts hold from the start.  The loop is
+    // unrolled by four so that stage and ring offsets are constants; tiles
+    // with no usable token (past the end) are not computed.
     const bool run_compute = __builtin_amdgcn_readfirstlane(int(active)) != 0;
     auto sync = [] {
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
     };
-    uint32_t vq0, vq1, vq2, vq3;              // usable tokens of tiles t .. t + 3
     slot_load(0, 0);
     slot_load(1, 1);
+    slot_load(2, 2);
+    slot_load(3, 3);
     wait_vmem<0>();
     sync();
-    slot_load(2, 2);
-    vq0 = record_load(0, 0);
-    slot_load(3, 3);
-    vq1 = record_load(1, 1);
-    wait_vmem<7>();                           // S(2)
-    sync();
+    Fetch f = prep(0, 0);
+    uint32_t vq0 = f.valid;                   // usable tokens of tiles t .. t + 3
+    issue(f, 0);
+    f = prep(1, 1);
+    uint32_t vq1 = f.valid;
+    sync();                                   // ring slots 0 and 1 are read by every wave
     slot_load(4, 0);
-    vq2 = record_load(2, 2);
+    issue(f, 1);
+    f = prep(2, 2);
+    uint32_t vq2 = f.valid;
+    slot_load(5, 1);
+    issue(f, 2);
+    f = prep(3, 3);
+    uint32_t vq3 = f.valid;
     auto step = [&](int t, auto K) {
         constexpr int k = decltype(K)::value;             // t % 4
         wait_vmem<7>();
         sync();
-        slot_load(t + 5, (k + 1) & 3);
-        vq3 = record_load(t + 3, (k + 3) & 3);
+        slot_load(t + 6, (k + 2) & 3);
+        issue(f, (k + 3) & 3);                            // R(t + 3)
         if (run_compute && vq0 != 0u) compute(K, vq0);
+        f = prep(t + 4, k);
         vq0 = vq1;
         vq1 = vq2;
         vq2 = vq3;
+        vq3 = f.valid;
     };
     for (int t = 0; t < n_tiles; t += 4) {
         step(t, std::integral_constant<int, 0>{});

@@ -13,6 +13,11 @@ the split-K kernel's achieved bandwidth against the HBM roofline (timed live
 with HIP events on the launch stream), the quant-append throughput of the
 131,072-token append workload, and the fp64 CPU oracle's rate on a bounded
 sample of the same decode workload.
+
+The default run times 2,000 steps after 500 warm-up steps: under this load the
+part runs at its board power limit, and its clocks take a few hundred
+milliseconds of sustained work to settle, so short runs read the ramp rather
+than the steady serving rate.
 """
 
 from __future__ import annotations
@@ -192,7 +197,7 @@ def run_append(args, torch, B, workloads):
     slots = dev(workloads.slot_table(w)[0])
     after = dev(np.array([n], np.int32))
     stream = torch.cuda.current_stream()
-    for _ in range(3):
+    for _ in range(max(3, args.warmup // 10)):
         B.oscar_quant_append(lay, pool, k, v, req, pos, slots, after, rk_d, rv_d, stream=stream)
     reps = max(5, args.steps // 2)
     evs = []
@@ -250,8 +255,8 @@ def cpu_baseline(workloads):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default="decode_b32")
     ap.add_argument("--history-chunk", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -53,16 +53,12 @@ struct AppendArgs {
     float alpha;
 };
 
-// The exact sum a + b of two fp32 values, rounded toward +infinity: the
-// round-to-nearest sum S and its exact error e (Knuth's TwoSum, no fused
-// operations), then one ulp up if e > 0.  S is never zero when e != 0.
-__device__ __forceinline__ float round_up_sum(float a, float b) {
-    const float s = __fadd_rn(a, b);
-    const float bb = __fsub_rn(s, a);
-    const float e = __fadd_rn(__fsub_rn(a, __fsub_rn(s, bb)), __fsub_rn(b, bb));
-    const int u = __float_as_int(s);
-    const float up = __int_as_float(u >= 0 ? u + 1 : u - 1);
-    return e > 0.0f ? up : s;
+// The fp32 value nearest above (or equal to) t: t rounded to nearest, then one
+// ulp toward +infinity if that fell below t.  t is never in (0, 2^-25) here,
+// so a rounded value of zero is exact and needs no step.
+__device__ __forceinline__ float round_up_f32(double t) {
+    const float f = float(t);
+    return double(f) < t ? __int_as_float(__float_as_int(f) + (f >= 0.0f ? 1 : -1)) : f;
 }
 
 // Split an fp32 value into three bf16 terms whose sum is the value.
@@ -280,23 +276,27 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(AppendArgs a) {
         const float lo_c = lo < 0.0f ? __fmul_rn(a.alpha, lo) : lo;
         const float hi_c = hi > 0.0f ? __fmul_rn(a.alpha, hi) : hi;
         const float range = __fsub_rn(hi_c, lo_c);
-        const __half s = __float2half_rn(__fdiv_rn(range, 3.0f));
+        // range / 3 rounded to nearest fp32: the fp64 product is within 2^-52
+        // (relative) of the quotient, and a quotient by 3 of an fp32 value is
+        // never within 2^-25 (relative) of a midpoint between fp32 values
+        const __half s = __float2half_rn(float(double(range) * (1.0 / 3.0)));
         const __half z = __float2half_rn(lo_c);
-        // thresholds z + (k + 1/2) s, rounded up to fp32, so that "x >= T" is
-        // exact for fp32 x; a scale of zero gives +inf thresholds (codes 0)
-        const float sf = __half2float(s), zf = __half2float(z);
-        const float t0 = round_up_sum(zf, 0.5f * sf);
-        const float t1 = round_up_sum(zf, 1.5f * sf);
-        const float t2 = round_up_sum(zf, 2.5f * sf);
-        const bool zero_scale = sf == 0.0f;
-        const float u0 = zero_scale ? INFINITY : t0;
-        const float u1 = zero_scale ? INFINITY : t1;
-        const float u2 = zero_scale ? INFINITY : t2;
+        // thresholds z + (k + 1/2) s: exact in fp64 (fp16 operands, sums below
+        // 2^19 on a 2^-25 grid), rounded up to fp32 so that "x >= T" is exact
+        // for fp32 x; a scale of zero gives +inf thresholds (codes 0)
+        const double sd = double(__half2float(s)), zd = double(__half2float(z));
+        const bool zero_scale = sd == 0.0;
+        const float u0 = zero_scale ? INFINITY : round_up_f32(zd + 0.5 * sd);
+        const float u1 = zero_scale ? INFINITY : round_up_f32(zd + 1.5 * sd);
+        const float u2 = zero_scale ? INFINITY : round_up_f32(zd + 2.5 * sd);
+        // code = number of thresholds at or below x (u0 <= u1 <= u2): one
+        // comparison picks the upper or lower pair, a second settles it
         uint32_t packed = 0;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const float xc = __builtin_amdgcn_fmed3f(vals[j], lo_c, hi_c);   // lo_c <= hi_c
-            const uint32_t c = uint32_t(xc >= u0) + uint32_t(xc >= u1) + uint32_t(xc >= u2);
+            const bool upper = xc >= u1;
+            const uint32_t c = (upper ? 2u : 0u) + uint32_t(xc >= (upper ? u2 : u0));
             packed |= c << (2 * j);
         }
         uint8_t *rec = a.records + int64_t(slot) * rec_bytes + h * kHeadRecord;

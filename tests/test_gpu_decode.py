@@ -169,3 +169,38 @@ def test_end_to_end_against_full_oracle(wname, lens):
                              128 ** -0.5)
     _compare(o_gpu, o_ref, f"end-to-end {wname}")
     torch.cuda.synchronize()
+
+
+def test_decode_skips_out_of_range_slot_ids():
+    """History positions whose slot id is negative or >= num_slots are left out
+    of the softmax (the index-table contract of oscar_decode_attn), including a
+    whole 32-token tile of them and the ragged end of a split."""
+    w = workloads.custom("decode_small", batch=2, seq_lens=(1500, 777))
+    lens = w.seq_lens
+    lay_b, lay_o, opool, table, r_k, r_v = _oracle_pool_case(w, lens, seed=6)
+    bad = {0: [100, 101, 517] + list(range(640, 672)) + [1500 - w.recent - 1],
+           1: [w.sink, 300, 301, 302]}
+    n = lay_b.num_slots
+    vals = np.array([-1, n, n + 12345, np.iinfo(np.int32).max, np.iinfo(np.int32).min], np.int64)
+    bad_table = table.copy()
+    for b, ps in bad.items():
+        for i, p in enumerate(ps):
+            assert w.sink <= p < lens[b] - w.recent
+            bad_table[b, p] = vals[i % len(vals)]
+    qh, qd = _queries(w, 2, 11, "bf16")
+    gs.say("decode with out-of-range slot ids")
+    o_gpu = _gpu_decode(lay_b, gs.upload_oracle_pool(opool), qd, lens, bad_table, r_k, r_v,
+                        history_chunk=96)
+    # reference: the oracle's attention over the positions that remain
+    g = w.num_q_heads // w.num_kv_heads
+    o_ref = np.zeros_like(o_gpu, dtype=np.float64)
+    rk = r_k.astype(np.float64)
+    rv = r_v.astype(np.float64)
+    for b in range(2):
+        kv = cache.gather(opool, lay_o, b, lens[b], table[b])
+        keep = np.setdiff1d(np.arange(lens[b]), bad[b])
+        for hk in range(w.num_kv_heads):
+            qr = qh[b, hk * g:(hk + 1) * g, :].astype(np.float64) @ rk[hk]
+            o_rot = attention.attention(qr, kv[keep, hk, 0, :], kv[keep, hk, 1, :], w.head_dim ** -0.5)
+            o_ref[b, hk * g:(hk + 1) * g, :] = o_rot @ rv[hk].T
+    _compare(o_gpu, o_ref, "out-of-range slots")

@@ -70,9 +70,10 @@ oscar_status make_decode_plan(const oscar_layout &lay, int32_t batch,
         if (chunk < 32 || chunk > 65536 || chunk % 32)
             return fail(OSCAR_ERR_INVALID_ARG, "history_chunk must be a multiple of 32 in [32, 65536]");
     } else {
-        // about 2048 history work items over the batch (8 per compute unit
-        // of a 256-CU device), each at least 256 and at most 8192 tokens
-        chunk = (total_hist + 2047) / 2048;
+        // about 1024 history work items over the batch (four per compute
+        // unit of a 256-CU device, where three run at once), each at least
+        // 256 and at most 8192 tokens
+        chunk = (total_hist + 1023) / 1024;
         chunk = (chunk + 31) / 32 * 32;
         chunk = std::min<int64_t>(8192, std::max<int64_t>(256, chunk));
     }

@@ -148,7 +148,7 @@ def test_decode_plan_and_workspace():
     chunk, items = B.oscar_decode_plan(lay, lens)
     hist = 100000 - 64 - 256
     assert chunk % 32 == 0 and 256 <= chunk <= 8192
-    assert chunk == -(-(-(-32 * hist // 2048)) // 32) * 32
+    assert chunk == -(-(-(-32 * hist // 1024)) // 32) * 32
     assert items == 2 + -(-hist // chunk)
     ws = B.oscar_decode_workspace_size(lay, lens)
     # rotated q, per-head group sums + operand scales (8 floats), partial o', (m, l), zero record

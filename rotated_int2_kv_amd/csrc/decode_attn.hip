@@ -316,6 +316,9 @@ __device__ __forceinline__ void lds_st(uint32_t addr, T v) {
 }
 __device__ __forceinline__ lds_void *lds_ptr(uint32_t addr) { return reinterpret_cast<lds_void *>(uintptr_t(addr)); }
 
+// Cache policy of the record loads: non-temporal (each record is read once).
+constexpr int kNonTemporal = 2;
+
 // Wait until at most N vector-memory operations of this wave are pending.
 // The compiler does not track global_load_lds, so the pipeline below waits
 // by hand; the memory clobber keeps LDS accesses on their side of the wait.
@@ -440,7 +443,7 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, in
     auto issue = [&](const Fetch &f, int k) {
 #pragma unroll
         for (int u = 0; u < 3; ++u)
-            __builtin_amdgcn_global_load_lds(f.src[u], lds_ptr(st0 + k * kStage + 1024 * (3 * w + u)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(f.src[u], lds_ptr(st0 + k * kStage + 1024 * (3 * w + u)), 16, 0, kNonTemporal);
     };
     // LDS is used by this wave alone and runs a wave's operations in order;
     // the fences keep the compiler from moving LDS accesses across them

@@ -129,10 +129,10 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(AppendArgs a) {
             const size_t elem = (size_t(tok) * a.hkv + h) * kHeadDim + 8 * st_col;
             if (a.in_dtype == OSCAR_F32) {
                 const u32x4 *p = reinterpret_cast<const u32x4 *>(static_cast<const float *>(X) + elem);
-                r0 = p[0];
-                r1 = p[1];
+                r0 = __builtin_nontemporal_load(p);        // input read once
+                r1 = __builtin_nontemporal_load(p + 1);
             } else {
-                r0 = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(X) + elem);
+                r0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(X) + elem));
             }
         }
     };

@@ -348,7 +348,7 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, in
     // ---- per-item operands
     f16x8 qA[HS][4][2];   // QK A: row n = (h = n / 4, g = n % 4), nonzero in K block g
     float qz[HS][4];      // Qbar[head kb][g] 2^(K - 24): zero-point term in the MFMA's units
-    float qout[HS];       // 2^(24 - K) of head kb: back to logit units
+    float qout[HS];       // 2^(24 - K) of head kb: MFMA units -> logit units (log2)
 #pragma unroll
     for (int hs = 0; hs < HS; ++hs) {
         {
@@ -381,7 +381,7 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, in
             const float *info = a.qsum + (head0 + (hv ? h : 0)) * 8;
 #pragma unroll
             for (int g = 0; g < 4; ++g) qz[hs][g] = hv ? info[g] / info[5] : 0.0f;
-            qout[hs] = hv ? info[5] : 0.0f;
+            qout[hs] = hv ? info[5] : 1.0f;
         }
     }
 
@@ -519,12 +519,15 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, in
                     acc = mfma_f16(qA[hs][r][0], B[r], acc);
                     acc = mfma_f16(qA[hs][r][1], B[r], acc);
                 }
-                // acc[g] = group g's dot product; s_g, z_g are halves of szk[g]
-                float xa = fmaf(acc[0], half_lo(szk[0]), half_hi(szk[0]) * qz[hs][0]);
-                float xb = fmaf(acc[2], half_lo(szk[2]), half_hi(szk[2]) * qz[hs][2]);
-                xa = fmaf(half_hi(szk[1]), qz[hs][1], fmaf(acc[1], half_lo(szk[1]), xa));
-                xb = fmaf(half_hi(szk[3]), qz[hs][3], fmaf(acc[3], half_lo(szk[3]), xb));
-                lg[hs][hf] = fmaf(xa + xb, qout[hs], live ? 0.0f : -INFINITY);
+                // acc[g] = group g's dot product; s_g, z_g are halves of szk[g].
+                // The logit stays in the MFMA's units (a factor 2^(K - 24) of the
+                // log2 logit, K fixed per head); masked tokens start from -inf.
+                float x = live ? 0.0f : -INFINITY;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) x = fmaf(half_hi(szk[g]), qz[hs][g], x);
+#pragma unroll
+                for (int g = 0; g < 4; ++g) x = fmaf(acc[g], half_lo(szk[g]), x);
+                lg[hs][hf] = x;
             }
         }
         // ---- online softmax
@@ -536,17 +539,18 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, in
             const float m_new = fmaxf(m_run[hs], mx);
             grow[hs] = __any(m_new > m_run[hs]);
             if (__builtin_expect(grow[hs], 0)) {
-                alpha[hs] = (m_new > m_run[hs]) ? __builtin_amdgcn_exp2f(m_run[hs] - m_new) : 1.0f;
+                alpha[hs] = (m_new > m_run[hs]) ? __builtin_amdgcn_exp2f((m_run[hs] - m_new) * qout[hs]) : 1.0f;
                 l_lane[hs] *= alpha[hs];
 #pragma unroll
                 for (int g = 0; g < 4; ++g) zl[hs][g] *= alpha[hs];
                 m_run[hs] = m_new;
             }
-            // exponent reference: a finite stand-in while every token so far is masked
-            const float m_ref = m_run[hs] == -INFINITY ? 0.0f : m_run[hs];
+            // exponent reference in log2 units: a finite stand-in while every
+            // token so far is masked
+            const float m_ref = m_run[hs] == -INFINITY ? 0.0f : m_run[hs] * qout[hs];
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
-                const float p = __builtin_amdgcn_exp2f(lg[hs][hf] - m_ref);   // 0 for masked tokens
+                const float p = __builtin_amdgcn_exp2f(fmaf(lg[hs][hf], qout[hs], -m_ref));   // 0 for masked tokens
                 pw[hs][hf] = p;
                 l_lane[hs] += p;
 #pragma unroll
@@ -678,7 +682,7 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, in
 #pragma unroll
         for (int g = 0; g < 4; ++g) zt[g] = row16_sum(zl[hs][g]);
         if (n == 0 && 4 * hs + kb < GQ) {
-            a.part_ml[(row0 + 4 * hs + kb) * 2 + 0] = m_run[hs];
+            a.part_ml[(row0 + 4 * hs + kb) * 2 + 0] = m_run[hs] * qout[hs];   // log2 units
             a.part_ml[(row0 + 4 * hs + kb) * 2 + 1] = l_row;
         }
         // lane (n, kb) holds rows (g = kb, h = i); the row whose group matches

@@ -237,9 +237,9 @@ __device__ __forceinline__ float half_hi(uint32_t w) { return __half2float(__ush
 // waves together fetch the chunk's 384 bytes of every token as whole 128-byte
 // lines (wave w fetches tokens 8 w .. 8 w + 7), so that each request fills a
 // line.  Token t of a tile occupies 384 bytes of the stage; within each of
-// its three 128-byte lines the 16-byte units are permuted by XOR with
-// (t / 2) % 8, so that the same field of 16 consecutive tokens falls in 16
-// different LDS bank groups.  Four stages let three tiles be in flight while
+// its three 128-byte lines the 16-byte units are permuted by XOR with a
+// per-token value (tok_swizzle) chosen so that every read pattern below hits
+// distinct banks, whether the LDS serves 128 or 256 bytes per cycle.  Four stages let three tiles be in flight while
 // a fourth is computed; one workgroup barrier per tile publishes a landed
 // tile and retires the stage that the next loads overwrite.  The slot ids of
 // a tile go to a ring shared by the workgroup (each wave fetches 8 of them)
@@ -260,13 +260,12 @@ __device__ __forceinline__ float half_hi(uint32_t w) { return __half2float(__ush
 // row whose group is c's group.  K-slot 8 kb + i of the PV products is token
 // 2 (i % 2) + 8 (i / 2) + (kb % 2) + 4 (kb / 2): the four lane groups read V
 // codes of tokens t, t + 1, t + 4, t + 5 at once, which the token swizzle
-// puts in disjoint LDS banks.  Weight rows are 64 bytes with their 16-byte
-// units permuted by XOR with row / 4, which keeps both the 16-bit weight
-// writes and the 128-bit operand reads free of bank conflicts.  The weight
-// rows live in the stage itself: once a wave has read its K codes and both
-// (s, z) of the tile into registers, those 128 units of its head are dead,
-// and each 16-byte unit of the weight rows takes a dead unit at the same
-// address modulo 256 (so the same banks as a dense layout).
+// puts in disjoint LDS banks.  Weight rows hold 4 units of 16 bytes (8
+// K-slots each), the physical unit of logical unit v in row (g, h) being
+// v ^ g.  The rows live in the stage itself: once a wave has read its K codes
+// and both (s, z) of the tile into registers, those 128 units of its head are
+// dead, and each weight unit takes a dead unit in a bank group chosen so that
+// the 16-bit weight writes and the 128-bit operand reads hit distinct banks.
 constexpr int kTokBytes = 4 * kHeadRecord;             // 384: one token of a head chunk
 constexpr int kStage = kTileTokens * kTokBytes;        // 12 KiB per tile
 constexpr int kStages = 4;                             // three tiles in flight while one is computed
@@ -275,20 +274,35 @@ constexpr int kRing = 4;                               // slot-id ring of the wo
 constexpr int kHalfTok = 16 * kTokBytes;               // token 16 + t of a stage is this far after token t
 __host__ __device__ constexpr int int2_lds_bytes() { return kStages * kStage + kRing * kRingBytes; }
 
-// byte offset of 16-byte unit q (0..23) of token t inside a stage
-__device__ __forceinline__ int unit_addr(int t, int q) {
-    return t * kTokBytes + 16 * ((q & ~7) | ((q & 7) ^ ((t >> 1) & 7)));
+// XOR applied to the unit index (within its 128-byte line) of token t: bits
+// 0 and 1 of t % 8 swapped, bit 1 flipped for t % 16 >= 8.  Tokens t and
+// t + 16 share it (token 16 + t is kHalfTok after token t).  It makes the
+// units read by any 8 consecutive tokens distinct, the (line parity, unit)
+// pairs of tokens 0..15 distinct, and the V-code units of tokens t, t + 1
+// (and t + 4, t + 5) read by one PV load distinct.
+__host__ __device__ constexpr int tok_swizzle(int t) {
+    return (((t & 1) << 1) | ((t >> 1) & 1) | (t & 4)) ^ (2 * ((t >> 3) & 1));
 }
 
-// Byte offset inside a stage of unit u (0..3) of row r (0..15) of wave w's
-// PV weight plane 0 (hi parts); plane 1 (lo parts) is kHalfTok further.
-// Row r's units go to K-code or (s, z) unit {0, 1, 4, 5}[r / 4] of w's head
-// record, of the token among 0..15 whose swizzle puts the unit at bank group
-// (4 r + u) % 16: the bank group of unit (r, u) in a dense 64-byte-row plane.
+// byte offset of 16-byte unit q (0..23) of token t inside a stage
+__device__ __forceinline__ int unit_addr(int t, int q) {
+    return t * kTokBytes + 16 * ((q & ~7) | ((q & 7) ^ tok_swizzle(t)));
+}
+
+// Byte offset inside a stage of physical unit u (0..3) of row r (0..15) of
+// wave w's PV weight plane 0 (hi parts); plane 1 (lo parts) is kHalfTok
+// further.  Row r's units go to K-code or (s, z) unit {0, 1, 4, 5}[r / 4] of
+// w's head record, of the one token among 0..15 that puts the unit in bank
+// group (4 r + (u ^ 2 ((r / 2) % 2))) % 16 (16-byte groups of a 256-byte
+// window).  Those groups keep the weight writes (rows 4 g .. 4 g + 3, all
+// units) and the operand reads (rows 8 j .. 8 j + 7 or 0 .. 15, one unit
+// each) in distinct banks.
 __device__ __forceinline__ int wunit_addr(int w, int r, int u) {
     const int q = 6 * w + ((r >> 2) & 1) + 4 * (r >> 3);
-    const int bg = 4 * (r & 3) + u;
-    const int t = 2 * ((bg & 7) ^ (q & 7)) + ((bg >> 3) ^ ((q >> 3) & 1));
+    const int bg = (4 * r + (u ^ (2 * ((r >> 1) & 1)))) & 15;
+    const int par = (bg >> 3) ^ ((q >> 3) & 1);     // t % 2: line parity within the 256-byte window
+    const int sw = (bg & 7) ^ (q & 7);              // tok_swizzle(t) needed
+    const int t = par | ((sw & 1) << 1) | (sw & 4) | ((((sw >> 1) & 1) ^ par) << 3);
     return unit_addr(t, q);
 }
 
@@ -394,7 +408,7 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, in
     for (int u = 0; u < 3; ++u) {
         const int P = 64 * (3 * w + u) + lane;
         const int t = P / 24, U = P % 24;
-        const int q = (U & ~7) | ((U & 7) ^ ((t >> 1) & 7));
+        const int q = (U & ~7) | ((U & 7) ^ tok_swizzle(t));
         tq[u] = t;
         src_base[u] = a.records + hc * kTokBytes + 16 * (q / 6 < nh ? q : q % 6);
     }

@@ -218,6 +218,50 @@ oscar_status oscar_decode_plan(const oscar_layout *layout, int32_t batch,
                                const oscar_launch_opts *opts, int32_t *history_chunk,
                                int32_t *items_per_request);
 
+/*
+ * Workspace bytes that oscar_extend_attn needs for n_new new tokens over a
+ * prefix of prefix_len tokens.  opts may be NULL.
+ */
+oscar_status oscar_extend_workspace_size(const oscar_layout *layout, int32_t n_new, int32_t prefix_len,
+                                         const oscar_launch_opts *opts, size_t *bytes);
+
+/*
+ * oscar_extend_attn: attention of n_new new tokens of one request (a
+ * prefill or extend chunk) over the request's cached prefix and, causally,
+ * over themselves.  Follows the prefill path that the Qiita article (its first
+ * pitfall, INT2 KV using memory outside the pool) and its KV-pool follow-up
+ * (section on the buffer that is not the pool) describe: each chunk attends to
+ * the whole cached prefix, which those pages expand to dense 16-bit outside
+ * the pool before attention.  Here the stored prefix is read in place, with
+ * dequantisation fused into the attention, so no buffer grows with P.
+ *
+ * q:             [n_new][Hq][128] of q_dtype (F32, BF16 or F16); row i is
+ *                the new token at position prefix_len + i.
+ * k_new, v_new:  [n_new][Hkv][128] of kv_dtype (F32, BF16 or F16), the new
+ *                tokens' raw keys and values.
+ * req_id:        the request's row of the stores and of req_to_slot.
+ * prefix_len:    cached tokens before the chunk (>= 0).  The prefix is read
+ *                as the pool holds it at that length: sink [0, min(S, P))
+ *                and recent [max(S, P - W), P) BF16, history [S, P - W) INT2.
+ *                Call this before oscar_quant_append of the same tokens (the
+ *                append overwrites the recent ring).
+ * req_to_slot:   as for oscar_decode_attn; the stride must cover prefix_len.
+ * out:           [n_new][Hq][128] of out_dtype.
+ * workspace:     >= oscar_extend_workspace_size bytes, 256-byte aligned.
+ * Computes, for new token i and q head h reading KV head h / g: keys and
+ *   values of positions [0, P) from the prefix as stored, and of new tokens
+ *   0 .. i as bf16_rn(x R) (x R formed in fp32); softmax over all of them
+ *   with q' = q R_K; out = o' R_V^T.
+ */
+oscar_status oscar_extend_attn(hipStream_t stream, const oscar_layout *layout,
+                               const oscar_pool *pool, const void *q, oscar_dtype q_dtype,
+                               const void *k_new, const void *v_new, oscar_dtype kv_dtype,
+                               int32_t n_new, int32_t req_id, int32_t prefix_len,
+                               const int32_t *req_to_slot, int64_t req_to_slot_stride,
+                               const float *R_K, const float *R_V, float sm_scale,
+                               void *out, oscar_dtype out_dtype, void *workspace,
+                               size_t workspace_bytes, const oscar_launch_opts *opts);
+
 /* Thread-local message of the last non-OK status of this thread. */
 const char *oscar_last_error(void);
 

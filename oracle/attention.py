@@ -11,17 +11,31 @@ Sources:
 Readings: sm_scale is an argument (1/sqrt(d) by default); softmax is the plain
 max-subtracted softmax over every cached position [0, L) of the request.
 
+  * Qiita article, first pitfall (INT2 KV using memory outside the pool), and
+    its KV-pool follow-up (section on the buffer that is not the pool): a
+    prefill or extend chunk attends to the request's whole cached prefix, read
+    from the pool as stored, and to the chunk's own tokens at model precision.
+
+Readings: sm_scale is an argument (1/sqrt(d) by default); softmax is the plain
+max-subtracted softmax over every cached position [0, L) of the request.  In
+``extend`` the prefix is read as the pool holds it at length P (the chunk has
+not been appended yet), and a new token enters attention as the recent window
+would hold it once appended: bf16_rn of its rotated vector.  New token i sees
+the prefix and new tokens 0..i (causal).
+
 Pins (tests/test_oracle_attention.py): explicit-loop brute force on tiny
 cases, torch's scaled_dot_product_attention (CPU, fp64) when R = I and the whole
-cache is BF16, rotation invariance without quantisation, and the GQA head
-mapping with g = 6.
+cache is BF16 (for extend with an offset causal mask, and with P = 0 torch's own
+causal mode), rotation invariance without quantisation, the GQA head mapping
+with g = 6, and extend of one token equal to decode after appending it where
+appending moves no prefix token out of the BF16 window.
 """
 
 from __future__ import annotations
 
 import numpy as np
 
-from . import cache
+from . import cache, quant
 
 
 def attention(q, k, v, sm_scale: float) -> np.ndarray:
@@ -59,4 +73,32 @@ def decode(pool: cache.Pool, lay: cache.Layout, q, req_ids, seq_lens, req_to_slo
             qh = q[b, hk * g:(hk + 1) * g, :] @ rk[hk]
             o_rot = attention(qh, kv[:, hk, 0, :], kv[:, hk, 1, :], sm_scale)
             out[b, hk * g:(hk + 1) * g, :] = o_rot @ rv[hk].T
+    return out
+
+
+def extend(pool: cache.Pool, lay: cache.Layout, q, k_new, v_new, req: int, prefix_len: int,
+           slots_of_req, r_k, r_v, sm_scale: float) -> np.ndarray:
+    """Attention of a chunk of n new tokens of request ``req`` (fp64, original basis).
+
+    q [n, Hq, d]; k_new, v_new [n, Hkv, d] raw (unrotated) keys and values of
+    the tokens at positions P .. P + n - 1, P = prefix_len; slots_of_req maps
+    positions [S, P) to pool slots.  Returns o [n, Hq, d].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    n, hq, d = q.shape
+    g = hq // lay.num_kv_heads
+    rk = np.asarray(r_k, dtype=np.float32)
+    rv = np.asarray(r_v, dtype=np.float32)
+    prefix = cache.gather(pool, lay, req, int(prefix_len), slots_of_req)
+    out = np.zeros((n, hq, d))
+    for hk in range(lay.num_kv_heads):
+        kn = quant.bf16_round(quant.rotate(np.asarray(k_new)[:, hk, :], rk[hk])).astype(np.float64)
+        vn = quant.bf16_round(quant.rotate(np.asarray(v_new)[:, hk, :], rv[hk])).astype(np.float64)
+        keys = np.concatenate([prefix[:, hk, 0, :], kn])
+        vals = np.concatenate([prefix[:, hk, 1, :], vn])
+        for i in range(n):
+            qh = q[i, hk * g:(hk + 1) * g, :] @ rk[hk].astype(np.float64)
+            m = int(prefix_len) + i + 1
+            o_rot = attention(qh, keys[:m], vals[:m], sm_scale)
+            out[i, hk * g:(hk + 1) * g, :] = o_rot @ rv[hk].astype(np.float64).T
     return out

@@ -31,7 +31,7 @@ OSCAR_ROT_EIG, OSCAR_ROT_HAD, OSCAR_ROT_PBR, OSCAR_ROT_OSCAR = 1, 2, 4, 7
 EXPORTED = (
     "oscar_layout_check", "oscar_pool_bytes", "oscar_build_rotation", "oscar_quant_append",
     "oscar_decode_workspace_size", "oscar_decode_attn", "oscar_decode_plan",
-    "oscar_last_error", "oscar_version",
+    "oscar_extend_workspace_size", "oscar_extend_attn", "oscar_last_error", "oscar_version",
 )
 
 
@@ -80,6 +80,9 @@ def _load() -> ctypes.CDLL:
         "oscar_decode_attn": (I32, [P, LP, PP, P, I32, I32, P, P, P, P, I64, P, P, F32, P, I32,
                                     P, SZ, OP]),
         "oscar_decode_plan": (I32, [LP, I32, P, OP, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
+        "oscar_extend_workspace_size": (I32, [LP, I32, I32, OP, ctypes.POINTER(SZ)]),
+        "oscar_extend_attn": (I32, [P, LP, PP, P, I32, P, P, I32, I32, I32, I32, P, I64, P, P, F32,
+                                    P, I32, P, SZ, OP]),
         "oscar_last_error": (ctypes.c_char_p, []),
         "oscar_version": (ctypes.c_char_p, []),
     }
@@ -235,6 +238,28 @@ def oscar_decode_attn(layout: Layout, pool: Pool, q, req_ids, seq_lens, seq_lens
     _check(_lib.oscar_decode_attn(
         _stream(stream), ctypes.byref(layout.c()), ctypes.byref(pool.c()), _ptr(q),
         _dtype_code(q), int(q.shape[0]), _ptr(req_ids), _ptr(seq_lens), lens.ctypes.data,
+        _ptr(req_to_slot), int(req_to_slot.shape[-1]), _ptr(R_K), _ptr(R_V), float(sm_scale),
+        _ptr(out), _dtype_code(out), _ptr(workspace), int(workspace.numel() * workspace.element_size()),
+        _opts(kernel_begin, kernel_end, history_chunk)))
+
+
+def oscar_extend_workspace_size(layout: Layout, n_new: int, prefix_len: int,
+                                history_chunk: int = 0) -> int:
+    out = ctypes.c_size_t(0)
+    _check(_lib.oscar_extend_workspace_size(ctypes.byref(layout.c()), int(n_new), int(prefix_len),
+                                            _opts(history_chunk=history_chunk), ctypes.byref(out)))
+    return int(out.value)
+
+
+def oscar_extend_attn(layout: Layout, pool: Pool, q, k_new, v_new, req_id: int, prefix_len: int,
+                      req_to_slot, R_K, R_V, sm_scale: float, out, workspace, stream=None,
+                      kernel_begin=None, kernel_end=None, history_chunk: int = 0) -> None:
+    _dev(q, k_new, v_new, req_to_slot, R_K, R_V, out, workspace)
+    if k_new.dtype != v_new.dtype:
+        raise TypeError("k_new and v_new must share a dtype")
+    _check(_lib.oscar_extend_attn(
+        _stream(stream), ctypes.byref(layout.c()), ctypes.byref(pool.c()), _ptr(q), _dtype_code(q),
+        _ptr(k_new), _ptr(v_new), _dtype_code(k_new), int(q.shape[0]), int(req_id), int(prefix_len),
         _ptr(req_to_slot), int(req_to_slot.shape[-1]), _ptr(R_K), _ptr(R_V), float(sm_scale),
         _ptr(out), _dtype_code(out), _ptr(workspace), int(workspace.numel() * workspace.element_size()),
         _opts(kernel_begin, kernel_end, history_chunk)))

@@ -15,11 +15,19 @@
 //               BF16 windows run on fp32 VALU.  Each item writes (m, l, o')
 //               with m in log2 units.
 //   3. merge:   log-sum-exp merge of the items and o = o' R_V^T.
+//
+// oscar_extend_attn runs the same kernels for the new tokens of one request:
+// every new token is a row of the batch that reads the request's cached
+// prefix as it is stored at the prefix length, plus one more work item per
+// row: the new tokens up to and including its own, as BF16 rotated keys and
+// values (rotated here by extend_rotate_kernel).
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
 #include <cmath>
+#include <string>
 #include <type_traits>
+#include <vector>
 
 #include "common.cuh"
 #include "internal.h"
@@ -64,6 +72,12 @@ struct DecodeArgs {
     int32_t items;
     int32_t waves;     // KV heads per workgroup
     int32_t head_chunks;
+    // extend: every batch row is request fixed_req at length fixed_len, and
+    // item extra_item reads the rotated new tokens 0 .. row (causal)
+    int32_t fixed_req;        // -1 for decode
+    int32_t fixed_len;
+    int32_t extra_item;       // -1 for decode
+    const uint16_t *newkv;    // [rows][Hkv][2][128] BF16 rotated K, V of the new tokens
 };
 
 // Position range [p0, p1) of work item j of a request of length L.
@@ -83,8 +97,8 @@ __device__ __forceinline__ void item_range(const DecodeArgs &a, int L, int j, in
 }
 
 __device__ __forceinline__ int request_length(const DecodeArgs &a, int b, int &req) {
-    req = a.req_ids[b];
-    int L = a.seq_lens[b];
+    req = a.fixed_req >= 0 ? a.fixed_req : a.req_ids[b];
+    int L = a.fixed_req >= 0 ? a.fixed_len : a.seq_lens[b];
     if (req < 0 || req >= a.max_requests || L < 0) return 0;
     // never read past a row of the index table
     return int(min<int64_t>(L, a.r2s_stride));
@@ -743,6 +757,7 @@ __device__ void bf16_item(const DecodeArgs &a, int b, int req, int j, int hk, in
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const bool is_sink = (j == 0);
+    const bool is_new = (j == a.extra_item);
     float m_run[kMaxGroup], l_lane[kMaxGroup], o0[kMaxGroup], o1[kMaxGroup];
 #pragma unroll
     for (int h = 0; h < kMaxGroup; ++h) {
@@ -752,6 +767,7 @@ __device__ void bf16_item(const DecodeArgs &a, int b, int req, int j, int hk, in
         o1[h] = 0.0f;
     }
     auto row_ptr = [&](int pos, int t) -> const uint16_t * {
+        if (is_new) return a.newkv + (size_t(pos) * a.hkv + hk) * 2 * kHeadDim + t * kHeadDim;
         if (is_sink)
             return a.sink + ((size_t(req) * a.sink_tokens + pos) * a.hkv + hk) * 2 * kHeadDim + t * kHeadDim;
         return a.recent + ((size_t(req) * a.recent_tokens + pos % a.recent_tokens) * a.hkv + hk) * 2 * kHeadDim +
@@ -869,12 +885,17 @@ __global__ __launch_bounds__(64 * kPartialWaves) void partial_kernel(DecodeArgs 
     int req = 0;
     const int L = request_length(a, b, req);
     int p0, p1;
-    item_range(a, L, j, p0, p1);
+    if (j == a.extra_item) {                    // extend: new tokens 0 .. b
+        p0 = 0;
+        p1 = b + 1;
+    } else {
+        item_range(a, L, j, p0, p1);
+    }
     if (p0 >= p1) return;                       // uniform over the workgroup
     const int w = threadIdx.x >> 6;
     const int hk = hc * kPartialWaves + w;
     const bool active = hk < a.hkv;
-    if (j < 2) {
+    if (j < 2 || j == a.extra_item) {
         float *pbuf = reinterpret_cast<float *>(smem) + w * kBf16WaveFloats;
         bf16_item(a, b, req, j, active ? hk : 0, p0, p1, active, pbuf);
     } else if (a.num_slots > 0) {
@@ -906,9 +927,14 @@ __global__ __launch_bounds__(512) void merge_kernel(DecodeArgs a) {
     item_range(a, L, 1, p0, p1);
     const bool recent_ok = p0 < p1;
     const int hist = max(0, max(a.sink_tokens, L - a.recent_tokens) - a.sink_tokens);
-    const int n_items = a.num_slots > 0 ? 2 + (hist + a.chunk - 1) / a.chunk : 2;
+    const int n_hist_items = a.num_slots > 0 ? 2 + (hist + a.chunk - 1) / a.chunk : 2;
+    // the extend's new-token item is the last one and always holds a partial;
+    // items between the request's chunks and it hold none
+    const int n_items = a.extra_item >= 0 ? a.extra_item + 1 : n_hist_items;
     const size_t row_b = size_t(b) * a.items * a.hq + size_t(hk) * a.g;   // item 0, head 0
-    auto item_ok = [&](int j) { return j >= 2 || (j == 0 ? sink_ok : recent_ok); };
+    auto item_ok = [&](int j) {
+        return j == a.extra_item || (j >= 2 && j < n_hist_items) || (j == 0 && sink_ok) || (j == 1 && recent_ok);
+    };
 
     const int wv = t >> 6;
     if (wv < a.g) {
@@ -947,8 +973,12 @@ __global__ __launch_bounds__(512) void merge_kernel(DecodeArgs a) {
                 acc = fmaf(__builtin_amdgcn_exp2f(a.part_ml[row * 2] - M), a.part_o[row * kHeadDim + c], acc);
             }
 #pragma unroll 8
-            for (int j = 2; j < n_items; ++j) {
+            for (int j = 2; j < n_hist_items; ++j) {
                 const size_t row = row_h + size_t(j) * a.hq;
+                acc = fmaf(__builtin_amdgcn_exp2f(a.part_ml[row * 2] - M), a.part_o[row * kHeadDim + c], acc);
+            }
+            if (a.extra_item >= 0) {
+                const size_t row = row_h + size_t(a.extra_item) * a.hq;
                 acc = fmaf(__builtin_amdgcn_exp2f(a.part_ml[row * 2] - M), a.part_o[row * kHeadDim + c], acc);
             }
         }
@@ -977,6 +1007,36 @@ __global__ __launch_bounds__(512) void merge_kernel(DecodeArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// 4. extend: rotated BF16 keys and values of the new tokens
+// ---------------------------------------------------------------------------
+// One workgroup per (token, KV head, K or V); thread c forms channel c of
+// x R in fp32 and rounds it to BF16, as the recent window stores it.
+struct RotateArgs {
+    const void *k;
+    const void *v;
+    const float *r_k;
+    const float *r_v;
+    uint16_t *out;     // [n][Hkv][2][128]
+    int32_t hkv;
+    int32_t dtype;
+};
+
+__global__ __launch_bounds__(kHeadDim) void extend_rotate_kernel(RotateArgs a) {
+    __shared__ float xs[kHeadDim];
+    const int t = blockIdx.x & 1;
+    const int hk = (blockIdx.x >> 1) % a.hkv;
+    const int i = (blockIdx.x >> 1) / a.hkv;
+    const int c = threadIdx.x;
+    xs[c] = load_as_f32(t ? a.v : a.k, a.dtype, (size_t(i) * a.hkv + hk) * kHeadDim + c);
+    __syncthreads();
+    const float *R = (t ? a.r_v : a.r_k) + size_t(hk) * kHeadDim * kHeadDim + c;
+    float acc = 0.0f;
+#pragma unroll 16
+    for (int r = 0; r < kHeadDim; ++r) acc = fmaf(xs[r], R[size_t(r) * kHeadDim], acc);
+    a.out[((size_t(i) * a.hkv + hk) * 2 + t) * kHeadDim + c] = bf16_bits_rn(acc);
+}
+
 // Dynamic LDS of the partial kernel: the four record stages and the slot-id
 // ring of the INT2 items, or each wave's softmax buffer for the BF16 items.
 size_t partial_lds_bytes(const DecodeArgs &) {
@@ -996,17 +1056,14 @@ hipError_t launch_partial(const DecodeArgs &a, int blocks, hipStream_t stream) {
 
 using namespace oscar;
 
-extern "C" oscar_status oscar_decode_attn(hipStream_t stream, const oscar_layout *layout,
-                                          const oscar_pool *pool, const void *q, oscar_dtype q_dtype,
-                                          int32_t batch, const int32_t *req_ids,
-                                          const int32_t *seq_lens, const int32_t *seq_lens_host,
-                                          const int32_t *req_to_slot, int64_t req_to_slot_stride,
-                                          const float *R_K, const float *R_V, float sm_scale,
-                                          void *out, oscar_dtype out_dtype, void *workspace,
-                                          size_t workspace_bytes, const oscar_launch_opts *opts) {
+namespace {
+
+oscar_status check_decode_common(const oscar_layout *layout, const oscar_pool *pool, const void *q,
+                                 oscar_dtype q_dtype, const int32_t *req_to_slot, const float *R_K,
+                                 const float *R_V, float sm_scale, void *out, oscar_dtype out_dtype) {
     oscar_status st = check_layout(layout);
     if (st != OSCAR_OK) return st;
-    if (!pool || !q || !req_ids || !seq_lens || !req_to_slot || !R_K || !R_V || !out)
+    if (!pool || !q || !req_to_slot || !R_K || !R_V || !out)
         return fail(OSCAR_ERR_INVALID_ARG, "a required pointer is null");
     if (!pool->records || !pool->recent || (layout->sink_tokens > 0 && !pool->sink))
         return fail(OSCAR_ERR_INVALID_ARG, "a pool pointer is null");
@@ -1015,20 +1072,28 @@ extern "C" oscar_status oscar_decode_attn(hipStream_t stream, const oscar_layout
     if (out_dtype != OSCAR_F32 && out_dtype != OSCAR_BF16 && out_dtype != OSCAR_F16)
         return fail(OSCAR_ERR_INVALID_ARG, "out_dtype must be F32, BF16 or F16");
     if (!std::isfinite(sm_scale)) return fail(OSCAR_ERR_INVALID_ARG, "sm_scale must be finite");
-    DecodePlan plan;
-    st = make_decode_plan(*layout, batch, seq_lens_host, opts, &plan);
-    if (st != OSCAR_OK) return st;
+    return OSCAR_OK;
+}
+
+oscar_status check_workspace(const DecodePlan &plan, int64_t req_to_slot_stride, void *workspace,
+                             size_t workspace_bytes) {
     if (req_to_slot_stride < plan.max_len)
         return fail(OSCAR_ERR_INVALID_ARG, "req_to_slot_stride is smaller than the longest sequence");
     if (!workspace || workspace_bytes < plan.ws_bytes)
-        return fail(OSCAR_ERR_WORKSPACE, "workspace is smaller than oscar_decode_workspace_size");
+        return fail(OSCAR_ERR_WORKSPACE, "workspace is smaller than the size the library reported");
     if (reinterpret_cast<uintptr_t>(workspace) % 256)
         return fail(OSCAR_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    return OSCAR_OK;
+}
 
+DecodeArgs make_args(const oscar_layout *layout, const oscar_pool *pool, const void *q, oscar_dtype q_dtype,
+                     int32_t batch, const int32_t *req_to_slot, int64_t req_to_slot_stride,
+                     const float *R_K, const float *R_V, float sm_scale, void *out, oscar_dtype out_dtype,
+                     void *workspace, const DecodePlan &plan) {
     DecodeArgs a;
     a.q = q;
-    a.req_ids = req_ids;
-    a.seq_lens = seq_lens;
+    a.req_ids = nullptr;
+    a.seq_lens = nullptr;
     a.req_to_slot = req_to_slot;
     a.r_k = R_K;
     a.r_v = R_V;
@@ -1058,14 +1123,25 @@ extern "C" oscar_status oscar_decode_attn(hipStream_t stream, const oscar_layout
     a.items = plan.items;
     a.waves = kPartialWaves;
     a.head_chunks = (a.hkv + kPartialWaves - 1) / kPartialWaves;
+    a.fixed_req = -1;
+    a.fixed_len = 0;
+    a.extra_item = plan.extra_item;
+    a.newkv = plan.extra_item >= 0 ? reinterpret_cast<const uint16_t *>(ws + plan.ws_newkv) : nullptr;
+    return a;
+}
 
-    hipLaunchKernelGGL(prep_kernel, dim3(batch * a.hkv), dim3(512), 0, stream, a);
+// prep, split-K partials and merge on `stream`
+oscar_status launch_decode(const DecodeArgs &a, const DecodePlan &plan, hipStream_t stream,
+                           const oscar_launch_opts *opts) {
+    if (int64_t(plan.items) * a.batch * a.head_chunks > INT32_MAX)
+        return fail(OSCAR_ERR_UNSUPPORTED, "batch x work items exceeds one launch grid");
+    hipLaunchKernelGGL(prep_kernel, dim3(a.batch * a.hkv), dim3(512), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(OSCAR_ERR_HIP, std::string("prep launch: ") + hipGetErrorString(e));
 
     if (opts && opts->kernel_begin && hipEventRecord(opts->kernel_begin, stream) != hipSuccess)
         return fail(OSCAR_ERR_HIP, "hipEventRecord failed");
-    const int blocks = plan.items * batch * a.head_chunks;
+    const int blocks = plan.items * a.batch * a.head_chunks;
     switch (a.g) {
         case 1: e = launch_partial<1>(a, blocks, stream); break;
         case 2: e = launch_partial<2>(a, blocks, stream); break;
@@ -1080,8 +1156,82 @@ extern "C" oscar_status oscar_decode_attn(hipStream_t stream, const oscar_layout
     if (opts && opts->kernel_end && hipEventRecord(opts->kernel_end, stream) != hipSuccess)
         return fail(OSCAR_ERR_HIP, "hipEventRecord failed");
 
-    hipLaunchKernelGGL(merge_kernel, dim3(batch * a.hkv), dim3(512), 0, stream, a);
+    hipLaunchKernelGGL(merge_kernel, dim3(a.batch * a.hkv), dim3(512), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(OSCAR_ERR_HIP, std::string("merge launch: ") + hipGetErrorString(e));
     return OSCAR_OK;
+}
+
+}  // namespace
+
+extern "C" oscar_status oscar_decode_attn(hipStream_t stream, const oscar_layout *layout,
+                                          const oscar_pool *pool, const void *q, oscar_dtype q_dtype,
+                                          int32_t batch, const int32_t *req_ids,
+                                          const int32_t *seq_lens, const int32_t *seq_lens_host,
+                                          const int32_t *req_to_slot, int64_t req_to_slot_stride,
+                                          const float *R_K, const float *R_V, float sm_scale,
+                                          void *out, oscar_dtype out_dtype, void *workspace,
+                                          size_t workspace_bytes, const oscar_launch_opts *opts) {
+    oscar_status st = check_decode_common(layout, pool, q, q_dtype, req_to_slot, R_K, R_V, sm_scale, out,
+                                          out_dtype);
+    if (st != OSCAR_OK) return st;
+    if (!req_ids || !seq_lens) return fail(OSCAR_ERR_INVALID_ARG, "a required pointer is null");
+    DecodePlan plan;
+    st = make_decode_plan(*layout, batch, seq_lens_host, opts, &plan);
+    if (st != OSCAR_OK) return st;
+    st = check_workspace(plan, req_to_slot_stride, workspace, workspace_bytes);
+    if (st != OSCAR_OK) return st;
+    DecodeArgs a = make_args(layout, pool, q, q_dtype, batch, req_to_slot, req_to_slot_stride, R_K, R_V,
+                             sm_scale, out, out_dtype, workspace, plan);
+    a.req_ids = req_ids;
+    a.seq_lens = seq_lens;
+    return launch_decode(a, plan, stream, opts);
+}
+
+extern "C" oscar_status oscar_extend_attn(hipStream_t stream, const oscar_layout *layout,
+                                          const oscar_pool *pool, const void *q, oscar_dtype q_dtype,
+                                          const void *k_new, const void *v_new, oscar_dtype kv_dtype,
+                                          int32_t n_new, int32_t req_id, int32_t prefix_len,
+                                          const int32_t *req_to_slot, int64_t req_to_slot_stride,
+                                          const float *R_K, const float *R_V, float sm_scale,
+                                          void *out, oscar_dtype out_dtype, void *workspace,
+                                          size_t workspace_bytes, const oscar_launch_opts *opts) {
+    oscar_status st = check_decode_common(layout, pool, q, q_dtype, req_to_slot, R_K, R_V, sm_scale, out,
+                                          out_dtype);
+    if (st != OSCAR_OK) return st;
+    if (!k_new || !v_new) return fail(OSCAR_ERR_INVALID_ARG, "a required pointer is null");
+    if (kv_dtype != OSCAR_F32 && kv_dtype != OSCAR_BF16 && kv_dtype != OSCAR_F16)
+        return fail(OSCAR_ERR_INVALID_ARG, "kv_dtype must be F32, BF16 or F16");
+    if (n_new < 1) return fail(OSCAR_ERR_INVALID_ARG, "n_new must be >= 1");
+    if (req_id < 0 || req_id >= layout->max_requests)
+        return fail(OSCAR_ERR_INVALID_ARG, "req_id must be in [0, max_requests)");
+    if (prefix_len < 0) return fail(OSCAR_ERR_INVALID_ARG, "prefix_len must be >= 0");
+    if (int64_t(prefix_len) + n_new > int64_t(INT32_MAX))
+        return fail(OSCAR_ERR_INVALID_ARG, "prefix_len + n_new must fit int32");
+    if (int64_t(n_new) * layout->num_kv_heads * 2 > INT32_MAX)
+        return fail(OSCAR_ERR_UNSUPPORTED, "n_new x KV heads exceeds one launch grid");
+    const std::vector<int32_t> lens(size_t(n_new), prefix_len);
+    DecodePlan plan;
+    st = make_decode_plan(*layout, n_new, lens.data(), opts, &plan, true);
+    if (st != OSCAR_OK) return st;
+    st = check_workspace(plan, req_to_slot_stride, workspace, workspace_bytes);
+    if (st != OSCAR_OK) return st;
+    DecodeArgs a = make_args(layout, pool, q, q_dtype, n_new, req_to_slot, req_to_slot_stride, R_K, R_V,
+                             sm_scale, out, out_dtype, workspace, plan);
+    a.fixed_req = req_id;
+    a.fixed_len = prefix_len;
+
+    RotateArgs r;
+    r.k = k_new;
+    r.v = v_new;
+    r.r_k = R_K;
+    r.r_v = R_V;
+    r.out = reinterpret_cast<uint16_t *>(static_cast<uint8_t *>(workspace) + plan.ws_newkv);
+    r.hkv = layout->num_kv_heads;
+    r.dtype = kv_dtype;
+    hipLaunchKernelGGL(extend_rotate_kernel, dim3(n_new * layout->num_kv_heads * 2), dim3(kHeadDim), 0,
+                       stream, r);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(OSCAR_ERR_HIP, std::string("rotate launch: ") + hipGetErrorString(e));
+    return launch_decode(a, plan, stream, opts);
 }

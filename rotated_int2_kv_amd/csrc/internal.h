@@ -39,11 +39,16 @@ struct DecodePlan {
     size_t ws_part_o = 0;
     size_t ws_part_ml = 0;
     size_t ws_zero = 0;          // 256 bytes the decode clears: stand-in record of unusable tokens
+    size_t ws_newkv = 0;         // extend: BF16 rotated K, V of the new tokens
+    int32_t extra_item = -1;     // extend: work item of the new tokens (the last one)
     size_t ws_bytes = 0;
 };
 
+// Work split and workspace layout of a decode step, or (extend = true) of an
+// extend call whose `batch` rows are new tokens reading a prefix of length
+// seq_lens_host[row] (which may then be 0) plus the new tokens themselves.
 oscar_status make_decode_plan(const oscar_layout &lay, int32_t batch,
                               const int32_t *seq_lens_host, const oscar_launch_opts *opts,
-                              DecodePlan *plan);
+                              DecodePlan *plan, bool extend = false);
 
 }  // namespace oscar

@@ -51,14 +51,15 @@ oscar_status check_layout(const oscar_layout *lay) {
 
 oscar_status make_decode_plan(const oscar_layout &lay, int32_t batch,
                               const int32_t *seq_lens_host, const oscar_launch_opts *opts,
-                              DecodePlan *plan) {
+                              DecodePlan *plan, bool extend) {
     if (batch < 1) return fail(OSCAR_ERR_INVALID_ARG, "batch must be >= 1");
     if (!seq_lens_host) return fail(OSCAR_ERR_INVALID_ARG, "seq_lens_host is null");
     const int64_t S = lay.sink_tokens, W = lay.recent_tokens;
     int64_t total_hist = 0, max_hist = 0, max_len = 0;
     for (int32_t b = 0; b < batch; ++b) {
         const int64_t L = seq_lens_host[b];
-        if (L < 1) return fail(OSCAR_ERR_INVALID_ARG, "every sequence length must be >= 1");
+        if (L < (extend ? 0 : 1))
+            return fail(OSCAR_ERR_INVALID_ARG, extend ? "prefix_len must be >= 0" : "every sequence length must be >= 1");
         const int64_t hist = std::max<int64_t>(0, std::max(S, L - W) - S);
         total_hist += hist;
         max_hist = std::max(max_hist, hist);
@@ -77,7 +78,7 @@ oscar_status make_decode_plan(const oscar_layout &lay, int32_t batch,
         chunk = (chunk + 31) / 32 * 32;
         chunk = std::min<int64_t>(8192, std::max<int64_t>(256, chunk));
     }
-    const int64_t items = 2 + (max_hist + chunk - 1) / chunk;
+    const int64_t items = 2 + (max_hist + chunk - 1) / chunk + (extend ? 1 : 0);
     const int64_t hq = lay.num_q_heads;
     auto align = [](size_t x) { return (x + 255) / 256 * 256; };
     plan->chunk = static_cast<int32_t>(chunk);
@@ -94,6 +95,11 @@ oscar_status make_decode_plan(const oscar_layout &lay, int32_t batch,
     off += align(size_t(batch) * items * hq * 2 * sizeof(float));
     plan->ws_zero = off;
     off += 256;
+    if (extend) {
+        plan->extra_item = static_cast<int32_t>(items - 1);
+        plan->ws_newkv = off;
+        off += align(size_t(batch) * lay.num_kv_heads * 2 * kHeadDim * sizeof(uint16_t));
+    }
     plan->ws_bytes = off;
     return OSCAR_OK;
 }
@@ -279,6 +285,20 @@ oscar_status oscar_decode_workspace_size(const oscar_layout *layout, int32_t bat
     if (!bytes) return fail(OSCAR_ERR_INVALID_ARG, "bytes is null");
     DecodePlan plan;
     st = make_decode_plan(*layout, batch, seq_lens_host, opts, &plan);
+    if (st != OSCAR_OK) return st;
+    *bytes = plan.ws_bytes;
+    return OSCAR_OK;
+}
+
+oscar_status oscar_extend_workspace_size(const oscar_layout *layout, int32_t n_new, int32_t prefix_len,
+                                         const oscar_launch_opts *opts, size_t *bytes) {
+    oscar_status st = check_layout(layout);
+    if (st != OSCAR_OK) return st;
+    if (!bytes) return fail(OSCAR_ERR_INVALID_ARG, "bytes is null");
+    if (n_new < 1) return fail(OSCAR_ERR_INVALID_ARG, "n_new must be >= 1");
+    const std::vector<int32_t> lens(size_t(n_new), prefix_len);
+    DecodePlan plan;
+    st = make_decode_plan(*layout, n_new, lens.data(), opts, &plan, true);
     if (st != OSCAR_OK) return st;
     *bytes = plan.ws_bytes;
     return OSCAR_OK;

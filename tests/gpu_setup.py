@@ -66,12 +66,13 @@ def exact_rotations(kind: str, hkv: int, d: int = 128, seed: int = 0):
     return r, r[::-1].copy()
 
 
-def kv_values(w: workloads.Workload, n: int, stream: int = 0):
-    """Host float32 values of the K/V inputs (after the workload's dtype) and
-    the device tensors in that dtype."""
+def kv_values(w: workloads.Workload, n: int, stream: int = 0, dtype=None):
+    """Host float32 values of the K/V inputs (after the workload's dtype, or
+    `dtype` if given: "f32", "bf16" or "f16") and the device tensors in it."""
     torch = torch_gpu()
     k, v = workloads.raw_kv_host(w, n, stream)
-    dt = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32
+    name = dtype or w.kv_dtype
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[name]
     kd = torch.from_numpy(k).to(dt).cuda()
     vd = torch.from_numpy(v).to(dt).cuda()
     return kd.float().cpu().numpy(), vd.float().cpu().numpy(), kd, vd

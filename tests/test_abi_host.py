@@ -203,3 +203,49 @@ def test_build_rotation_degenerate_and_small():
     assert np.abs(r @ r.T - np.eye(4)).max() < 1e-15
     r, ev = B.oscar_build_rotation(np.array([[2.0]]), 1)
     assert r[0, 0] == 1.0 and ev[0] == 2.0
+
+
+def _extend(lay, n_new, prefix, **over):
+    args = dict(stream=None, layout=ctypes.byref(lay.c()),
+                pool=ctypes.byref(B.CPool(FAKE.value, FAKE.value, FAKE.value)), q=FAKE,
+                qd=B.OSCAR_BF16, k=FAKE, v=FAKE, kvd=B.OSCAR_BF16, n=n_new, req=0, P=prefix,
+                r2s=FAKE, stride=max(prefix, 1), rk=FAKE, rv=FAKE, sm=0.088, out=FAKE, od=B.OSCAR_F32,
+                ws=ctypes.c_void_p(0x100000), ws_bytes=1 << 40, opts=None)
+    args.update(over)
+    return B._lib.oscar_extend_attn(*args.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), B.OSCAR_ERR_INVALID_ARG),
+    (dict(k=None), B.OSCAR_ERR_INVALID_ARG),
+    (dict(v=None), B.OSCAR_ERR_INVALID_ARG),
+    (dict(kvd=7), B.OSCAR_ERR_INVALID_ARG),
+    (dict(n=0), B.OSCAR_ERR_INVALID_ARG),
+    (dict(req=-1), B.OSCAR_ERR_INVALID_ARG),
+    (dict(req=4), B.OSCAR_ERR_INVALID_ARG),          # max_requests = 4
+    (dict(P=-1), B.OSCAR_ERR_INVALID_ARG),
+    (dict(P=2 ** 31 - 10), B.OSCAR_ERR_INVALID_ARG),  # P + n overflows int32
+    (dict(stride=100), B.OSCAR_ERR_INVALID_ARG),     # must cover the prefix
+    (dict(ws_bytes=100), B.OSCAR_ERR_WORKSPACE),
+    (dict(ws=ctypes.c_void_p(0x100040)), B.OSCAR_ERR_INVALID_ARG),
+    (dict(sm=float("nan")), B.OSCAR_ERR_INVALID_ARG),
+])
+def test_extend_rejects_before_launch(over, status):
+    assert _extend(L(), 37, 5000, **over) == status
+
+
+def test_extend_workspace_size():
+    lay = L()
+    n, P = 37, 100000
+    chunk, items = B.oscar_decode_plan(lay, [P] * n)
+    ws = B.oscar_extend_workspace_size(lay, n, P)
+    # the decode workspace of n rows at length P, one more work item per row
+    # (the new tokens), and the new tokens' BF16 rotated K and V
+    need = (n * 32 * 128 * 4 + n * 32 * 8 * 4 + n * (items + 1) * 32 * (128 + 2) * 4 + 256
+            + n * 8 * 2 * 128 * 2)
+    assert need <= ws <= need + 6 * 256
+    assert B.oscar_extend_workspace_size(lay, 1, 0) > 0
+    with pytest.raises(B.OscarError):
+        B.oscar_extend_workspace_size(lay, 0, 10)
+    with pytest.raises(B.OscarError):
+        B.oscar_extend_workspace_size(lay, 4, -1)

@@ -12,14 +12,14 @@ import parity_tools as pt
 pytestmark = pytest.mark.gpu
 
 
-def _run_append(w, lens, r_k, r_v, alpha=1.0, seed=0, slack=1.25, rot_out=True):
+def _run_append(w, lens, r_k, r_v, alpha=1.0, seed=0, slack=1.25, rot_out=True, dtype=None):
     torch = gs.torch_gpu()
     from rotated_int2_kv_amd import binding as B
     total = int(sum(lens))
     num_slots = int(np.ceil(slack * total)) + 7
     lay_b, lay_o = gs.layouts(w, num_slots, len(lens))
     req, pos, slots, table = gs.append_batch(lens, num_slots, seed)
-    kh, vh, kd, vd = gs.kv_values(w, total, stream=seed)
+    kh, vh, kd, vd = gs.kv_values(w, total, stream=seed, dtype=dtype)
     pool = B.new_pool(lay_b)
     rot = torch.zeros((total, w.num_kv_heads, 2, w.head_dim), dtype=torch.float32,
                       device="cuda") if rot_out else None
@@ -48,6 +48,24 @@ def test_append_bit_exact_with_exact_rotations(kind, wname, lens):
     assert np.array_equal(recent, opool.recent)
     assert np.array_equal(out["rot"][:, :, 0, :], rot["k"])
     assert np.array_equal(out["rot"][:, :, 1, :], rot["v"])
+
+
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_append_other_input_dtypes_bit_exact(dtype):
+    """fp16 and fp32 K/V inputs (converted exactly to fp32 by the kernel) with
+    rotations whose products are exact: every byte equals the oracle's."""
+    w = workloads.workload("layer_small")
+    lens = (700, 333, 40)
+    r_k, r_v = gs.exact_rotations("signed_perm", w.num_kv_heads)
+    out = _run_append(w, lens, r_k, r_v, dtype=dtype)
+    lay_o = out["lay_o"]
+    opool = cache.new_pool(lay_o)
+    cache.append(opool, lay_o, out["k"], out["v"], out["req"], out["pos"], out["slots"],
+                 np.asarray(lens), r_k, r_v)
+    rec, sink, recent = gs.pool_host(out["pool"], lay_o)
+    assert np.array_equal(rec, opool.records)
+    assert np.array_equal(sink, opool.sink)
+    assert np.array_equal(recent, opool.recent)
 
 
 def _check_general(out, w, rots_oracle, alpha):

@@ -3,6 +3,7 @@
 import math
 
 import numpy as np
+import pytest
 import torch
 
 from oracle import attention, cache, quant, rotation
@@ -93,3 +94,69 @@ def test_decode_rotation_round_trip_without_quantisation():
     ref = attention.attention(q[0].astype(np.float64) @ rk[0].astype(np.float64), kr, vr,
                               128 ** -0.5) @ rv[0].astype(np.float64).T
     assert np.abs(o[0] - ref).max() < 1e-12
+
+
+def _sdpa_ref(qt, kb, vb, mask):
+    """torch SDPA (CPU, fp64) for one head: qt [n, d], kb/vb [m, d], mask [n, m] bool."""
+    return torch.nn.functional.scaled_dot_product_attention(
+        qt[None, None], kb[None, None], vb[None, None], attn_mask=mask[None, None])[0, 0].numpy()
+
+
+def test_extend_equals_sdpa_with_offset_causal_mask():
+    """R = I and a prefix inside the BF16 regions: extend is causal attention
+    over [prefix; chunk] where new token i sees positions 0 .. P + i."""
+    P, n, hkv, g = 150, 23, 2, 3
+    lay, pool, _, k, v, slots, eye = _bf16_only_case(P + n, hkv, g, 8)
+    pool = cache.new_pool(lay)
+    cache.append(pool, lay, k[:P], v[:P], np.zeros(P, int), np.arange(P), slots[:P], [P], eye, eye)
+    rng = np.random.default_rng(2)
+    q = rng.standard_normal((n, g * hkv, 128)).astype(np.float32)
+    o = attention.extend(pool, lay, q, k[P:], v[P:], 0, P, slots, eye, eye, 0.11)
+    kb = torch.from_numpy(quant.bf16_round(k)).double()
+    vb = torch.from_numpy(quant.bf16_round(v)).double()
+    mask = torch.from_numpy(np.arange(P + n)[None, :] <= P + np.arange(n)[:, None])
+    for h in range(g * hkv):
+        ref = _sdpa_ref(torch.from_numpy(q[:, h]).double() * (0.11 * 128 ** 0.5), kb[:, h // g],
+                        vb[:, h // g], mask)
+        assert np.allclose(o[:, h], ref, atol=1e-12, rtol=1e-12)
+
+
+def test_extend_empty_prefix_is_causal_self_attention():
+    n, hkv, g = 40, 1, 4
+    lay = cache.Layout(128, 32, hkv, g, 64, 256, num_slots=1, max_requests=1)
+    pool = cache.new_pool(lay)
+    rng = np.random.default_rng(5)
+    k, v = rng.standard_normal((2, n, hkv, 128)).astype(np.float32)
+    q = rng.standard_normal((n, g, 128)).astype(np.float32)
+    eye = np.eye(128, dtype=np.float32)[None]
+    o = attention.extend(pool, lay, q, k, v, 0, 0, np.zeros(0, int), eye, eye, 128 ** -0.5)
+    kb = torch.from_numpy(quant.bf16_round(k[:, 0])).double()[None, None]
+    vb = torch.from_numpy(quant.bf16_round(v[:, 0])).double()[None, None]
+    for h in range(g):
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[:, h]).double()[None, None], kb, vb, is_causal=True)[0, 0].numpy()
+        assert np.allclose(o[:, h], ref, atol=1e-12, rtol=1e-12)
+
+
+@pytest.mark.parametrize("P", [0, 30, 64, 200, 319])
+def test_extend_one_token_equals_decode_after_append(P):
+    """With P + 1 <= S + W no prefix token leaves the BF16 window when the new
+    token is appended, so extend of that token equals decode at length P + 1
+    of the cache with the token appended (OSCAR rotations live, so a wrong
+    rotation of the new key or value, or of the query, shows)."""
+    hkv, g = 2, 2
+    w = workloads.custom("tiny", num_kv_heads=hkv, num_q_heads=g * hkv, seq_lens=(P + 1,), seed=3)
+    cov = workloads.covariances(w)
+    rk = np.stack([rotation.composite_rotation(c) for c in cov.sigma_q]).astype(np.float32)
+    rv = np.stack([rotation.composite_rotation(c) for c in cov.sigma_s]).astype(np.float32)
+    lay = cache.Layout(128, 32, hkv, g * hkv, 64, 256, num_slots=P + 1, max_requests=1)
+    k, v = workloads.raw_kv_host(w, P + 1)
+    q = workloads.queries(w)
+    slots = np.random.default_rng(P).permutation(P + 1)
+    pool = cache.new_pool(lay)
+    if P:
+        cache.append(pool, lay, k[:P], v[:P], np.zeros(P, int), np.arange(P), slots[:P], [P], rk, rv)
+    o_ext = attention.extend(pool, lay, q, k[P:], v[P:], 0, P, slots, rk, rv, 128 ** -0.5)
+    cache.append(pool, lay, k[P:], v[P:], np.zeros(1, int), [P], slots[P:], [P + 1], rk, rv)
+    o_dec = attention.decode(pool, lay, q, [0], [P + 1], slots[None, :], rk, rv, 128 ** -0.5)
+    assert np.abs(o_ext - o_dec).max() < 1e-12

@@ -11,8 +11,9 @@ input resident in HBM before timing starts.
 Printed: one JSON line with KV tokens/s (sum of context lengths / step time),
 the split-K kernel's achieved bandwidth against the HBM roofline (timed live
 with HIP events on the launch stream), the quant-append throughput of the
-131,072-token append workload, and the fp64 CPU oracle's rate on a bounded
-sample of the same decode workload.
+131,072-token append workload, one extend call (an 8,192-token prefill chunk
+over a 122,880-token cached prefix), and the fp64 CPU oracle's rate on a
+bounded sample of the same decode workload.
 
 The default run times 2,000 steps after 500 warm-up steps: under this load the
 part runs at its board power limit, and its clocks take a few hundred
@@ -37,6 +38,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "INT2 decode-attn KV tokens/s & % HBM roofline @100K ctx bs32; quant tok/s"
 HBM_PEAK_GBS = 8000.0
+F16_MFMA_PEAK_TFLOPS = 2500.0          # dense fp16/bf16 matrix-core peak
 HISTORY_BYTES_PER_TOKEN_HEAD = 96      # K codes 32 + V codes 32 + K (s,z) 16 + V (s,z) 16
 SLOT_BYTES_PER_TOKEN = 4
 BF16_BYTES_PER_TOKEN_HEAD = 512        # K and V, 128 bf16 each
@@ -221,6 +223,65 @@ def run_append(args, torch, B, workloads):
                 rotation_tflops=flops / (ms * 1e-3) / 1e12)
 
 
+def run_extend(args, torch, B, workloads):
+    """One extend call of the extend workload: the last 8,192-token chunk of a
+    131,072-token prompt attends to the 122,880-token INT2/BF16 prefix."""
+    w = workloads.workload("extend_8k")
+    n = workloads.EXTEND_CHUNK
+    P = w.seq_lens[0] - n
+    hkv, hq = w.num_kv_heads, w.num_q_heads
+    lay = B.Layout(128, 32, hkv, hq, w.sink, w.recent, num_slots=w.num_slots, max_requests=1)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    rk, rv = build_rotations(B, w)
+    rk_d, rv_d = dev(rk), dev(rv)
+    slots = workloads.slot_table(w)[0]
+    pool = B.new_pool(lay)
+    k, v = workloads.raw_kv_device(w, P, stream=0, device="cuda")
+    B.oscar_quant_append(lay, pool, k.to(torch.bfloat16), v.to(torch.bfloat16), dev(np.zeros(P, np.int32)),
+                         dev(np.arange(P, dtype=np.int32)), dev(slots[:P]), dev(np.array([P], np.int32)),
+                         rk_d, rv_d)
+    del k, v
+    kn, vn = workloads.raw_kv_device(w, n, stream=1, device="cuda")
+    kn, vn = kn.to(torch.bfloat16), vn.to(torch.bfloat16)
+    q = dev(workloads.queries(w, n_rows=n, stream=9)).to(torch.bfloat16)
+    table = dev(slots[None, :].astype(np.int32))
+    ws = torch.empty(B.oscar_extend_workspace_size(lay, n, P), dtype=torch.uint8, device="cuda")
+    out = torch.empty((n, hq, 128), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call(ev=None):
+        B.oscar_extend_attn(lay, pool, q, kn, vn, 0, P, table, rk_d, rv_d, 128 ** -0.5, out, ws,
+                            stream=stream, kernel_begin=None if ev is None else ev[0],
+                            kernel_end=None if ev is None else ev[1])
+
+    call()
+    torch.cuda.synchronize()
+    reps = 3
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record(stream)
+        b.record(stream)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(reps):
+        call(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    # attention flops: q.k and p.v over every key each new token sees
+    keys_seen = n * P + n * (n + 1) // 2
+    flops = 4 * 128 * hq * keys_seen
+    prefix_bytes = decode_kernel_bytes([P], hkv, w.sink, w.recent)
+    return dict(workload=w.name, new_tokens=n, prefix_len=P, q_heads=hq, kv_heads=hkv, ms=ms,
+                kernel_ms=kern_ms, new_tokens_per_s=n / (ms * 1e-3),
+                attention_tflops=flops / (kern_ms * 1e-3) / 1e12,
+                frac_f16_mfma=flops / (kern_ms * 1e-3) / 1e12 / F16_MFMA_PEAK_TFLOPS,
+                prefix_bytes=prefix_bytes, prefix_reads_gb_per_s=n * prefix_bytes / (kern_ms * 1e-3) / 1e9,
+                output_finite=bool(torch.isfinite(out.float()).all().item()))
+
+
 def cpu_baseline(workloads):
     """The oracle, as it stands, on one request of the decode workload."""
     from threadpoolctl import threadpool_limits
@@ -261,6 +322,7 @@ def main():
     ap.add_argument("--history-chunk", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-append", action="store_true")
+    ap.add_argument("--no-extend", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -291,6 +353,10 @@ def main():
     app = None if args.no_append else run_append(args, torch, B, workloads)
     if app:
         log(f"[bench] append {app['ms']:.3f} ms, {app['tokens_per_s']:.3e} tok/s, {app['gb_per_s']:.0f} GB/s")
+    ext = None if args.no_extend else run_extend(args, torch, B, workloads)
+    if ext:
+        log(f"[bench] extend {ext['ms']:.2f} ms ({ext['new_tokens']} new tokens over {ext['prefix_len']}), "
+            f"{ext['attention_tflops']:.1f} TFLOP/s")
     base = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle ...")
@@ -319,6 +385,7 @@ def main():
                      "algorithmic_bytes": d["kbytes"]},
         "decode_steps_per_s": 1e3 / ms,
         "quant_append": app,
+        "extend": ext,
         "cpu_baseline": base,
         "output_finite": d["o_finite"],
     }

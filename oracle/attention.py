@@ -77,12 +77,13 @@ def decode(pool: cache.Pool, lay: cache.Layout, q, req_ids, seq_lens, req_to_slo
 
 
 def extend(pool: cache.Pool, lay: cache.Layout, q, k_new, v_new, req: int, prefix_len: int,
-           slots_of_req, r_k, r_v, sm_scale: float) -> np.ndarray:
+           slots_of_req, r_k, r_v, sm_scale: float, rows=None) -> np.ndarray:
     """Attention of a chunk of n new tokens of request ``req`` (fp64, original basis).
 
     q [n, Hq, d]; k_new, v_new [n, Hkv, d] raw (unrotated) keys and values of
     the tokens at positions P .. P + n - 1, P = prefix_len; slots_of_req maps
-    positions [S, P) to pool slots.  Returns o [n, Hq, d].
+    positions [S, P) to pool slots.  Returns o [n, Hq, d]; ``rows`` restricts
+    the work to some new tokens (the others stay NaN).
     """
     q = np.asarray(q, dtype=np.float64)
     n, hq, d = q.shape
@@ -90,13 +91,14 @@ def extend(pool: cache.Pool, lay: cache.Layout, q, k_new, v_new, req: int, prefi
     rk = np.asarray(r_k, dtype=np.float32)
     rv = np.asarray(r_v, dtype=np.float32)
     prefix = cache.gather(pool, lay, req, int(prefix_len), slots_of_req)
-    out = np.zeros((n, hq, d))
+    out = np.full((n, hq, d), np.nan)
+    rows = range(n) if rows is None else rows
     for hk in range(lay.num_kv_heads):
         kn = quant.bf16_round(quant.rotate(np.asarray(k_new)[:, hk, :], rk[hk])).astype(np.float64)
         vn = quant.bf16_round(quant.rotate(np.asarray(v_new)[:, hk, :], rv[hk])).astype(np.float64)
         keys = np.concatenate([prefix[:, hk, 0, :], kn])
         vals = np.concatenate([prefix[:, hk, 1, :], vn])
-        for i in range(n):
+        for i in rows:
             qh = q[i, hk * g:(hk + 1) * g, :] @ rk[hk].astype(np.float64)
             m = int(prefix_len) + i + 1
             o_rot = attention(qh, keys[:m], vals[:m], sm_scale)

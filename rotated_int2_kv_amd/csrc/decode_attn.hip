@@ -356,7 +356,7 @@ __device__ __forceinline__ void wait_vmem() {
 }
 
 template <int GQ>
-__device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, int p0, int p1,
+__device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, int p0, int p1,
                           uint8_t *smem) {
     constexpr int HS = (GQ + 3) / 4;          // sets of 4 query heads
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform over the wave
@@ -746,7 +746,7 @@ __device__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, in
 // `pbuf` is this wave's LDS scratch: q' [kMaxGroup][128] then p [kMaxGroup][64].
 constexpr int kBf16WaveFloats = kMaxGroup * kHeadDim + kMaxGroup * kBf16Chunk;
 
-__device__ void bf16_item(const DecodeArgs &a, int b, int req, int j, int hk, int p0, int p1,
+__device__ __forceinline__ void bf16_item(const DecodeArgs &a, int b, int req, int j, int hk, int p0, int p1,
                           bool active, float *pbuf) {
     const int lane = threadIdx.x & 63;
     const int g = a.g;

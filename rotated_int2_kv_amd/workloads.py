@@ -31,6 +31,9 @@ HEAD_DIM = 128
 GROUP_SIZE = 32
 SINK_TOKENS = 64
 RECENT_TOKENS = 256
+# prefill chunk of the extend workload: the chunked-prefill size the Qiita
+# article settles on (third pitfall, chunk size against state-cache slots)
+EXTEND_CHUNK = 8192
 
 
 @dataclasses.dataclass(frozen=True)
@@ -77,13 +80,17 @@ def _mixed_lengths(batch: int, lo: int, hi: int, seed: int) -> Tuple[int, ...]:
 
 
 def workload(name: str) -> Workload:
-    """The five workloads at full size, plus reduced sizes for oracle runs.
+    """The six workloads at full size, plus reduced sizes for oracle runs.
 
     ``tiny``       1 request, 4 q heads / 1 KV head, L = 1,024, fp32 K/V.
     ``layer_32k``  Qwen3-8B-shaped layer: 32 q / 8 KV heads, L = 32,768.
     ``decode_b32`` Qwen3-4B-shaped decode batch: 32 requests at L = 100,000.
     ``append_131k``Qwen3-32B-shaped append: 131,072 new tokens, 8 KV heads.
     ``mixed_b64``  64 requests, L ~ U{4,096..131,072}, 24 q / 4 KV heads.
+    ``extend_8k``  the last chunked-prefill chunk of a 131,072-token prompt:
+                   EXTEND_CHUNK = 8,192 new tokens over a 122,880-token
+                   prefix, 32 q / 8 KV heads (seq_lens holds the length
+                   after the chunk).
     A ``_small`` suffix keeps each shape but shortens the contexts so that
     the fp64 oracle finishes in seconds while still spanning several tiles
     and a ragged tail.
@@ -100,6 +107,8 @@ def workload(name: str) -> Workload:
                          1.5, 1.5, False, 1.0, False, 3),
         "mixed_b64": W("mixed_b64", 64, 24, 4, _mixed_lengths(64, 4096, 131072, 4), "bf16",
                        "bf16", 3, 10.0, 50.0, 1.5, 1.5, False, 1.25, True, 4),
+        "extend_8k": W("extend_8k", 1, 32, 8, (131072,), "bf16", "bf16", 3, 10.0, 50.0,
+                       1.5, 1.5, False, 1.0, False, 5),
         # reduced sizes (same per-head shapes and value recipes)
         "layer_small": W("layer_small", 1, 32, 8, (2413,), "bf16", "bf16", 3, 10.0, 50.0,
                          1.5, 1.5, False, 1.0, False, 11),

@@ -43,6 +43,57 @@ def test_library_is_built_for_gfx950():
     assert b"amdgcn-amd-amdhsa--gfx950" in blob
 
 
+def _kernel_metadata():
+    """Kernel descriptors of every gfx950 code object embedded in liboscar.so
+    (clang offload bundles -> ELF note of type NT_AMDGPU_METADATA, msgpack)."""
+    import struct
+
+    import msgpack
+    blob = open(B.LIB_PATH, "rb").read()
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    kernels = []
+    at = blob.find(magic)
+    while at >= 0:
+        n, = struct.unpack_from("<Q", blob, at + 24)
+        o = at + 32
+        for _ in range(n):
+            off, size, tl = struct.unpack_from("<QQQ", blob, o)
+            triple = blob[o + 24:o + 24 + tl].decode()
+            o += 24 + tl
+            if "gfx950" not in triple:
+                continue
+            elf = blob[at + off:at + off + size]
+            assert elf[:4] == b"\x7fELF"
+            shoff, = struct.unpack_from("<Q", elf, 0x28)
+            shentsize, shnum = struct.unpack_from("<HH", elf, 0x3A)
+            for sidx in range(shnum):
+                sh = shoff + sidx * shentsize
+                if struct.unpack_from("<I", elf, sh + 4)[0] != 7:        # SHT_NOTE
+                    continue
+                soff, ssize = struct.unpack_from("<QQ", elf, sh + 0x18)
+                p = soff
+                while p < soff + ssize:
+                    nsz, dsz, ntype = struct.unpack_from("<III", elf, p)
+                    p += 12 + (nsz + 3) // 4 * 4
+                    if ntype == 32:                                      # NT_AMDGPU_METADATA
+                        kernels += msgpack.unpackb(elf[p:p + dsz])["amdhsa.kernels"]
+                    p += (dsz + 3) // 4 * 4
+        at = blob.find(magic, at + 1)
+    return kernels
+
+
+def test_kernels_use_no_scratch_and_do_not_spill():
+    """Every kernel keeps its state in registers and LDS: a private segment
+    (an out-of-line call or a spilled array) would put the hot loops on
+    scratch memory."""
+    ks = _kernel_metadata()
+    names = [k[".name"] for k in ks]
+    assert any("partial_kernel" in n for n in names) and any("quant_append" in n for n in names)
+    for k in ks:
+        assert k[".private_segment_fixed_size"] == 0, k[".name"]
+        assert k.get(".vgpr_spill_count", 0) == 0 and k.get(".sgpr_spill_count", 0) == 0, k[".name"]
+
+
 def L(**kw):
     base = dict(head_dim=128, group_size=32, num_kv_heads=8, num_q_heads=32, sink_tokens=64,
                 recent_tokens=256, num_slots=1000, max_requests=4)

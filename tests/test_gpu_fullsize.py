@@ -8,6 +8,9 @@ The fp64 oracle cannot redo a whole step of these workloads, so:
   is decoded on the GPU with the default split-K plan, and the sampled
   requests' outputs are compared with the oracle's fp64 decode of those bytes
   (max over q heads of ||o - o_ref||_inf / ||o_ref||_inf <= 2e-3);
+* extend: the oracle writes the 122,880-token prefix of the extend workload,
+  the GPU runs the 8,192-token chunk over it with the default plan, and sampled
+  new tokens are compared with the oracle's fp64 extend (same bound);
 * append: one call appends all 131,072 tokens of the append workload; on a
   seeded sample of tokens the rotated values are checked against the exact
   product (normwise <= 1e-5 and inside the per-element bound of the matrix-core
@@ -178,3 +181,43 @@ def test_append_131k_full_size_sampled():
     assert np.array_equal(sink[0, idx[sk]], bits[sk])
     rg = idx >= n - w.recent
     assert np.array_equal(recent[0, idx[rg] % w.recent], bits[rg])
+
+
+def test_extend_8k_full_size_sampled():
+    """8,192 new tokens over a 122,880-token prefix, 32 q / 8 KV heads."""
+    torch = gs.torch_gpu()
+    from rotated_int2_kv_amd import binding as B
+    w = workloads.workload("extend_8k")
+    n = workloads.EXTEND_CHUNK
+    L = w.seq_lens[0]
+    P = L - n
+    lay_b, lay_o = gs.layouts(w, w.num_slots, 1)
+    r_k, r_v = gs.oracle_rotations(w)
+    slots = workloads.slot_table(w)[0]
+    k, v = workloads.raw_kv_host(w, P, stream=0)
+    gs.say(f"extend_8k full size: oracle append of the {P}-token prefix")
+    opool = cache.new_pool(lay_o)
+    cache.append(opool, lay_o, quant.bf16_round(k), quant.bf16_round(v), np.zeros(P, np.int64),
+                 np.arange(P), slots[:P], [P], r_k, r_v)
+    del k, v
+    pool = gs.upload_oracle_pool(opool)
+    kn, vn = workloads.raw_kv_device(w, n, stream=1, device="cuda")
+    kn, vn = kn.to(torch.bfloat16), vn.to(torch.bfloat16)
+    qd = torch.from_numpy(workloads.queries(w, n_rows=n, stream=9)).to(torch.bfloat16).cuda()
+    table = gs.dev(slots[None, :].astype(np.int32))
+    ws = torch.empty(B.oscar_extend_workspace_size(lay_b, n, P), dtype=torch.uint8, device="cuda")
+    out = torch.empty((n, w.num_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    gs.say(f"  extend of {n} tokens over P = {P}")
+    B.oscar_extend_attn(lay_b, pool, qd, kn, vn, 0, P, table, gs.dev(r_k), gs.dev(r_v),
+                        w.head_dim ** -0.5, out, ws)
+    torch.cuda.synchronize()
+    o_gpu = out.cpu().numpy()
+    assert np.all(np.isfinite(o_gpu))
+    rows = sorted({0, 1, 2, 31, 32, 4095, n - 2, n - 1}
+                  | set(np.random.default_rng(17).choice(n, 4, replace=False).tolist()))
+    o_ref = attention.extend(opool, lay_o, qd.float().cpu().numpy(), kn.float().cpu().numpy(),
+                             vn.float().cpu().numpy(), 0, P, slots, r_k, r_v, w.head_dim ** -0.5,
+                             rows=rows)
+    err = pt.normwise_rel(o_gpu[rows], o_ref[rows])
+    gs.say(f"  extend_8k rows {rows}: max normwise rel err {err.max():.3e} (median {np.median(err):.3e})")
+    assert err.max() <= TOL

@@ -11,9 +11,11 @@ input resident in HBM before timing starts.
 Printed: one JSON line with KV tokens/s (sum of context lengths / step time),
 the split-K kernel's achieved bandwidth against the HBM roofline (timed live
 with HIP events on the launch stream), the quant-append throughput of the
-131,072-token append workload, one extend call (an 8,192-token prefill chunk
-over a 122,880-token cached prefix), and the fp64 CPU oracle's rate on a
-bounded sample of the same decode workload.
+131,072-token append workload, the same decode step on a BF16 paged cache
+(the baseline of the OSCAR page's speed-ups) with the INT2/BF16 ratio, one
+extend call (an 8,192-token prefill chunk over a 122,880-token cached
+prefix), and the fp64 CPU oracle's rate on a bounded sample of the same
+decode workload.
 
 The default run times 2,000 steps after 500 warm-up steps: under this load the
 part runs at its board power limit, and its clocks take a few hundred
@@ -223,6 +225,63 @@ def run_append(args, torch, B, workloads):
                 rotation_tflops=flops / (ms * 1e-3) / 1e12)
 
 
+def run_bf16(args, torch, B, workloads):
+    """The same decode step on the BF16 paged cache (the baseline the OSCAR
+    page's speed-ups are quoted against): append one token per request, then
+    oscar_bf16_decode_attn over every position."""
+    w = workloads.workload(args.workload)
+    lens = np.asarray(w.seq_lens, np.int32)
+    bsz, hkv = w.batch, w.num_kv_heads
+    lay = B.Layout(128, 32, hkv, w.num_q_heads, w.sink, w.recent, num_slots=w.num_slots,
+                   max_requests=bsz)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    slots = workloads.slot_table(w)
+    table = dev(workloads.req_to_slot_matrix(w, slots, fill=0))
+    pool = B.new_bf16_pool(lay)
+    for b in range(bsz):
+        n = int(lens[b]) - 1
+        k, v = workloads.raw_kv_device(w, n, stream=b * 1000, device="cuda")
+        B.oscar_bf16_append(lay, pool, k.to(torch.bfloat16), v.to(torch.bfloat16), dev(slots[b][:n]))
+        del k, v
+    q = dev(workloads.queries(w, n_rows=bsz, stream=7)).to(torch.bfloat16)
+    kn, vn = workloads.raw_kv_device(w, bsz, stream=999_999, device="cuda")
+    kn, vn = kn.to(torch.bfloat16), vn.to(torch.bfloat16)
+    req_ids = dev(np.arange(bsz, dtype=np.int32))
+    new_slots = dev(np.array([slots[b][lens[b] - 1] for b in range(bsz)], np.int32))
+    lens_d = dev(lens)
+    ws = torch.empty(B.oscar_bf16_decode_workspace_size(lay, lens), dtype=torch.uint8, device="cuda")
+    out = torch.empty((bsz, w.num_q_heads, 128), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        B.oscar_bf16_append(lay, pool, kn, vn, new_slots, stream=stream)
+        B.oscar_bf16_decode_attn(lay, pool, q, req_ids, lens_d, lens, table, 128 ** -0.5, out, ws,
+                                 stream=stream, kernel_begin=None if ev is None else ev[0],
+                                 kernel_end=None if ev is None else ev[1])
+
+    for _ in range(args.warmup):
+        step()
+    steps = max(10, args.steps // 2)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        step(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    kbytes = int(lens.sum()) * (hkv * BF16_BYTES_PER_TOKEN_HEAD + SLOT_BYTES_PER_TOKEN)
+    return dict(workload=w.name, steps=steps, ms_per_step=ms, kernel_ms=kern_ms,
+                kv_tokens_per_s=int(lens.sum()) / (ms * 1e-3), algorithmic_bytes=kbytes,
+                gb_per_s=kbytes / (kern_ms * 1e-3) / 1e9, frac_hbm=kbytes / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                output_finite=bool(torch.isfinite(out.float()).all().item()))
+
+
 def run_extend(args, torch, B, workloads):
     """One extend call of the extend workload: the last 8,192-token chunk of a
     131,072-token prompt attends to the 122,880-token INT2/BF16 prefix."""
@@ -323,6 +382,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-append", action="store_true")
     ap.add_argument("--no-extend", action="store_true")
+    ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -353,6 +413,13 @@ def main():
     app = None if args.no_append else run_append(args, torch, B, workloads)
     if app:
         log(f"[bench] append {app['ms']:.3f} ms, {app['tokens_per_s']:.3e} tok/s, {app['gb_per_s']:.0f} GB/s")
+    bf = None if args.no_bf16 else run_bf16(args, torch, B, workloads)
+    if bf:
+        bf["int2_speedup_kernel"] = bf["kernel_ms"] / d["kern_ms"]
+        bf["int2_speedup_step"] = bf["ms_per_step"] / ms
+        log(f"[bench] bf16 baseline step {bf['ms_per_step']:.3f} ms, kernel {bf['kernel_ms']:.3f} ms, "
+            f"{bf['gb_per_s']:.0f} GB/s; INT2 speed-up {bf['int2_speedup_kernel']:.2f}x (kernel), "
+            f"{bf['int2_speedup_step']:.2f}x (step)")
     ext = None if args.no_extend else run_extend(args, torch, B, workloads)
     if ext:
         log(f"[bench] extend {ext['ms']:.2f} ms ({ext['new_tokens']} new tokens over {ext['prefix_len']}), "
@@ -385,6 +452,7 @@ def main():
                      "algorithmic_bytes": d["kbytes"]},
         "decode_steps_per_s": 1e3 / ms,
         "quant_append": app,
+        "bf16_baseline": bf,
         "extend": ext,
         "cpu_baseline": base,
         "output_finite": d["o_finite"],

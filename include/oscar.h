@@ -262,6 +262,49 @@ oscar_status oscar_extend_attn(hipStream_t stream, const oscar_layout *layout,
                                void *out, oscar_dtype out_dtype, void *workspace,
                                size_t workspace_bytes, const oscar_launch_opts *opts);
 
+/*
+ * BF16 paged KV cache: the baseline that the OSCAR announcement's "Results"
+ * section measures its decode speed-up and batch-32 throughput against.  The
+ * same page_size-1 slots hold every token's K and V in BF16, unrotated:
+ *   kv_pool: [num_slots][Hkv][2][128] bf16 bits (K then V of each KV head),
+ *            oscar_bf16_pool_bytes(layout) bytes, caller-owned.
+ * Only head_dim, num_kv_heads, num_q_heads, num_slots and max_requests of the
+ * layout matter here (it must still pass oscar_layout_check).
+ */
+size_t oscar_bf16_pool_bytes(const oscar_layout *layout);   /* 0 if the layout is invalid */
+
+/*
+ * oscar_bf16_append: kv_pool[slots[i]][h][0] = bf16_rn(k[i][h]),
+ * kv_pool[slots[i]][h][1] = bf16_rn(v[i][h]) for every token i and KV head h.
+ * k, v: [n_tokens][Hkv][128] of dtype (F32, BF16 or F16).  Slots outside
+ * [0, num_slots) are skipped.  n_tokens = 0 is a no-op.  Asynchronous on
+ * `stream`.
+ */
+oscar_status oscar_bf16_append(hipStream_t stream, const oscar_layout *layout, uint16_t *kv_pool,
+                               const void *k, const void *v, oscar_dtype dtype, int32_t n_tokens,
+                               const int32_t *slots);
+
+/* Workspace bytes oscar_bf16_decode_attn needs for these lengths.  opts may be NULL. */
+oscar_status oscar_bf16_decode_workspace_size(const oscar_layout *layout, int32_t batch,
+                                              const int32_t *seq_lens_host,
+                                              const oscar_launch_opts *opts, size_t *bytes);
+
+/*
+ * oscar_bf16_decode_attn: o[b][h] = softmax(sm_scale q[b][h] K^T) V over the
+ * positions [0, L_b) of request req_ids[b], K and V rows read from the slots
+ * req_to_slot[req][p] (tokens with a slot outside [0, num_slots) are left
+ * out), query head h reading KV head h / g.  No rotation.  Arguments as for
+ * oscar_decode_attn; history_chunk in opts sets the positions per work item
+ * (a multiple of 32).  Requires num_slots >= 1.
+ */
+oscar_status oscar_bf16_decode_attn(hipStream_t stream, const oscar_layout *layout,
+                                    const uint16_t *kv_pool, const void *q, oscar_dtype q_dtype,
+                                    int32_t batch, const int32_t *req_ids, const int32_t *seq_lens,
+                                    const int32_t *seq_lens_host, const int32_t *req_to_slot,
+                                    int64_t req_to_slot_stride, float sm_scale, void *out,
+                                    oscar_dtype out_dtype, void *workspace, size_t workspace_bytes,
+                                    const oscar_launch_opts *opts);
+
 /* Thread-local message of the last non-OK status of this thread. */
 const char *oscar_last_error(void);
 

@@ -31,7 +31,8 @@ OSCAR_ROT_EIG, OSCAR_ROT_HAD, OSCAR_ROT_PBR, OSCAR_ROT_OSCAR = 1, 2, 4, 7
 EXPORTED = (
     "oscar_layout_check", "oscar_pool_bytes", "oscar_build_rotation", "oscar_quant_append",
     "oscar_decode_workspace_size", "oscar_decode_attn", "oscar_decode_plan",
-    "oscar_extend_workspace_size", "oscar_extend_attn", "oscar_last_error", "oscar_version",
+    "oscar_extend_workspace_size", "oscar_extend_attn", "oscar_bf16_pool_bytes", "oscar_bf16_append",
+    "oscar_bf16_decode_workspace_size", "oscar_bf16_decode_attn", "oscar_last_error", "oscar_version",
 )
 
 
@@ -83,6 +84,11 @@ def _load() -> ctypes.CDLL:
         "oscar_extend_workspace_size": (I32, [LP, I32, I32, OP, ctypes.POINTER(SZ)]),
         "oscar_extend_attn": (I32, [P, LP, PP, P, I32, P, P, I32, I32, I32, I32, P, I64, P, P, F32,
                                     P, I32, P, SZ, OP]),
+        "oscar_bf16_pool_bytes": (SZ, [LP]),
+        "oscar_bf16_append": (I32, [P, LP, P, P, P, I32, I32, P]),
+        "oscar_bf16_decode_workspace_size": (I32, [LP, I32, P, OP, ctypes.POINTER(SZ)]),
+        "oscar_bf16_decode_attn": (I32, [P, LP, P, P, I32, I32, P, P, P, P, I64, F32, P, I32, P, SZ,
+                                         OP]),
         "oscar_last_error": (ctypes.c_char_p, []),
         "oscar_version": (ctypes.c_char_p, []),
     }
@@ -263,3 +269,44 @@ def oscar_extend_attn(layout: Layout, pool: Pool, q, k_new, v_new, req_id: int, 
         _ptr(req_to_slot), int(req_to_slot.shape[-1]), _ptr(R_K), _ptr(R_V), float(sm_scale),
         _ptr(out), _dtype_code(out), _ptr(workspace), int(workspace.numel() * workspace.element_size()),
         _opts(kernel_begin, kernel_end, history_chunk)))
+
+
+def oscar_bf16_pool_bytes(layout: Layout) -> int:
+    return int(_lib.oscar_bf16_pool_bytes(ctypes.byref(layout.c())))
+
+
+def new_bf16_pool(layout: Layout, device="cuda"):
+    """Device BF16 pool [num_slots][Hkv][2][head_dim] (int16 storage of bf16 bits)."""
+    import torch
+    n = oscar_bf16_pool_bytes(layout)
+    if n == 0:
+        raise OscarError(OSCAR_ERR_INVALID_ARG, oscar_last_error())
+    return torch.zeros(n // 2, dtype=torch.int16, device=device)
+
+
+def oscar_bf16_append(layout: Layout, kv_pool, k, v, slots, stream=None) -> None:
+    _dev(kv_pool, k, v, slots)
+    if k.dtype != v.dtype:
+        raise TypeError("k and v must share a dtype")
+    _check(_lib.oscar_bf16_append(_stream(stream), ctypes.byref(layout.c()), _ptr(kv_pool), _ptr(k),
+                                  _ptr(v), _dtype_code(k), int(k.shape[0]), _ptr(slots)))
+
+
+def oscar_bf16_decode_workspace_size(layout: Layout, seq_lens_host, history_chunk: int = 0) -> int:
+    lens = np.ascontiguousarray(seq_lens_host, dtype=np.int32)
+    out = ctypes.c_size_t(0)
+    _check(_lib.oscar_bf16_decode_workspace_size(ctypes.byref(layout.c()), len(lens), lens.ctypes.data,
+                                                 _opts(history_chunk=history_chunk), ctypes.byref(out)))
+    return int(out.value)
+
+
+def oscar_bf16_decode_attn(layout: Layout, kv_pool, q, req_ids, seq_lens, seq_lens_host, req_to_slot,
+                           sm_scale: float, out, workspace, stream=None, kernel_begin=None,
+                           kernel_end=None, history_chunk: int = 0) -> None:
+    _dev(kv_pool, q, req_ids, seq_lens, req_to_slot, out, workspace)
+    lens = np.ascontiguousarray(seq_lens_host, dtype=np.int32)
+    _check(_lib.oscar_bf16_decode_attn(
+        _stream(stream), ctypes.byref(layout.c()), _ptr(kv_pool), _ptr(q), _dtype_code(q), int(q.shape[0]),
+        _ptr(req_ids), _ptr(seq_lens), lens.ctypes.data, _ptr(req_to_slot), int(req_to_slot.shape[-1]),
+        float(sm_scale), _ptr(out), _dtype_code(out), _ptr(workspace),
+        int(workspace.numel() * workspace.element_size()), _opts(kernel_begin, kernel_end, history_chunk)))

@@ -24,7 +24,7 @@ FAKE = ctypes.c_void_p(0x1000)     # never dereferenced: validation fails first
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(oscar_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(oscar_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_every_declared_symbol_is_exported():
@@ -300,3 +300,58 @@ def test_extend_workspace_size():
         B.oscar_extend_workspace_size(lay, 0, 10)
     with pytest.raises(B.OscarError):
         B.oscar_extend_workspace_size(lay, 4, -1)
+
+
+def _bf16_decode(lay, lens, **over):
+    lens = np.asarray(lens, np.int32)
+    args = dict(stream=None, layout=ctypes.byref(lay.c()), kv=FAKE, q=FAKE, qd=B.OSCAR_BF16,
+                batch=len(lens), req=FAKE, lens=FAKE, lens_host=lens.ctypes.data, r2s=FAKE,
+                stride=int(lens.max()), sm=0.088, out=FAKE, od=B.OSCAR_F32,
+                ws=ctypes.c_void_p(0x100000), ws_bytes=1 << 40, opts=None)
+    args.update(over)
+    return B._lib.oscar_bf16_decode_attn(*args.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(kv=None), B.OSCAR_ERR_INVALID_ARG),
+    (dict(q=None), B.OSCAR_ERR_INVALID_ARG),
+    (dict(out=None), B.OSCAR_ERR_INVALID_ARG),
+    (dict(qd=5), B.OSCAR_ERR_INVALID_ARG),
+    (dict(od=5), B.OSCAR_ERR_INVALID_ARG),
+    (dict(sm=float("inf")), B.OSCAR_ERR_INVALID_ARG),
+    (dict(batch=0), B.OSCAR_ERR_INVALID_ARG),
+    (dict(stride=10), B.OSCAR_ERR_INVALID_ARG),
+    (dict(ws_bytes=100), B.OSCAR_ERR_WORKSPACE),
+    (dict(ws=ctypes.c_void_p(0x100008)), B.OSCAR_ERR_INVALID_ARG),
+])
+def test_bf16_decode_rejects_before_launch(over, status):
+    assert _bf16_decode(L(), [1000, 50000], **over) == status
+
+
+def test_bf16_decode_rejects_empty_pool_and_sequence():
+    assert _bf16_decode(L(num_slots=0), [10]) == B.OSCAR_ERR_INVALID_ARG
+    assert _bf16_decode(L(), [10, 0]) == B.OSCAR_ERR_INVALID_ARG
+
+
+def test_bf16_pool_bytes_and_workspace():
+    lay = L()
+    assert B.oscar_bf16_pool_bytes(lay) == 1000 * 8 * 2 * 128 * 2
+    assert B.oscar_bf16_pool_bytes(L(head_dim=64)) == 0
+    lens = [100000] * 32
+    ws = B.oscar_bf16_decode_workspace_size(lay, lens)
+    chunk = -(-(-(-32 * 100000 // 1024)) // 32) * 32
+    items = -(-100000 // chunk)
+    need = 32 * items * 32 * 128 * 4 + 32 * items * 32 * 2 * 4
+    assert need <= ws <= need + 2 * 256
+    assert B.oscar_bf16_decode_workspace_size(lay, [300], history_chunk=64) >= 5 * 32 * 130 * 4
+    with pytest.raises(B.OscarError):
+        B.oscar_bf16_decode_workspace_size(lay, [300], history_chunk=40)
+
+
+def test_bf16_append_validation():
+    lay = L()
+    f = B._lib.oscar_bf16_append
+    assert f(None, ctypes.byref(lay.c()), None, None, None, B.OSCAR_BF16, 0, None) == B.OSCAR_OK
+    assert f(None, ctypes.byref(lay.c()), FAKE, FAKE, FAKE, B.OSCAR_BF16, -1, FAKE) == B.OSCAR_ERR_INVALID_ARG
+    assert f(None, ctypes.byref(lay.c()), None, FAKE, FAKE, B.OSCAR_BF16, 4, FAKE) == B.OSCAR_ERR_INVALID_ARG
+    assert f(None, ctypes.byref(lay.c()), FAKE, FAKE, FAKE, 3, 4, FAKE) == B.OSCAR_ERR_INVALID_ARG

@@ -50,6 +50,10 @@ BF16_BYTES_PER_TOKEN_HEAD = 512        # K and V, 128 bf16 each
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "partial_kernel_decode_b32_hbm_bytes.md")
 KERNEL_SOURCES = ("rotated_int2_kv_amd/csrc/decode_attn.hip", "rotated_int2_kv_amd/csrc/common.cuh",
                   "rotated_int2_kv_amd/csrc/internal.h", "rotated_int2_kv_amd/build.py")
+# the same for the BF16 baseline's split-K kernel
+BF16_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bf16_partial_kernel_decode_b32_hbm_bytes.md")
+BF16_KERNEL_SOURCES = ("rotated_int2_kv_amd/csrc/bf16_decode.hip", "rotated_int2_kv_amd/csrc/common.cuh",
+                       "rotated_int2_kv_amd/csrc/internal.h", "rotated_int2_kv_amd/build.py")
 CPU_BASELINE_SECONDS = 10.0
 
 
@@ -57,25 +61,25 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
-    """sha256 over the sources and build flags the split-K kernel is compiled from."""
+def kernel_source_hash(sources=KERNEL_SOURCES):
+    """sha256 over the sources and build flags a split-K kernel is compiled from."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic():
+def measured_traffic(path=TRAFFIC_FILE, sources=KERNEL_SOURCES):
     """HBM bytes per launch from the committed counter summary, or None if the
     kernel has changed since the counters were taken."""
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(path).read()
     except OSError:
         return None
     sha = re.search(r"^source_sha256:\s*([0-9a-f]{64})", text, re.M)
     val = re.search(r"^traffic_bytes_per_launch:\s*([0-9]+)", text, re.M)
-    if not sha or not val or sha.group(1) != kernel_source_hash():
+    if not sha or not val or sha.group(1) != kernel_source_hash(sources):
         return None
     return int(val.group(1))
 
@@ -279,6 +283,7 @@ def run_bf16(args, torch, B, workloads):
     return dict(workload=w.name, steps=steps, ms_per_step=ms, kernel_ms=kern_ms,
                 kv_tokens_per_s=int(lens.sum()) / (ms * 1e-3), algorithmic_bytes=kbytes,
                 gb_per_s=kbytes / (kern_ms * 1e-3) / 1e9, frac_hbm=kbytes / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                traffic=measured_traffic(BF16_TRAFFIC_FILE, BF16_KERNEL_SOURCES),
                 output_finite=bool(torch.isfinite(out.float()).all().item()))
 
 
@@ -383,6 +388,8 @@ def main():
     ap.add_argument("--no-append", action="store_true")
     ap.add_argument("--no-extend", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--only-extend", action="store_true",
+                    help="run only the extend call (prints its own JSON object; for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -404,6 +411,11 @@ def main():
         torch.cuda.synchronize()
         log("[bench] calibration copy: 1 GiB read + 1 GiB written")
         del src, dst
+    if args.only_extend:
+        ext = run_extend(args, torch, B, workloads)
+        log(f"[bench] extend {ext['ms']:.2f} ms, kernel {ext['kernel_ms']:.2f} ms")
+        print(json.dumps({"extend": ext}))
+        return
     d = run_decode(args, torch, B, workloads)
     w = d["w"]
     ms = d["ms"]

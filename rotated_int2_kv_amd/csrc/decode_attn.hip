@@ -16,11 +16,12 @@
 //               with m in log2 units.
 //   3. merge:   log-sum-exp merge of the items and o = o' R_V^T.
 //
-// oscar_extend_attn runs the same kernels for the new tokens of one request:
-// every new token is a row of the batch that reads the request's cached
-// prefix as it is stored at the prefix length, plus one more work item per
-// row: the new tokens up to and including its own, as BF16 rotated keys and
-// values (rotated here by extend_rotate_kernel).
+// oscar_extend_attn treats the new tokens of one request as rows that read
+// the request's cached prefix as stored at the prefix length, plus one more
+// work item per row: the new tokens up to and including its own, as BF16
+// rotated keys and values (rotated here by extend_rotate_kernel).  It shares
+// the query rotation and the merge; its work items run on the matrix-core
+// kernels of extend_hist.hip, which take many rows per loaded tile.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
@@ -757,7 +758,6 @@ __device__ __forceinline__ void bf16_item(const DecodeArgs &a, int b, int req, i
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const bool is_sink = (j == 0);
-    const bool is_new = (j == a.extra_item);
     float m_run[kMaxGroup], l_lane[kMaxGroup], o0[kMaxGroup], o1[kMaxGroup];
 #pragma unroll
     for (int h = 0; h < kMaxGroup; ++h) {
@@ -767,7 +767,6 @@ __device__ __forceinline__ void bf16_item(const DecodeArgs &a, int b, int req, i
         o1[h] = 0.0f;
     }
     auto row_ptr = [&](int pos, int t) -> const uint16_t * {
-        if (is_new) return a.newkv + (size_t(pos) * a.hkv + hk) * 2 * kHeadDim + t * kHeadDim;
         if (is_sink)
             return a.sink + ((size_t(req) * a.sink_tokens + pos) * a.hkv + hk) * 2 * kHeadDim + t * kHeadDim;
         return a.recent + ((size_t(req) * a.recent_tokens + pos % a.recent_tokens) * a.hkv + hk) * 2 * kHeadDim +
@@ -885,17 +884,12 @@ __global__ __launch_bounds__(64 * kPartialWaves) void partial_kernel(DecodeArgs 
     int req = 0;
     const int L = request_length(a, b, req);
     int p0, p1;
-    if (j == a.extra_item) {                    // extend: new tokens 0 .. b
-        p0 = 0;
-        p1 = b + 1;
-    } else {
-        item_range(a, L, j, p0, p1);
-    }
+    item_range(a, L, j, p0, p1);
     if (p0 >= p1) return;                       // uniform over the workgroup
     const int w = threadIdx.x >> 6;
     const int hk = hc * kPartialWaves + w;
     const bool active = hk < a.hkv;
-    if (j < 2 || j == a.extra_item) {
+    if (j < 2) {
         float *pbuf = reinterpret_cast<float *>(smem) + w * kBf16WaveFloats;
         bf16_item(a, b, req, j, active ? hk : 0, p0, p1, active, pbuf);
     } else if (a.num_slots > 0) {
@@ -1132,7 +1126,7 @@ DecodeArgs make_args(const oscar_layout *layout, const oscar_pool *pool, const v
 
 // prep, split-K partials and merge on `stream`
 oscar_status launch_decode(const DecodeArgs &a, const DecodePlan &plan, hipStream_t stream,
-                           const oscar_launch_opts *opts) {
+                           const oscar_launch_opts *opts, const ExtendHistArgs *xh = nullptr) {
     if (int64_t(plan.items) * a.batch * a.head_chunks > INT32_MAX)
         return fail(OSCAR_ERR_UNSUPPORTED, "batch x work items exceeds one launch grid");
     hipLaunchKernelGGL(prep_kernel, dim3(a.batch * a.hkv), dim3(512), 0, stream, a);
@@ -1142,17 +1136,28 @@ oscar_status launch_decode(const DecodeArgs &a, const DecodePlan &plan, hipStrea
     if (opts && opts->kernel_begin && hipEventRecord(opts->kernel_begin, stream) != hipSuccess)
         return fail(OSCAR_ERR_HIP, "hipEventRecord failed");
     const int blocks = plan.items * a.batch * a.head_chunks;
-    switch (a.g) {
-        case 1: e = launch_partial<1>(a, blocks, stream); break;
-        case 2: e = launch_partial<2>(a, blocks, stream); break;
-        case 3: e = launch_partial<3>(a, blocks, stream); break;
-        case 4: e = launch_partial<4>(a, blocks, stream); break;
-        case 5: e = launch_partial<5>(a, blocks, stream); break;
-        case 6: e = launch_partial<6>(a, blocks, stream); break;
-        case 7: e = launch_partial<7>(a, blocks, stream); break;
-        default: e = launch_partial<8>(a, blocks, stream); break;
+    if (xh) {
+        // extend: every work item on the matrix cores, a block of new tokens per workgroup
+        if (xh->hist_items > 0 && xh->num_slots > 0) {
+            e = launch_extend_history(*xh, stream);
+            if (e != hipSuccess)
+                return fail(OSCAR_ERR_HIP, std::string("extend history launch: ") + hipGetErrorString(e));
+        }
+        e = launch_extend_bf16(*xh, stream);
+        if (e != hipSuccess) return fail(OSCAR_ERR_HIP, std::string("extend bf16 launch: ") + hipGetErrorString(e));
+    } else {
+        switch (a.g) {
+            case 1: e = launch_partial<1>(a, blocks, stream); break;
+            case 2: e = launch_partial<2>(a, blocks, stream); break;
+            case 3: e = launch_partial<3>(a, blocks, stream); break;
+            case 4: e = launch_partial<4>(a, blocks, stream); break;
+            case 5: e = launch_partial<5>(a, blocks, stream); break;
+            case 6: e = launch_partial<6>(a, blocks, stream); break;
+            case 7: e = launch_partial<7>(a, blocks, stream); break;
+            default: e = launch_partial<8>(a, blocks, stream); break;
+        }
+        if (e != hipSuccess) return fail(OSCAR_ERR_HIP, std::string("partial launch: ") + hipGetErrorString(e));
     }
-    if (e != hipSuccess) return fail(OSCAR_ERR_HIP, std::string("partial launch: ") + hipGetErrorString(e));
     if (opts && opts->kernel_end && hipEventRecord(opts->kernel_end, stream) != hipSuccess)
         return fail(OSCAR_ERR_HIP, "hipEventRecord failed");
 
@@ -1221,6 +1226,36 @@ extern "C" oscar_status oscar_extend_attn(hipStream_t stream, const oscar_layout
     a.fixed_req = req_id;
     a.fixed_len = prefix_len;
 
+    // history items on the matrix cores, 64 / g new tokens per workgroup
+    ExtendHistArgs xh;
+    xh.records = pool->records;
+    xh.slot_row = req_to_slot + size_t(req_id) * req_to_slot_stride;
+    xh.zero_rec = a.zero_rec;
+    xh.qrot = a.qrot;
+    xh.qsum = a.qsum;
+    xh.part_o = a.part_o;
+    xh.part_ml = a.part_ml;
+    xh.num_slots = layout->num_slots;
+    xh.hkv = a.hkv;
+    xh.hq = a.hq;
+    xh.g = a.g;
+    xh.items = a.items;
+    xh.chunk = a.chunk;
+    xh.sink = a.sink_tokens;
+    xh.recent = a.recent_tokens;
+    xh.prefix_len = prefix_len;
+    xh.n_new = n_new;
+    xh.tok_per_block = 64 / a.g;
+    xh.row_blocks = (n_new + xh.tok_per_block - 1) / xh.tok_per_block;
+    xh.hist_items = plan.extra_item - 2;
+    xh.sink_store = pool->sink;
+    xh.recent_store = pool->recent;
+    xh.newkv = a.newkv;
+    xh.req = req_id;
+    xh.extra_item = plan.extra_item;
+    if (extend_history_blocks(xh) > INT32_MAX || extend_bf16_blocks(xh) > INT32_MAX)
+        return fail(OSCAR_ERR_UNSUPPORTED, "new tokens x work items exceeds one launch grid");
+
     RotateArgs r;
     r.k = k_new;
     r.v = v_new;
@@ -1233,5 +1268,5 @@ extern "C" oscar_status oscar_extend_attn(hipStream_t stream, const oscar_layout
                        stream, r);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(OSCAR_ERR_HIP, std::string("rotate launch: ") + hipGetErrorString(e));
-    return launch_decode(a, plan, stream, opts);
+    return launch_decode(a, plan, stream, opts, &xh);
 }

@@ -1,0 +1,487 @@
+// History part of an extend call: many new tokens against the INT2 prefix on
+// the matrix cores.
+//
+// The decode kernel's history path is shaped for one query row per KV head
+// and reads every history tile once per row; a prefill chunk has thousands of
+// rows over the same prefix.  Here one workgroup takes 64 query rows of one
+// KV head (64 / g new tokens x g heads) and one history work item, and for
+// every 32-token tile of the item:
+//   1. the tile's 96-byte head records (K, V codes and (s, z)) are staged in
+//      LDS; records of the next tile are in flight meanwhile;
+//   2. the workgroup dequantises the tile once: x = s c + z, scaled by 1/8
+//      (exact) so that any fp16 (s, z) stays inside the fp16 range, split into
+//      fp16 hi + lo.  K goes to a token-major tile, V to a channel-major
+//      (transposed) tile;
+//   3. each wave (16 rows) runs flash attention on v_mfma_f32_16x16x32_f16:
+//      S^T = K q'^T with hi.hi + hi.lo + lo.hi products (about 22 bits of
+//      each operand), online softmax in log2 units on the 16-row state, and
+//      O += P V with P taken straight from the S^T output registers (their
+//      token order is the k-slot order of the PV product, and the V fragments
+//      are read in that order), again with three products.
+// Partials (m, l, o) go to the decode layout, where the merge combines them
+// with the BF16 windows' and the new tokens' items.
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+#include <cmath>
+
+#include "common.cuh"
+#include "internal.h"
+
+namespace oscar {
+namespace {
+
+constexpr int kTile = 32;                    // history tokens per tile
+constexpr int kKdStride = kHeadDim + 8;      // halves per K row (272 bytes: conflict-free 16-byte reads)
+constexpr int kVtStride = kTile + 4;         // halves per V^T row (72 bytes: conflict-free 8-byte reads)
+constexpr float kDqScale = 0.125f;           // dequantised values are stored times 1/8
+
+__device__ __forceinline__ uint32_t pk_f16(float x0, float x1) {
+    const f16x2 h = {static_cast<_Float16>(x0), static_cast<_Float16>(x1)};
+    return __builtin_bit_cast(uint32_t, h);
+}
+__device__ __forceinline__ float f16_lo(uint32_t w) { return __half2float(__ushort_as_half(uint16_t(w))); }
+__device__ __forceinline__ float f16_hi(uint32_t w) { return __half2float(__ushort_as_half(uint16_t(w >> 16))); }
+
+// (x0, x1) ~ hi + lo, both fp16 pairs rounded to nearest
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t &hi, uint32_t &lo) {
+    hi = pk_f16(x0, x1);
+    lo = pk_f16(x0 - f16_lo(hi), x1 - f16_hi(hi));
+}
+
+__device__ __forceinline__ float sz_s(uint32_t w) { return f16_lo(w); }
+__device__ __forceinline__ float sz_z(uint32_t w) { return f16_hi(w); }
+
+// The wave's 16 query rows: row rho = 16 w + col is new token
+// rb * tok_per_block + rho / g, query head hk * g + rho % g.  Lane (col, kq)
+// holds that row's q' (times 2^K) as the B operand of S^T = K q'^T: k-slots
+// = channels 32 s + 8 kq .. + 7, split into fp16 hi + lo.
+struct Rows {
+    f16x8 bq_hi[4], bq_lo[4];
+    float unscale;      // logit (log2 units) = S^T element x unscale
+    int tok;
+    bool row_ok;
+};
+
+__device__ __forceinline__ void load_rows(const ExtendHistArgs &a, int rb, int hk, int w, int col, int kq, Rows &r) {
+    const int rho = 16 * w + col;
+    const int tl = rho / a.g;
+    const int head = rho - tl * a.g;
+    r.tok = rb * a.tok_per_block + tl;
+    r.row_ok = tl < a.tok_per_block && r.tok < a.n_new;
+    const size_t qrow = size_t(r.row_ok ? r.tok : 0) * a.hq + size_t(hk) * a.g + head;
+    float qscale = 0.0f;
+    r.unscale = 0.0f;
+    if (r.row_ok) {
+        qscale = a.qsum[qrow * 8 + 4];                      // 2^K: max |q'| 2^K < 2^15
+        r.unscale = a.qsum[qrow * 8 + 5] * (1.0f / (16777216.0f * kDqScale));   // 2^-K x 8
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float x0 = 0.0f, x1 = 0.0f;
+            if (r.row_ok) {
+                const float2 q2 = *reinterpret_cast<const float2 *>(a.qrot + qrow * kHeadDim + 32 * s + 8 * kq + 2 * e);
+                x0 = q2.x * qscale;
+                x1 = q2.y * qscale;
+            }
+            split2(x0, x1, h[e], l[e]);
+        }
+        r.bq_hi[s] = __builtin_bit_cast(f16x8, u32x4{h[0], h[1], h[2], h[3]});
+        r.bq_lo[s] = __builtin_bit_cast(f16x8, u32x4{l[0], l[1], l[2], l[3]});
+    }
+}
+
+// Partials of work item j: (m, l) of row 16 w + col from the lanes of kq 0;
+// o rows 16 w + 4 kq + i, channels 16 n + col (stored times 8, undoing the
+// 1/8 of the V tile).
+__device__ __forceinline__ void store_partials(const ExtendHistArgs &a, int rb, int hk, int j, int w, int col, int kq,
+                                               const Rows &r, float m_run, float l_run, const f32x4 *o) {
+    if (kq == 0 && r.row_ok) {
+        const int rho = 16 * w + col;
+        const int head = rho - (rho / a.g) * a.g;
+        float *ml = a.part_ml + ((size_t(r.tok) * a.items + j) * a.hq + size_t(hk) * a.g + head) * 2;
+        ml[0] = m_run;
+        ml[1] = l_run;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int rr = 16 * w + 4 * kq + i;
+        const int tli = rr / a.g;
+        const int hi = rr - tli * a.g;
+        const int toki = rb * a.tok_per_block + tli;
+        if (tli < a.tok_per_block && toki < a.n_new) {
+            float *dst = a.part_o + ((size_t(toki) * a.items + j) * a.hq + size_t(hk) * a.g + hi) * kHeadDim;
+#pragma unroll
+            for (int n = 0; n < 8; ++n) dst[16 * n + col] = o[n][i] * (1.0f / kDqScale);
+        }
+    }
+}
+
+// One 32-token tile of flash attention for the wave's 16 query rows.
+// kd: K tile [hi, lo][token][channel]; vt: V tile [hi, lo][channel][token]
+// (fp16, times 1/8).  S^T = K q'^T leaves lane (col, kq) with tokens
+// 16 u + 4 kq + i of row col; bit 4 u + i of `valid` keeps that token.  With
+// kLo false the lo tiles are zero (BF16 sources are exact in fp16) and their
+// products are skipped.
+template <bool kLo>
+__device__ __forceinline__ void flash_step(const _Float16 (*kd)[kTile][kKdStride],
+                                           const _Float16 (*vt)[kHeadDim][kVtStride], const f16x8 *bq_hi,
+                                           const f16x8 *bq_lo, float unscale, uint32_t valid, float &m_run,
+                                           float &l_run, f32x4 *o, int col, int kq) {
+    f32x4 d[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const f16x8 kh = *reinterpret_cast<const f16x8 *>(&kd[0][16 * u + col][32 * s + 8 * kq]);
+            acc = mfma_f16(kh, bq_hi[s], acc);
+            acc = mfma_f16(kh, bq_lo[s], acc);
+            if constexpr (kLo) {
+                const f16x8 kl = *reinterpret_cast<const f16x8 *>(&kd[1][16 * u + col][32 * s + 8 * kq]);
+                acc = mfma_f16(kl, bq_hi[s], acc);
+            }
+        }
+        d[u] = acc;
+    }
+    float x[2][4];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[u][i] = ((valid >> (4 * u + i)) & 1u) ? d[u][i] * unscale : -INFINITY;
+            mt = fmaxf(mt, x[u][i]);
+        }
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float p[2][4];
+    float lsum = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[u][i] = x[u][i] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x[u][i] - m_new);
+            lsum += p[u][i];
+        }
+    }
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    l_run = fmaf(l_run, alpha, lsum);
+
+    // O += P V: A = P (row col, k-slot 4 u + i = token 16 u + 4 kq + i)
+    uint32_t ph[4], pl[4];
+    split2(p[0][0], p[0][1], ph[0], pl[0]);
+    split2(p[0][2], p[0][3], ph[1], pl[1]);
+    split2(p[1][0], p[1][1], ph[2], pl[2]);
+    split2(p[1][2], p[1][3], ph[3], pl[3]);
+    const f16x8 a_hi = __builtin_bit_cast(f16x8, u32x4{ph[0], ph[1], ph[2], ph[3]});
+    const f16x8 a_lo = __builtin_bit_cast(f16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
+    float al[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * kq + i);    // alpha of output row 4 kq + i
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+        const int ch = 16 * n + col;
+        const u32x2 v0h = *reinterpret_cast<const u32x2 *>(&vt[0][ch][4 * kq]);
+        const u32x2 v1h = *reinterpret_cast<const u32x2 *>(&vt[0][ch][16 + 4 * kq]);
+        const f16x8 vh = __builtin_bit_cast(f16x8, u32x4{v0h[0], v0h[1], v1h[0], v1h[1]});
+        f32x4 acc = o[n];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] *= al[i];
+        acc = mfma_f16(a_hi, vh, acc);
+        acc = mfma_f16(a_lo, vh, acc);
+        if constexpr (kLo) {
+            const u32x2 v0l = *reinterpret_cast<const u32x2 *>(&vt[1][ch][4 * kq]);
+            const u32x2 v1l = *reinterpret_cast<const u32x2 *>(&vt[1][ch][16 + 4 * kq]);
+            const f16x8 vl = __builtin_bit_cast(f16x8, u32x4{v0l[0], v0l[1], v1l[0], v1l[1]});
+            acc = mfma_f16(a_hi, vl, acc);
+        }
+        o[n] = acc;
+    }
+}
+
+__global__ __launch_bounds__(256) void extend_hist_kernel(ExtendHistArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t raw[kTile * kHeadRecord];
+    __shared__ __attribute__((aligned(16))) uint8_t flag[kTile];
+    __shared__ __attribute__((aligned(16))) _Float16 kd[2][kTile][kKdStride];
+    __shared__ __attribute__((aligned(16))) _Float16 vt[2][kHeadDim][kVtStride];
+
+    const int id = blockIdx.x;
+    const int rb = id % a.row_blocks;
+    const int rest = id / a.row_blocks;
+    const int hk = rest % a.hkv;
+    const int jj = rest / a.hkv;
+    const int j = 2 + jj;                                   // work item index in the decode layout
+    const int hist_end = max(a.sink, a.prefix_len - a.recent);
+    const int p0 = a.sink + jj * a.chunk;
+    const int p1 = min(p0 + a.chunk, hist_end);
+    if (p0 >= p1) return;                                   // uniform over the workgroup
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int lane = tid & 63;
+    const int col = lane & 15;
+    const int kq = lane >> 4;
+
+    Rows r;
+    load_rows(a, rb, hk, w, col, kq, r);
+    float m_run = -INFINITY, l_run = 0.0f;
+    f32x4 o[8];
+#pragma unroll
+    for (int n = 0; n < 8; ++n) o[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // ---- producers: thread < 192 stages 16 bytes (unit pu) of token pt's head record
+    const bool producer = tid < kTile * 6;
+    const int pt = tid / 6;
+    const int pu = tid - 6 * pt;
+    const size_t rec_bytes = size_t(a.hkv) * kHeadRecord;
+    auto slot_of = [&](int c) -> int {
+        const int p = c + pt;
+        return (producer && p < p1) ? __builtin_nontemporal_load(a.slot_row + p) : -1;
+    };
+    auto usable = [&](int slot) { return slot >= 0 && slot < a.num_slots; };
+    auto load_rec = [&](int slot) -> u32x4 {
+        const uint8_t *base = usable(slot) ? a.records + size_t(slot) * rec_bytes + size_t(hk) * kHeadRecord
+                                           : a.zero_rec;
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(base + 16 * pu));
+    };
+    int slot_cur = slot_of(p0);
+    u32x4 rec = producer ? load_rec(slot_cur) : u32x4{0u, 0u, 0u, 0u};
+    bool ok_cur = usable(slot_cur);
+    int slot_nxt = slot_of(p0 + kTile);
+
+    for (int cb = p0; cb < p1; cb += kTile) {
+        // ---- 1. stage this tile; next tile's records and the slot ids after it in flight
+        if (producer) {
+            *reinterpret_cast<u32x4 *>(raw + pt * kHeadRecord + 16 * pu) = rec;
+            if (pu == 0) flag[pt] = ok_cur ? 1 : 0;
+        }
+        if (cb + kTile < p1) {
+            if (producer) rec = load_rec(slot_nxt);
+            ok_cur = usable(slot_nxt);
+            slot_nxt = slot_of(cb + 2 * kTile);
+        }
+        __syncthreads();
+
+        // ---- 2. dequantise: K rows (token t, channels 16 part .. +15)
+        {
+            const int t = tid >> 3, part = tid & 7;
+            const uint32_t cw = *reinterpret_cast<const uint32_t *>(raw + t * kHeadRecord + 4 * part);
+            const uint32_t szw = *reinterpret_cast<const uint32_t *>(raw + t * kHeadRecord + 64 + 4 * (part >> 1));
+            const float s = sz_s(szw) * kDqScale, z = sz_z(szw) * kDqScale;     // exact
+            uint32_t hi[8], lo[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x0 = fmaf(s, float((cw >> (4 * e)) & 3u), z);
+                const float x1 = fmaf(s, float((cw >> (4 * e + 2)) & 3u), z);
+                split2(x0, x1, hi[e], lo[e]);
+            }
+            u32x4 *dh = reinterpret_cast<u32x4 *>(&kd[0][t][16 * part]);
+            u32x4 *dl = reinterpret_cast<u32x4 *>(&kd[1][t][16 * part]);
+            dh[0] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+            dh[1] = u32x4{hi[4], hi[5], hi[6], hi[7]};
+            dl[0] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+            dl[1] = u32x4{lo[4], lo[5], lo[6], lo[7]};
+        }
+        // V^T rows (channels 2 cp, 2 cp + 1; tokens 8 tg .. 8 tg + 7)
+        {
+            const int cp = tid & 63, tg = tid >> 6;
+            const int byte = 32 + (cp >> 1), sh = 4 * (cp & 1), sz_off = 80 + 4 * (cp >> 4);
+            uint32_t h0[4], l0[4], h1[4], l1[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float x0[2], x1[2];
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const int t = 8 * tg + 2 * e + k;
+                    const uint32_t c = raw[t * kHeadRecord + byte] >> sh;
+                    const uint32_t szw = *reinterpret_cast<const uint32_t *>(raw + t * kHeadRecord + sz_off);
+                    const float s = sz_s(szw) * kDqScale, z = sz_z(szw) * kDqScale;
+                    x0[k] = fmaf(s, float(c & 3u), z);
+                    x1[k] = fmaf(s, float((c >> 2) & 3u), z);
+                }
+                split2(x0[0], x0[1], h0[e], l0[e]);
+                split2(x1[0], x1[1], h1[e], l1[e]);
+            }
+            u32x2 *r0h = reinterpret_cast<u32x2 *>(&vt[0][2 * cp][8 * tg]);
+            u32x2 *r0l = reinterpret_cast<u32x2 *>(&vt[1][2 * cp][8 * tg]);
+            u32x2 *r1h = reinterpret_cast<u32x2 *>(&vt[0][2 * cp + 1][8 * tg]);
+            u32x2 *r1l = reinterpret_cast<u32x2 *>(&vt[1][2 * cp + 1][8 * tg]);
+            r0h[0] = u32x2{h0[0], h0[1]};
+            r0h[1] = u32x2{h0[2], h0[3]};
+            r0l[0] = u32x2{l0[0], l0[1]};
+            r0l[1] = u32x2{l0[2], l0[3]};
+            r1h[0] = u32x2{h1[0], h1[1]};
+            r1h[1] = u32x2{h1[2], h1[3]};
+            r1l[0] = u32x2{l1[0], l1[1]};
+            r1l[1] = u32x2{l1[2], l1[3]};
+        }
+        // usable-token flags of the tile (read now: the next tile's staging
+        // overwrites them before every wave has finished this tile)
+        const uint32_t fl0 = *reinterpret_cast<const uint32_t *>(flag + 4 * kq);
+        const uint32_t fl1 = *reinterpret_cast<const uint32_t *>(flag + 16 + 4 * kq);
+        __syncthreads();
+
+        // ---- 3./4. flash step over the tile
+        uint32_t valid = 0;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 16 * u + 4 * kq + i;
+                const bool use = (((u ? fl1 : fl0) >> (8 * i)) & 1u) && cb + t < p1;
+                valid |= uint32_t(use) << (4 * u + i);
+            }
+        flash_step<true>(kd, vt, r.bq_hi, r.bq_lo, r.unscale, valid, m_run, l_run, o, col, kq);
+    }
+
+    store_partials(a, rb, hk, j, w, col, kq, r, m_run, l_run, o);
+}
+
+// BF16 items: kind 0 = sink window [0, min(S, P)), kind 1 = recent window
+// [max(S, P - W), P), kind 2 = the new tokens themselves, causal (row token
+// i sees new tokens 0..i).  Rows are exact in fp16 once scaled by 1/8 (bf16
+// has fewer mantissa bits), so there is no lo tile.  Each thread loads 32
+// bytes of a K row and 4 bytes of 8 V rows per tile, one tile ahead.
+__global__ __launch_bounds__(256) void extend_bf16_kernel(ExtendHistArgs a) {
+    __shared__ __attribute__((aligned(16))) _Float16 kd[1][kTile][kKdStride];
+    __shared__ __attribute__((aligned(16))) _Float16 vt[1][kHeadDim][kVtStride];
+
+    const int id = blockIdx.x;
+    const int rb = id % a.row_blocks;
+    const int rest = id / a.row_blocks;
+    const int hk = rest % a.hkv;
+    const int kind = rest / a.hkv;
+    const int P = a.prefix_len;
+    int p0, p1, j;
+    if (kind == 0) {
+        p0 = 0;
+        p1 = min(a.sink, P);
+        j = 0;
+    } else if (kind == 1) {
+        p0 = max(a.sink, P - a.recent);
+        p1 = P;
+        j = 1;
+    } else {
+        p0 = 0;
+        p1 = min(a.n_new, (rb + 1) * a.tok_per_block);
+        j = a.extra_item;
+    }
+    if (p0 >= p1) return;                                   // uniform over the workgroup
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int lane = tid & 63;
+    const int col = lane & 15;
+    const int kq = lane >> 4;
+    Rows r;
+    load_rows(a, rb, hk, w, col, kq, r);
+    float m_run = -INFINITY, l_run = 0.0f;
+    f32x4 o[8];
+#pragma unroll
+    for (int n = 0; n < 8; ++n) o[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    auto row_ptr = [&](int pos) -> const uint16_t * {
+        size_t row;
+        if (kind == 0)
+            row = (size_t(a.req) * a.sink + pos) * a.hkv + hk;
+        else if (kind == 1)
+            row = (size_t(a.req) * a.recent + pos % a.recent) * a.hkv + hk;
+        else
+            row = size_t(pos) * a.hkv + hk;
+        const uint16_t *base = kind == 0 ? a.sink_store : kind == 1 ? a.recent_store : a.newkv;
+        return base + row * (2 * kHeadDim);
+    };
+    // K: token kt, channels 16 kp .. +15; V: channels 2 cp, 2 cp + 1 of tokens 8 tg .. +7
+    const int kt = tid >> 3, kp = tid & 7;
+    const int cp = tid & 63, tg = tid >> 6;
+    u32x4 kreg[2];
+    uint32_t vreg[8];
+    auto load_tile = [&](int c) {
+        const int pk = c + kt;
+        if (pk < p1) {
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(row_ptr(pk) + 16 * kp);
+            kreg[0] = __builtin_nontemporal_load(src);
+            kreg[1] = __builtin_nontemporal_load(src + 1);
+        } else {
+            kreg[0] = kreg[1] = u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int pv = c + 8 * tg + k;
+            vreg[k] = pv < p1 ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(row_ptr(pv) + kHeadDim) + cp)
+                              : 0u;
+        }
+    };
+    auto bf = [](uint32_t u, int half) { return __uint_as_float(half ? (u & 0xFFFF0000u) : (u << 16)) * kDqScale; };
+    load_tile(p0);
+    for (int cb = p0; cb < p1; cb += kTile) {
+        __syncthreads();                                    // every wave is done with the previous tile
+        {
+            uint32_t hk4[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t u = kreg[e >> 2][e & 3];
+                hk4[e] = pk_f16(bf(u, 0), bf(u, 1));
+            }
+            u32x4 *dh = reinterpret_cast<u32x4 *>(&kd[0][kt][16 * kp]);
+            dh[0] = u32x4{hk4[0], hk4[1], hk4[2], hk4[3]};
+            dh[1] = u32x4{hk4[4], hk4[5], hk4[6], hk4[7]};
+            uint32_t h0[4], h1[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                h0[e] = pk_f16(bf(vreg[2 * e], 0), bf(vreg[2 * e + 1], 0));
+                h1[e] = pk_f16(bf(vreg[2 * e], 1), bf(vreg[2 * e + 1], 1));
+            }
+            u32x2 *r0 = reinterpret_cast<u32x2 *>(&vt[0][2 * cp][8 * tg]);
+            u32x2 *r1 = reinterpret_cast<u32x2 *>(&vt[0][2 * cp + 1][8 * tg]);
+            r0[0] = u32x2{h0[0], h0[1]};
+            r0[1] = u32x2{h0[2], h0[3]};
+            r1[0] = u32x2{h1[0], h1[1]};
+            r1[1] = u32x2{h1[2], h1[3]};
+        }
+        if (cb + kTile < p1) load_tile(cb + kTile);
+        __syncthreads();
+        uint32_t valid = 0;
+        const int lim = kind == 2 ? r.tok : INT32_MAX;      // causal: key position <= row token
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int pos = cb + 16 * u + 4 * kq + i;
+                valid |= uint32_t(pos < p1 && pos <= lim) << (4 * u + i);
+            }
+        flash_step<false>(kd, vt, r.bq_hi, r.bq_lo, r.unscale, valid, m_run, l_run, o, col, kq);
+    }
+    store_partials(a, rb, hk, j, w, col, kq, r, m_run, l_run, o);
+}
+
+}  // namespace
+
+int64_t extend_bf16_blocks(const ExtendHistArgs &a) { return int64_t(a.row_blocks) * 3 * a.hkv; }
+
+hipError_t launch_extend_bf16(const ExtendHistArgs &a, hipStream_t stream) {
+    hipLaunchKernelGGL(extend_bf16_kernel, dim3(unsigned(extend_bf16_blocks(a))), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+int64_t extend_history_blocks(const ExtendHistArgs &a) {
+    return int64_t(a.row_blocks) * a.hist_items * a.hkv;
+}
+
+hipError_t launch_extend_history(const ExtendHistArgs &a, hipStream_t stream) {
+    const int64_t blocks = extend_history_blocks(a);
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(extend_hist_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace oscar

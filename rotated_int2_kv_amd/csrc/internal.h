@@ -6,6 +6,8 @@
 #include <cstdint>
 #include <string>
 
+#include <hip/hip_runtime.h>
+
 #include "../../include/oscar.h"
 
 namespace oscar {
@@ -50,5 +52,44 @@ struct DecodePlan {
 oscar_status make_decode_plan(const oscar_layout &lay, int32_t batch,
                               const int32_t *seq_lens_host, const oscar_launch_opts *opts,
                               DecodePlan *plan, bool extend = false);
+
+// Extend attention on the matrix cores (extend_hist.hip): for every work
+// item (history chunks; sink, recent and new-token windows), a workgroup
+// takes a block of new tokens of one KV head and writes their split-K
+// partials in the decode layout (part_o [rows][items][Hq][128], part_ml
+// [rows][items][Hq][2]).
+struct ExtendHistArgs {
+    const uint8_t *records;
+    const int32_t *slot_row;      // req_to_slot row of the request
+    const uint8_t *zero_rec;      // 256 zero bytes (cleared before this kernel runs)
+    const float *qrot;            // [rows][Hq][128] log2-scaled rotated queries
+    const float *qsum;            // [rows][Hq][8]; [4] = 2^K, [5] = 2^(24-K)
+    float *part_o;
+    float *part_ml;
+    int64_t num_slots;
+    int32_t hkv;
+    int32_t hq;
+    int32_t g;
+    int32_t items;
+    int32_t chunk;
+    int32_t sink;
+    int32_t recent;
+    int32_t prefix_len;
+    int32_t n_new;
+    int32_t tok_per_block;        // new tokens per workgroup: 64 / g
+    int32_t row_blocks;
+    int32_t hist_items;
+    // BF16 items (sink window, recent window, the new tokens themselves)
+    const uint16_t *sink_store;   // [max_requests][S][Hkv][2][128]
+    const uint16_t *recent_store; // [max_requests][W][Hkv][2][128], row p mod W
+    const uint16_t *newkv;        // [n_new][Hkv][2][128] rotated new tokens
+    int32_t req;
+    int32_t extra_item;           // work item of the new tokens
+};
+// Grid sizes of the two launches (row_blocks x items x hkv).
+int64_t extend_history_blocks(const ExtendHistArgs &a);
+int64_t extend_bf16_blocks(const ExtendHistArgs &a);
+hipError_t launch_extend_history(const ExtendHistArgs &a, hipStream_t stream);
+hipError_t launch_extend_bf16(const ExtendHistArgs &a, hipStream_t stream);
 
 }  // namespace oscar

@@ -124,9 +124,12 @@ __device__ __forceinline__ void store_partials(const ExtendHistArgs &a, int rb, 
 // kd: K tile [hi, lo][token][channel]; vt: V tile [hi, lo][channel][token]
 // (fp16, times 1/8).  S^T = K q'^T leaves lane (col, kq) with tokens
 // 16 u + 4 kq + i of row col; bit 4 u + i of `valid` keeps that token.  With
-// kLo false the lo tiles are zero (BF16 sources are exact in fp16) and their
-// products are skipped.
-template <bool kLo>
+// kKLo false the K lo tile is zero (BF16 sources are exact in fp16) and its
+// products are skipped.  V is one fp16 per value: its rounding (relative
+// 2^-12, unbiased) enters the output as a weighted average, so it stays near
+// 2^-12 of the output's scale, while a K rounding error is amplified by the
+// logit's magnitude and keeps its lo part.
+template <bool kKLo>
 __device__ __forceinline__ void flash_step(const _Float16 (*kd)[kTile][kKdStride],
                                            const _Float16 (*vt)[kHeadDim][kVtStride], const f16x8 *bq_hi,
                                            const f16x8 *bq_lo, float unscale, uint32_t valid, float &m_run,
@@ -140,7 +143,7 @@ __device__ __forceinline__ void flash_step(const _Float16 (*kd)[kTile][kKdStride
             const f16x8 kh = *reinterpret_cast<const f16x8 *>(&kd[0][16 * u + col][32 * s + 8 * kq]);
             acc = mfma_f16(kh, bq_hi[s], acc);
             acc = mfma_f16(kh, bq_lo[s], acc);
-            if constexpr (kLo) {
+            if constexpr (kKLo) {
                 const f16x8 kl = *reinterpret_cast<const f16x8 *>(&kd[1][16 * u + col][32 * s + 8 * kq]);
                 acc = mfma_f16(kl, bq_hi[s], acc);
             }
@@ -186,33 +189,29 @@ __device__ __forceinline__ void flash_step(const _Float16 (*kd)[kTile][kKdStride
     const f16x8 a_lo = __builtin_bit_cast(f16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
     float al[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * kq + i);    // alpha of output row 4 kq + i
+    for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * kq + i);        // alpha of output row 4 kq + i
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[n][i] *= al[i];
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
         const int ch = 16 * n + col;
-        const u32x2 v0h = *reinterpret_cast<const u32x2 *>(&vt[0][ch][4 * kq]);
-        const u32x2 v1h = *reinterpret_cast<const u32x2 *>(&vt[0][ch][16 + 4 * kq]);
-        const f16x8 vh = __builtin_bit_cast(f16x8, u32x4{v0h[0], v0h[1], v1h[0], v1h[1]});
-        f32x4 acc = o[n];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] *= al[i];
-        acc = mfma_f16(a_hi, vh, acc);
-        acc = mfma_f16(a_lo, vh, acc);
-        if constexpr (kLo) {
-            const u32x2 v0l = *reinterpret_cast<const u32x2 *>(&vt[1][ch][4 * kq]);
-            const u32x2 v1l = *reinterpret_cast<const u32x2 *>(&vt[1][ch][16 + 4 * kq]);
-            const f16x8 vl = __builtin_bit_cast(f16x8, u32x4{v0l[0], v0l[1], v1l[0], v1l[1]});
-            acc = mfma_f16(a_hi, vl, acc);
-        }
-        o[n] = acc;
+        const u32x2 v0 = *reinterpret_cast<const u32x2 *>(&vt[0][ch][4 * kq]);
+        const u32x2 v1 = *reinterpret_cast<const u32x2 *>(&vt[0][ch][16 + 4 * kq]);
+        const f16x8 vh = __builtin_bit_cast(f16x8, u32x4{v0[0], v0[1], v1[0], v1[1]});
+        o[n] = mfma_f16(a_hi, vh, o[n]);
+        o[n] = mfma_f16(a_lo, vh, o[n]);
     }
 }
 
-__global__ __launch_bounds__(256) void extend_hist_kernel(ExtendHistArgs a) {
+// At most 128 VGPRs (launch bound of 4 waves per SIMD): four workgroups per
+// compute unit overlap one another's dequantisation, barriers and MFMA work.
+__global__ __launch_bounds__(256, 4) void extend_hist_kernel(ExtendHistArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t raw[kTile * kHeadRecord];
     __shared__ __attribute__((aligned(16))) uint8_t flag[kTile];
     __shared__ __attribute__((aligned(16))) _Float16 kd[2][kTile][kKdStride];
-    __shared__ __attribute__((aligned(16))) _Float16 vt[2][kHeadDim][kVtStride];
+    __shared__ __attribute__((aligned(16))) _Float16 vt[1][kHeadDim][kVtStride];
 
     const int id = blockIdx.x;
     const int rb = id % a.row_blocks;
@@ -271,18 +270,27 @@ __global__ __launch_bounds__(256) void extend_hist_kernel(ExtendHistArgs a) {
         }
         __syncthreads();
 
-        // ---- 2. dequantise: K rows (token t, channels 16 part .. +15)
+        // ---- 2. dequantise.  K rows (token t, channels 16 part .. +15): the
+        // group's four levels (s c + z) / 8, c = 0..3, as fp16 hi and lo pairs,
+        // then one byte-select (v_perm) per two channels picks their levels
         {
             const int t = tid >> 3, part = tid & 7;
             const uint32_t cw = *reinterpret_cast<const uint32_t *>(raw + t * kHeadRecord + 4 * part);
             const uint32_t szw = *reinterpret_cast<const uint32_t *>(raw + t * kHeadRecord + 64 + 4 * (part >> 1));
             const float s = sz_s(szw) * kDqScale, z = sz_z(szw) * kDqScale;     // exact
+            uint32_t h01, l01, h23, l23;
+            split2(z, s + z, h01, l01);                       // s + z: fmaf(s, 1, z)
+            split2(fmaf(s, 2.0f, z), fmaf(s, 3.0f, z), h23, l23);
+            const uint32_t c0s = cw & 0x33333333u;             // code of channel 2e at bits 4e
+            const uint32_t c1s = (cw >> 2) & 0x33333333u;      // code of channel 2e + 1 at bits 4e
             uint32_t hi[8], lo[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float x0 = fmaf(s, float((cw >> (4 * e)) & 3u), z);
-                const float x1 = fmaf(s, float((cw >> (4 * e + 2)) & 3u), z);
-                split2(x0, x1, hi[e], lo[e]);
+                // selector bytes 2 c0, 2 c0 + 1, 2 c1, 2 c1 + 1 (levels 0, 1 in h01, 2, 3 in h23)
+                const uint32_t y = ((c0s >> (4 * e)) & 3u) | (((c1s >> (4 * e)) & 3u) << 16);
+                const uint32_t sel = y * 0x0202u + 0x01000100u;
+                hi[e] = __builtin_amdgcn_perm(h23, h01, sel);
+                lo[e] = __builtin_amdgcn_perm(l23, l01, sel);
             }
             u32x4 *dh = reinterpret_cast<u32x4 *>(&kd[0][t][16 * part]);
             u32x4 *dl = reinterpret_cast<u32x4 *>(&kd[1][t][16 * part]);
@@ -291,38 +299,25 @@ __global__ __launch_bounds__(256) void extend_hist_kernel(ExtendHistArgs a) {
             dl[0] = u32x4{lo[0], lo[1], lo[2], lo[3]};
             dl[1] = u32x4{lo[4], lo[5], lo[6], lo[7]};
         }
-        // V^T rows (channels 2 cp, 2 cp + 1; tokens 8 tg .. 8 tg + 7)
+        // V^T rows (channels 4 cq .. 4 cq + 3, one code byte; tokens 4 tg .. 4 tg + 3),
+        // one fp16 per value
         {
-            const int cp = tid & 63, tg = tid >> 6;
-            const int byte = 32 + (cp >> 1), sh = 4 * (cp & 1), sz_off = 80 + 4 * (cp >> 4);
-            uint32_t h0[4], l0[4], h1[4], l1[4];
+            const int cq = tid & 31, tg = tid >> 5;
+            const int byte = 32 + cq, sz_off = 80 + 4 * (cq >> 3);
+            float x[4][4];                                      // [channel][token]
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float x0[2], x1[2];
+            for (int k = 0; k < 4; ++k) {
+                const int t = 4 * tg + k;
+                const uint32_t c = raw[t * kHeadRecord + byte];
+                const uint32_t szw = *reinterpret_cast<const uint32_t *>(raw + t * kHeadRecord + sz_off);
+                const float s = sz_s(szw) * kDqScale, z = sz_z(szw) * kDqScale;
 #pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                    const int t = 8 * tg + 2 * e + k;
-                    const uint32_t c = raw[t * kHeadRecord + byte] >> sh;
-                    const uint32_t szw = *reinterpret_cast<const uint32_t *>(raw + t * kHeadRecord + sz_off);
-                    const float s = sz_s(szw) * kDqScale, z = sz_z(szw) * kDqScale;
-                    x0[k] = fmaf(s, float(c & 3u), z);
-                    x1[k] = fmaf(s, float((c >> 2) & 3u), z);
-                }
-                split2(x0[0], x0[1], h0[e], l0[e]);
-                split2(x1[0], x1[1], h1[e], l1[e]);
+                for (int m = 0; m < 4; ++m) x[m][k] = fmaf(s, float((c >> (2 * m)) & 3u), z);
             }
-            u32x2 *r0h = reinterpret_cast<u32x2 *>(&vt[0][2 * cp][8 * tg]);
-            u32x2 *r0l = reinterpret_cast<u32x2 *>(&vt[1][2 * cp][8 * tg]);
-            u32x2 *r1h = reinterpret_cast<u32x2 *>(&vt[0][2 * cp + 1][8 * tg]);
-            u32x2 *r1l = reinterpret_cast<u32x2 *>(&vt[1][2 * cp + 1][8 * tg]);
-            r0h[0] = u32x2{h0[0], h0[1]};
-            r0h[1] = u32x2{h0[2], h0[3]};
-            r0l[0] = u32x2{l0[0], l0[1]};
-            r0l[1] = u32x2{l0[2], l0[3]};
-            r1h[0] = u32x2{h1[0], h1[1]};
-            r1h[1] = u32x2{h1[2], h1[3]};
-            r1l[0] = u32x2{l1[0], l1[1]};
-            r1l[1] = u32x2{l1[2], l1[3]};
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                *reinterpret_cast<u32x2 *>(&vt[0][4 * cq + m][4 * tg]) =
+                    u32x2{pk_f16(x[m][0], x[m][1]), pk_f16(x[m][2], x[m][3])};
         }
         // usable-token flags of the tile (read now: the next tile's staging
         // overwrites them before every wave has finished this tile)
@@ -351,7 +346,7 @@ __global__ __launch_bounds__(256) void extend_hist_kernel(ExtendHistArgs a) {
 // i sees new tokens 0..i).  Rows are exact in fp16 once scaled by 1/8 (bf16
 // has fewer mantissa bits), so there is no lo tile.  Each thread loads 32
 // bytes of a K row and 4 bytes of 8 V rows per tile, one tile ahead.
-__global__ __launch_bounds__(256) void extend_bf16_kernel(ExtendHistArgs a) {
+__global__ __launch_bounds__(256, 4) void extend_bf16_kernel(ExtendHistArgs a) {
     __shared__ __attribute__((aligned(16))) _Float16 kd[1][kTile][kKdStride];
     __shared__ __attribute__((aligned(16))) _Float16 vt[1][kHeadDim][kVtStride];
 

@@ -1226,7 +1226,7 @@ extern "C" oscar_status oscar_extend_attn(hipStream_t stream, const oscar_layout
     a.fixed_req = req_id;
     a.fixed_len = prefix_len;
 
-    // history items on the matrix cores, 64 / g new tokens per workgroup
+    // work items on the matrix cores, 128 / g new tokens per workgroup
     ExtendHistArgs xh;
     xh.records = pool->records;
     xh.slot_row = req_to_slot + size_t(req_id) * req_to_slot_stride;
@@ -1245,7 +1245,7 @@ extern "C" oscar_status oscar_extend_attn(hipStream_t stream, const oscar_layout
     xh.recent = a.recent_tokens;
     xh.prefix_len = prefix_len;
     xh.n_new = n_new;
-    xh.tok_per_block = 64 / a.g;
+    xh.tok_per_block = 128 / a.g;
     xh.row_blocks = (n_new + xh.tok_per_block - 1) / xh.tok_per_block;
     xh.hist_items = plan.extra_item - 2;
     xh.sink_store = pool->sink;

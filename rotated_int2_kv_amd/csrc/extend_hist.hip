@@ -3,8 +3,8 @@
 //
 // The decode kernel's history path is shaped for one query row per KV head
 // and reads every history tile once per row; a prefill chunk has thousands of
-// rows over the same prefix.  Here one workgroup takes 64 query rows of one
-// KV head (64 / g new tokens x g heads) and one history work item, and for
+// rows over the same prefix.  Here one workgroup takes 128 query rows of one
+// KV head (128 / g new tokens x g heads) and one history work item, and for
 // every 32-token tile of the item:
 //   1. the tile's 96-byte head records (K, V codes and (s, z)) are staged in
 //      LDS; records of the next tile are in flight meanwhile;
@@ -32,6 +32,7 @@ namespace oscar {
 namespace {
 
 constexpr int kTile = 32;                    // history tokens per tile
+constexpr int kThreads = 512;                // 8 waves x 16 query rows per workgroup
 constexpr int kKdStride = kHeadDim + 8;      // halves per K row (272 bytes: conflict-free 16-byte reads)
 constexpr int kVtStride = kTile + 4;         // halves per V^T row (72 bytes: conflict-free 8-byte reads)
 constexpr float kDqScale = 0.125f;           // dequantised values are stored times 1/8
@@ -205,9 +206,9 @@ __device__ __forceinline__ void flash_step(const _Float16 (*kd)[kTile][kKdStride
     }
 }
 
-// At most 128 VGPRs (launch bound of 4 waves per SIMD): four workgroups per
+// At most 128 VGPRs (launch bound of 4 waves per SIMD): two workgroups per
 // compute unit overlap one another's dequantisation, barriers and MFMA work.
-__global__ __launch_bounds__(256, 4) void extend_hist_kernel(ExtendHistArgs a) {
+__global__ __launch_bounds__(kThreads, 4) void extend_hist_kernel(ExtendHistArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t raw[kTile * kHeadRecord];
     __shared__ __attribute__((aligned(16))) uint8_t flag[kTile];
     __shared__ __attribute__((aligned(16))) _Float16 kd[2][kTile][kKdStride];
@@ -270,44 +271,40 @@ __global__ __launch_bounds__(256, 4) void extend_hist_kernel(ExtendHistArgs a) {
         }
         __syncthreads();
 
-        // ---- 2. dequantise.  K rows (token t, channels 16 part .. +15): the
+        // ---- 2. dequantise.  K rows (token t, channels 8 part .. +7): the
         // group's four levels (s c + z) / 8, c = 0..3, as fp16 hi and lo pairs,
         // then one byte-select (v_perm) per two channels picks their levels
         {
-            const int t = tid >> 3, part = tid & 7;
-            const uint32_t cw = *reinterpret_cast<const uint32_t *>(raw + t * kHeadRecord + 4 * part);
-            const uint32_t szw = *reinterpret_cast<const uint32_t *>(raw + t * kHeadRecord + 64 + 4 * (part >> 1));
+            const int t = tid >> 4, part = tid & 15;
+            const uint32_t cw = *reinterpret_cast<const uint16_t *>(raw + t * kHeadRecord + 2 * part);
+            const uint32_t szw = *reinterpret_cast<const uint32_t *>(raw + t * kHeadRecord + 64 + 4 * (part >> 2));
             const float s = sz_s(szw) * kDqScale, z = sz_z(szw) * kDqScale;     // exact
             uint32_t h01, l01, h23, l23;
             split2(z, s + z, h01, l01);                       // s + z: fmaf(s, 1, z)
             split2(fmaf(s, 2.0f, z), fmaf(s, 3.0f, z), h23, l23);
-            const uint32_t c0s = cw & 0x33333333u;             // code of channel 2e at bits 4e
-            const uint32_t c1s = (cw >> 2) & 0x33333333u;      // code of channel 2e + 1 at bits 4e
-            uint32_t hi[8], lo[8];
+            const uint32_t c0s = cw & 0x3333u;                 // code of channel 2e at bits 4e
+            const uint32_t c1s = (cw >> 2) & 0x3333u;          // code of channel 2e + 1 at bits 4e
+            uint32_t hi[4], lo[4];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
+            for (int e = 0; e < 4; ++e) {
                 // selector bytes 2 c0, 2 c0 + 1, 2 c1, 2 c1 + 1 (levels 0, 1 in h01, 2, 3 in h23)
                 const uint32_t y = ((c0s >> (4 * e)) & 3u) | (((c1s >> (4 * e)) & 3u) << 16);
                 const uint32_t sel = y * 0x0202u + 0x01000100u;
                 hi[e] = __builtin_amdgcn_perm(h23, h01, sel);
                 lo[e] = __builtin_amdgcn_perm(l23, l01, sel);
             }
-            u32x4 *dh = reinterpret_cast<u32x4 *>(&kd[0][t][16 * part]);
-            u32x4 *dl = reinterpret_cast<u32x4 *>(&kd[1][t][16 * part]);
-            dh[0] = u32x4{hi[0], hi[1], hi[2], hi[3]};
-            dh[1] = u32x4{hi[4], hi[5], hi[6], hi[7]};
-            dl[0] = u32x4{lo[0], lo[1], lo[2], lo[3]};
-            dl[1] = u32x4{lo[4], lo[5], lo[6], lo[7]};
+            *reinterpret_cast<u32x4 *>(&kd[0][t][8 * part]) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+            *reinterpret_cast<u32x4 *>(&kd[1][t][8 * part]) = u32x4{lo[0], lo[1], lo[2], lo[3]};
         }
-        // V^T rows (channels 4 cq .. 4 cq + 3, one code byte; tokens 4 tg .. 4 tg + 3),
+        // V^T rows (channels 4 cq .. 4 cq + 3, one code byte; tokens 2 tg, 2 tg + 1),
         // one fp16 per value
         {
             const int cq = tid & 31, tg = tid >> 5;
             const int byte = 32 + cq, sz_off = 80 + 4 * (cq >> 3);
-            float x[4][4];                                      // [channel][token]
+            float x[4][2];                                      // [channel][token]
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int t = 4 * tg + k;
+            for (int k = 0; k < 2; ++k) {
+                const int t = 2 * tg + k;
                 const uint32_t c = raw[t * kHeadRecord + byte];
                 const uint32_t szw = *reinterpret_cast<const uint32_t *>(raw + t * kHeadRecord + sz_off);
                 const float s = sz_s(szw) * kDqScale, z = sz_z(szw) * kDqScale;
@@ -316,8 +313,7 @@ __global__ __launch_bounds__(256, 4) void extend_hist_kernel(ExtendHistArgs a) {
             }
 #pragma unroll
             for (int m = 0; m < 4; ++m)
-                *reinterpret_cast<u32x2 *>(&vt[0][4 * cq + m][4 * tg]) =
-                    u32x2{pk_f16(x[m][0], x[m][1]), pk_f16(x[m][2], x[m][3])};
+                *reinterpret_cast<uint32_t *>(&vt[0][4 * cq + m][2 * tg]) = pk_f16(x[m][0], x[m][1]);
         }
         // usable-token flags of the tile (read now: the next tile's staging
         // overwrites them before every wave has finished this tile)
@@ -346,7 +342,7 @@ __global__ __launch_bounds__(256, 4) void extend_hist_kernel(ExtendHistArgs a) {
 // i sees new tokens 0..i).  Rows are exact in fp16 once scaled by 1/8 (bf16
 // has fewer mantissa bits), so there is no lo tile.  Each thread loads 32
 // bytes of a K row and 4 bytes of 8 V rows per tile, one tile ahead.
-__global__ __launch_bounds__(256, 4) void extend_bf16_kernel(ExtendHistArgs a) {
+__global__ __launch_bounds__(kThreads, 4) void extend_bf16_kernel(ExtendHistArgs a) {
     __shared__ __attribute__((aligned(16))) _Float16 kd[1][kTile][kKdStride];
     __shared__ __attribute__((aligned(16))) _Float16 vt[1][kHeadDim][kVtStride];
 
@@ -395,23 +391,18 @@ __global__ __launch_bounds__(256, 4) void extend_bf16_kernel(ExtendHistArgs a) {
         const uint16_t *base = kind == 0 ? a.sink_store : kind == 1 ? a.recent_store : a.newkv;
         return base + row * (2 * kHeadDim);
     };
-    // K: token kt, channels 16 kp .. +15; V: channels 2 cp, 2 cp + 1 of tokens 8 tg .. +7
-    const int kt = tid >> 3, kp = tid & 7;
+    // K: token kt, channels 8 kp .. +7; V: channels 2 cp, 2 cp + 1 of tokens 4 tg .. +3
+    const int kt = tid >> 4, kp = tid & 15;
     const int cp = tid & 63, tg = tid >> 6;
-    u32x4 kreg[2];
-    uint32_t vreg[8];
+    u32x4 kreg;
+    uint32_t vreg[4];
     auto load_tile = [&](int c) {
         const int pk = c + kt;
-        if (pk < p1) {
-            const u32x4 *src = reinterpret_cast<const u32x4 *>(row_ptr(pk) + 16 * kp);
-            kreg[0] = __builtin_nontemporal_load(src);
-            kreg[1] = __builtin_nontemporal_load(src + 1);
-        } else {
-            kreg[0] = kreg[1] = u32x4{0u, 0u, 0u, 0u};
-        }
+        kreg = pk < p1 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(row_ptr(pk) + 8 * kp))
+                       : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int pv = c + 8 * tg + k;
+        for (int k = 0; k < 4; ++k) {
+            const int pv = c + 4 * tg + k;
             vreg[k] = pv < p1 ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(row_ptr(pv) + kHeadDim) + cp)
                               : 0u;
         }
@@ -421,27 +412,18 @@ __global__ __launch_bounds__(256, 4) void extend_bf16_kernel(ExtendHistArgs a) {
     for (int cb = p0; cb < p1; cb += kTile) {
         __syncthreads();                                    // every wave is done with the previous tile
         {
-            uint32_t hk4[8];
+            uint32_t hk4[4];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t u = kreg[e >> 2][e & 3];
-                hk4[e] = pk_f16(bf(u, 0), bf(u, 1));
-            }
-            u32x4 *dh = reinterpret_cast<u32x4 *>(&kd[0][kt][16 * kp]);
-            dh[0] = u32x4{hk4[0], hk4[1], hk4[2], hk4[3]};
-            dh[1] = u32x4{hk4[4], hk4[5], hk4[6], hk4[7]};
-            uint32_t h0[4], h1[4];
+            for (int e = 0; e < 4; ++e) hk4[e] = pk_f16(bf(kreg[e], 0), bf(kreg[e], 1));
+            *reinterpret_cast<u32x4 *>(&kd[0][kt][8 * kp]) = u32x4{hk4[0], hk4[1], hk4[2], hk4[3]};
+            uint32_t h0[2], h1[2];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
+            for (int e = 0; e < 2; ++e) {
                 h0[e] = pk_f16(bf(vreg[2 * e], 0), bf(vreg[2 * e + 1], 0));
                 h1[e] = pk_f16(bf(vreg[2 * e], 1), bf(vreg[2 * e + 1], 1));
             }
-            u32x2 *r0 = reinterpret_cast<u32x2 *>(&vt[0][2 * cp][8 * tg]);
-            u32x2 *r1 = reinterpret_cast<u32x2 *>(&vt[0][2 * cp + 1][8 * tg]);
-            r0[0] = u32x2{h0[0], h0[1]};
-            r0[1] = u32x2{h0[2], h0[3]};
-            r1[0] = u32x2{h1[0], h1[1]};
-            r1[1] = u32x2{h1[2], h1[3]};
+            *reinterpret_cast<u32x2 *>(&vt[0][2 * cp][4 * tg]) = u32x2{h0[0], h0[1]};
+            *reinterpret_cast<u32x2 *>(&vt[0][2 * cp + 1][4 * tg]) = u32x2{h1[0], h1[1]};
         }
         if (cb + kTile < p1) load_tile(cb + kTile);
         __syncthreads();
@@ -464,7 +446,7 @@ __global__ __launch_bounds__(256, 4) void extend_bf16_kernel(ExtendHistArgs a) {
 int64_t extend_bf16_blocks(const ExtendHistArgs &a) { return int64_t(a.row_blocks) * 3 * a.hkv; }
 
 hipError_t launch_extend_bf16(const ExtendHistArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL(extend_bf16_kernel, dim3(unsigned(extend_bf16_blocks(a))), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(extend_bf16_kernel, dim3(unsigned(extend_bf16_blocks(a))), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -475,7 +457,7 @@ int64_t extend_history_blocks(const ExtendHistArgs &a) {
 hipError_t launch_extend_history(const ExtendHistArgs &a, hipStream_t stream) {
     const int64_t blocks = extend_history_blocks(a);
     if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL(extend_hist_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(extend_hist_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -76,7 +76,7 @@ struct ExtendHistArgs {
     int32_t recent;
     int32_t prefix_len;
     int32_t n_new;
-    int32_t tok_per_block;        // new tokens per workgroup: 64 / g
+    int32_t tok_per_block;        // new tokens per workgroup: 128 / g
     int32_t row_blocks;
     int32_t hist_items;
     // BF16 items (sink window, recent window, the new tokens themselves)

@@ -14,7 +14,8 @@ with HIP events on the launch stream), the quant-append throughput of the
 131,072-token append workload, the same decode step on a BF16 paged cache
 (the baseline of the OSCAR page's speed-ups) with the INT2/BF16 ratio, one
 extend call (an 8,192-token prefill chunk over a 122,880-token cached
-prefix), and the fp64 CPU oracle's rate on a bounded sample of the same
+prefix), one calibration-statistics call (C_Q Gram sums of 131,072 query
+tokens), and the fp64 CPU oracle's rate on a bounded sample of the same
 decode workload.
 
 The default run times 2,000 steps after 500 warm-up steps: under this load the
@@ -41,6 +42,7 @@ sys.path.insert(0, ROOT)
 METRIC = "INT2 decode-attn KV tokens/s & % HBM roofline @100K ctx bs32; quant tok/s"
 HBM_PEAK_GBS = 8000.0
 F16_MFMA_PEAK_TFLOPS = 2500.0          # dense fp16/bf16 matrix-core peak
+FP32_PEAK_TFLOPS = 157.3               # fp32 peak (matrix and vector)
 HISTORY_BYTES_PER_TOKEN_HEAD = 96      # K codes 32 + V codes 32 + K (s,z) 16 + V (s,z) 16
 SLOT_BYTES_PER_TOKEN = 4
 BF16_BYTES_PER_TOKEN_HEAD = 512        # K and V, 128 bf16 each
@@ -346,6 +348,33 @@ def run_extend(args, torch, B, workloads):
                 output_finite=bool(torch.isfinite(out.float()).all().item()))
 
 
+def run_covariance(args, torch, B, workloads):
+    """Calibration statistics: C_Q Gram sums of 131,072 captured query tokens of
+    a 32 q / 8 KV head layer (bf16), one oscar_covariance_accumulate call."""
+    w = workloads.workload("layer_32k")
+    n = 131072
+    lay = B.Layout(128, 32, w.num_kv_heads, w.num_q_heads, w.sink, w.recent, num_slots=1, max_requests=1)
+    x = torch.randn((n, w.num_q_heads, 128), device="cuda", generator=torch.Generator("cuda").manual_seed(5))
+    x = x.to(torch.bfloat16)
+    acc = torch.zeros((w.num_kv_heads, 128, 128), dtype=torch.float64, device="cuda")
+    ws = torch.empty(B.oscar_covariance_workspace_size(lay, n), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    B.oscar_covariance_accumulate(lay, x, acc, ws, stream=stream)
+    reps = 10
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(reps):
+        B.oscar_covariance_accumulate(lay, x, acc, ws, stream=stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
+    flops = 2 * 128 * 128 * n * w.num_q_heads
+    return dict(rows=n * w.num_q_heads, ms=ms, rows_per_s=n * w.num_q_heads / (ms * 1e-3),
+                tflops=flops / (ms * 1e-3) / 1e12, frac_fp32_matrix=flops / (ms * 1e-3) / 1e12 / FP32_PEAK_TFLOPS,
+                gb_per_s=x.numel() * 2 / (ms * 1e-3) / 1e9)
+
+
 def cpu_baseline(workloads):
     """The oracle, as it stands, on one request of the decode workload."""
     from threadpoolctl import threadpool_limits
@@ -388,6 +417,7 @@ def main():
     ap.add_argument("--no-append", action="store_true")
     ap.add_argument("--no-extend", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--no-covariance", action="store_true")
     ap.add_argument("--only-extend", action="store_true",
                     help="run only the extend call (prints its own JSON object; for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -436,6 +466,9 @@ def main():
     if ext:
         log(f"[bench] extend {ext['ms']:.2f} ms ({ext['new_tokens']} new tokens over {ext['prefix_len']}), "
             f"{ext['attention_tflops']:.1f} TFLOP/s")
+    cov = None if args.no_covariance else run_covariance(args, torch, B, workloads)
+    if cov:
+        log(f"[bench] covariance {cov['ms']:.3f} ms for {cov['rows']} rows, {cov['tflops']:.1f} TFLOP/s")
     base = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle ...")
@@ -466,6 +499,7 @@ def main():
         "quant_append": app,
         "bf16_baseline": bf,
         "extend": ext,
+        "covariance": cov,
         "cpu_baseline": base,
         "output_finite": d["o_finite"],
     }

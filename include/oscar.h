@@ -305,6 +305,27 @@ oscar_status oscar_bf16_decode_attn(hipStream_t stream, const oscar_layout *layo
                                     oscar_dtype out_dtype, void *workspace, size_t workspace_bytes,
                                     const oscar_launch_opts *opts);
 
+/*
+ * Calibration statistics (OSCAR page, "What OSCAR does differently"): the
+ * key basis comes from the query covariance C_Q = (1/N) sum q^T q and the
+ * value basis from C_S = (1/N) V^T S^T S V = (1/N) sum o^T o over the
+ * attention outputs o = S V.  Both are Gram sums of 128-wide rows, the g
+ * query heads of a KV head pooled into its rows.
+ *
+ * oscar_covariance_accumulate: acc[h] += sum over n < n_rows and the query
+ * heads q of KV head h of x[n][q]^T x[n][q] (128 x 128, row-major).
+ *   x:    [n_rows][Hq][128] of dtype (F32, BF16 or F16), device.
+ *   acc:  [Hkv][128][128] fp64, device, accumulated into (the caller zeroes
+ *         it first and divides by the row count, n_rows * g, at the end).
+ *   workspace: >= oscar_covariance_workspace_size bytes, 256-byte aligned.
+ * Products are exact in fp32 (fp32 matrix cores), each slab of rows sums in
+ * fp32 and the slabs add in fp64.  n_rows = 0 is a no-op.  Asynchronous.
+ */
+oscar_status oscar_covariance_workspace_size(const oscar_layout *layout, int64_t n_rows, size_t *bytes);
+oscar_status oscar_covariance_accumulate(hipStream_t stream, const oscar_layout *layout, const void *x,
+                                         oscar_dtype dtype, int64_t n_rows, double *acc, void *workspace,
+                                         size_t workspace_bytes);
+
 /* Thread-local message of the last non-OK status of this thread. */
 const char *oscar_last_error(void);
 

@@ -32,7 +32,8 @@ EXPORTED = (
     "oscar_layout_check", "oscar_pool_bytes", "oscar_build_rotation", "oscar_quant_append",
     "oscar_decode_workspace_size", "oscar_decode_attn", "oscar_decode_plan",
     "oscar_extend_workspace_size", "oscar_extend_attn", "oscar_bf16_pool_bytes", "oscar_bf16_append",
-    "oscar_bf16_decode_workspace_size", "oscar_bf16_decode_attn", "oscar_last_error", "oscar_version",
+    "oscar_bf16_decode_workspace_size", "oscar_bf16_decode_attn", "oscar_covariance_workspace_size",
+    "oscar_covariance_accumulate", "oscar_last_error", "oscar_version",
 )
 
 
@@ -89,6 +90,8 @@ def _load() -> ctypes.CDLL:
         "oscar_bf16_decode_workspace_size": (I32, [LP, I32, P, OP, ctypes.POINTER(SZ)]),
         "oscar_bf16_decode_attn": (I32, [P, LP, P, P, I32, I32, P, P, P, P, I64, F32, P, I32, P, SZ,
                                          OP]),
+        "oscar_covariance_workspace_size": (I32, [LP, I64, ctypes.POINTER(SZ)]),
+        "oscar_covariance_accumulate": (I32, [P, LP, P, I32, I64, P, P, SZ]),
         "oscar_last_error": (ctypes.c_char_p, []),
         "oscar_version": (ctypes.c_char_p, []),
     }
@@ -310,3 +313,17 @@ def oscar_bf16_decode_attn(layout: Layout, kv_pool, q, req_ids, seq_lens, seq_le
         _ptr(req_ids), _ptr(seq_lens), lens.ctypes.data, _ptr(req_to_slot), int(req_to_slot.shape[-1]),
         float(sm_scale), _ptr(out), _dtype_code(out), _ptr(workspace),
         int(workspace.numel() * workspace.element_size()), _opts(kernel_begin, kernel_end, history_chunk)))
+
+
+def oscar_covariance_workspace_size(layout: Layout, n_rows: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(_lib.oscar_covariance_workspace_size(ctypes.byref(layout.c()), int(n_rows), ctypes.byref(out)))
+    return int(out.value)
+
+
+def oscar_covariance_accumulate(layout: Layout, x, acc, workspace, stream=None) -> None:
+    """acc [Hkv, 128, 128] float64 (device) += Gram sums of x [n, Hq, 128] per KV head."""
+    _dev(x, acc, workspace)
+    _check(_lib.oscar_covariance_accumulate(
+        _stream(stream), ctypes.byref(layout.c()), _ptr(x), _dtype_code(x), int(x.shape[0]), _ptr(acc),
+        _ptr(workspace), int(workspace.numel() * workspace.element_size())))

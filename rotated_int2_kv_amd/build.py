@@ -18,7 +18,7 @@ OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liboscar.so")
 ARCH = "gfx950"
 
-SOURCES = ["oscar_host.cpp", "quant_append.hip", "decode_attn.hip", "bf16_decode.hip", "extend_hist.hip"]
+SOURCES = ["oscar_host.cpp", "quant_append.hip", "decode_attn.hip", "bf16_decode.hip", "extend_hist.hip", "calib.hip"]
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -209,10 +209,12 @@ __device__ __forceinline__ void flash_step(const _Float16 (*kd)[kTile][kKdStride
 // At most 128 VGPRs (launch bound of 4 waves per SIMD): two workgroups per
 // compute unit overlap one another's dequantisation, barriers and MFMA work.
 __global__ __launch_bounds__(kThreads, 4) void extend_hist_kernel(ExtendHistArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t raw[kTile * kHeadRecord];
-    __shared__ __attribute__((aligned(16))) uint8_t flag[kTile];
-    __shared__ __attribute__((aligned(16))) _Float16 kd[2][kTile][kKdStride];
-    __shared__ __attribute__((aligned(16))) _Float16 vt[1][kHeadDim][kVtStride];
+    // two of everything: tile k is computed from one buffer while tile k + 1
+    // is dequantised into the other, one workgroup barrier per tile
+    __shared__ __attribute__((aligned(16))) uint8_t raw_all[2][kTile * kHeadRecord];
+    __shared__ __attribute__((aligned(16))) uint8_t flag_all[2][kTile];
+    __shared__ __attribute__((aligned(16))) _Float16 kd_all[2][2][kTile][kKdStride];
+    __shared__ __attribute__((aligned(16))) _Float16 vt_all[2][1][kHeadDim][kVtStride];
 
     const int id = blockIdx.x;
     const int rb = id % a.row_blocks;
@@ -253,24 +255,27 @@ __global__ __launch_bounds__(kThreads, 4) void extend_hist_kernel(ExtendHistArgs
                                            : a.zero_rec;
         return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(base + 16 * pu));
     };
+    // records of the next tile to stage, its usability, and the slot ids of the one after
     int slot_cur = slot_of(p0);
     u32x4 rec = producer ? load_rec(slot_cur) : u32x4{0u, 0u, 0u, 0u};
     bool ok_cur = usable(slot_cur);
     int slot_nxt = slot_of(p0 + kTile);
-
-    for (int cb = p0; cb < p1; cb += kTile) {
-        // ---- 1. stage this tile; next tile's records and the slot ids after it in flight
+    // stage the records held in `rec` (tile at cb) into buffer b, then start loading the next
+    auto stage = [&](int b, int cb) {
         if (producer) {
-            *reinterpret_cast<u32x4 *>(raw + pt * kHeadRecord + 16 * pu) = rec;
-            if (pu == 0) flag[pt] = ok_cur ? 1 : 0;
+            *reinterpret_cast<u32x4 *>(raw_all[b] + pt * kHeadRecord + 16 * pu) = rec;
+            if (pu == 0) flag_all[b][pt] = ok_cur ? 1 : 0;
         }
         if (cb + kTile < p1) {
             if (producer) rec = load_rec(slot_nxt);
             ok_cur = usable(slot_nxt);
             slot_nxt = slot_of(cb + 2 * kTile);
         }
-        __syncthreads();
-
+    };
+    auto dequant = [&](int b) {
+        const uint8_t *raw = raw_all[b];
+        _Float16(*kd)[kTile][kKdStride] = kd_all[b];
+        _Float16(*vt)[kHeadDim][kVtStride] = vt_all[b];
         // ---- 2. dequantise.  K rows (token t, channels 8 part .. +7): the
         // group's four levels (s c + z) / 8, c = 0..3, as fp16 hi and lo pairs,
         // then one byte-select (v_perm) per two channels picks their levels
@@ -315,13 +320,20 @@ __global__ __launch_bounds__(kThreads, 4) void extend_hist_kernel(ExtendHistArgs
             for (int m = 0; m < 4; ++m)
                 *reinterpret_cast<uint32_t *>(&vt[0][4 * cq + m][2 * tg]) = pk_f16(x[m][0], x[m][1]);
         }
-        // usable-token flags of the tile (read now: the next tile's staging
-        // overwrites them before every wave has finished this tile)
-        const uint32_t fl0 = *reinterpret_cast<const uint32_t *>(flag + 4 * kq);
-        const uint32_t fl1 = *reinterpret_cast<const uint32_t *>(flag + 16 + 4 * kq);
-        __syncthreads();
+    };
 
-        // ---- 3./4. flash step over the tile
+    stage(0, p0);
+    __syncthreads();
+    dequant(0);
+    int buf = 0;
+    for (int cb = p0; cb < p1; cb += kTile, buf ^= 1) {
+        const bool more = cb + kTile < p1;
+        if (more) stage(buf ^ 1, cb + kTile);
+        // usable-token flags of tile cb (read before the barrier: the staging of
+        // tile cb + 2 overwrites them once every wave has passed it)
+        const uint32_t fl0 = *reinterpret_cast<const uint32_t *>(&flag_all[buf][4 * kq]);
+        const uint32_t fl1 = *reinterpret_cast<const uint32_t *>(&flag_all[buf][16 + 4 * kq]);
+        __syncthreads();
         uint32_t valid = 0;
 #pragma unroll
         for (int u = 0; u < 2; ++u)
@@ -331,7 +343,8 @@ __global__ __launch_bounds__(kThreads, 4) void extend_hist_kernel(ExtendHistArgs
                 const bool use = (((u ? fl1 : fl0) >> (8 * i)) & 1u) && cb + t < p1;
                 valid |= uint32_t(use) << (4 * u + i);
             }
-        flash_step<true>(kd, vt, r.bq_hi, r.bq_lo, r.unscale, valid, m_run, l_run, o, col, kq);
+        flash_step<true>(kd_all[buf], vt_all[buf], r.bq_hi, r.bq_lo, r.unscale, valid, m_run, l_run, o, col, kq);
+        if (more) dequant(buf ^ 1);                         // overlaps the step's matrix-core work
     }
 
     store_partials(a, rb, hk, j, w, col, kq, r, m_run, l_run, o);

@@ -301,24 +301,23 @@ __global__ __launch_bounds__(kThreads, 4) void extend_hist_kernel(ExtendHistArgs
             *reinterpret_cast<u32x4 *>(&kd[0][t][8 * part]) = u32x4{hi[0], hi[1], hi[2], hi[3]};
             *reinterpret_cast<u32x4 *>(&kd[1][t][8 * part]) = u32x4{lo[0], lo[1], lo[2], lo[3]};
         }
-        // V^T rows (channels 4 cq .. 4 cq + 3, one code byte; tokens 2 tg, 2 tg + 1),
-        // one fp16 per value
+        // V^T rows (channels 2 cp, 2 cp + 1; tokens 4 tq .. 4 tq + 3), one fp16 per
+        // value; 8-byte row writes (at most 2 lanes of 16 per bank)
         {
-            const int cq = tid & 31, tg = tid >> 5;
-            const int byte = 32 + cq, sz_off = 80 + 4 * (cq >> 3);
-            float x[4][2];                                      // [channel][token]
+            const int cp = tid & 63, tq = tid >> 6;
+            const int byte = 32 + (cp >> 1), sh = 4 * (cp & 1), sz_off = 80 + 4 * (cp >> 4);
+            float x0[4], x1[4];
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int t = 2 * tg + k;
-                const uint32_t c = raw[t * kHeadRecord + byte];
+            for (int k = 0; k < 4; ++k) {
+                const int t = 4 * tq + k;
+                const uint32_t c = uint32_t(raw[t * kHeadRecord + byte]) >> sh;
                 const uint32_t szw = *reinterpret_cast<const uint32_t *>(raw + t * kHeadRecord + sz_off);
                 const float s = sz_s(szw) * kDqScale, z = sz_z(szw) * kDqScale;
-#pragma unroll
-                for (int m = 0; m < 4; ++m) x[m][k] = fmaf(s, float((c >> (2 * m)) & 3u), z);
+                x0[k] = fmaf(s, float(c & 3u), z);
+                x1[k] = fmaf(s, float((c >> 2) & 3u), z);
             }
-#pragma unroll
-            for (int m = 0; m < 4; ++m)
-                *reinterpret_cast<uint32_t *>(&vt[0][4 * cq + m][2 * tg]) = pk_f16(x[m][0], x[m][1]);
+            *reinterpret_cast<u32x2 *>(&vt[0][2 * cp][4 * tq]) = u32x2{pk_f16(x0[0], x0[1]), pk_f16(x0[2], x0[3])};
+            *reinterpret_cast<u32x2 *>(&vt[0][2 * cp + 1][4 * tq]) = u32x2{pk_f16(x1[0], x1[1]), pk_f16(x1[2], x1[3])};
         }
     };
 

@@ -24,6 +24,7 @@
 #include <hip/hip_fp16.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "common.cuh"
 #include "internal.h"
@@ -36,6 +37,7 @@ constexpr int kThreads = 512;                // 8 waves x 16 query rows per work
 constexpr int kKdStride = kHeadDim + 8;      // halves per K row (272 bytes: conflict-free 16-byte reads)
 constexpr int kVtStride = kTile + 4;         // halves per V^T row (72 bytes: conflict-free 8-byte reads)
 constexpr float kDqScale = 0.125f;           // dequantised values are stored times 1/8
+constexpr float kSlack = 15.0f;              // log2 headroom of the softmax reference (weights < 2^15)
 
 __device__ __forceinline__ uint32_t pk_f16(float x0, float x1) {
     const f16x2 h = {static_cast<_Float16>(x0), static_cast<_Float16>(x1)};
@@ -72,7 +74,7 @@ __device__ __forceinline__ void load_rows(const ExtendHistArgs &a, int rb, int h
     r.row_ok = tl < a.tok_per_block && r.tok < a.n_new;
     const size_t qrow = size_t(r.row_ok ? r.tok : 0) * a.hq + size_t(hk) * a.g + head;
     float qscale = 0.0f;
-    r.unscale = 0.0f;
+    r.unscale = 1.0f;                                       // rows past the block: q = 0, S = 0
     if (r.row_ok) {
         qscale = a.qsum[qrow * 8 + 4];                      // 2^K: max |q'| 2^K < 2^15
         r.unscale = a.qsum[qrow * 8 + 5] * (1.0f / (16777216.0f * kDqScale));   // 2^-K x 8
@@ -151,20 +153,20 @@ __device__ __forceinline__ void flash_step(const _Float16 (*kd)[kTile][kKdStride
         }
         d[u] = acc;
     }
-    float x[2][4];
+    // row maximum of the tile in S^T units (unscale > 0 keeps the order)
     float mt = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            x[u][i] = ((valid >> (4 * u + i)) & 1u) ? d[u][i] * unscale : -INFINITY;
-            mt = fmaxf(mt, x[u][i]);
-        }
-    }
+        for (int i = 0; i < 4; ++i) mt = fmaxf(mt, ((valid >> (4 * u + i)) & 1u) ? d[u][i] : -INFINITY);
     mt = fmaxf(mt, __shfl_xor(mt, 16));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+    mt *= unscale;                                          // log2 units
+    // The reference maximum moves only when a logit exceeds it by more than
+    // kSlack (weights stay below 2^kSlack, inside fp16), so alpha is mostly 1.
+    const bool move = mt > m_run + kSlack;
+    const float m_new = move ? mt : m_run;
+    const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
     m_run = m_new;
     float p[2][4];
     float lsum = 0.0f;
@@ -172,7 +174,8 @@ __device__ __forceinline__ void flash_step(const _Float16 (*kd)[kTile][kKdStride
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            p[u][i] = x[u][i] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x[u][i] - m_new);
+            const float e = __builtin_amdgcn_exp2f(fmaf(d[u][i], unscale, -m_new));
+            p[u][i] = ((valid >> (4 * u + i)) & 1u) ? e : 0.0f;
             lsum += p[u][i];
         }
     }
@@ -324,8 +327,10 @@ __global__ __launch_bounds__(kThreads, 4) void extend_hist_kernel(ExtendHistArgs
     stage(0, p0);
     __syncthreads();
     dequant(0);
-    int buf = 0;
-    for (int cb = p0; cb < p1; cb += kTile, buf ^= 1) {
+    // one tile from buffer `buf` (a compile-time constant: the loop runs two tiles per
+    // iteration, so every LDS address is an immediate offset)
+    auto tile = [&](auto bufc, int cb) {
+        constexpr int buf = decltype(bufc)::value;
         const bool more = cb + kTile < p1;
         if (more) stage(buf ^ 1, cb + kTile);
         // usable-token flags of tile cb (read before the barrier: the staging of
@@ -338,12 +343,15 @@ __global__ __launch_bounds__(kThreads, 4) void extend_hist_kernel(ExtendHistArgs
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int t = 16 * u + 4 * kq + i;
-                const bool use = (((u ? fl1 : fl0) >> (8 * i)) & 1u) && cb + t < p1;
+                const bool use = ((u ? fl1 : fl0) >> (8 * i)) & 1u;    // tokens past the item are unusable
                 valid |= uint32_t(use) << (4 * u + i);
             }
         flash_step<true>(kd_all[buf], vt_all[buf], r.bq_hi, r.bq_lo, r.unscale, valid, m_run, l_run, o, col, kq);
         if (more) dequant(buf ^ 1);                         // overlaps the step's matrix-core work
+    };
+    for (int cb = p0; cb < p1; cb += 2 * kTile) {
+        tile(std::integral_constant<int, 0>{}, cb);
+        if (cb + kTile < p1) tile(std::integral_constant<int, 1>{}, cb + kTile);
     }
 
     store_partials(a, rb, hk, j, w, col, kq, r, m_run, l_run, o);

@@ -1161,6 +1161,11 @@ oscar_status launch_decode(const DecodeArgs &a, const DecodePlan &plan, hipStrea
     if (opts && opts->kernel_end && hipEventRecord(opts->kernel_end, stream) != hipSuccess)
         return fail(OSCAR_ERR_HIP, "hipEventRecord failed");
 
+    if (xh) {
+        e = launch_extend_merge(*xh, stream);
+        if (e != hipSuccess) return fail(OSCAR_ERR_HIP, std::string("extend merge launch: ") + hipGetErrorString(e));
+        return OSCAR_OK;
+    }
     hipLaunchKernelGGL(merge_kernel, dim3(a.batch * a.hkv), dim3(512), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(OSCAR_ERR_HIP, std::string("merge launch: ") + hipGetErrorString(e));
@@ -1253,6 +1258,9 @@ extern "C" oscar_status oscar_extend_attn(hipStream_t stream, const oscar_layout
     xh.newkv = a.newkv;
     xh.req = req_id;
     xh.extra_item = plan.extra_item;
+    xh.r_v = R_V;
+    xh.out = out;
+    xh.out_dtype = out_dtype;
     if (extend_history_blocks(xh) > INT32_MAX || extend_bf16_blocks(xh) > INT32_MAX)
         return fail(OSCAR_ERR_UNSUPPORTED, "new tokens x work items exceeds one launch grid");
 

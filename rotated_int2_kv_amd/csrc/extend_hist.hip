@@ -461,7 +461,92 @@ __global__ __launch_bounds__(kThreads, 4) void extend_bf16_kernel(ExtendHistArgs
     store_partials(a, rb, hk, j, w, col, kq, r, m_run, l_run, o);
 }
 
+// Merge of the work items and un-rotation, o = o' R_V^T, for 8 new tokens
+// (8 g query rows) of one KV head per workgroup, so that R_V is read once per
+// 8 tokens instead of once per token.  Thread (c, rq) first merges channel c
+// of rows rq, rq + 4, ... into LDS, then computes output channel c of those
+// rows from its row of R_V.
+constexpr int kMergeTokens = 8;
+
+__global__ __launch_bounds__(512) void extend_merge_kernel(ExtendHistArgs a) {
+    __shared__ float ob[kMergeTokens * kMaxGroup][kHeadDim];
+    const int rbm = blockIdx.x;
+    const int hk = blockIdx.y;
+    const int c = threadIdx.x & (kHeadDim - 1);
+    const int rq = threadIdx.x >> 7;
+    const int g = a.g;
+    const int rows = kMergeTokens * g;
+    const int P = a.prefix_len;
+    const bool sink_ok = min(a.sink, P) > 0;
+    const bool recent_ok = P > a.sink;
+    const int hist = max(0, max(a.sink, P - a.recent) - a.sink);
+    const int n_hist = (a.num_slots > 0 && hist > 0) ? a.hist_items : 0;
+    auto item_ok = [&](int jj) {
+        return jj == a.extra_item || (jj == 0 && sink_ok) || (jj == 1 && recent_ok) || (jj >= 2 && jj < 2 + n_hist);
+    };
+    for (int rr = rq; rr < rows; rr += 4) {
+        const int tok = rbm * kMergeTokens + rr / g;
+        const int h = rr - (rr / g) * g;
+        float o = 0.0f;
+        if (tok < a.n_new) {
+            const size_t row_h = size_t(tok) * a.items * a.hq + size_t(hk) * g + h;    // item 0
+            float M = -INFINITY;
+            for (int jj = 0; jj <= a.extra_item; ++jj)
+                if (item_ok(jj)) M = fmaxf(M, a.part_ml[(row_h + size_t(jj) * a.hq) * 2]);
+            float l = 0.0f, acc = 0.0f;
+            if (M != -INFINITY) {
+                for (int jj = 0; jj <= a.extra_item; ++jj) {
+                    if (!item_ok(jj)) continue;
+                    const size_t row = row_h + size_t(jj) * a.hq;
+                    const float e = __builtin_amdgcn_exp2f(a.part_ml[row * 2] - M);
+                    l = fmaf(e, a.part_ml[row * 2 + 1], l);
+                    acc = fmaf(e, a.part_o[row * kHeadDim + c], acc);
+                }
+            }
+            o = l > 0.0f ? acc / l : 0.0f;
+        }
+        ob[rr][c] = o;
+    }
+    __syncthreads();
+    const float *R = a.r_v + (size_t(hk) * kHeadDim + c) * kHeadDim;
+    float acc[kMergeTokens * kMaxGroup / 4];
+#pragma unroll
+    for (int k = 0; k < kMergeTokens * kMaxGroup / 4; ++k) acc[k] = 0.0f;
+    for (int i = 0; i < kHeadDim; i += 4) {
+        const f32x4 r = *reinterpret_cast<const f32x4 *>(R + i);
+#pragma unroll
+        for (int k = 0; k < kMergeTokens * kMaxGroup / 4; ++k) {
+            const int rr = rq + 4 * k;
+            if (rr < rows) {
+                acc[k] = fmaf(ob[rr][i], r[0], acc[k]);
+                acc[k] = fmaf(ob[rr][i + 1], r[1], acc[k]);
+                acc[k] = fmaf(ob[rr][i + 2], r[2], acc[k]);
+                acc[k] = fmaf(ob[rr][i + 3], r[3], acc[k]);
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kMergeTokens * kMaxGroup / 4; ++k) {
+        const int rr = rq + 4 * k;
+        const int tok = rbm * kMergeTokens + rr / g;
+        if (rr >= rows || tok >= a.n_new) continue;
+        const size_t idx = (size_t(tok) * a.hq + size_t(hk) * g + (rr - (rr / g) * g)) * kHeadDim + c;
+        if (a.out_dtype == OSCAR_F32)
+            static_cast<float *>(a.out)[idx] = acc[k];
+        else if (a.out_dtype == OSCAR_BF16)
+            static_cast<uint16_t *>(a.out)[idx] = bf16_bits_rn(acc[k]);
+        else
+            static_cast<__half *>(a.out)[idx] = __float2half_rn(acc[k]);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_extend_merge(const ExtendHistArgs &a, hipStream_t stream) {
+    const unsigned blocks = unsigned((a.n_new + kMergeTokens - 1) / kMergeTokens);
+    hipLaunchKernelGGL(extend_merge_kernel, dim3(blocks, a.hkv), dim3(512), 0, stream, a);
+    return hipGetLastError();
+}
 
 int64_t extend_bf16_blocks(const ExtendHistArgs &a) { return int64_t(a.row_blocks) * 3 * a.hkv; }
 

@@ -85,11 +85,16 @@ struct ExtendHistArgs {
     const uint16_t *newkv;        // [n_new][Hkv][2][128] rotated new tokens
     int32_t req;
     int32_t extra_item;           // work item of the new tokens
+    // merge and un-rotation
+    const float *r_v;             // [Hkv][128][128]
+    void *out;                    // [n_new][Hq][128] of out_dtype
+    int32_t out_dtype;
 };
 // Grid sizes of the two launches (row_blocks x items x hkv).
 int64_t extend_history_blocks(const ExtendHistArgs &a);
 int64_t extend_bf16_blocks(const ExtendHistArgs &a);
 hipError_t launch_extend_history(const ExtendHistArgs &a, hipStream_t stream);
 hipError_t launch_extend_bf16(const ExtendHistArgs &a, hipStream_t stream);
+hipError_t launch_extend_merge(const ExtendHistArgs &a, hipStream_t stream);
 
 }  // namespace oscar

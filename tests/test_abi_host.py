@@ -287,14 +287,19 @@ def test_extend_rejects_before_launch(over, status):
 
 def test_extend_workspace_size():
     lay = L()
-    n, P = 37, 100000
-    chunk, items = B.oscar_decode_plan(lay, [P] * n)
-    ws = B.oscar_extend_workspace_size(lay, n, P)
-    # the decode workspace of n rows at length P, one more work item per row
-    # (the new tokens), and the new tokens' BF16 rotated K and V
-    need = (n * 32 * 128 * 4 + n * 32 * 8 * 4 + n * (items + 1) * 32 * (128 + 2) * 4 + 256
-            + n * 8 * 2 * 128 * 2)
-    assert need <= ws <= need + 6 * 256
+    for n, P in ((37, 100000), (8192, 122880), (5, 300)):
+        hist = max(0, max(64, P - 256) - 64)
+        # about 4096 history workgroups of 128 / g = 32 rows x 8 KV heads
+        blocks = -(-n // 32)
+        want = max(1, -(-4096 // (blocks * 8)))
+        chunk = max(256, -(-(-(-hist // want)) // 32) * 32)
+        items = 2 + -(-hist // chunk) + 1
+        ws = B.oscar_extend_workspace_size(lay, n, P)
+        # the decode workspace of n rows at length P with `items` work items per
+        # row (the last one is the new tokens), and their BF16 rotated K and V
+        need = (n * 32 * 128 * 4 + n * 32 * 8 * 4 + n * items * 32 * (128 + 2) * 4 + 256
+                + n * 8 * 2 * 128 * 2)
+        assert need <= ws <= need + 6 * 256, (n, P)
     assert B.oscar_extend_workspace_size(lay, 1, 0) > 0
     with pytest.raises(B.OscarError):
         B.oscar_extend_workspace_size(lay, 0, 10)

@@ -26,9 +26,9 @@
  *   - Calls are re-entrant.  The only global state is a thread-local error
  *     message (oscar_last_error).  Two calls that write the same pool bytes
  *     concurrently race; serialise them on one stream.
- *   - Supported shapes: head_dim 128, group_size 32, 1 <= num_kv_heads <= 16,
- *     num_q_heads = g * num_kv_heads with 1 <= g <= 8.  Other shapes return
- *     OSCAR_ERR_UNSUPPORTED.
+ *   - Supported shapes: head_dim 128, group_size 32, 64 or 128,
+ *     1 <= num_kv_heads <= 16, num_q_heads = g * num_kv_heads with
+ *     1 <= g <= 8.  Other shapes return OSCAR_ERR_UNSUPPORTED.
  */
 #ifndef OSCAR_H
 #define OSCAR_H
@@ -56,7 +56,7 @@ typedef enum { OSCAR_F32 = 0, OSCAR_BF16 = 1, OSCAR_F16 = 2 } oscar_dtype;
 /* Shape of one attention layer's cache. */
 typedef struct {
     int32_t head_dim;       /* d; must be 128 */
-    int32_t group_size;     /* G, channels per scale/zero group; must be 32 */
+    int32_t group_size;     /* G, channels per scale/zero group: 32, 64 or 128 */
     int32_t num_kv_heads;   /* Hkv, 1..16 */
     int32_t num_q_heads;    /* Hq = g * Hkv, 1 <= g <= 8 */
     int32_t sink_tokens;    /* S, BF16 sink window (the pages use 64); 0..4096 */
@@ -68,13 +68,15 @@ typedef struct {
 /*
  * Cache storage.  Byte formats (little endian):
  *
- * records: [num_slots][Hkv * 96] bytes.  The record of a slot holds one
- *   96-byte head record per KV head, head h at byte 96 h:
+ * records: [num_slots][Hkv * B] bytes, B = 64 + 8 * (128 / G) (96 at G = 32,
+ *   80 at 64, 72 at 128; the smaller metadata is the lower bits per element
+ *   of the OSCAR page's summary).  The record of a slot holds one B-byte
+ *   head record per KV head, head h at byte B h, n_g = 128 / G:
  *     [0, 32)   K codes      [32, 64)  V codes
- *     [64, 80)  K (s, z)     [80, 96)  V (s, z)
+ *     [64, 64 + 4 n_g)  K (s, z)     [64 + 4 n_g, 64 + 8 n_g)  V (s, z)
  *   Codes: the 128 rotated channels, 2 bits each, four per byte, least
  *   significant bits first: byte j holds channels 4j .. 4j+3 at bit offsets
- *   0, 2, 4, 6.  (s, z): for each of the 4 groups of 32 contiguous rotated
+ *   0, 2, 4, 6.  (s, z): for each of the n_g groups of G contiguous rotated
  *   channels, fp16 scale s then fp16 zero z.  Element value = s * code + z.
  * sink:    [max_requests][S][Hkv][2][128] bf16 (2 = K, V), rotated basis,
  *          position p < S at index p.

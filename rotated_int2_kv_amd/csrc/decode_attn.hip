@@ -73,6 +73,7 @@ struct DecodeArgs {
     int32_t items;
     int32_t waves;     // KV heads per workgroup
     int32_t head_chunks;
+    int32_t group_size;
     // extend: every batch row is request fixed_req at length fixed_len, and
     // item extra_item reads the rotated new tokens 0 .. row (causal)
     int32_t fixed_req;        // -1 for decode
@@ -897,6 +898,167 @@ __global__ __launch_bounds__(64 * kPartialWaves) void partial_kernel(DecodeArgs 
     }
 }
 
+// History items of the lower-metadata layouts: groups of G = 64 or 128
+// channels (NG = 2 or 1 groups per head vector) and 80- or 72-byte head
+// records.  fp32 VALU, 64 tokens per step.  QK: lane = token, the 128 codes of
+// its K against q' in LDS, factored per group as s_g (q'_g . c_g) + z_g Q_g
+// (Q_g the group's sum of q').  PV: lane = channel pair, the step's V codes and
+// (s, z) staged in LDS, v = s c + z formed per token.
+constexpr int kLmChunk = 64;
+
+template <int NG>
+__global__ __launch_bounds__(64 * kPartialWaves) void hist_lowmeta_kernel(DecodeArgs a) {
+    constexpr int kRec = 2 * kCodeBytes + 8 * NG;          // head record bytes
+    constexpr int kG = kHeadDim / NG;                       // channels per group
+    __shared__ float qs_all[kPartialWaves][kMaxGroup][kHeadDim];
+    __shared__ float ps_all[kPartialWaves][kMaxGroup][kLmChunk];
+    __shared__ uint32_t vc_all[kPartialWaves][kLmChunk][kCodeBytes / 4];
+    __shared__ uint32_t vsz_all[kPartialWaves][kLmChunk][NG];
+    const int id = blockIdx.x;
+    const int hc = id % a.head_chunks;
+    const int rest = id / a.head_chunks;
+    const int b = rest % a.batch;
+    const int j = 2 + rest / a.batch;
+    int req = 0;
+    const int L = request_length(a, b, req);
+    int p0, p1;
+    item_range(a, L, j, p0, p1);
+    const int w = threadIdx.x >> 6;
+    const int hk = hc * kPartialWaves + w;
+    if (p0 >= p1 || hk >= a.hkv) return;                    // no workgroup barrier below
+    const int lane = threadIdx.x & 63;
+    const int g = a.g;
+    float(*qs)[kHeadDim] = qs_all[w];
+    float(*ps)[kLmChunk] = ps_all[w];
+    uint32_t(*vc)[kCodeBytes / 4] = vc_all[w];
+    uint32_t(*vsz)[NG] = vsz_all[w];
+    const size_t row0q = size_t(b) * a.hq + size_t(hk) * g;
+    for (int e = lane; e < g * kHeadDim; e += 64) qs[e / kHeadDim][e % kHeadDim] = a.qrot[row0q * kHeadDim + e];
+    float qg[kMaxGroup][NG];                                // group sums of q' (from the 32-channel sums)
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h)
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+            float sum = 0.0f;
+            if (h < g)
+#pragma unroll
+                for (int sub = 0; sub < kG / kGroup; ++sub) sum += a.qsum[(row0q + h) * 8 + gi * (kG / kGroup) + sub];
+            qg[h][gi] = sum;
+        }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    float m_run[kMaxGroup], l_lane[kMaxGroup], o0[kMaxGroup], o1[kMaxGroup];
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h) {
+        m_run[h] = -INFINITY;
+        l_lane[h] = 0.0f;
+        o0[h] = 0.0f;
+        o1[h] = 0.0f;
+    }
+    const int32_t *tab = a.req_to_slot + size_t(req) * a.r2s_stride;
+    const size_t rec_bytes = size_t(a.hkv) * kRec;
+    for (int cb = p0; cb < p1; cb += kLmChunk) {
+        const int cnt = min(kLmChunk, p1 - cb);
+        const int slot = lane < cnt ? tab[cb + lane] : -1;
+        const bool ok = slot >= 0 && slot < a.num_slots;
+        const uint8_t *base = ok ? a.records + size_t(slot) * rec_bytes + size_t(hk) * kRec : a.zero_rec;
+        u32x2 kc[4], vv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            kc[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(base) + i);
+            vv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(base + kCodeBytes) + i);
+        }
+        uint32_t ksz[NG];
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+            ksz[gi] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(base + 2 * kCodeBytes) + gi);
+            vsz[lane][gi] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(base + 2 * kCodeBytes + 4 * NG) + gi);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            vc[lane][2 * i] = vv[i][0];
+            vc[lane][2 * i + 1] = vv[i][1];
+        }
+        // ---- QK: lane = token
+        float dot[kMaxGroup][NG];
+#pragma unroll
+        for (int h = 0; h < kMaxGroup; ++h)
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) dot[h][gi] = 0.0f;
+#pragma unroll
+        for (int wd = 0; wd < 8; ++wd) {                    // 16 channels per code word
+            const uint32_t cw = kc[wd >> 1][wd & 1];
+            const int gi = (16 * wd) / kG;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float c = float((cw >> (2 * e)) & 3u);
+#pragma unroll
+                for (int h = 0; h < kMaxGroup; ++h)
+                    if (h < g) dot[h][gi] = fmaf(qs[h][16 * wd + e], c, dot[h][gi]);
+            }
+        }
+        float alpha[kMaxGroup];
+#pragma unroll
+        for (int h = 0; h < kMaxGroup; ++h) {
+            float x = 0.0f;
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                const float sg = __half2float(__ushort_as_half(uint16_t(ksz[gi])));
+                const float zg = __half2float(__ushort_as_half(uint16_t(ksz[gi] >> 16)));
+                x = fmaf(sg, dot[h][gi], x);
+                x = fmaf(zg, qg[h][gi], x);
+            }
+            x = ok ? x : -INFINITY;
+            const float mx = wave_max(x);
+            const float m_new = fmaxf(m_run[h], mx);
+            alpha[h] = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run[h] - m_new);
+            m_run[h] = m_new;
+            const float p = x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x - m_new);
+            l_lane[h] = fmaf(l_lane[h], alpha[h], p);
+            if (h < g) ps[h][lane] = p;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // ---- PV: lane = channels 2 lane, 2 lane + 1
+#pragma unroll
+        for (int h = 0; h < kMaxGroup; ++h) {
+            o0[h] *= alpha[h];
+            o1[h] *= alpha[h];
+        }
+        const int cword = lane >> 3, cshift = 4 * (lane & 7), cg = (2 * lane) / kG;
+        for (int u = 0; u < cnt; ++u) {
+            const uint32_t cw = vc[u][cword] >> cshift;
+            const uint32_t szw = vsz[u][cg];
+            const float s = __half2float(__ushort_as_half(uint16_t(szw)));
+            const float z = __half2float(__ushort_as_half(uint16_t(szw >> 16)));
+            const float v0 = fmaf(s, float(cw & 3u), z), v1 = fmaf(s, float((cw >> 2) & 3u), z);
+#pragma unroll
+            for (int h = 0; h < kMaxGroup; ++h) {
+                if (h < g) {
+                    const float p = ps[h][u];
+                    o0[h] = fmaf(p, v0, o0[h]);
+                    o1[h] = fmaf(p, v1, o1[h]);
+                }
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    const size_t row0 = (size_t(b) * a.items + j) * a.hq + size_t(hk) * g;
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h) {
+        if (h >= g) break;
+        const float l = wave_sum(l_lane[h]);
+        if (lane == 0) {
+            a.part_ml[(row0 + h) * 2 + 0] = m_run[h];
+            a.part_ml[(row0 + h) * 2 + 1] = l;
+        }
+        float2 *dst = reinterpret_cast<float2 *>(a.part_o + (row0 + h) * kHeadDim) + lane;
+        *dst = make_float2(o0[h], o1[h]);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // 3. merge + un-rotation
 // ---------------------------------------------------------------------------
@@ -1117,6 +1279,7 @@ DecodeArgs make_args(const oscar_layout *layout, const oscar_pool *pool, const v
     a.items = plan.items;
     a.waves = kPartialWaves;
     a.head_chunks = (a.hkv + kPartialWaves - 1) / kPartialWaves;
+    a.group_size = layout->group_size;
     a.fixed_req = -1;
     a.fixed_len = 0;
     a.extra_item = plan.extra_item;
@@ -1145,6 +1308,30 @@ oscar_status launch_decode(const DecodeArgs &a, const DecodePlan &plan, hipStrea
         }
         e = launch_extend_bf16(*xh, stream);
         if (e != hipSuccess) return fail(OSCAR_ERR_HIP, std::string("extend bf16 launch: ") + hipGetErrorString(e));
+    } else if (a.group_size != kGroup) {
+        // lower-metadata layouts: the BF16 windows (items 0, 1) on partial_kernel,
+        // the history items on hist_lowmeta_kernel
+        const int bf_blocks = 2 * a.batch * a.head_chunks;
+        switch (a.g) {
+            case 1: e = launch_partial<1>(a, bf_blocks, stream); break;
+            case 2: e = launch_partial<2>(a, bf_blocks, stream); break;
+            case 3: e = launch_partial<3>(a, bf_blocks, stream); break;
+            case 4: e = launch_partial<4>(a, bf_blocks, stream); break;
+            case 5: e = launch_partial<5>(a, bf_blocks, stream); break;
+            case 6: e = launch_partial<6>(a, bf_blocks, stream); break;
+            case 7: e = launch_partial<7>(a, bf_blocks, stream); break;
+            default: e = launch_partial<8>(a, bf_blocks, stream); break;
+        }
+        if (e != hipSuccess) return fail(OSCAR_ERR_HIP, std::string("partial launch: ") + hipGetErrorString(e));
+        const int h_blocks = (plan.items - 2) * a.batch * a.head_chunks;
+        if (h_blocks > 0 && a.num_slots > 0) {
+            if (a.group_size == 64)
+                hipLaunchKernelGGL(hist_lowmeta_kernel<2>, dim3(h_blocks), dim3(64 * kPartialWaves), 0, stream, a);
+            else
+                hipLaunchKernelGGL(hist_lowmeta_kernel<1>, dim3(h_blocks), dim3(64 * kPartialWaves), 0, stream, a);
+            e = hipGetLastError();
+            if (e != hipSuccess) return fail(OSCAR_ERR_HIP, std::string("history launch: ") + hipGetErrorString(e));
+        }
     } else {
         switch (a.g) {
             case 1: e = launch_partial<1>(a, blocks, stream); break;
@@ -1209,6 +1396,7 @@ extern "C" oscar_status oscar_extend_attn(hipStream_t stream, const oscar_layout
     oscar_status st = check_decode_common(layout, pool, q, q_dtype, req_to_slot, R_K, R_V, sm_scale, out,
                                           out_dtype);
     if (st != OSCAR_OK) return st;
+    if (layout->group_size != kGroup) return fail(OSCAR_ERR_UNSUPPORTED, "extend supports group_size 32");
     if (!k_new || !v_new) return fail(OSCAR_ERR_INVALID_ARG, "a required pointer is null");
     if (kv_dtype != OSCAR_F32 && kv_dtype != OSCAR_BF16 && kv_dtype != OSCAR_F16)
         return fail(OSCAR_ERR_INVALID_ARG, "kv_dtype must be F32, BF16 or F16");

@@ -27,8 +27,12 @@ oscar_status ok();
 // Full validation of a layout (shape support included).
 oscar_status check_layout(const oscar_layout *lay);
 
+// Head record of group size G: K codes, V codes, then (s, z) of K and of V per
+// group: 96 bytes at G = 32, 80 at 64, 72 at 128.
+inline int head_record_bytes(int group_size) { return 2 * kCodeBytes + 2 * 4 * (kHeadDim / group_size); }
+
 inline int64_t record_bytes(const oscar_layout &lay) {
-    return static_cast<int64_t>(lay.num_kv_heads) * kHeadRecord;
+    return static_cast<int64_t>(lay.num_kv_heads) * head_record_bytes(lay.group_size);
 }
 
 // Split-K plan of one decode call (pure function of the host lengths).

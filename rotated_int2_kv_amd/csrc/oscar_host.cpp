@@ -30,7 +30,8 @@ oscar_status check_layout(const oscar_layout *lay) {
         return fail(OSCAR_ERR_UNSUPPORTED, "head_dim must be 128");
     if (lay->head_dim % lay->group_size != 0)
         return fail(OSCAR_ERR_INVALID_ARG, "group_size must divide head_dim");
-    if (lay->group_size != kGroup) return fail(OSCAR_ERR_UNSUPPORTED, "group_size must be 32");
+    if (lay->group_size != 32 && lay->group_size != 64 && lay->group_size != 128)
+        return fail(OSCAR_ERR_UNSUPPORTED, "group_size must be 32, 64 or 128");
     if (lay->num_q_heads % lay->num_kv_heads != 0)
         return fail(OSCAR_ERR_INVALID_ARG, "num_q_heads must be a multiple of num_kv_heads");
     if (lay->num_kv_heads > kMaxKvHeads)
@@ -204,7 +205,7 @@ size_t oscar_pool_bytes(const oscar_layout *layout, int32_t part) {
     if (check_layout(layout) != OSCAR_OK) return 0;
     const size_t hkv = size_t(layout->num_kv_heads);
     switch (part) {
-        case 0: return size_t(layout->num_slots) * hkv * kHeadRecord;
+        case 0: return size_t(layout->num_slots) * size_t(record_bytes(*layout));
         case 1: return size_t(layout->max_requests) * layout->sink_tokens * hkv * 2 * kHeadDim * 2;
         case 2: return size_t(layout->max_requests) * layout->recent_tokens * hkv * 2 * kHeadDim * 2;
         default: fail(OSCAR_ERR_INVALID_ARG, "part must be 0, 1 or 2"); return 0;

@@ -10,7 +10,9 @@
 // accumulated in fp32 on the matrix cores.  Tiles of 16 tokens are staged
 // through LDS as the B operand (x^T), and each lane ends up with 8 contiguous
 // rotated channels of one token, which it quantises, packs into 16 bits and
-// stores.  Group min/max need two cross-lane steps (the 4 lanes of a token).
+// stores.  Group min/max need two cross-lane steps (the 4 lanes of a token);
+// with groups of 64 or 128 channels (NGW = 2 or 4 waves per group) the waves
+// of a group also exchange their minima and maxima through LDS.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
@@ -70,9 +72,10 @@ __device__ __forceinline__ void split3(float x, uint16_t &a, uint16_t &b, uint16
     c = bf16_bits_rn(r2);
 }
 
-template <int XT>
+template <int XT, int NGW>
 __global__ __launch_bounds__(kThreads) void quant_append_kernel(AppendArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds_buf[2][XT * kPlaneBytes];
+    __shared__ float2 grp_stat[kWaves][kTile];             // per wave and token: (min, max)
 
     // XCD-aware block order: blocks are dealt round-robin to the 8 XCDs, so
     // all 2*Hkv workgroups of one token chunk land on the same XCD and its L2
@@ -171,7 +174,9 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(AppendArgs a) {
         }
     };
 
-    const int64_t rec_bytes = int64_t(a.hkv) * kHeadRecord;
+    constexpr int kHeadRec = 2 * kCodeBytes + 2 * 4 * (kWaves / NGW);     // head record of this group size
+    constexpr int kSzTensor = 4 * (kWaves / NGW);                          // (s, z) bytes per tensor
+    const int64_t rec_bytes = int64_t(a.hkv) * kHeadRec;
     // kDepth tiles of input in flight in registers (the waits are the
     // compiler's); the LDS tile is double-buffered, so one barrier per tile
     // both publishes the new tile and retires the buffer it overwrites next
@@ -244,6 +249,18 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(AppendArgs a) {
         hi = fmaxf(hi, __shfl_xor(hi, 16));
         lo = fminf(lo, __shfl_xor(lo, 32));
         hi = fmaxf(hi, __shfl_xor(hi, 32));
+        if constexpr (NGW > 1) {
+            // the other waves of this group: every wave passes here (no lane has
+            // left the iteration yet)
+            if (kb == 0) grp_stat[w][n] = make_float2(lo, hi);
+            __syncthreads();
+#pragma unroll
+            for (int o = 1; o < NGW; ++o) {
+                const float2 st = grp_stat[(w & ~(NGW - 1)) | ((w + o) & (NGW - 1))][n];
+                lo = fminf(lo, st.x);
+                hi = fmaxf(hi, st.y);
+            }
+        }
 
         const int tok = tb + n;
         const int req = req0, pos = pos0, slot = slot0, L = len0;
@@ -299,11 +316,11 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(AppendArgs a) {
             const uint32_t c = (upper ? 2u : 0u) + uint32_t(xc >= (upper ? u2 : u0));
             packed |= c << (2 * j);
         }
-        uint8_t *rec = a.records + int64_t(slot) * rec_bytes + h * kHeadRecord;
+        uint8_t *rec = a.records + int64_t(slot) * rec_bytes + h * kHeadRec;
         *reinterpret_cast<uint16_t *>(rec + t * kCodeBytes + 8 * w + 2 * kb) = uint16_t(packed);
-        if (kb == 0) {
+        if (kb == 0 && (w & (NGW - 1)) == 0) {            // one writer per group
             const uint32_t sz = uint32_t(__half_as_ushort(s)) | (uint32_t(__half_as_ushort(z)) << 16);
-            *reinterpret_cast<uint32_t *>(rec + 2 * kCodeBytes + t * kSzBytes + 4 * w) = sz;
+            *reinterpret_cast<uint32_t *>(rec + 2 * kCodeBytes + t * kSzTensor + 4 * (w / NGW)) = sz;
         }
         if (pos >= L - a.recent_tokens) {
             uint16_t *dst = a.recent +
@@ -312,6 +329,19 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(AppendArgs a) {
             *reinterpret_cast<u32x4 *>(dst) = bf;
         }
     }
+    }
+}
+
+// the kernel for (input dtype, group size)
+const void *append_kernel(oscar_dtype in_dtype, int group_size) {
+    const bool bf = in_dtype == OSCAR_BF16;
+    switch (group_size) {
+        case 64: return bf ? reinterpret_cast<const void *>(quant_append_kernel<1, 2>)
+                           : reinterpret_cast<const void *>(quant_append_kernel<3, 2>);
+        case 128: return bf ? reinterpret_cast<const void *>(quant_append_kernel<1, 4>)
+                            : reinterpret_cast<const void *>(quant_append_kernel<3, 4>);
+        default: return bf ? reinterpret_cast<const void *>(quant_append_kernel<1, 1>)
+                           : reinterpret_cast<const void *>(quant_append_kernel<3, 1>);
     }
 }
 
@@ -352,8 +382,7 @@ extern "C" oscar_status oscar_quant_append(hipStream_t stream, const oscar_layou
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return fail(OSCAR_ERR_HIP, "querying the device failed");
-        const void *kern = in_dtype == OSCAR_BF16 ? reinterpret_cast<const void *>(quant_append_kernel<1>)
-                                                  : reinterpret_cast<const void *>(quant_append_kernel<3>);
+        const void *kern = append_kernel(in_dtype, layout->group_size);
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, 0) != hipSuccess)
             return fail(OSCAR_ERR_HIP, "occupancy query failed");
         const int slots = std::max(1, cus * std::max(1, per_cu));
@@ -392,11 +421,10 @@ extern "C" oscar_status oscar_quant_append(hipStream_t stream, const oscar_layou
         if (hipEventRecord(opts->kernel_begin, stream) != hipSuccess)
             return fail(OSCAR_ERR_HIP, "hipEventRecord failed");
     }
-    if (in_dtype == OSCAR_BF16)
-        hipLaunchKernelGGL(quant_append_kernel<1>, dim3(blocks), dim3(kThreads), 0, stream, args);
-    else
-        hipLaunchKernelGGL(quant_append_kernel<3>, dim3(blocks), dim3(kThreads), 0, stream, args);
-    hipError_t e = hipGetLastError();
+    void *kargs[] = {&args};
+    hipError_t e = hipLaunchKernel(append_kernel(in_dtype, layout->group_size), dim3(blocks), dim3(kThreads),
+                                   kargs, 0, stream);
+    if (e == hipSuccess) e = hipGetLastError();
     if (e != hipSuccess) return fail(OSCAR_ERR_HIP, std::string("quant_append launch: ") + hipGetErrorString(e));
     if (opts && opts->kernel_end) {
         if (hipEventRecord(opts->kernel_end, stream) != hipSuccess)

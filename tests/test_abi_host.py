@@ -104,7 +104,7 @@ def L(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=64), B.OSCAR_ERR_UNSUPPORTED),
     (dict(head_dim=0), B.OSCAR_ERR_INVALID_ARG),
-    (dict(group_size=64), B.OSCAR_ERR_UNSUPPORTED),
+    (dict(group_size=16), B.OSCAR_ERR_UNSUPPORTED),
     (dict(group_size=48), B.OSCAR_ERR_INVALID_ARG),
     (dict(num_q_heads=30), B.OSCAR_ERR_INVALID_ARG),
     (dict(num_q_heads=72), B.OSCAR_ERR_UNSUPPORTED),
@@ -360,3 +360,15 @@ def test_bf16_append_validation():
     assert f(None, ctypes.byref(lay.c()), FAKE, FAKE, FAKE, B.OSCAR_BF16, -1, FAKE) == B.OSCAR_ERR_INVALID_ARG
     assert f(None, ctypes.byref(lay.c()), None, FAKE, FAKE, B.OSCAR_BF16, 4, FAKE) == B.OSCAR_ERR_INVALID_ARG
     assert f(None, ctypes.byref(lay.c()), FAKE, FAKE, FAKE, 3, 4, FAKE) == B.OSCAR_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("G,head_record", [(32, 96), (64, 80), (128, 72)])
+def test_lower_metadata_layouts(G, head_record):
+    """Groups of 32, 64 and 128 channels: K and V codes plus one (s, z) per group."""
+    lay = L(group_size=G)
+    B.oscar_layout_check(lay)
+    assert B.oscar_pool_bytes(lay, 0) == 1000 * 8 * head_record
+
+
+def test_extend_rejects_lower_metadata_layouts():
+    assert _extend(L(group_size=64), 8, 100) == B.OSCAR_ERR_UNSUPPORTED

@@ -204,3 +204,52 @@ def test_decode_skips_out_of_range_slot_ids():
             o_rot = attention.attention(qr, kv[keep, hk, 0, :], kv[keep, hk, 1, :], w.head_dim ** -0.5)
             o_ref[b, hk * g:(hk + 1) * g, :] = o_rot @ rv[hk].T
     _compare(o_gpu, o_ref, "out-of-range slots")
+
+
+@pytest.mark.parametrize("G", [64, 128])
+@pytest.mark.parametrize("wname,lens,chunk", [
+    ("tiny", (1024,), 0),
+    ("decode_small", (1500, 777, 3001, 321), 0),
+    ("decode_small", (1500, 777, 3001, 321), 96),
+    ("mixed_small", (1, 63, 64, 65, 319, 320, 321, 352, 353, 385), 32),
+])
+def test_decode_lower_metadata(G, wname, lens, chunk):
+    """Groups of 64 and 128 channels (80- and 72-byte head records) decode the
+    oracle-written pool to the same bar."""
+    w = workloads.custom(wname, batch=len(lens), seq_lens=tuple(lens), group_size=G)
+    lay_b, lay_o, opool, table, r_k, r_v = _oracle_pool_case(w, lens)
+    qh, qd = _queries(w, len(lens), 1, "bf16")
+    gs.say(f"decode G={G} {wname} lens={lens} chunk={chunk}")
+    o_gpu = _gpu_decode(lay_b, gs.upload_oracle_pool(opool), qd, lens, table, r_k, r_v,
+                        history_chunk=chunk)
+    o_ref = attention.decode(opool, lay_o, qh, np.arange(len(lens)), lens, table, r_k, r_v,
+                             w.head_dim ** -0.5)
+    _compare(o_gpu, o_ref, f"G={G}")
+
+
+@pytest.mark.parametrize("G", [64, 128])
+def test_decode_lower_metadata_gqa_and_bad_slots(G):
+    w = workloads.custom("layer_small", num_kv_heads=2, num_q_heads=12, batch=2,
+                         seq_lens=(900, 1333), seed=77, group_size=G)
+    lens = w.seq_lens
+    lay_b, lay_o, opool, table, r_k, r_v = _oracle_pool_case(w, lens, seed=4)
+    table = table.copy()
+    table[0, 100:140] = -1
+    table[1, 500] = lay_b.num_slots + 5
+    qh, qd = _queries(w, 2, 6, "bf16")
+    gs.say(f"decode G={G} g=6 with unusable slots")
+    o_gpu = _gpu_decode(lay_b, gs.upload_oracle_pool(opool), qd, lens, table, r_k, r_v)
+    # the oracle leaves unusable history slots out: emulate by decoding the usable positions
+    o_ref = np.zeros_like(o_gpu)
+    for b in range(2):
+        L = lens[b]
+        kv = cache.gather(opool, lay_o, b, L, np.where(table[b] >= 0, table[b], 0).clip(max=lay_b.num_slots - 1))
+        keep = np.ones(L, bool)
+        hist = np.arange(L)
+        keep &= ~((hist >= w.sink) & (hist < max(w.sink, L - w.recent)) &
+                  ((table[b][:L] < 0) | (table[b][:L] >= lay_b.num_slots)))
+        for hk in range(2):
+            qrot = qh[b, 6 * hk:6 * hk + 6].astype(np.float64) @ r_k[hk].astype(np.float64)
+            o_rot = attention.attention(qrot, kv[keep, hk, 0], kv[keep, hk, 1], 128 ** -0.5)
+            o_ref[b, 6 * hk:6 * hk + 6] = o_rot @ r_v[hk].astype(np.float64).T
+    _compare(o_gpu, o_ref, f"G={G} bad slots")

@@ -175,3 +175,40 @@ def test_append_skips_out_of_range_tokens_and_handles_tiny_calls():
     assert out is not None
     B.oscar_quant_append(lay_b, pool, kd[:0], vd[:0], gs.dev(req[:0]), gs.dev(pos[:0]),
                          gs.dev(slots[:0]), gs.dev(lens), gs.dev(r_k), gs.dev(r_v))
+
+
+@pytest.mark.parametrize("G", [64, 128])
+@pytest.mark.parametrize("kind,dtype", [("identity", None), ("signed_perm", None), ("signed_perm", "f32")])
+@pytest.mark.parametrize("wname,lens", [("tiny", (1024,)), ("layer_small", (700, 333, 40))])
+def test_append_lower_metadata_bit_exact(G, kind, dtype, wname, lens):
+    """Groups of 64 and 128 channels (one (s, z) per group: 80- and 72-byte head
+    records) with exactly representable rotations: every byte equals the oracle's."""
+    w = workloads.custom(wname, group_size=G)
+    r_k, r_v = gs.exact_rotations(kind, w.num_kv_heads)
+    out = _run_append(w, lens, r_k, r_v, dtype=dtype)
+    lay_o = out["lay_o"]
+    assert lay_o.head_record_bytes == {64: 80, 128: 72}[G]
+    opool = cache.new_pool(lay_o)
+    cache.append(opool, lay_o, out["k"], out["v"], out["req"], out["pos"], out["slots"],
+                 np.asarray(lens), r_k, r_v)
+    rec, sink, recent = gs.pool_host(out["pool"], lay_o)
+    assert np.array_equal(rec, opool.records)
+    assert np.array_equal(sink, opool.sink)
+    assert np.array_equal(recent, opool.recent)
+
+
+@pytest.mark.parametrize("G", [64, 128])
+def test_append_lower_metadata_oscar_rotation_matches_where_unique(G):
+    w = workloads.custom("layer_small", group_size=G)
+    r_k, r_v = gs.product_rotations(w)
+    out = _run_append(w, (2413,), r_k, r_v)
+    lay_o = out["lay_o"]
+    ork, orv = gs.oracle_rotations(w)
+    opool = cache.new_pool(lay_o)
+    cache.append(opool, lay_o, out["k"], out["v"], out["req"], out["pos"], out["slots"],
+                 np.asarray([2413]), ork, orv)
+    rec, _, _ = gs.pool_host(out["pool"], lay_o)
+    pool_slots = out["slots"][out["pos"] >= lay_o.sink]
+    same = (rec[pool_slots] == opool.records[pool_slots]).mean()
+    gs.say(f"  G={G} byte agreement {same:.6f}")
+    assert same > 0.999

@@ -1396,7 +1396,6 @@ extern "C" oscar_status oscar_extend_attn(hipStream_t stream, const oscar_layout
     oscar_status st = check_decode_common(layout, pool, q, q_dtype, req_to_slot, R_K, R_V, sm_scale, out,
                                           out_dtype);
     if (st != OSCAR_OK) return st;
-    if (layout->group_size != kGroup) return fail(OSCAR_ERR_UNSUPPORTED, "extend supports group_size 32");
     if (!k_new || !v_new) return fail(OSCAR_ERR_INVALID_ARG, "a required pointer is null");
     if (kv_dtype != OSCAR_F32 && kv_dtype != OSCAR_BF16 && kv_dtype != OSCAR_F16)
         return fail(OSCAR_ERR_INVALID_ARG, "kv_dtype must be F32, BF16 or F16");
@@ -1449,6 +1448,7 @@ extern "C" oscar_status oscar_extend_attn(hipStream_t stream, const oscar_layout
     xh.r_v = R_V;
     xh.out = out;
     xh.out_dtype = out_dtype;
+    xh.group_size = layout->group_size;
     if (extend_history_blocks(xh) > INT32_MAX || extend_bf16_blocks(xh) > INT32_MAX)
         return fail(OSCAR_ERR_UNSUPPORTED, "new tokens x work items exceeds one launch grid");
 

@@ -211,10 +211,17 @@ __device__ __forceinline__ void flash_step(const _Float16 (*kd)[kTile][kKdStride
 
 // At most 128 VGPRs (launch bound of 4 waves per SIMD): two workgroups per
 // compute unit overlap one another's dequantisation, barriers and MFMA work.
+// NG = groups per head vector (4, 2, 1 for G = 32, 64, 128): head records of
+// 96, 80 or 72 bytes, staged in 16-byte units (8-byte units for 72).
+template <int NG>
 __global__ __launch_bounds__(kThreads, 4) void extend_hist_kernel(ExtendHistArgs a) {
+    constexpr int kRec = 2 * kCodeBytes + 8 * NG;
+    constexpr int kUnit = kRec % 16 == 0 ? 16 : 8;
+    constexpr int kUnits = kRec / kUnit;
+    using Unit = std::conditional_t<kUnit == 16, u32x4, u32x2>;
     // two of everything: tile k is computed from one buffer while tile k + 1
     // is dequantised into the other, one workgroup barrier per tile
-    __shared__ __attribute__((aligned(16))) uint8_t raw_all[2][kTile * kHeadRecord];
+    __shared__ __attribute__((aligned(16))) uint8_t raw_all[2][kTile * kRec];
     __shared__ __attribute__((aligned(16))) uint8_t flag_all[2][kTile];
     __shared__ __attribute__((aligned(16))) _Float16 kd_all[2][2][kTile][kKdStride];
     __shared__ __attribute__((aligned(16))) _Float16 vt_all[2][1][kHeadDim][kVtStride];
@@ -243,30 +250,29 @@ __global__ __launch_bounds__(kThreads, 4) void extend_hist_kernel(ExtendHistArgs
 #pragma unroll
     for (int n = 0; n < 8; ++n) o[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // ---- producers: thread < 192 stages 16 bytes (unit pu) of token pt's head record
-    const bool producer = tid < kTile * 6;
-    const int pt = tid / 6;
-    const int pu = tid - 6 * pt;
-    const size_t rec_bytes = size_t(a.hkv) * kHeadRecord;
+    // ---- producers: thread < 32 kUnits stages unit pu of token pt's head record
+    const bool producer = tid < kTile * kUnits;
+    const int pt = tid / kUnits;
+    const int pu = tid - kUnits * pt;
+    const size_t rec_bytes = size_t(a.hkv) * kRec;
     auto slot_of = [&](int c) -> int {
         const int p = c + pt;
         return (producer && p < p1) ? __builtin_nontemporal_load(a.slot_row + p) : -1;
     };
     auto usable = [&](int slot) { return slot >= 0 && slot < a.num_slots; };
-    auto load_rec = [&](int slot) -> u32x4 {
-        const uint8_t *base = usable(slot) ? a.records + size_t(slot) * rec_bytes + size_t(hk) * kHeadRecord
-                                           : a.zero_rec;
-        return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(base + 16 * pu));
+    auto load_rec = [&](int slot) -> Unit {
+        const uint8_t *base = usable(slot) ? a.records + size_t(slot) * rec_bytes + size_t(hk) * kRec : a.zero_rec;
+        return __builtin_nontemporal_load(reinterpret_cast<const Unit *>(base + kUnit * pu));
     };
     // records of the next tile to stage, its usability, and the slot ids of the one after
     int slot_cur = slot_of(p0);
-    u32x4 rec = producer ? load_rec(slot_cur) : u32x4{0u, 0u, 0u, 0u};
+    Unit rec = producer ? load_rec(slot_cur) : Unit{};
     bool ok_cur = usable(slot_cur);
     int slot_nxt = slot_of(p0 + kTile);
     // stage the records held in `rec` (tile at cb) into buffer b, then start loading the next
     auto stage = [&](int b, int cb) {
         if (producer) {
-            *reinterpret_cast<u32x4 *>(raw_all[b] + pt * kHeadRecord + 16 * pu) = rec;
+            *reinterpret_cast<Unit *>(raw_all[b] + pt * kRec + kUnit * pu) = rec;
             if (pu == 0) flag_all[b][pt] = ok_cur ? 1 : 0;
         }
         if (cb + kTile < p1) {
@@ -284,8 +290,8 @@ __global__ __launch_bounds__(kThreads, 4) void extend_hist_kernel(ExtendHistArgs
         // then one byte-select (v_perm) per two channels picks their levels
         {
             const int t = tid >> 4, part = tid & 15;
-            const uint32_t cw = *reinterpret_cast<const uint16_t *>(raw + t * kHeadRecord + 2 * part);
-            const uint32_t szw = *reinterpret_cast<const uint32_t *>(raw + t * kHeadRecord + 64 + 4 * (part >> 2));
+            const uint32_t cw = *reinterpret_cast<const uint16_t *>(raw + t * kRec + 2 * part);
+            const uint32_t szw = *reinterpret_cast<const uint32_t *>(raw + t * kRec + 64 + 4 * (part * NG / 16));
             const float s = sz_s(szw) * kDqScale, z = sz_z(szw) * kDqScale;     // exact
             uint32_t h01, l01, h23, l23;
             split2(z, s + z, h01, l01);                       // s + z: fmaf(s, 1, z)
@@ -308,13 +314,13 @@ __global__ __launch_bounds__(kThreads, 4) void extend_hist_kernel(ExtendHistArgs
         // value; 8-byte row writes (at most 2 lanes of 16 per bank)
         {
             const int cp = tid & 63, tq = tid >> 6;
-            const int byte = 32 + (cp >> 1), sh = 4 * (cp & 1), sz_off = 80 + 4 * (cp >> 4);
+            const int byte = 32 + (cp >> 1), sh = 4 * (cp & 1), sz_off = 64 + 4 * NG + 4 * (cp * NG / 64);
             float x0[4], x1[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int t = 4 * tq + k;
-                const uint32_t c = uint32_t(raw[t * kHeadRecord + byte]) >> sh;
-                const uint32_t szw = *reinterpret_cast<const uint32_t *>(raw + t * kHeadRecord + sz_off);
+                const uint32_t c = uint32_t(raw[t * kRec + byte]) >> sh;
+                const uint32_t szw = *reinterpret_cast<const uint32_t *>(raw + t * kRec + sz_off);
                 const float s = sz_s(szw) * kDqScale, z = sz_z(szw) * kDqScale;
                 x0[k] = fmaf(s, float(c & 3u), z);
                 x1[k] = fmaf(s, float((c >> 2) & 3u), z);
@@ -562,7 +568,11 @@ int64_t extend_history_blocks(const ExtendHistArgs &a) {
 hipError_t launch_extend_history(const ExtendHistArgs &a, hipStream_t stream) {
     const int64_t blocks = extend_history_blocks(a);
     if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL(extend_hist_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a);
+    switch (a.group_size) {
+        case 64: hipLaunchKernelGGL(extend_hist_kernel<2>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a); break;
+        case 128: hipLaunchKernelGGL(extend_hist_kernel<1>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a); break;
+        default: hipLaunchKernelGGL(extend_hist_kernel<4>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a); break;
+    }
     return hipGetLastError();
 }
 

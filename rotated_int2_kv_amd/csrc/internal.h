@@ -93,6 +93,7 @@ struct ExtendHistArgs {
     const float *r_v;             // [Hkv][128][128]
     void *out;                    // [n_new][Hq][128] of out_dtype
     int32_t out_dtype;
+    int32_t group_size;
 };
 // Grid sizes of the two launches (row_blocks x items x hkv).
 int64_t extend_history_blocks(const ExtendHistArgs &a);

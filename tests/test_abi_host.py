@@ -368,7 +368,3 @@ def test_lower_metadata_layouts(G, head_record):
     lay = L(group_size=G)
     B.oscar_layout_check(lay)
     assert B.oscar_pool_bytes(lay, 0) == 1000 * 8 * head_record
-
-
-def test_extend_rejects_lower_metadata_layouts():
-    assert _extend(L(group_size=64), 8, 100) == B.OSCAR_ERR_UNSUPPORTED

@@ -139,3 +139,12 @@ def test_extend_then_append_matches_decode():
     err = pt.normwise_rel(out.cpu().numpy(), o_ext)
     gs.say(f"  extend vs decode after append: {err.max():.3e}")
     assert err.max() <= 1e-3
+
+
+@pytest.mark.parametrize("G", [64, 128])
+@pytest.mark.parametrize("wname,P,n", [("tiny", 1000, 16), ("layer_small", 2413, 100),
+                                       ("layer_small", 300, 37)])
+def test_extend_lower_metadata(G, wname, P, n):
+    """Groups of 64 and 128 channels (80- and 72-byte head records)."""
+    w = workloads.custom(wname, group_size=G)
+    _run(w, P, n, seed=P + n + G)

@@ -12,7 +12,8 @@ Printed: one JSON line with KV tokens/s (sum of context lengths / step time),
 the split-K kernel's achieved bandwidth against the HBM roofline (timed live
 with HIP events on the launch stream), the quant-append throughput of the
 131,072-token append workload, the same decode step on a BF16 paged cache
-(the baseline of the OSCAR page's speed-ups) with the INT2/BF16 ratio, one
+(the baseline of the OSCAR page's speed-ups) with the INT2/BF16 ratio, the
+same step with one scale and zero per 64 and per 128 channels, one
 extend call (an 8,192-token prefill chunk over a 122,880-token cached
 prefix), one calibration-statistics call (C_Q Gram sums of 131,072 query
 tokens), and the fp64 CPU oracle's rate on a bounded sample of the same
@@ -86,13 +87,13 @@ def measured_traffic(path=TRAFFIC_FILE, sources=KERNEL_SOURCES):
     return int(val.group(1))
 
 
-def decode_kernel_bytes(lens, hkv, sink=64, recent=256):
-    """Algorithmic bytes read by the split-K kernel for one decode step."""
+def decode_kernel_bytes(lens, hkv, sink=64, recent=256, head_record=HISTORY_BYTES_PER_TOKEN_HEAD):
+    """Algorithmic bytes read by the split-K kernels for one decode step."""
     total = 0
     for L in lens:
         bf16 = min(L, sink + recent)
         hist = L - bf16
-        total += hist * (hkv * HISTORY_BYTES_PER_TOKEN_HEAD + SLOT_BYTES_PER_TOKEN)
+        total += hist * (hkv * head_record + SLOT_BYTES_PER_TOKEN)
         total += bf16 * hkv * BF16_BYTES_PER_TOKEN_HEAD
     return total
 
@@ -348,6 +349,69 @@ def run_extend(args, torch, B, workloads):
                 output_finite=bool(torch.isfinite(out.float()).all().item()))
 
 
+def run_lower_metadata(args, torch, B, workloads, group_size):
+    """The decode step of the decode workload with one (s, z) per group_size
+    channels (80- or 72-byte head records): append one token per request, then
+    decode.  Fewer steps than the headline run (a comparison line)."""
+    w = workloads.custom(args.workload, group_size=group_size)
+    lens = np.asarray(w.seq_lens, np.int32)
+    bsz, hkv = w.batch, w.num_kv_heads
+    lay = B.Layout(128, group_size, hkv, w.num_q_heads, w.sink, w.recent, num_slots=w.num_slots,
+                   max_requests=bsz)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    rk, rv = build_rotations(B, w)
+    rk_d, rv_d = dev(rk), dev(rv)
+    slots = workloads.slot_table(w)
+    table = dev(workloads.req_to_slot_matrix(w, slots, fill=0))
+    pool = B.new_pool(lay)
+    after = dev(lens - 1)
+    for b in range(bsz):
+        n = int(lens[b]) - 1
+        k, v = workloads.raw_kv_device(w, n, stream=b * 1000, device="cuda")
+        B.oscar_quant_append(lay, pool, k.to(torch.bfloat16), v.to(torch.bfloat16), dev(np.full(n, b, np.int32)),
+                             dev(np.arange(n, dtype=np.int32)), dev(slots[b][:n]), after, rk_d, rv_d)
+        del k, v
+    q = dev(workloads.queries(w, n_rows=bsz, stream=7)).to(torch.bfloat16)
+    kn, vn = workloads.raw_kv_device(w, bsz, stream=999_999, device="cuda")
+    kn, vn = kn.to(torch.bfloat16), vn.to(torch.bfloat16)
+    req_ids = dev(np.arange(bsz, dtype=np.int32))
+    pos = dev(lens - 1)
+    new_slots = dev(np.array([slots[b][lens[b] - 1] for b in range(bsz)], np.int32))
+    lens_d = dev(lens)
+    ws = torch.empty(B.oscar_decode_workspace_size(lay, lens), dtype=torch.uint8, device="cuda")
+    out = torch.empty((bsz, w.num_q_heads, 128), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        B.oscar_quant_append(lay, pool, kn, vn, req_ids, pos, new_slots, lens_d, rk_d, rv_d, stream=stream)
+        B.oscar_decode_attn(lay, pool, q, req_ids, lens_d, lens, table, rk_d, rv_d, 128 ** -0.5, out, ws,
+                            stream=stream, kernel_begin=None if ev is None else ev[0],
+                            kernel_end=None if ev is None else ev[1])
+
+    for _ in range(max(10, args.warmup // 5)):
+        step()
+    steps = max(10, args.steps // 5)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a_, b_ in evs:
+        a_.record(stream)
+        b_.record(stream)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        step(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    kern_ms = float(np.mean([a_.elapsed_time(b_) for a_, b_ in evs]))
+    head_rec = 64 + 8 * (128 // group_size)
+    kbytes = decode_kernel_bytes(lens.tolist(), hkv, w.sink, w.recent, head_record=head_rec)
+    return dict(group_size=group_size, head_record_bytes=head_rec, steps=steps, ms_per_step=ms,
+                kernel_ms=kern_ms, kv_tokens_per_s=int(lens.sum()) / (ms * 1e-3), algorithmic_bytes=kbytes,
+                gb_per_s=kbytes / (kern_ms * 1e-3) / 1e9, frac_hbm=kbytes / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                output_finite=bool(torch.isfinite(out.float()).all().item()))
+
+
 def run_covariance(args, torch, B, workloads):
     """Calibration statistics: C_Q Gram sums of 131,072 captured query tokens of
     a 32 q / 8 KV head layer (bf16), one oscar_covariance_accumulate call."""
@@ -418,6 +482,7 @@ def main():
     ap.add_argument("--no-extend", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-covariance", action="store_true")
+    ap.add_argument("--no-lower-metadata", action="store_true")
     ap.add_argument("--only-extend", action="store_true",
                     help="run only the extend call (prints its own JSON object; for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -462,6 +527,12 @@ def main():
         log(f"[bench] bf16 baseline step {bf['ms_per_step']:.3f} ms, kernel {bf['kernel_ms']:.3f} ms, "
             f"{bf['gb_per_s']:.0f} GB/s; INT2 speed-up {bf['int2_speedup_kernel']:.2f}x (kernel), "
             f"{bf['int2_speedup_step']:.2f}x (step)")
+    lowmeta = None
+    if not args.no_lower_metadata:
+        lowmeta = [run_lower_metadata(args, torch, B, workloads, g) for g in (64, 128)]
+        for lm in lowmeta:
+            log(f"[bench] G={lm['group_size']} step {lm['ms_per_step']:.3f} ms, history kernels "
+                f"{lm['kernel_ms']:.3f} ms, {lm['gb_per_s']:.0f} GB/s")
     ext = None if args.no_extend else run_extend(args, torch, B, workloads)
     if ext:
         log(f"[bench] extend {ext['ms']:.2f} ms ({ext['new_tokens']} new tokens over {ext['prefix_len']}), "
@@ -498,6 +569,7 @@ def main():
         "decode_steps_per_s": 1e3 / ms,
         "quant_append": app,
         "bf16_baseline": bf,
+        "lower_metadata": lowmeta,
         "extend": ext,
         "covariance": cov,
         "cpu_baseline": base,

@@ -910,10 +910,10 @@ template <int NG>
 __global__ __launch_bounds__(64 * kPartialWaves) void hist_lowmeta_kernel(DecodeArgs a) {
     constexpr int kRec = 2 * kCodeBytes + 8 * NG;          // head record bytes
     constexpr int kG = kHeadDim / NG;                       // channels per group
-    __shared__ float qs_all[kPartialWaves][kMaxGroup][kHeadDim];
-    __shared__ float ps_all[kPartialWaves][kMaxGroup][kLmChunk];
+    __shared__ __attribute__((aligned(16))) float qs_all[kPartialWaves][kMaxGroup][kHeadDim];
+    __shared__ __attribute__((aligned(16))) float ps_all[kPartialWaves][kLmChunk][kMaxGroup];
     __shared__ uint32_t vc_all[kPartialWaves][kLmChunk][kCodeBytes / 4];
-    __shared__ uint32_t vsz_all[kPartialWaves][kLmChunk][NG];
+    __shared__ float2 vsz_all[kPartialWaves][kLmChunk][NG];
     const int id = blockIdx.x;
     const int hc = id % a.head_chunks;
     const int rest = id / a.head_chunks;
@@ -929,9 +929,9 @@ __global__ __launch_bounds__(64 * kPartialWaves) void hist_lowmeta_kernel(Decode
     const int lane = threadIdx.x & 63;
     const int g = a.g;
     float(*qs)[kHeadDim] = qs_all[w];
-    float(*ps)[kLmChunk] = ps_all[w];
+    float(*ps)[kMaxGroup] = ps_all[w];
     uint32_t(*vc)[kCodeBytes / 4] = vc_all[w];
-    uint32_t(*vsz)[NG] = vsz_all[w];
+    float2(*vsz)[NG] = vsz_all[w];
     const size_t row0q = size_t(b) * a.hq + size_t(hk) * g;
     for (int e = lane; e < g * kHeadDim; e += 64) qs[e / kHeadDim][e % kHeadDim] = a.qrot[row0q * kHeadDim + e];
     float qg[kMaxGroup][NG];                                // group sums of q' (from the 32-channel sums)
@@ -973,7 +973,9 @@ __global__ __launch_bounds__(64 * kPartialWaves) void hist_lowmeta_kernel(Decode
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) {
             ksz[gi] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(base + 2 * kCodeBytes) + gi);
-            vsz[lane][gi] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(base + 2 * kCodeBytes + 4 * NG) + gi);
+            const uint32_t vw = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(base + 2 * kCodeBytes + 4 * NG) + gi);
+            vsz[lane][gi] = make_float2(__half2float(__ushort_as_half(uint16_t(vw))),
+                                        __half2float(__ushort_as_half(uint16_t(vw >> 16))));
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -990,12 +992,21 @@ __global__ __launch_bounds__(64 * kPartialWaves) void hist_lowmeta_kernel(Decode
         for (int wd = 0; wd < 8; ++wd) {                    // 16 channels per code word
             const uint32_t cw = kc[wd >> 1][wd & 1];
             const int gi = (16 * wd) / kG;
+            float c[16];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float c = float((cw >> (2 * e)) & 3u);
+            for (int e = 0; e < 16; ++e) c[e] = float((cw >> (2 * e)) & 3u);
 #pragma unroll
-                for (int h = 0; h < kMaxGroup; ++h)
-                    if (h < g) dot[h][gi] = fmaf(qs[h][16 * wd + e], c, dot[h][gi]);
+            for (int h = 0; h < kMaxGroup; ++h) {
+                if (h < g) {
+#pragma unroll
+                    for (int e4 = 0; e4 < 16; e4 += 4) {
+                        const f32x4 q4 = *reinterpret_cast<const f32x4 *>(&qs[h][16 * wd + e4]);
+                        dot[h][gi] = fmaf(q4[0], c[e4], dot[h][gi]);
+                        dot[h][gi] = fmaf(q4[1], c[e4 + 1], dot[h][gi]);
+                        dot[h][gi] = fmaf(q4[2], c[e4 + 2], dot[h][gi]);
+                        dot[h][gi] = fmaf(q4[3], c[e4 + 3], dot[h][gi]);
+                    }
+                }
             }
         }
         float alpha[kMaxGroup];
@@ -1016,7 +1027,7 @@ __global__ __launch_bounds__(64 * kPartialWaves) void hist_lowmeta_kernel(Decode
             m_run[h] = m_new;
             const float p = x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x - m_new);
             l_lane[h] = fmaf(l_lane[h], alpha[h], p);
-            if (h < g) ps[h][lane] = p;
+            if (h < g) ps[lane][h] = p;
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -1029,16 +1040,22 @@ __global__ __launch_bounds__(64 * kPartialWaves) void hist_lowmeta_kernel(Decode
         const int cword = lane >> 3, cshift = 4 * (lane & 7), cg = (2 * lane) / kG;
         for (int u = 0; u < cnt; ++u) {
             const uint32_t cw = vc[u][cword] >> cshift;
-            const uint32_t szw = vsz[u][cg];
-            const float s = __half2float(__ushort_as_half(uint16_t(szw)));
-            const float z = __half2float(__ushort_as_half(uint16_t(szw >> 16)));
-            const float v0 = fmaf(s, float(cw & 3u), z), v1 = fmaf(s, float((cw >> 2) & 3u), z);
+            const float2 sz = vsz[u][cg];
+            const float v0 = fmaf(sz.x, float(cw & 3u), sz.y), v1 = fmaf(sz.x, float((cw >> 2) & 3u), sz.y);
+            float p[kMaxGroup];
+#pragma unroll
+            for (int h4 = 0; h4 < kMaxGroup; h4 += 4) {
+                if (h4 < g) {
+                    const f32x4 p4 = *reinterpret_cast<const f32x4 *>(&ps[u][h4]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) p[h4 + e] = p4[e];
+                }
+            }
 #pragma unroll
             for (int h = 0; h < kMaxGroup; ++h) {
                 if (h < g) {
-                    const float p = ps[h][u];
-                    o0[h] = fmaf(p, v0, o0[h]);
-                    o1[h] = fmaf(p, v1, o1[h]);
+                    o0[h] = fmaf(p[h], v0, o0[h]);
+                    o1[h] = fmaf(p[h], v1, o1[h]);
                 }
             }
         }

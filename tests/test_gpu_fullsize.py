@@ -44,7 +44,8 @@ def _fill_and_sample(w, sampled, q_stream):
     slots = workloads.slot_table(w)
     pool = B.new_pool(lay_b)
     after = gs.dev(lens)
-    rec_view = pool.records[: w.num_slots * lay_b.num_kv_heads * 96].view(w.num_slots, -1)
+    rec_bytes = lay_b.num_kv_heads * (64 + 8 * (128 // w.group_size))
+    rec_view = pool.records[: w.num_slots * rec_bytes].view(w.num_slots, -1)
     shp = (bsz, w.sink, w.num_kv_heads, 2, w.head_dim)
     sink_view = pool.sink[: int(np.prod(shp))].view(shp)
     shp_r = (bsz, w.recent, w.num_kv_heads, 2, w.head_dim)
@@ -221,3 +222,10 @@ def test_extend_8k_full_size_sampled():
     err = pt.normwise_rel(o_gpu[rows], o_ref[rows])
     gs.say(f"  extend_8k rows {rows}: max normwise rel err {err.max():.3e} (median {np.median(err):.3e})")
     assert err.max() <= TOL
+
+
+def test_decode_b32_full_size_sampled_group_128():
+    """The decode workload with one (s, z) per 128 channels (72-byte head records)."""
+    w = workloads.custom("decode_b32", group_size=128)
+    gs.say("decode_b32 full size, G = 128")
+    _check(_fill_and_sample(w, sampled={21}, q_stream=11), "decode_b32 G=128")

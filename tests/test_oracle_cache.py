@@ -106,3 +106,30 @@ def test_int2_cost_per_token_matches_page(golden):
         assert code_bytes / 1024 == g["value"]
         assert accounting.int2_code_bytes_per_token(g["layers"], g["kv_heads"],
                                                     g["head_dim"]) / 1024 == g["value"]
+
+
+@pytest.mark.parametrize("G,head_record", [(64, 80), (128, 72)])
+def test_record_byte_offsets_lower_metadata(G, head_record):
+    """One (s, z) per G channels: the record shrinks to 64 + 8 (128 / G) bytes and
+    each group's scale and zero come from the min and max of all G channels."""
+    lay = cache.Layout(128, G, 2, 8, S, W, num_slots=3, max_requests=1)
+    assert lay.head_record_bytes == head_record and lay.record_bytes == 2 * head_record
+    pool = cache.new_pool(lay)
+    rng = np.random.default_rng(G)
+    x = (rng.standard_normal((1, 2, 128)) * 2).astype(np.float32)
+    eye = np.stack([np.eye(128, dtype=np.float32)] * 2)
+    cache.append(pool, lay, x, 3 * x, [0], [S + 1], [1], [S + 2], eye, eye)
+    rec = pool.records[1]
+    ng = 128 // G
+    for h in range(2):
+        base = head_record * h
+        for t, xt in enumerate((x[0, h], 3 * x[0, h])):
+            sz = rec[base + 64 + 4 * ng * t:base + 64 + 4 * ng * (t + 1)].view("<f2")
+            for g in range(ng):
+                lo, hi = xt[g * G:(g + 1) * G].min(), xt[g * G:(g + 1) * G].max()
+                # s = fp16(fl32(hi - lo) / 3), z = fp16(lo), written out by hand
+                assert sz[2 * g] == np.float16(np.float32(np.float32(hi - lo) / np.float32(3)))
+                assert sz[2 * g + 1] == np.float16(lo)
+            codes = quant.unpack(rec[base + 32 * t:base + 32 * (t + 1)])
+            c, _, _ = quant.quantize(xt, G)
+            assert np.array_equal(codes, c)

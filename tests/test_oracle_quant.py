@@ -86,12 +86,13 @@ def test_pack_example_and_round_trip(golden):
     assert np.array_equal(quant.unpack(p), c)
 
 
-def test_dequantisation_error_bound():
+@pytest.mark.parametrize("G", [32, 64, 128])
+def test_dequantisation_error_bound(G):
     rng = np.random.default_rng(2)
     x = (rng.standard_normal((500, 128)) * 3).astype(np.float32)
-    c, s, z = quant.quantize(x, 32)
-    xh = quant.dequantize(c, s, z, 32)
-    err = np.abs(xh - x.astype(np.float64)).reshape(500, 4, 32).max(axis=-1)
+    c, s, z = quant.quantize(x, G)
+    xh = quant.dequantize(c, s, z, G)
+    err = np.abs(xh - x.astype(np.float64)).reshape(500, 128 // G, G).max(axis=-1)
     s64 = s.astype(np.float64)
     # half a step plus the fp16 rounding of z and of the top level
     ulp = np.abs(x).max() * 2.0 ** -10

@@ -11,7 +11,10 @@
 //               KV head; the workgroup holds all KV heads of the item so that
 //               the slot-major records are read as whole cache lines.
 //               History tiles of 32 tokens run on f16 MFMA with the INT2 codes
-//               as exact fp16 denormal operands (see int2_item).
+//               as exact fp16 denormal operands (see int2_item), for 96-, 80-
+//               and 72-byte head records (G = 32, 64, 128).
+//               With G = 128 and an odd number of KV heads the history runs on
+//               a VALU kernel instead (hist_lowmeta_kernel).
 //               BF16 windows run on fp32 VALU.  Each item writes (m, l, o')
 //               with m in log2 units.
 //   3. merge:   log-sum-exp merge of the items and o = o' R_V^T.
@@ -290,6 +293,19 @@ constexpr int kRing = 4;                               // slot-id ring of the wo
 constexpr int kHalfTok = 16 * kTokBytes;               // token 16 + t of a stage is this far after token t
 __host__ __device__ constexpr int int2_lds_bytes() { return kStages * kStage + kRing * kRingBytes; }
 
+// The same pipeline for the lower-metadata records: 80 bytes (G = 64, two
+// groups; the K and V (s, z) of a head share one 16-byte unit) and 72 bytes
+// (G = 128, one group).  A token of a 4-head chunk is 320 or 288 bytes (20 or
+// 18 units), stored in token order without a swizzle; a tile takes 640 or 576
+// of the stage's 768 unit positions, the rest receive zero-record loads so
+// that every lane still issues three.  The A rows (h, g) of the QK products
+// are block-diagonal over the two groups, or a single group.  The PV weights
+// get their own LDS area (a head has too few dead units per token): per wave
+// two planes (hi, lo) of up to 8 rows (g, h) x 32 K-slots of fp16.
+constexpr int kWeightPlane = 8 * kTileTokens * 2;      // 512 bytes
+constexpr int kWeightWave = 2 * kWeightPlane;          // 1 KiB
+__host__ __device__ constexpr int int2_lds_bytes_lowmeta() { return int2_lds_bytes() + 4 * kWeightWave; }
+
 // XOR applied to the unit index (within its 128-byte line) of token t: bits
 // 0 and 1 of t % 8 swapped, bit 1 flipped for t % 16 >= 8.  Tokens t and
 // t + 16 share it (token 16 + t is kHalfTok after token t).  It makes the
@@ -357,10 +373,16 @@ __device__ __forceinline__ void wait_vmem() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int GQ>
+template <int GQ, int NG>
 __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, int p0, int p1,
                           uint8_t *smem) {
+    static_assert(NG == 4 || NG == 2 || NG == 1, "four, two or one (s, z) groups per head vector");
     constexpr int HS = (GQ + 3) / 4;          // sets of 4 query heads
+    constexpr int kRecH = 2 * kCodeBytes + 8 * NG;        // head record: 96 or 80 bytes
+    constexpr int kUnitsH = kRecH / 16;                   // whole units of a head record
+    constexpr int kTokB = 4 * kRecH;                      // one token of the 4-head chunk
+    constexpr int kTokUnits = kTokB / 16;                 // 24, 20 or 18 units
+    constexpr int kTileUnits = kTileTokens * kTokUnits;   // 768, 640 or 576 units per tile
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform over the wave
     const int lane = threadIdx.x & 63;
     const int n = lane & 15;
@@ -368,7 +390,7 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
     const int hk = hc * kPartialWaves + w;    // this wave's KV head
     const bool active = hk < a.hkv;
     const int nh = min(kPartialWaves, a.hkv - hc * kPartialWaves);   // KV heads of the chunk
-    const uint32_t rec_bytes = uint32_t(a.hkv) * kHeadRecord;
+    const uint32_t rec_bytes = uint32_t(a.hkv) * kRecH;
     const int32_t *r2s = a.req_to_slot + int64_t(req) * a.r2s_stride;
     const int n_tiles = (p1 - p0 + kTileTokens - 1) / kTileTokens;
     const uint32_t st0 = lds_addr(smem);                                // stage 0
@@ -386,7 +408,7 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
             const bool hv = h < GQ && active;
             const float *qr = a.qrot + (head0 + (hv ? h : 0)) * kHeadDim;
             const float k2 = a.qsum[(head0 + (hv ? h : 0)) * 8 + 4];
-            const bool nz = hv && (n & 3) == kb;
+            const bool nz = hv && (n & 3) == (kb * NG) / 4;   // row group = group of K block kb
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 uint32_t whi[4], wlo[4];
@@ -410,7 +432,11 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
             const bool hv = h < GQ && active;
             const float *info = a.qsum + (head0 + (hv ? h : 0)) * 8;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) qz[hs][g] = hv ? info[g] / info[5] : 0.0f;
+            for (int g = 0; g < NG; ++g)
+                qz[hs][g] = hv ? (NG == 4 ? info[g]
+                                 : NG == 2 ? info[2 * g] + info[2 * g + 1]
+                                           : (info[0] + info[1]) + (info[2] + info[3])) / info[5]
+                               : 0.0f;
             qout[hs] = hv ? info[5] : 1.0f;
         }
     }
@@ -420,13 +446,21 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
     // units of KV heads past the chunk (never read) repeat the chunk's first head
     int tq[3];
     const uint8_t *src_base[3];
+    bool in_tile[3];                          // false: a padding position of the 80-byte layout
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
         const int P = 64 * (3 * w + u) + lane;
-        const int t = P / 24, U = P % 24;
-        const int q = (U & ~7) | ((U & 7) ^ tok_swizzle(t));
+        in_tile[u] = NG == 4 || P < kTileUnits;      // the 96-byte layout fills the stage
+        const int Pc = in_tile[u] ? P : 0;
+        const int t = Pc / kTokUnits, U = Pc % kTokUnits;
+        const int q = NG == 4 ? ((U & ~7) | ((U & 7) ^ tok_swizzle(t))) : U;
         tq[u] = t;
-        src_base[u] = a.records + hc * kTokBytes + 16 * (q / 6 < nh ? q : q % 6);
+        // units past the chunk's heads (never read) repeat an in-range unit; with
+        // 72-byte records the chunk holds an even number of heads (whole units)
+        if constexpr (NG == 1)
+            src_base[u] = a.records + hc * kTokB + 16 * (16 * q + 16 <= nh * kRecH ? q : 0);
+        else
+            src_base[u] = a.records + hc * kTokB + 16 * (q / kUnitsH < nh ? q : q % kUnitsH);
     }
 
     // ---- loads.  Iteration t issues S(t + 6), this wave's 8 of the slot ids
@@ -462,7 +496,7 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
         const int s_own = lds_ld<int>(slot_own + rs * kRingBytes);
 #pragma unroll
         for (int u = 0; u < 3; ++u) {
-            const bool ok = uint32_t(slot[u]) < uint32_t(a.num_slots);
+            const bool ok = uint32_t(slot[u]) < uint32_t(a.num_slots) && in_tile[u];
             f.src[u] = ok ? src_base[u] + uint64_t(uint32_t(slot[u])) * rec_bytes : a.zero_rec;
         }
         const uint32_t left = span - uint32_t(T * kTileTokens);   // positions left in the item (may wrap: none)
@@ -483,54 +517,87 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
     };
 
     // running state, per lane = (token n, head kb of each set)
-    float m_run[HS], l_lane[HS], zl[HS][4];
+    float m_run[HS], l_lane[HS], zl[HS][NG];
     f32x4 oacc[HS][8];    // PV output: lane (n, kb) rows (g = kb, h = i), channel 8 n + jj
 #pragma unroll
     for (int hs = 0; hs < HS; ++hs) {
         m_run[hs] = -INFINITY;
         l_lane[hs] = 0.0f;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) zl[hs][g] = 0.0f;
+        for (int g = 0; g < NG; ++g) zl[hs][g] = 0.0f;
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) oacc[hs][jj] = f32x4{0, 0, 0, 0};
     }
 
     // this lane's LDS addresses in stage 0 (head w of token t); token 16 + t
     // of a stage is 6144 bytes after token t (same swizzle)
-    constexpr int kHalfTok = 16 * kTokBytes;
-    const uint32_t qk_at = lds_pin(st0 + unit_addr(n, 6 * w + (kb >> 1)) + 8 * (kb & 1));   // K codes
-    const uint32_t szk_at = lds_pin(st0 + unit_addr(n, 6 * w + 4));
-    const uint32_t szv_at = lds_pin(st0 + unit_addr(n, 6 * w + 5));
-    uint32_t pv_at[8];    // V codes (channels 8 n .. 8 n + 7) of the tokens of K-slots 8 kb + i
+    constexpr int kHalfTok = 16 * kTokB;
+    // byte b of head w's record of token t in stage 0 (80-byte layout)
+    auto rec_at = [&](int t, int byte) { return st0 + t * kTokB + kRecH * w + byte; };
     const int kb_tok = (kb & 1) + 4 * (kb >> 1);
+    uint32_t qk_at, szk_at, szv_at, a_at;
+    constexpr uint32_t wlo_off = NG == 4 ? kHalfTok : kWeightPlane;   // lo plane of the PV weights
+    uint32_t pv_at[8];    // V codes (channels 8 n .. 8 n + 7) of the tokens of K-slots 8 kb + i
+    uint32_t w_at[NG];    // PV weight of token t of this lane's row (g, kb); token 16 + t 8 bytes further
+    const int w_unit = (n & 1) + 2 * ((n >> 2) & 1);            // K-slot / 8 of token n
+    const int w_i = ((n >> 1) & 1) + 2 * (n >> 3);              // K-slot % 8
+    if constexpr (NG == 4) {
+        qk_at = lds_pin(st0 + unit_addr(n, 6 * w + (kb >> 1)) + 8 * (kb & 1));   // K codes
+        szk_at = lds_pin(st0 + unit_addr(n, 6 * w + 4));
+        szv_at = lds_pin(st0 + unit_addr(n, 6 * w + 5));
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        pv_at[i] = lds_pin(st0 + unit_addr(2 * (i & 1) + 8 * (i >> 1) + kb_tok, 6 * w + 2 + (n >> 3)) + ((2 * n) & 15));
-    // PV weight of token t (0..15; token 16 + t sits 8 bytes further) for this
-    // lane's row (g, kb): K-slot 8 unit + i of the row, unit XOR-permuted by g
-    uint32_t w_at[4];
-    {
-        const int unit = (n & 1) + 2 * ((n >> 2) & 1);              // K-slot / 8
-        const int i = ((n >> 1) & 1) + 2 * (n >> 3);                // K-slot % 8
+        for (int i = 0; i < 8; ++i)
+            pv_at[i] = lds_pin(st0 + unit_addr(2 * (i & 1) + 8 * (i >> 1) + kb_tok, 6 * w + 2 + (n >> 3)) + ((2 * n) & 15));
+        // K-slot 8 unit + i of the row, unit XOR-permuted by g
 #pragma unroll
-        for (int g = 0; g < 4; ++g) w_at[g] = lds_pin(st0 + wunit_addr(w, 4 * g + kb, unit ^ g) + 2 * i);
+        for (int g = 0; g < 4; ++g) w_at[g] = lds_pin(st0 + wunit_addr(w, 4 * g + kb, w_unit ^ g) + 2 * w_i);
+        // A-operand read of row n, K-slots 8 kb .. 8 kb + 7
+        a_at = lds_pin(st0 + wunit_addr(w, n, kb ^ (n >> 2)));
+    } else {
+        qk_at = lds_pin(rec_at(n, 8 * kb));
+        szk_at = lds_pin(rec_at(n, 2 * kCodeBytes));
+        szv_at = lds_pin(rec_at(n, 2 * kCodeBytes + 4 * NG));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pv_at[i] = lds_pin(rec_at(2 * (i & 1) + 8 * (i >> 1) + kb_tok, kCodeBytes + 2 * n));
+        const uint32_t wb = st0 + int2_lds_bytes() + w * kWeightWave;   // after the stages and the ring
+#pragma unroll
+        for (int g = 0; g < NG; ++g) w_at[g] = lds_pin(wb + (4 * g + kb) * 64 + 16 * w_unit + 2 * w_i);
+        // rows of absent groups repeat written rows; their outputs are never read
+        a_at = lds_pin(wb + (n & (4 * NG - 1)) * 64 + 16 * kb);
     }
-    // A-operand read of row n, K-slots 8 kb .. 8 kb + 7
-    const uint32_t a_at = lds_pin(st0 + wunit_addr(w, n, kb ^ (n >> 2)));
+    // the weight area of the 80-byte layout does not move with the stage
+    constexpr bool kWeightsInStage = NG == 4;
 
     // one tile: QK, online softmax, PV (LDS stage K)
     auto compute = [&](auto K, uint32_t valid) {
         constexpr uint32_t so = decltype(K)::value * kStage;   // stage offset
         // ---- QK: logit of (token 16 hf + n, head 4 hs + kb)
         float lg[HS][2];
-        u32x4 szv[2];
+        uint32_t szv[2][NG];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             const int tk = 16 * hf + n;
             const uint32_t ho = so + hf * kHalfTok;
             const u32x2 kc = lds_ld<u32x2>(qk_at + ho);
-            const u32x4 szk = lds_ld<u32x4>(szk_at + ho);
-            szv[hf] = lds_ld<u32x4>(szv_at + ho);
+            uint32_t szk[NG];
+            if constexpr (NG == 4) {
+                const u32x4 k4 = lds_ld<u32x4>(szk_at + ho), v4 = lds_ld<u32x4>(szv_at + ho);
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    szk[g] = k4[g];
+                    szv[hf][g] = v4[g];
+                }
+            } else if constexpr (NG == 2) {
+                const u32x2 k2 = lds_ld<u32x2>(szk_at + ho), v2 = lds_ld<u32x2>(szv_at + ho);
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    szk[g] = k2[g];
+                    szv[hf][g] = v2[g];
+                }
+            } else {
+                szk[0] = lds_ld<uint32_t>(szk_at + ho);
+                szv[hf][0] = lds_ld<uint32_t>(szv_at + ho);
+            }
             const uint32_t d0s = kc[0] >> 6, d1s = kc[1] >> 6;
             f16x8 B[4];
 #pragma unroll
@@ -554,9 +621,9 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
                 // log2 logit, K fixed per head); masked tokens start from -inf.
                 float x = live ? 0.0f : -INFINITY;
 #pragma unroll
-                for (int g = 0; g < 4; ++g) x = fmaf(half_hi(szk[g]), qz[hs][g], x);
+                for (int g = 0; g < NG; ++g) x = fmaf(half_hi(szk[g]), qz[hs][g], x);
 #pragma unroll
-                for (int g = 0; g < 4; ++g) x = fmaf(acc[g], half_lo(szk[g]), x);
+                for (int g = 0; g < NG; ++g) x = fmaf(acc[g], half_lo(szk[g]), x);
                 lg[hs][hf] = x;
             }
         }
@@ -572,7 +639,7 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
                 alpha[hs] = (m_new > m_run[hs]) ? __builtin_amdgcn_exp2f((m_run[hs] - m_new) * qout[hs]) : 1.0f;
                 l_lane[hs] *= alpha[hs];
 #pragma unroll
-                for (int g = 0; g < 4; ++g) zl[hs][g] *= alpha[hs];
+                for (int g = 0; g < NG; ++g) zl[hs][g] *= alpha[hs];
                 m_run[hs] = m_new;
             }
             // exponent reference in log2 units: a finite stand-in while every
@@ -584,7 +651,7 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
                 pw[hs][hf] = p;
                 l_lane[hs] += p;
 #pragma unroll
-                for (int g = 0; g < 4; ++g) zl[hs][g] = fmaf(p, half_hi(szv[hf][g]), zl[hs][g]);
+                for (int g = 0; g < NG; ++g) zl[hs][g] = fmaf(p, half_hi(szv[hf][g]), zl[hs][g]);
             }
         }
         // ---- PV: A rows (g, h) = weights of K-slots 8 kb .. 8 kb + 7; B = V
@@ -605,18 +672,21 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
                 const float p = pw[hs][hf];
-                uint32_t hw[2], lw[2];
+                constexpr int kPairs = (NG + 1) / 2;
+                uint32_t hw[kPairs], lw[kPairs];
 #pragma unroll
-                for (int q2 = 0; q2 < 2; ++q2) {
-                    const float s0 = half_lo(szv[hf][2 * q2]), s1 = half_lo(szv[hf][2 * q2 + 1]);
+                for (int q2 = 0; q2 < kPairs; ++q2) {
+                    const float s0 = half_lo(szv[hf][2 * q2]);
+                    const float s1 = NG > 1 ? half_lo(szv[hf][(2 * q2 + 1) % NG]) : 0.0f;
                     hw[q2] = pk_rn(fmaf(p, s0, 0.0f), fmaf(p, s1, 0.0f));
                     lw[q2] = pk_rn(fmaf(p, s0, -half_lo(hw[q2])), fmaf(p, s1, -half_hi(hw[q2])));
                 }
+                constexpr uint32_t wso = kWeightsInStage ? so : 0u;
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
+                for (int g = 0; g < NG; ++g) {
                     const int sh = 16 * (g & 1);
-                    lds_st<uint16_t>(w_at[g] + so + 8 * hf, uint16_t(hw[g >> 1] >> sh));
-                    lds_st<uint16_t>(w_at[g] + so + 8 * hf + kHalfTok, uint16_t(lw[g >> 1] >> sh));
+                    lds_st<uint16_t>(w_at[g] + wso + 8 * hf, uint16_t(hw[g >> 1] >> sh));
+                    lds_st<uint16_t>(w_at[g] + wso + 8 * hf + wlo_off, uint16_t(lw[g >> 1] >> sh));
                 }
             }
             lds_order();
@@ -631,8 +701,9 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
                     for (int jj = 0; jj < 8; ++jj) oacc[hs][jj][i] *= ai;
                 }
             }
-            const f16x8 ahi = lds_ld<f16x8>(a_at + so);
-            const f16x8 alo = lds_ld<f16x8>(a_at + so + kHalfTok);
+            constexpr uint32_t aso = kWeightsInStage ? so : 0u;
+            const f16x8 ahi = lds_ld<f16x8>(a_at + aso);
+            const f16x8 alo = lds_ld<f16x8>(a_at + aso + wlo_off);
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) {
                 const f16x8 Bj = u4_as_h8(code_bits(xw[0], xs[0], jj), code_bits(xw[1], xs[1], jj),
@@ -704,13 +775,13 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
 
     // ---- write the partial (m, l, o') of the GQ heads
     const size_t row0 = (size_t(b) * a.items + j) * a.hq + hk * GQ;
-    const int cg = n >> 2;                    // group of output channels 8 n .. 8 n + 7
+    const int cg = (8 * n) / (kHeadDim / NG);   // group of output channels 8 n .. 8 n + 7
 #pragma unroll
     for (int hs = 0; hs < HS; ++hs) {
         const float l_row = row16_sum(l_lane[hs]);
-        float zt[4];
+        float zt[NG];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) zt[g] = row16_sum(zl[hs][g]);
+        for (int g = 0; g < NG; ++g) zt[g] = row16_sum(zl[hs][g]);
         if (n == 0 && 4 * hs + kb < GQ) {
             a.part_ml[(row0 + 4 * hs + kb) * 2 + 0] = m_run[hs] * qout[hs];   // log2 units
             a.part_ml[(row0 + 4 * hs + kb) * 2 + 1] = l_row;
@@ -723,7 +794,7 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
             // p z summed over the item for head i, group cg (held by row i of lanes)
             float z = 0.0f;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
+            for (int g = 0; g < NG; ++g) {
                 const float zi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, zt[g]), 16 * i));
                 z = g == cg ? zi : z;
             }
@@ -874,7 +945,7 @@ __device__ __forceinline__ void bf16_item(const DecodeArgs &a, int b, int req, i
     }
 }
 
-template <int GQ>
+template <int GQ, int NG>
 __global__ __launch_bounds__(64 * kPartialWaves) void partial_kernel(DecodeArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int id = blockIdx.x;
@@ -894,13 +965,13 @@ __global__ __launch_bounds__(64 * kPartialWaves) void partial_kernel(DecodeArgs 
         float *pbuf = reinterpret_cast<float *>(smem) + w * kBf16WaveFloats;
         bf16_item(a, b, req, j, active ? hk : 0, p0, p1, active, pbuf);
     } else if (a.num_slots > 0) {
-        int2_item<GQ>(a, b, req, j, hc, p0, p1, smem);   // every wave: the loads are shared
+        int2_item<GQ, NG>(a, b, req, j, hc, p0, p1, smem);   // every wave: the loads are shared
     }
 }
 
-// History items of the lower-metadata layouts: groups of G = 64 or 128
-// channels (NG = 2 or 1 groups per head vector) and 80- or 72-byte head
-// records.  fp32 VALU, 64 tokens per step.  QK: lane = token, the 128 codes of
+// History items of the 72-byte layout (G = 128, one group per head vector)
+// when the number of KV heads is odd; the kernel also takes G = 64 (NG = 2).
+// fp32 VALU, 64 tokens per step.  QK: lane = token, the 128 codes of
 // its K against q' in LDS, factored per group as s_g (q'_g . c_g) + z_g Q_g
 // (Q_g the group's sum of q').  PV: lane = channel pair, the step's V codes and
 // (s, z) staged in LDS, v = s c + z formed per token.
@@ -1212,15 +1283,21 @@ __global__ __launch_bounds__(kHeadDim) void extend_rotate_kernel(RotateArgs a) {
 
 // Dynamic LDS of the partial kernel: the four record stages and the slot-id
 // ring of the INT2 items, or each wave's softmax buffer for the BF16 items.
-size_t partial_lds_bytes(const DecodeArgs &) {
-    const size_t int2 = int2_lds_bytes();
+size_t partial_lds_bytes(const DecodeArgs &a) {
+    const size_t int2 = a.group_size == kGroup ? int2_lds_bytes() : int2_lds_bytes_lowmeta();
     const size_t pbuf = size_t(kPartialWaves) * kBf16WaveFloats * sizeof(float);
     return int2 > pbuf ? int2 : pbuf;
 }
 
 template <int GQ>
 hipError_t launch_partial(const DecodeArgs &a, int blocks, hipStream_t stream) {
-    hipLaunchKernelGGL(partial_kernel<GQ>, dim3(blocks), dim3(64 * kPartialWaves), partial_lds_bytes(a), stream, a);
+    const size_t lds = partial_lds_bytes(a);
+    if (a.group_size == 64)
+        hipLaunchKernelGGL((partial_kernel<GQ, 2>), dim3(blocks), dim3(64 * kPartialWaves), lds, stream, a);
+    else if (a.group_size == 128)
+        hipLaunchKernelGGL((partial_kernel<GQ, 1>), dim3(blocks), dim3(64 * kPartialWaves), lds, stream, a);
+    else
+        hipLaunchKernelGGL((partial_kernel<GQ, 4>), dim3(blocks), dim3(64 * kPartialWaves), lds, stream, a);
     return hipGetLastError();
 }
 
@@ -1325,9 +1402,10 @@ oscar_status launch_decode(const DecodeArgs &a, const DecodePlan &plan, hipStrea
         }
         e = launch_extend_bf16(*xh, stream);
         if (e != hipSuccess) return fail(OSCAR_ERR_HIP, std::string("extend bf16 launch: ") + hipGetErrorString(e));
-    } else if (a.group_size != kGroup) {
-        // lower-metadata layouts: the BF16 windows (items 0, 1) on partial_kernel,
-        // the history items on hist_lowmeta_kernel
+    } else if (a.group_size == 128 && (a.hkv & 1)) {
+        // 72-byte records and an odd number of KV heads (a 4-head chunk would
+        // end inside a 16-byte unit): the BF16 windows (items 0, 1) on
+        // partial_kernel, the history items on hist_lowmeta_kernel
         const int bf_blocks = 2 * a.batch * a.head_chunks;
         switch (a.g) {
             case 1: e = launch_partial<1>(a, bf_blocks, stream); break;
@@ -1342,10 +1420,7 @@ oscar_status launch_decode(const DecodeArgs &a, const DecodePlan &plan, hipStrea
         if (e != hipSuccess) return fail(OSCAR_ERR_HIP, std::string("partial launch: ") + hipGetErrorString(e));
         const int h_blocks = (plan.items - 2) * a.batch * a.head_chunks;
         if (h_blocks > 0 && a.num_slots > 0) {
-            if (a.group_size == 64)
-                hipLaunchKernelGGL(hist_lowmeta_kernel<2>, dim3(h_blocks), dim3(64 * kPartialWaves), 0, stream, a);
-            else
-                hipLaunchKernelGGL(hist_lowmeta_kernel<1>, dim3(h_blocks), dim3(64 * kPartialWaves), 0, stream, a);
+            hipLaunchKernelGGL(hist_lowmeta_kernel<1>, dim3(h_blocks), dim3(64 * kPartialWaves), 0, stream, a);
             e = hipGetLastError();
             if (e != hipSuccess) return fail(OSCAR_ERR_HIP, std::string("history launch: ") + hipGetErrorString(e));
         }

@@ -228,6 +228,22 @@ def test_decode_lower_metadata(G, wname, lens, chunk):
 
 
 @pytest.mark.parametrize("G", [64, 128])
+@pytest.mark.parametrize("g,hkv", [(1, 5), (3, 2), (5, 3), (8, 1)])
+def test_decode_lower_metadata_gqa_sweep(G, g, hkv):
+    """Every query-head group size (one and two sets of 4 heads) and KV-head
+    counts that leave a 4-head workgroup partly empty."""
+    w = workloads.custom("layer_small", num_kv_heads=hkv, num_q_heads=g * hkv, batch=2,
+                         seq_lens=(1100, 413), seed=30 + g, group_size=G)
+    lens = w.seq_lens
+    lay_b, lay_o, opool, table, r_k, r_v = _oracle_pool_case(w, lens, seed=g)
+    qh, qd = _queries(w, 2, g, "bf16")
+    gs.say(f"decode G={G} g={g} hkv={hkv}")
+    o_gpu = _gpu_decode(lay_b, gs.upload_oracle_pool(opool), qd, lens, table, r_k, r_v)
+    o_ref = attention.decode(opool, lay_o, qh, np.arange(2), lens, table, r_k, r_v, w.head_dim ** -0.5)
+    _compare(o_gpu, o_ref, f"G={G} g={g} hkv={hkv}")
+
+
+@pytest.mark.parametrize("G", [64, 128])
 def test_decode_lower_metadata_gqa_and_bad_slots(G):
     w = workloads.custom("layer_small", num_kv_heads=2, num_q_heads=12, batch=2,
                          seq_lens=(900, 1333), seed=77, group_size=G)

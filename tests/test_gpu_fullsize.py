@@ -224,8 +224,10 @@ def test_extend_8k_full_size_sampled():
     assert err.max() <= TOL
 
 
-def test_decode_b32_full_size_sampled_group_128():
-    """The decode workload with one (s, z) per 128 channels (72-byte head records)."""
-    w = workloads.custom("decode_b32", group_size=128)
-    gs.say("decode_b32 full size, G = 128")
-    _check(_fill_and_sample(w, sampled={21}, q_stream=11), "decode_b32 G=128")
+@pytest.mark.parametrize("G,req", [(64, 9), (128, 21)])
+def test_decode_b32_full_size_sampled_lower_metadata(G, req):
+    """The decode workload with one (s, z) per 64 or 128 channels (80- and
+    72-byte head records)."""
+    w = workloads.custom("decode_b32", group_size=G)
+    gs.say(f"decode_b32 full size, G = {G}")
+    _check(_fill_and_sample(w, sampled={req}, q_stream=11), f"decode_b32 G={G}")

@@ -26,7 +26,9 @@ Pool format (the library header states the same bytes):
       [32, 64)  V codes
       [64, 80)  K (s, z) per group: 4 x (fp16 s, fp16 z), little endian
       [80, 96)  V (s, z)
-  In general code bytes = d/4 and (s, z) bytes = 4 d/G per tensor.
+  In general code bytes = d/4 and (s, z) bytes = 4 d/G per tensor; with
+  8-bit scale/zero (scale_bits = 8, G = 64: 72-byte head records) each
+  group's (s, z) is two E4M3 codes, s first, 2 d/G bytes per tensor.
   sink store  [max_requests][S][Hkv][2 (K, V)][d] bf16
   recent ring [max_requests][W][Hkv][2 (K, V)][d] bf16, index p mod W
 
@@ -55,6 +57,7 @@ class Layout:
     recent: int
     num_slots: int
     max_requests: int
+    scale_bits: int = 16      # 16: fp16 (s, z); 8: E4M3 (s, z)
 
     @property
     def code_bytes(self) -> int:
@@ -62,7 +65,7 @@ class Layout:
 
     @property
     def sz_bytes(self) -> int:
-        return 4 * (self.head_dim // self.group_size)
+        return 2 * (self.scale_bits // 8) * (self.head_dim // self.group_size)
 
     @property
     def head_record_bytes(self) -> int:
@@ -108,15 +111,22 @@ def _offsets(lay: Layout, h: int):
     }
 
 
-def sz_to_bytes(s, z) -> np.ndarray:
-    """(s, z) fp16 [..., n_g] -> interleaved little-endian bytes [..., 4 n_g]."""
+def sz_to_bytes(s, z, scale_bits: int = 16) -> np.ndarray:
+    """(s, z) [..., n_g] -> interleaved bytes: fp16 little endian [..., 4 n_g],
+    or one E4M3 code each [..., 2 n_g] (s first) when scale_bits = 8."""
+    if scale_bits == 8:
+        pair = np.stack([quant.e4m3_bits(s), quant.e4m3_bits(z)], axis=-1)
+        return np.ascontiguousarray(pair).reshape(pair.shape[:-2] + (pair.shape[-2] * 2,))
     pair = np.stack([np.asarray(s, np.float16), np.asarray(z, np.float16)], axis=-1)
     pair = np.ascontiguousarray(pair.astype("<f2"))
     return pair.view(np.uint8).reshape(pair.shape[:-2] + (pair.shape[-2] * 4,))
 
 
-def sz_from_bytes(b):
+def sz_from_bytes(b, scale_bits: int = 16):
     b = np.ascontiguousarray(np.asarray(b, np.uint8))
+    if scale_bits == 8:
+        pair = quant.e4m3_value(b).reshape(b.shape[:-1] + (b.shape[-1] // 2, 2))
+        return pair[..., 0].astype(np.float16), pair[..., 1].astype(np.float16)
     pair = b.view("<f2").reshape(b.shape[:-1] + (b.shape[-1] // 4, 2))
     return pair[..., 0].astype(np.float16), pair[..., 1].astype(np.float16)
 
@@ -156,9 +166,9 @@ def append(pool: Pool, lay: Layout, k, v, req_ids, positions, slots, seq_len_aft
         if in_ring.any():
             pool.recent[req_ids[in_ring], positions[in_ring] % lay.recent, :, t, :] = bits[in_ring]
         if in_pool.any():
-            c, s, z = quant.quantize(xr[in_pool], lay.group_size, alpha)
+            c, s, z = quant.quantize(xr[in_pool], lay.group_size, alpha, lay.scale_bits)
             packed = quant.pack(c)                 # [m, Hkv, d/4]
-            szb = sz_to_bytes(s, z)                # [m, Hkv, 4 n_g]
+            szb = sz_to_bytes(s, z, lay.scale_bits)   # [m, Hkv, 4 n_g] (2 n_g with E4M3)
             for h in range(lay.num_kv_heads):
                 off = _offsets(lay, h)
                 a, b = off["kc" if t == 0 else "vc"]
@@ -182,7 +192,7 @@ def read_record(pool: Pool, lay: Layout, slots):
             a, b = off[ck]
             codes[:, h, t, :] = quant.unpack(rec[:, a:b])
             a, b = off[sk]
-            s[:, h, t, :], z[:, h, t, :] = sz_from_bytes(rec[:, a:b])
+            s[:, h, t, :], z[:, h, t, :] = sz_from_bytes(rec[:, a:b], lay.scale_bits)
     return codes, s, z
 
 

@@ -20,6 +20,13 @@ header and the design notes):
      alpha = 1 makes clipping a no-op.
   3. t = fl32(hi_c - lo_c); s = fp16_RNE(fl32(t / 3)); z = fp16_RNE(lo_c).
      Zero is a float offset, not an integer zero-point.
+     8-bit scale/zero (scale_bits = 8): the same with E4M3 in place of fp16,
+     rounded to nearest (ties to even), magnitudes above 448 saturating to
+     448.  E4M3 is the 8-bit float with 1 sign, 4 exponent (bias 7) and 3
+     mantissa bits whose all-ones exponent still encodes numbers (only
+     S.1111.111 is NaN), so the largest finite value is 1.75 * 2^8 = 448 and
+     the smallest subnormal 2^-9.  Every E4M3 value is exact in fp16, so the
+     rest of the recipe runs unchanged on the rounded values.
   4. Thresholds T_k = z + (k + 1/2) s (k = 0, 1, 2), exact (fp16 inputs, fp64 sum);
      code c = #{k : x_c >= T_k}; c = 0 when s == 0.  This is the nearest level
      of {z + c s}, ties upwards.
@@ -27,7 +34,9 @@ header and the design notes):
      codes 4j .. 4j+3 at bit offsets 0, 2, 4, 6.
   Dequantised value: s*c + z, exact in fp64.
 
-Pins (tests/test_oracle_quant.py): nearest level against brute force in exact
+Pins (tests/test_oracle_quant.py): the E4M3 value table against the
+format's defining formula at the landmark codes, nearest-value rounding
+against brute force over all finite codes, ties, saturation; nearest level against brute force in exact
 rational arithmetic (ties included), hand-computed scale/zero cases, the s = 0
 case, clip bounds, the pack example (1,2,3,0) -> 0x39, pack/unpack round trip,
 dequantisation error bound, bf16 rounding against torch's conversion, and the
@@ -78,12 +87,58 @@ def clip_bounds(lo, hi, alpha: float):
     return lo_c, hi_c
 
 
-def scale_zero(lo_c, hi_c):
-    """(s, z) as fp16 from the clip bounds, per the recipe."""
+E4M3_MAX = 448.0
+
+
+def e4m3_value(code) -> np.ndarray:
+    """Value (fp64) of E4M3 codes 0..255 by the format's definition: exponent
+    field E, mantissa M; E = 0 gives M * 2^-9, otherwise (1 + M/8) * 2^(E-7);
+    S.1111.111 is NaN."""
+    c = np.asarray(code, dtype=np.int64)
+    e, m = (c >> 3) & 15, c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(c & 0x80, -mag, mag)
+
+
+_E4M3_POS = e4m3_value(np.arange(0x7F))      # the 127 non-negative finite values, ascending
+
+
+def e4m3_round(x) -> np.ndarray:
+    """Nearest E4M3 value of fp32 input (ties to the even code), saturating at
+    448; returned as fp16 (exact).  The sign of a zero result follows x."""
+    a = np.abs(np.asarray(x, dtype=np.float32).astype(np.float64))
+    a = np.minimum(a, E4M3_MAX)
+    hi = np.searchsorted(_E4M3_POS, a, side="left").clip(max=len(_E4M3_POS) - 1)   # first value >= a
+    lo = np.maximum(hi - 1, 0)
+    vhi, vlo = _E4M3_POS[hi], _E4M3_POS[lo]
+    dhi, dlo = vhi - a, a - vlo
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    mag = np.where(a == vhi, vhi, np.where(pick_hi, vhi, vlo))
+    return np.where(np.signbit(np.asarray(x, np.float32)), -mag, mag).astype(np.float16)
+
+
+def e4m3_bits(v) -> np.ndarray:
+    """Codes (uint8) of E4M3 values given as fp16/fp32 (exact members of the format)."""
+    f = np.asarray(v, dtype=np.float64)
+    mag = np.abs(f)
+    idx = np.searchsorted(_E4M3_POS, mag)
+    if np.any(idx >= len(_E4M3_POS)) or np.any(_E4M3_POS[idx.clip(max=len(_E4M3_POS) - 1)] != mag):
+        raise ValueError("value is not an E4M3 number")
+    return (idx | np.where(np.signbit(f), 0x80, 0)).astype(np.uint8)
+
+
+def scale_zero(lo_c, hi_c, scale_bits: int = 16):
+    """(s, z) from the clip bounds, per the recipe: fp16, or E4M3 values held
+    in fp16 when scale_bits = 8."""
     t = (np.asarray(hi_c, np.float32) - np.asarray(lo_c, np.float32)).astype(np.float32)
-    s = (t / np.float32(3.0)).astype(np.float32).astype(np.float16)
-    z = np.asarray(lo_c, np.float32).astype(np.float16)
-    return s, z
+    s32 = (t / np.float32(3.0)).astype(np.float32)
+    z32 = np.asarray(lo_c, np.float32)
+    if scale_bits == 16:
+        return s32.astype(np.float16), z32.astype(np.float16)
+    if scale_bits == 8:
+        return e4m3_round(s32), e4m3_round(z32)
+    raise ValueError("scale_bits must be 16 or 8")
 
 
 def codes_from(xc, s, z) -> np.ndarray:
@@ -97,10 +152,11 @@ def codes_from(xc, s, z) -> np.ndarray:
     return np.where(s64 == 0.0, np.uint8(0), c).astype(np.uint8)
 
 
-def quantize(xr, group_size: int, alpha: float = 1.0):
+def quantize(xr, group_size: int, alpha: float = 1.0, scale_bits: int = 16):
     """Quantise rotated fp32 head-vectors xr [..., d].
 
-    Returns (codes uint8 [..., d], s fp16 [..., d/G], z fp16 [..., d/G]).
+    Returns (codes uint8 [..., d], s fp16 [..., d/G], z fp16 [..., d/G]); with
+    scale_bits = 8 the s and z are E4M3 values (held in fp16, exact).
     """
     xr = np.asarray(xr, dtype=np.float32)
     d = xr.shape[-1]
@@ -109,7 +165,7 @@ def quantize(xr, group_size: int, alpha: float = 1.0):
     g = xr.reshape(xr.shape[:-1] + (d // group_size, group_size))
     lo_c, hi_c = clip_bounds(g.min(axis=-1), g.max(axis=-1), alpha)
     xc = np.minimum(np.maximum(g, lo_c[..., None]), hi_c[..., None])
-    s, z = scale_zero(lo_c, hi_c)
+    s, z = scale_zero(lo_c, hi_c, scale_bits)
     c = codes_from(xc, s, z)
     return c.reshape(xr.shape), s, z
 

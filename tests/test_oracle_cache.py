@@ -133,3 +133,41 @@ def test_record_byte_offsets_lower_metadata(G, head_record):
             codes = quant.unpack(rec[base + 32 * t:base + 32 * (t + 1)])
             c, _, _ = quant.quantize(xt, G)
             assert np.array_equal(codes, c)
+
+
+def test_record_byte_offsets_8bit_scale_zero():
+    """G = 64 with E4M3 (s, z): 64 + 2 x 2 x 2 = 72-byte head records; byte
+    64 + 4 t + 2 g is group g's scale code of tensor t, the next byte its zero,
+    each decoded by the E4M3 definition (1 + M/8) 2^(E - 7)."""
+    lay = cache.Layout(128, 64, 2, 8, S, W, num_slots=3, max_requests=1, scale_bits=8)
+    assert lay.head_record_bytes == 72 and lay.record_bytes == 144
+    pool = cache.new_pool(lay)
+    rng = np.random.default_rng(64)
+    x = (rng.standard_normal((1, 2, 128)) * 2).astype(np.float32)
+    eye = np.stack([np.eye(128, dtype=np.float32)] * 2)
+    cache.append(pool, lay, x, 3 * x, [0], [S + 1], [2], [S + 2], eye, eye)
+    rec = pool.records[2]
+
+    def e4m3(b):                                # written out from the format
+        e, m = (b >> 3) & 15, b & 7
+        mag = m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+        return -mag if b & 0x80 else mag
+
+    for h in range(2):
+        base = 72 * h
+        for t, xt in enumerate((x[0, h], 3 * x[0, h])):
+            for g in range(2):
+                lo, hi = float(xt[g * 64:(g + 1) * 64].min()), float(xt[g * 64:(g + 1) * 64].max())
+                s_val, z_val = e4m3(int(rec[base + 64 + 4 * t + 2 * g])), e4m3(int(rec[base + 65 + 4 * t + 2 * g]))
+                s_ref = float(np.float32(np.float32(hi - lo) / np.float32(3)))
+                # nearest E4M3 values: within half a step (1/16 relative) of the fp32 inputs
+                assert abs(s_val - s_ref) <= s_ref / 16 + 2.0 ** -10
+                assert abs(z_val - lo) <= abs(lo) / 16 + 2.0 ** -10
+            codes = quant.unpack(rec[base + 32 * t:base + 32 * (t + 1)])
+            c, _, _ = quant.quantize(xt, 64, scale_bits=8)
+            assert np.array_equal(codes, c)
+    # the record reads back as the quantiser's codes, s and z
+    codes, s_rd, z_rd = cache.read_record(pool, lay, [2])
+    c, s8, z8 = quant.quantize(x[0], 64, scale_bits=8)
+    assert np.array_equal(codes[0, :, 0], c)
+    assert np.array_equal(s_rd[0, :, 0], s8) and np.array_equal(z_rd[0, :, 0], z8)

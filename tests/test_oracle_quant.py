@@ -122,3 +122,82 @@ def test_bf16_round_matches_torch():
     ref = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
     assert np.array_equal(quant.bf16_round(x), ref)
     assert np.array_equal(quant.bf16_from_bits(quant.bf16_bits(x)), ref)
+
+
+# ---------------------------------------------------------------------------
+# 8-bit (E4M3) scale and zero
+# ---------------------------------------------------------------------------
+
+def test_e4m3_landmark_codes():
+    """Values fixed by the format: 1 sign, 4 exponent bits (bias 7), 3 mantissa
+    bits, only S.1111.111 NaN."""
+    v = quant.e4m3_value
+    assert v(0x38) == 1.0 and v(0x40) == 2.0 and v(0x30) == 0.5
+    assert v(0x7E) == 448.0 and np.isnan(v(0x7F)) and np.isnan(v(0xFF))
+    assert v(0x01) == 2.0 ** -9 and v(0x07) == 7 * 2.0 ** -9 and v(0x08) == 2.0 ** -6
+    assert v(0x3C) == 1.5 and v(0xBC) == -1.5 and v(0x80) == 0.0
+    finite = v(np.arange(0x7F))
+    assert np.all(np.diff(finite) > 0)                      # codes 0..126 ascend
+    assert np.all(finite.astype(np.float16).astype(np.float64) == finite)   # exact in fp16
+
+
+def test_e4m3_round_is_nearest_with_even_ties():
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(4000) * 10.0 ** rng.uniform(-4, 3, 4000),
+                        [0.0, -0.0, 2.0 ** -10, 3 * 2.0 ** -10, 1.0625, 1.1875, 448.0, 464.0, 1e6, -1e6]])
+    x = x.astype(np.float32)
+    r = quant.e4m3_round(x).astype(np.float64)
+    finite = quant.e4m3_value(np.arange(0x7F))
+    for xi, ri in zip(x.astype(np.float64), r):
+        a = min(abs(xi), 448.0)
+        d = np.abs(finite - a)
+        best = finite[d == d.min()]
+        if len(best) == 1:
+            assert abs(ri) == best[0]
+        else:                                               # a tie: the even code
+            codes = [int(np.nonzero(finite == b)[0][0]) for b in best]
+            assert abs(ri) == finite[[c for c in codes if c % 2 == 0][0]]
+        assert (ri < 0) == (np.signbit(xi) and ri != 0) or ri == 0
+    # ties by hand: 1.0625 lies between 1.0 (0x38) and 1.125 (0x39): even code 0x38
+    assert quant.e4m3_round(np.float32(1.0625)) == 1.0
+    assert quant.e4m3_round(np.float32(1.1875)) == 1.25     # 0x39 / 0x3A: 0x3A
+    assert quant.e4m3_round(np.float32(3 * 2.0 ** -10)) == 2.0 ** -8   # 1.5 subnormal steps: even (2)
+    assert quant.e4m3_round(np.float32(1e6)) == 448.0 and quant.e4m3_round(np.float32(-500.0)) == -448.0
+
+
+def test_e4m3_bits_round_trip():
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)
+    vals = quant.e4m3_value(codes)
+    back = quant.e4m3_bits(vals)
+    assert np.array_equal(back, codes)
+    with pytest.raises(ValueError):
+        quant.e4m3_bits(np.array([1.0 + 2.0 ** -5]))
+
+
+def test_scale_zero_8bit_by_hand():
+    """Group min -1.3, max 2.2: t = 3.5, t/3 = 1.1666.. -> 1.125 (0x39: 1.1666 is nearer
+    1.125 than 1.25); z = -1.3 -> -1.25 (E4M3 neighbours -1.25, -1.375)."""
+    s, z = quant.scale_zero(np.float32(-1.3), np.float32(2.2), scale_bits=8)
+    assert float(s) == 1.125 and float(z) == -1.25
+    x = np.array([-1.3, -0.7, 0.45, 2.2, 1.0, 0.0] + [0.0] * 58, np.float32)
+    c, s8, z8 = quant.quantize(x[None], 64, scale_bits=8)
+    # thresholds z + (k + 1/2) s = -0.6875, 0.4375, 1.5625
+    assert list(c[0, :6]) == [0, 0, 2, 3, 2, 1]
+    assert float(s8[0, 0]) == 1.125 and float(z8[0, 0]) == -1.25
+
+
+def test_quantize_8bit_error_bound():
+    """|x - (s c + z)| <= s/2 + |z - lo| for every element: the levels sit on the
+    E4M3 grid, so the bound grows by how far z rounded from the group minimum,
+    and values above z + 3 s clip to the top level."""
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal((200, 128)) * rng.uniform(0.01, 30, (200, 1))).astype(np.float32)
+    c, s, z = quant.quantize(x, 64, scale_bits=8)
+    deq = quant.dequantize(c, s, z, 64)
+    g = x.reshape(200, 2, 64).astype(np.float64)
+    lo, hi = g.min(-1), g.max(-1)
+    s64, z64 = s.astype(np.float64), z.astype(np.float64)
+    top = z64 + 3 * s64
+    bound = s64 / 2 + np.abs(z64 - lo) + np.maximum(0, hi - top)
+    err = np.abs(g - deq.reshape(200, 2, 64)).max(-1)
+    assert np.all(err <= bound * (1 + 1e-12))

@@ -63,6 +63,8 @@ typedef struct {
     int32_t recent_tokens;  /* W, BF16 recent window (the pages use 256); 1..4096 */
     int64_t num_slots;      /* INT2 pool capacity in tokens (page_size = 1) */
     int32_t max_requests;   /* rows of the sink/recent stores */
+    int32_t scale_bits;     /* bits of each stored scale and zero: 16 (fp16) or
+                               8 (E4M3, G = 64 only); 0 means 16 */
 } oscar_layout;
 
 /*
@@ -78,6 +80,12 @@ typedef struct {
  *   significant bits first: byte j holds channels 4j .. 4j+3 at bit offsets
  *   0, 2, 4, 6.  (s, z): for each of the n_g groups of G contiguous rotated
  *   channels, fp16 scale s then fp16 zero z.  Element value = s * code + z.
+ *   With scale_bits = 8 (G = 64) each (s, z) is two E4M3 codes instead, s
+ *   first (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; largest
+ *   finite value 448, only S.1111.111 is NaN), so B = 72:
+ *     [64, 68)  K (s0, z0, s1, z1)     [68, 72)  V (s0, z0, s1, z1)
+ *   The quantiser rounds s and z to E4M3 to nearest (ties to even),
+ *   saturating at +-448, then picks codes against the rounded values.
  * sink:    [max_requests][S][Hkv][2][128] bf16 (2 = K, V), rotated basis,
  *          position p < S at index p.
  * recent:  [max_requests][W][Hkv][2][128] bf16 ring, rotated basis,

@@ -49,6 +49,7 @@ class CLayout(ctypes.Structure):
         ("num_kv_heads", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
         ("sink_tokens", ctypes.c_int32), ("recent_tokens", ctypes.c_int32),
         ("num_slots", ctypes.c_int64), ("max_requests", ctypes.c_int32),
+        ("scale_bits", ctypes.c_int32),
     ]
 
 
@@ -128,10 +129,12 @@ class Layout:
     recent_tokens: int = 256
     num_slots: int = 0
     max_requests: int = 1
+    scale_bits: int = 16      # 16: fp16 (s, z); 8: E4M3 (s, z), group_size 64 only
 
     def c(self) -> CLayout:
         return CLayout(self.head_dim, self.group_size, self.num_kv_heads, self.num_q_heads,
-                       self.sink_tokens, self.recent_tokens, self.num_slots, self.max_requests)
+                       self.sink_tokens, self.recent_tokens, self.num_slots, self.max_requests,
+                       self.scale_bits)
 
 
 def _ptr(t) -> Optional[int]:

@@ -37,3 +37,30 @@ __device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
 }
 
 }  // namespace oscar
+
+// E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; the all-ones
+// exponent still holds numbers, largest finite 448): the 8-bit scale/zero
+// format.  Value of a code (codes 0x7F / 0xFF, NaN, are never written).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
+    const uint32_t e = (code >> 3) & 15u, m = code & 7u;
+    const float mag = e == 0 ? float(m) * 0x1p-9f : __builtin_ldexpf(float(8u + m), int(e) - 10);
+    return (code & 0x80u) ? -mag : mag;
+}
+
+// Code of the E4M3 value nearest to x (ties to the even code), magnitudes
+// above 448 saturating to 448; a zero result keeps the sign of x.  The scaled
+// magnitude is exact in fp32 (a power-of-two scaling) and rounded once to an
+// integer with the current round-to-nearest-even mode.
+__device__ __forceinline__ uint32_t e4m3_code_rn(float x) {
+    const float a = fminf(fabsf(x), 448.0f);
+    uint32_t mag;
+    if (a < 0x1p-6f) {
+        mag = uint32_t(__builtin_rintf(a * 512.0f));        // subnormal steps of 2^-9; 8 is 2^-6 (code 8)
+    } else {
+        int e2 = 0;
+        (void)__builtin_frexpf(a, &e2);                     // a in [2^(e2 - 1), 2^e2)
+        const uint32_t q = uint32_t(__builtin_rintf(__builtin_ldexpf(a, 4 - e2)));   // 8 .. 16
+        mag = (uint32_t(e2 - 1 + 7) << 3) + (q - 8u);     // q = 16 carries into the exponent
+    }
+    return mag | (__builtin_signbitf(x) ? 0x80u : 0u);
+}

@@ -77,6 +77,7 @@ struct DecodeArgs {
     int32_t waves;     // KV heads per workgroup
     int32_t head_chunks;
     int32_t group_size;
+    int32_t scale_bits;       // 16 (fp16 s, z) or 8 (E4M3 s, z)
     // extend: every batch row is request fixed_req at length fixed_len, and
     // item extra_item reads the rotated new tokens 0 .. row (causal)
     int32_t fixed_req;        // -1 for decode
@@ -373,12 +374,14 @@ __device__ __forceinline__ void wait_vmem() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int GQ, int NG>
+// NG groups per head vector; SZB bytes per group's (s, z): 4 (fp16) or 2 (E4M3)
+template <int GQ, int NG, int SZB>
 __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, int j, int hc, int p0, int p1,
                           uint8_t *smem) {
     static_assert(NG == 4 || NG == 2 || NG == 1, "four, two or one (s, z) groups per head vector");
+    static_assert(SZB == 4 || (SZB == 2 && NG == 2), "E4M3 (s, z) with two groups");
     constexpr int HS = (GQ + 3) / 4;          // sets of 4 query heads
-    constexpr int kRecH = 2 * kCodeBytes + 8 * NG;        // head record: 96 or 80 bytes
+    constexpr int kRecH = 2 * kCodeBytes + 2 * NG * SZB;  // head record: 96, 80 or 72 bytes
     constexpr int kUnitsH = kRecH / 16;                   // whole units of a head record
     constexpr int kTokB = 4 * kRecH;                      // one token of the 4-head chunk
     constexpr int kTokUnits = kTokB / 16;                 // 24, 20 or 18 units
@@ -457,7 +460,7 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
         tq[u] = t;
         // units past the chunk's heads (never read) repeat an in-range unit; with
         // 72-byte records the chunk holds an even number of heads (whole units)
-        if constexpr (NG == 1)
+        if constexpr (kRecH % 16 != 0)
             src_base[u] = a.records + hc * kTokB + 16 * (16 * q + 16 <= nh * kRecH ? q : 0);
         else
             src_base[u] = a.records + hc * kTokB + 16 * (q / kUnitsH < nh ? q : q % kUnitsH);
@@ -556,7 +559,7 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
     } else {
         qk_at = lds_pin(rec_at(n, 8 * kb));
         szk_at = lds_pin(rec_at(n, 2 * kCodeBytes));
-        szv_at = lds_pin(rec_at(n, 2 * kCodeBytes + 4 * NG));
+        szv_at = lds_pin(rec_at(n, 2 * kCodeBytes + SZB * NG));
 #pragma unroll
         for (int i = 0; i < 8; ++i) pv_at[i] = lds_pin(rec_at(2 * (i & 1) + 8 * (i >> 1) + kb_tok, kCodeBytes + 2 * n));
         const uint32_t wb = st0 + int2_lds_bytes() + w * kWeightWave;   // after the stages and the ring
@@ -586,6 +589,14 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
                 for (int g = 0; g < 4; ++g) {
                     szk[g] = k4[g];
                     szv[hf][g] = v4[g];
+                }
+            } else if constexpr (SZB == 2) {
+                // E4M3 (s0, z0, s1, z1) bytes -> fp16 pairs (exact)
+                const uint32_t k4 = lds_ld<uint32_t>(szk_at + ho), v4 = lds_ld<uint32_t>(szv_at + ho);
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    szk[g] = pk_rn(e4m3_to_f32((k4 >> (16 * g)) & 0xFFu), e4m3_to_f32((k4 >> (16 * g + 8)) & 0xFFu));
+                    szv[hf][g] = pk_rn(e4m3_to_f32((v4 >> (16 * g)) & 0xFFu), e4m3_to_f32((v4 >> (16 * g + 8)) & 0xFFu));
                 }
             } else if constexpr (NG == 2) {
                 const u32x2 k2 = lds_ld<u32x2>(szk_at + ho), v2 = lds_ld<u32x2>(szv_at + ho);
@@ -945,7 +956,7 @@ __device__ __forceinline__ void bf16_item(const DecodeArgs &a, int b, int req, i
     }
 }
 
-template <int GQ, int NG>
+template <int GQ, int NG, int SZB>
 __global__ __launch_bounds__(64 * kPartialWaves) void partial_kernel(DecodeArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int id = blockIdx.x;
@@ -965,7 +976,7 @@ __global__ __launch_bounds__(64 * kPartialWaves) void partial_kernel(DecodeArgs 
         float *pbuf = reinterpret_cast<float *>(smem) + w * kBf16WaveFloats;
         bf16_item(a, b, req, j, active ? hk : 0, p0, p1, active, pbuf);
     } else if (a.num_slots > 0) {
-        int2_item<GQ, NG>(a, b, req, j, hc, p0, p1, smem);   // every wave: the loads are shared
+        int2_item<GQ, NG, SZB>(a, b, req, j, hc, p0, p1, smem);   // every wave: the loads are shared
     }
 }
 
@@ -977,9 +988,9 @@ __global__ __launch_bounds__(64 * kPartialWaves) void partial_kernel(DecodeArgs 
 // (s, z) staged in LDS, v = s c + z formed per token.
 constexpr int kLmChunk = 64;
 
-template <int NG>
+template <int NG, int SZB>
 __global__ __launch_bounds__(64 * kPartialWaves) void hist_lowmeta_kernel(DecodeArgs a) {
-    constexpr int kRec = 2 * kCodeBytes + 8 * NG;          // head record bytes
+    constexpr int kRec = 2 * kCodeBytes + 2 * NG * SZB;    // head record bytes
     constexpr int kG = kHeadDim / NG;                       // channels per group
     __shared__ __attribute__((aligned(16))) float qs_all[kPartialWaves][kMaxGroup][kHeadDim];
     __shared__ __attribute__((aligned(16))) float ps_all[kPartialWaves][kLmChunk][kMaxGroup];
@@ -1040,13 +1051,20 @@ __global__ __launch_bounds__(64 * kPartialWaves) void hist_lowmeta_kernel(Decode
             kc[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(base) + i);
             vv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(base + kCodeBytes) + i);
         }
-        uint32_t ksz[NG];
+        uint32_t ksz[NG];                                   // (s, z) of K as an fp16 pair
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) {
-            ksz[gi] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(base + 2 * kCodeBytes) + gi);
-            const uint32_t vw = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(base + 2 * kCodeBytes + 4 * NG) + gi);
-            vsz[lane][gi] = make_float2(__half2float(__ushort_as_half(uint16_t(vw))),
-                                        __half2float(__ushort_as_half(uint16_t(vw >> 16))));
+            if constexpr (SZB == 4) {
+                ksz[gi] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(base + 2 * kCodeBytes) + gi);
+                const uint32_t vw = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(base + 2 * kCodeBytes + 4 * NG) + gi);
+                vsz[lane][gi] = make_float2(__half2float(__ushort_as_half(uint16_t(vw))),
+                                            __half2float(__ushort_as_half(uint16_t(vw >> 16))));
+            } else {                                        // E4M3 codes, s first
+                const uint32_t kw = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(base + 2 * kCodeBytes) + gi);
+                const uint32_t vw = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(base + 2 * kCodeBytes + 2 * NG) + gi);
+                ksz[gi] = pk_rn(e4m3_to_f32(kw & 0xFFu), e4m3_to_f32(kw >> 8));
+                vsz[lane][gi] = make_float2(e4m3_to_f32(vw & 0xFFu), e4m3_to_f32(vw >> 8));
+            }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -1292,12 +1310,14 @@ size_t partial_lds_bytes(const DecodeArgs &a) {
 template <int GQ>
 hipError_t launch_partial(const DecodeArgs &a, int blocks, hipStream_t stream) {
     const size_t lds = partial_lds_bytes(a);
-    if (a.group_size == 64)
-        hipLaunchKernelGGL((partial_kernel<GQ, 2>), dim3(blocks), dim3(64 * kPartialWaves), lds, stream, a);
+    if (a.group_size == 64 && a.scale_bits == 8)
+        hipLaunchKernelGGL((partial_kernel<GQ, 2, 2>), dim3(blocks), dim3(64 * kPartialWaves), lds, stream, a);
+    else if (a.group_size == 64)
+        hipLaunchKernelGGL((partial_kernel<GQ, 2, 4>), dim3(blocks), dim3(64 * kPartialWaves), lds, stream, a);
     else if (a.group_size == 128)
-        hipLaunchKernelGGL((partial_kernel<GQ, 1>), dim3(blocks), dim3(64 * kPartialWaves), lds, stream, a);
+        hipLaunchKernelGGL((partial_kernel<GQ, 1, 4>), dim3(blocks), dim3(64 * kPartialWaves), lds, stream, a);
     else
-        hipLaunchKernelGGL((partial_kernel<GQ, 4>), dim3(blocks), dim3(64 * kPartialWaves), lds, stream, a);
+        hipLaunchKernelGGL((partial_kernel<GQ, 4, 4>), dim3(blocks), dim3(64 * kPartialWaves), lds, stream, a);
     return hipGetLastError();
 }
 
@@ -1374,6 +1394,7 @@ DecodeArgs make_args(const oscar_layout *layout, const oscar_pool *pool, const v
     a.waves = kPartialWaves;
     a.head_chunks = (a.hkv + kPartialWaves - 1) / kPartialWaves;
     a.group_size = layout->group_size;
+    a.scale_bits = scale_bits(*layout);
     a.fixed_req = -1;
     a.fixed_len = 0;
     a.extra_item = plan.extra_item;
@@ -1402,7 +1423,7 @@ oscar_status launch_decode(const DecodeArgs &a, const DecodePlan &plan, hipStrea
         }
         e = launch_extend_bf16(*xh, stream);
         if (e != hipSuccess) return fail(OSCAR_ERR_HIP, std::string("extend bf16 launch: ") + hipGetErrorString(e));
-    } else if (a.group_size == 128 && (a.hkv & 1)) {
+    } else if (head_record_bytes(a.group_size, a.scale_bits) % 16 != 0 && (a.hkv & 1)) {
         // 72-byte records and an odd number of KV heads (a 4-head chunk would
         // end inside a 16-byte unit): the BF16 windows (items 0, 1) on
         // partial_kernel, the history items on hist_lowmeta_kernel
@@ -1420,7 +1441,10 @@ oscar_status launch_decode(const DecodeArgs &a, const DecodePlan &plan, hipStrea
         if (e != hipSuccess) return fail(OSCAR_ERR_HIP, std::string("partial launch: ") + hipGetErrorString(e));
         const int h_blocks = (plan.items - 2) * a.batch * a.head_chunks;
         if (h_blocks > 0 && a.num_slots > 0) {
-            hipLaunchKernelGGL(hist_lowmeta_kernel<1>, dim3(h_blocks), dim3(64 * kPartialWaves), 0, stream, a);
+            if (a.scale_bits == 8)
+                hipLaunchKernelGGL((hist_lowmeta_kernel<2, 2>), dim3(h_blocks), dim3(64 * kPartialWaves), 0, stream, a);
+            else
+                hipLaunchKernelGGL((hist_lowmeta_kernel<1, 4>), dim3(h_blocks), dim3(64 * kPartialWaves), 0, stream, a);
             e = hipGetLastError();
             if (e != hipSuccess) return fail(OSCAR_ERR_HIP, std::string("history launch: ") + hipGetErrorString(e));
         }
@@ -1541,6 +1565,7 @@ extern "C" oscar_status oscar_extend_attn(hipStream_t stream, const oscar_layout
     xh.out = out;
     xh.out_dtype = out_dtype;
     xh.group_size = layout->group_size;
+    xh.scale_bits = scale_bits(*layout);
     if (extend_history_blocks(xh) > INT32_MAX || extend_bf16_blocks(xh) > INT32_MAX)
         return fail(OSCAR_ERR_UNSUPPORTED, "new tokens x work items exceeds one launch grid");
 

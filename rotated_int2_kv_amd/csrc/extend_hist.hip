@@ -211,11 +211,23 @@ __device__ __forceinline__ void flash_step(const _Float16 (*kd)[kTile][kKdStride
 
 // At most 128 VGPRs (launch bound of 4 waves per SIMD): two workgroups per
 // compute unit overlap one another's dequantisation, barriers and MFMA work.
-// NG = groups per head vector (4, 2, 1 for G = 32, 64, 128): head records of
-// 96, 80 or 72 bytes, staged in 16-byte units (8-byte units for 72).
-template <int NG>
+// NG = groups per head vector (4, 2, 1 for G = 32, 64, 128), SZB = bytes of
+// one group's (s, z) (4: fp16, 2: E4M3 codes): head records of 96, 80 or 72
+// bytes, staged in 16-byte units (8-byte units for 72).
+template <int NG, int SZB>
 __global__ __launch_bounds__(kThreads, 4) void extend_hist_kernel(ExtendHistArgs a) {
-    constexpr int kRec = 2 * kCodeBytes + 8 * NG;
+    constexpr int kRec = 2 * kCodeBytes + 2 * NG * SZB;
+    // (s, z) stored at p, times 1/8 (exact); group g of tensor t (0 = K, 1 = V)
+    // sits at byte 64 + (t NG + g) SZB of a head record
+    auto load_sz = [](const uint8_t *p) -> float2 {
+        if constexpr (SZB == 4) {
+            const uint32_t w = *reinterpret_cast<const uint32_t *>(p);
+            return make_float2(sz_s(w) * kDqScale, sz_z(w) * kDqScale);
+        } else {
+            const uint32_t w = *reinterpret_cast<const uint16_t *>(p);
+            return make_float2(e4m3_to_f32(w & 0xFFu) * kDqScale, e4m3_to_f32(w >> 8) * kDqScale);
+        }
+    };
     constexpr int kUnit = kRec % 16 == 0 ? 16 : 8;
     constexpr int kUnits = kRec / kUnit;
     using Unit = std::conditional_t<kUnit == 16, u32x4, u32x2>;
@@ -291,8 +303,8 @@ __global__ __launch_bounds__(kThreads, 4) void extend_hist_kernel(ExtendHistArgs
         {
             const int t = tid >> 4, part = tid & 15;
             const uint32_t cw = *reinterpret_cast<const uint16_t *>(raw + t * kRec + 2 * part);
-            const uint32_t szw = *reinterpret_cast<const uint32_t *>(raw + t * kRec + 64 + 4 * (part * NG / 16));
-            const float s = sz_s(szw) * kDqScale, z = sz_z(szw) * kDqScale;     // exact
+            const float2 sz = load_sz(raw + t * kRec + 2 * kCodeBytes + SZB * (part * NG / 16));
+            const float s = sz.x, z = sz.y;
             uint32_t h01, l01, h23, l23;
             split2(z, s + z, h01, l01);                       // s + z: fmaf(s, 1, z)
             split2(fmaf(s, 2.0f, z), fmaf(s, 3.0f, z), h23, l23);
@@ -314,14 +326,15 @@ __global__ __launch_bounds__(kThreads, 4) void extend_hist_kernel(ExtendHistArgs
         // value; 8-byte row writes (at most 2 lanes of 16 per bank)
         {
             const int cp = tid & 63, tq = tid >> 6;
-            const int byte = 32 + (cp >> 1), sh = 4 * (cp & 1), sz_off = 64 + 4 * NG + 4 * (cp * NG / 64);
+            const int byte = 32 + (cp >> 1), sh = 4 * (cp & 1);
+            const int sz_off = 2 * kCodeBytes + SZB * NG + SZB * (cp * NG / 64);
             float x0[4], x1[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int t = 4 * tq + k;
                 const uint32_t c = uint32_t(raw[t * kRec + byte]) >> sh;
-                const uint32_t szw = *reinterpret_cast<const uint32_t *>(raw + t * kRec + sz_off);
-                const float s = sz_s(szw) * kDqScale, z = sz_z(szw) * kDqScale;
+                const float2 sz = load_sz(raw + t * kRec + sz_off);
+                const float s = sz.x, z = sz.y;
                 x0[k] = fmaf(s, float(c & 3u), z);
                 x1[k] = fmaf(s, float((c >> 2) & 3u), z);
             }
@@ -568,10 +581,14 @@ int64_t extend_history_blocks(const ExtendHistArgs &a) {
 hipError_t launch_extend_history(const ExtendHistArgs &a, hipStream_t stream) {
     const int64_t blocks = extend_history_blocks(a);
     if (blocks <= 0) return hipSuccess;
+    if (a.scale_bits == 8) {
+        hipLaunchKernelGGL((extend_hist_kernel<2, 2>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a);
+        return hipGetLastError();
+    }
     switch (a.group_size) {
-        case 64: hipLaunchKernelGGL(extend_hist_kernel<2>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a); break;
-        case 128: hipLaunchKernelGGL(extend_hist_kernel<1>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a); break;
-        default: hipLaunchKernelGGL(extend_hist_kernel<4>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a); break;
+        case 64: hipLaunchKernelGGL((extend_hist_kernel<2, 4>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a); break;
+        case 128: hipLaunchKernelGGL((extend_hist_kernel<1, 4>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a); break;
+        default: hipLaunchKernelGGL((extend_hist_kernel<4, 4>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a); break;
     }
     return hipGetLastError();
 }

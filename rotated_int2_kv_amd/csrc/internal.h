@@ -27,12 +27,18 @@ oscar_status ok();
 // Full validation of a layout (shape support included).
 oscar_status check_layout(const oscar_layout *lay);
 
+// Bits of each stored scale and zero (0 in the struct means 16).
+inline int scale_bits(const oscar_layout &lay) { return lay.scale_bits == 0 ? 16 : lay.scale_bits; }
+
 // Head record of group size G: K codes, V codes, then (s, z) of K and of V per
-// group: 96 bytes at G = 32, 80 at 64, 72 at 128.
-inline int head_record_bytes(int group_size) { return 2 * kCodeBytes + 2 * 4 * (kHeadDim / group_size); }
+// group: 96 bytes at G = 32, 80 at 64, 72 at 128 with fp16 (s, z); 72 at
+// G = 64 with E4M3 (s, z).
+inline int head_record_bytes(int group_size, int sz_bits = 16) {
+    return 2 * kCodeBytes + 2 * 2 * (sz_bits / 8) * (kHeadDim / group_size);
+}
 
 inline int64_t record_bytes(const oscar_layout &lay) {
-    return static_cast<int64_t>(lay.num_kv_heads) * head_record_bytes(lay.group_size);
+    return static_cast<int64_t>(lay.num_kv_heads) * head_record_bytes(lay.group_size, scale_bits(lay));
 }
 
 // Split-K plan of one decode call (pure function of the host lengths).
@@ -94,6 +100,7 @@ struct ExtendHistArgs {
     void *out;                    // [n_new][Hq][128] of out_dtype
     int32_t out_dtype;
     int32_t group_size;
+    int32_t scale_bits;           // 16 (fp16 s, z) or 8 (E4M3 s, z)
 };
 // Grid sizes of the two launches (row_blocks x items x hkv).
 int64_t extend_history_blocks(const ExtendHistArgs &a);

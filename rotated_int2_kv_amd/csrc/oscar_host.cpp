@@ -32,6 +32,10 @@ oscar_status check_layout(const oscar_layout *lay) {
         return fail(OSCAR_ERR_INVALID_ARG, "group_size must divide head_dim");
     if (lay->group_size != 32 && lay->group_size != 64 && lay->group_size != 128)
         return fail(OSCAR_ERR_UNSUPPORTED, "group_size must be 32, 64 or 128");
+    if (lay->scale_bits != 0 && lay->scale_bits != 16 && lay->scale_bits != 8)
+        return fail(OSCAR_ERR_INVALID_ARG, "scale_bits must be 16 or 8 (0 means 16)");
+    if (lay->scale_bits == 8 && lay->group_size != 64)
+        return fail(OSCAR_ERR_UNSUPPORTED, "8-bit scale/zero needs group_size 64");
     if (lay->num_q_heads % lay->num_kv_heads != 0)
         return fail(OSCAR_ERR_INVALID_ARG, "num_q_heads must be a multiple of num_kv_heads");
     if (lay->num_kv_heads > kMaxKvHeads)

@@ -72,7 +72,8 @@ __device__ __forceinline__ void split3(float x, uint16_t &a, uint16_t &b, uint16
     c = bf16_bits_rn(r2);
 }
 
-template <int XT, int NGW>
+// SZB: bytes of one group's (s, z): 4 (two fp16) or 2 (two E4M3 codes)
+template <int XT, int NGW, int SZB>
 __global__ __launch_bounds__(kThreads) void quant_append_kernel(AppendArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds_buf[2][XT * kPlaneBytes];
     __shared__ float2 grp_stat[kWaves][kTile];             // per wave and token: (min, max)
@@ -174,8 +175,8 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(AppendArgs a) {
         }
     };
 
-    constexpr int kHeadRec = 2 * kCodeBytes + 2 * 4 * (kWaves / NGW);     // head record of this group size
-    constexpr int kSzTensor = 4 * (kWaves / NGW);                          // (s, z) bytes per tensor
+    constexpr int kHeadRec = 2 * kCodeBytes + 2 * SZB * (kWaves / NGW);   // head record of this layout
+    constexpr int kSzTensor = SZB * (kWaves / NGW);                        // (s, z) bytes per tensor
     const int64_t rec_bytes = int64_t(a.hkv) * kHeadRec;
     // kDepth tiles of input in flight in registers (the waits are the
     // compiler's); the LDS tile is double-buffered, so one barrier per tile
@@ -296,12 +297,25 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(AppendArgs a) {
         // range / 3 rounded to nearest fp32: the fp64 product is within 2^-52
         // (relative) of the quotient, and a quotient by 3 of an fp32 value is
         // never within 2^-25 (relative) of a midpoint between fp32 values
-        const __half s = __float2half_rn(float(double(range) * (1.0 / 3.0)));
-        const __half z = __float2half_rn(lo_c);
+        const float s32 = float(double(range) * (1.0 / 3.0));
+        // the stored (s, z): fp16, or E4M3 codes (every E4M3 value is an fp16 value)
+        uint32_t sz_word;
+        double sd, zd;
+        if constexpr (SZB == 4) {
+            const __half s = __float2half_rn(s32);
+            const __half z = __float2half_rn(lo_c);
+            sz_word = uint32_t(__half_as_ushort(s)) | (uint32_t(__half_as_ushort(z)) << 16);
+            sd = double(__half2float(s));
+            zd = double(__half2float(z));
+        } else {
+            const uint32_t sc = e4m3_code_rn(s32), zc = e4m3_code_rn(lo_c);
+            sz_word = sc | (zc << 8);
+            sd = double(e4m3_to_f32(sc));
+            zd = double(e4m3_to_f32(zc));
+        }
         // thresholds z + (k + 1/2) s: exact in fp64 (fp16 operands, sums below
         // 2^19 on a 2^-25 grid), rounded up to fp32 so that "x >= T" is exact
         // for fp32 x; a scale of zero gives +inf thresholds (codes 0)
-        const double sd = double(__half2float(s)), zd = double(__half2float(z));
         const bool zero_scale = sd == 0.0;
         const float u0 = zero_scale ? INFINITY : round_up_f32(zd + 0.5 * sd);
         const float u1 = zero_scale ? INFINITY : round_up_f32(zd + 1.5 * sd);
@@ -319,8 +333,11 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(AppendArgs a) {
         uint8_t *rec = a.records + int64_t(slot) * rec_bytes + h * kHeadRec;
         *reinterpret_cast<uint16_t *>(rec + t * kCodeBytes + 8 * w + 2 * kb) = uint16_t(packed);
         if (kb == 0 && (w & (NGW - 1)) == 0) {            // one writer per group
-            const uint32_t sz = uint32_t(__half_as_ushort(s)) | (uint32_t(__half_as_ushort(z)) << 16);
-            *reinterpret_cast<uint32_t *>(rec + 2 * kCodeBytes + t * kSzTensor + 4 * (w / NGW)) = sz;
+            uint8_t *dst = rec + 2 * kCodeBytes + t * kSzTensor + SZB * (w / NGW);
+            if constexpr (SZB == 4)
+                *reinterpret_cast<uint32_t *>(dst) = sz_word;
+            else
+                *reinterpret_cast<uint16_t *>(dst) = uint16_t(sz_word);
         }
         if (pos >= L - a.recent_tokens) {
             uint16_t *dst = a.recent +
@@ -332,16 +349,19 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(AppendArgs a) {
     }
 }
 
-// the kernel for (input dtype, group size)
-const void *append_kernel(oscar_dtype in_dtype, int group_size) {
+// the kernel for (input dtype, group size, scale/zero bits)
+const void *append_kernel(oscar_dtype in_dtype, int group_size, int sz_bits) {
     const bool bf = in_dtype == OSCAR_BF16;
+    if (sz_bits == 8)                                   // group size 64 (checked with the layout)
+        return bf ? reinterpret_cast<const void *>(quant_append_kernel<1, 2, 2>)
+                  : reinterpret_cast<const void *>(quant_append_kernel<3, 2, 2>);
     switch (group_size) {
-        case 64: return bf ? reinterpret_cast<const void *>(quant_append_kernel<1, 2>)
-                           : reinterpret_cast<const void *>(quant_append_kernel<3, 2>);
-        case 128: return bf ? reinterpret_cast<const void *>(quant_append_kernel<1, 4>)
-                            : reinterpret_cast<const void *>(quant_append_kernel<3, 4>);
-        default: return bf ? reinterpret_cast<const void *>(quant_append_kernel<1, 1>)
-                           : reinterpret_cast<const void *>(quant_append_kernel<3, 1>);
+        case 64: return bf ? reinterpret_cast<const void *>(quant_append_kernel<1, 2, 4>)
+                           : reinterpret_cast<const void *>(quant_append_kernel<3, 2, 4>);
+        case 128: return bf ? reinterpret_cast<const void *>(quant_append_kernel<1, 4, 4>)
+                            : reinterpret_cast<const void *>(quant_append_kernel<3, 4, 4>);
+        default: return bf ? reinterpret_cast<const void *>(quant_append_kernel<1, 1, 4>)
+                           : reinterpret_cast<const void *>(quant_append_kernel<3, 1, 4>);
     }
 }
 
@@ -382,7 +402,7 @@ extern "C" oscar_status oscar_quant_append(hipStream_t stream, const oscar_layou
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return fail(OSCAR_ERR_HIP, "querying the device failed");
-        const void *kern = append_kernel(in_dtype, layout->group_size);
+        const void *kern = append_kernel(in_dtype, layout->group_size, scale_bits(*layout));
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, 0) != hipSuccess)
             return fail(OSCAR_ERR_HIP, "occupancy query failed");
         const int slots = std::max(1, cus * std::max(1, per_cu));
@@ -422,7 +442,7 @@ extern "C" oscar_status oscar_quant_append(hipStream_t stream, const oscar_layou
             return fail(OSCAR_ERR_HIP, "hipEventRecord failed");
     }
     void *kargs[] = {&args};
-    hipError_t e = hipLaunchKernel(append_kernel(in_dtype, layout->group_size), dim3(blocks), dim3(kThreads),
+    hipError_t e = hipLaunchKernel(append_kernel(in_dtype, layout->group_size, scale_bits(*layout)), dim3(blocks), dim3(kThreads),
                                    kargs, 0, stream);
     if (e == hipSuccess) e = hipGetLastError();
     if (e != hipSuccess) return fail(OSCAR_ERR_HIP, std::string("quant_append launch: ") + hipGetErrorString(e));

@@ -58,6 +58,7 @@ class Workload:
     seed: int
     head_dim: int = HEAD_DIM
     group_size: int = GROUP_SIZE
+    scale_bits: int = 16        # stored scale/zero: fp16, or E4M3 (8) at group size 64
     sink: int = SINK_TOKENS
     recent: int = RECENT_TOKENS
 

@@ -27,7 +27,8 @@ def say(*a):
 def layouts(w: workloads.Workload, num_slots: int, max_requests: int):
     from rotated_int2_kv_amd import binding as B
     kw = dict(head_dim=w.head_dim, group_size=w.group_size, num_kv_heads=w.num_kv_heads,
-              num_q_heads=w.num_q_heads, num_slots=num_slots, max_requests=max_requests)
+              num_q_heads=w.num_q_heads, num_slots=num_slots, max_requests=max_requests,
+              scale_bits=w.scale_bits)
     return (B.Layout(sink_tokens=w.sink, recent_tokens=w.recent, **kw),
             cache.Layout(sink=w.sink, recent=w.recent, **kw))
 

@@ -368,3 +368,17 @@ def test_lower_metadata_layouts(G, head_record):
     lay = L(group_size=G)
     B.oscar_layout_check(lay)
     assert B.oscar_pool_bytes(lay, 0) == 1000 * 8 * head_record
+
+
+def test_eight_bit_scale_zero_layouts():
+    """E4M3 (s, z): G = 64 only, 72-byte head records; 0 reads as 16 bits."""
+    lay = L(group_size=64, scale_bits=8)
+    B.oscar_layout_check(lay)
+    assert B.oscar_pool_bytes(lay, 0) == 1000 * 8 * 72
+    assert B.oscar_pool_bytes(L(group_size=64, scale_bits=0), 0) == 1000 * 8 * 80
+    for bad, st in ((dict(group_size=32, scale_bits=8), B.OSCAR_ERR_UNSUPPORTED),
+                    (dict(group_size=128, scale_bits=8), B.OSCAR_ERR_UNSUPPORTED),
+                    (dict(group_size=64, scale_bits=12), B.OSCAR_ERR_INVALID_ARG)):
+        with pytest.raises(B.OscarError) as ei:
+            B.oscar_layout_check(L(**bad))
+        assert ei.value.status == st

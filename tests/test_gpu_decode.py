@@ -206,20 +206,20 @@ def test_decode_skips_out_of_range_slot_ids():
     _compare(o_gpu, o_ref, "out-of-range slots")
 
 
-@pytest.mark.parametrize("G", [64, 128])
+@pytest.mark.parametrize("G,sb", [(64, 16), (128, 16), (64, 8)])
 @pytest.mark.parametrize("wname,lens,chunk", [
     ("tiny", (1024,), 0),
     ("decode_small", (1500, 777, 3001, 321), 0),
     ("decode_small", (1500, 777, 3001, 321), 96),
     ("mixed_small", (1, 63, 64, 65, 319, 320, 321, 352, 353, 385), 32),
 ])
-def test_decode_lower_metadata(G, wname, lens, chunk):
-    """Groups of 64 and 128 channels (80- and 72-byte head records) decode the
-    oracle-written pool to the same bar."""
-    w = workloads.custom(wname, batch=len(lens), seq_lens=tuple(lens), group_size=G)
+def test_decode_lower_metadata(G, sb, wname, lens, chunk):
+    """Groups of 64 and 128 channels (80- and 72-byte head records; E4M3 (s, z)
+    at G = 64) decode the oracle-written pool to the same bar."""
+    w = workloads.custom(wname, batch=len(lens), seq_lens=tuple(lens), group_size=G, scale_bits=sb)
     lay_b, lay_o, opool, table, r_k, r_v = _oracle_pool_case(w, lens)
     qh, qd = _queries(w, len(lens), 1, "bf16")
-    gs.say(f"decode G={G} {wname} lens={lens} chunk={chunk}")
+    gs.say(f"decode G={G} sz{sb} {wname} lens={lens} chunk={chunk}")
     o_gpu = _gpu_decode(lay_b, gs.upload_oracle_pool(opool), qd, lens, table, r_k, r_v,
                         history_chunk=chunk)
     o_ref = attention.decode(opool, lay_o, qh, np.arange(len(lens)), lens, table, r_k, r_v,
@@ -227,33 +227,33 @@ def test_decode_lower_metadata(G, wname, lens, chunk):
     _compare(o_gpu, o_ref, f"G={G}")
 
 
-@pytest.mark.parametrize("G", [64, 128])
+@pytest.mark.parametrize("G,sb", [(64, 16), (128, 16), (64, 8)])
 @pytest.mark.parametrize("g,hkv", [(1, 5), (3, 2), (5, 3), (8, 1)])
-def test_decode_lower_metadata_gqa_sweep(G, g, hkv):
+def test_decode_lower_metadata_gqa_sweep(G, sb, g, hkv):
     """Every query-head group size (one and two sets of 4 heads) and KV-head
     counts that leave a 4-head workgroup partly empty."""
     w = workloads.custom("layer_small", num_kv_heads=hkv, num_q_heads=g * hkv, batch=2,
-                         seq_lens=(1100, 413), seed=30 + g, group_size=G)
+                         seq_lens=(1100, 413), seed=30 + g, group_size=G, scale_bits=sb)
     lens = w.seq_lens
     lay_b, lay_o, opool, table, r_k, r_v = _oracle_pool_case(w, lens, seed=g)
     qh, qd = _queries(w, 2, g, "bf16")
-    gs.say(f"decode G={G} g={g} hkv={hkv}")
+    gs.say(f"decode G={G} sz{sb} g={g} hkv={hkv}")
     o_gpu = _gpu_decode(lay_b, gs.upload_oracle_pool(opool), qd, lens, table, r_k, r_v)
     o_ref = attention.decode(opool, lay_o, qh, np.arange(2), lens, table, r_k, r_v, w.head_dim ** -0.5)
     _compare(o_gpu, o_ref, f"G={G} g={g} hkv={hkv}")
 
 
-@pytest.mark.parametrize("G", [64, 128])
-def test_decode_lower_metadata_gqa_and_bad_slots(G):
+@pytest.mark.parametrize("G,sb", [(64, 16), (128, 16), (64, 8)])
+def test_decode_lower_metadata_gqa_and_bad_slots(G, sb):
     w = workloads.custom("layer_small", num_kv_heads=2, num_q_heads=12, batch=2,
-                         seq_lens=(900, 1333), seed=77, group_size=G)
+                         seq_lens=(900, 1333), seed=77, group_size=G, scale_bits=sb)
     lens = w.seq_lens
     lay_b, lay_o, opool, table, r_k, r_v = _oracle_pool_case(w, lens, seed=4)
     table = table.copy()
     table[0, 100:140] = -1
     table[1, 500] = lay_b.num_slots + 5
     qh, qd = _queries(w, 2, 6, "bf16")
-    gs.say(f"decode G={G} g=6 with unusable slots")
+    gs.say(f"decode G={G} sz{sb} g=6 with unusable slots")
     o_gpu = _gpu_decode(lay_b, gs.upload_oracle_pool(opool), qd, lens, table, r_k, r_v)
     # the oracle leaves unusable history slots out: emulate by decoding the usable positions
     o_ref = np.zeros_like(o_gpu)

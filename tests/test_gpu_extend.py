@@ -141,10 +141,11 @@ def test_extend_then_append_matches_decode():
     assert err.max() <= 1e-3
 
 
-@pytest.mark.parametrize("G", [64, 128])
+@pytest.mark.parametrize("G,sb", [(64, 16), (128, 16), (64, 8)])
 @pytest.mark.parametrize("wname,P,n", [("tiny", 1000, 16), ("layer_small", 2413, 100),
                                        ("layer_small", 300, 37)])
-def test_extend_lower_metadata(G, wname, P, n):
-    """Groups of 64 and 128 channels (80- and 72-byte head records)."""
-    w = workloads.custom(wname, group_size=G)
+def test_extend_lower_metadata(G, sb, wname, P, n):
+    """Groups of 64 and 128 channels (80- and 72-byte head records; E4M3 (s, z)
+    at G = 64)."""
+    w = workloads.custom(wname, group_size=G, scale_bits=sb)
     _run(w, P, n, seed=P + n + G)

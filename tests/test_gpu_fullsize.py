@@ -44,7 +44,7 @@ def _fill_and_sample(w, sampled, q_stream):
     slots = workloads.slot_table(w)
     pool = B.new_pool(lay_b)
     after = gs.dev(lens)
-    rec_bytes = lay_b.num_kv_heads * (64 + 8 * (128 // w.group_size))
+    rec_bytes = lay_b.num_kv_heads * (64 + 4 * (w.scale_bits // 8) * (128 // w.group_size))
     rec_view = pool.records[: w.num_slots * rec_bytes].view(w.num_slots, -1)
     shp = (bsz, w.sink, w.num_kv_heads, 2, w.head_dim)
     sink_view = pool.sink[: int(np.prod(shp))].view(shp)
@@ -69,7 +69,7 @@ def _fill_and_sample(w, sampled, q_stream):
         vh = v.to(torch.bfloat16).float().cpu().numpy()
         del k, v
         lay_c = cache.Layout(w.head_dim, w.group_size, w.num_kv_heads, w.num_q_heads, w.sink,
-                             w.recent, L, 1)
+                             w.recent, L, 1, w.scale_bits)
         opool = cache.new_pool(lay_c)
         gs.say(f"  oracle append of request {b} (L = {L})")
         cache.append(opool, lay_c, kh, vh, np.zeros(L, np.int64), np.arange(L), np.arange(L), [L],
@@ -224,10 +224,10 @@ def test_extend_8k_full_size_sampled():
     assert err.max() <= TOL
 
 
-@pytest.mark.parametrize("G,req", [(64, 9), (128, 21)])
-def test_decode_b32_full_size_sampled_lower_metadata(G, req):
+@pytest.mark.parametrize("G,sb,req", [(64, 16, 9), (128, 16, 21), (64, 8, 14)])
+def test_decode_b32_full_size_sampled_lower_metadata(G, sb, req):
     """The decode workload with one (s, z) per 64 or 128 channels (80- and
-    72-byte head records)."""
-    w = workloads.custom("decode_b32", group_size=G)
+    72-byte head records; 72 bytes with E4M3 (s, z) at G = 64)."""
+    w = workloads.custom("decode_b32", group_size=G, scale_bits=sb)
     gs.say(f"decode_b32 full size, G = {G}")
     _check(_fill_and_sample(w, sampled={req}, q_stream=11), f"decode_b32 G={G}")

@@ -177,17 +177,18 @@ def test_append_skips_out_of_range_tokens_and_handles_tiny_calls():
                          gs.dev(slots[:0]), gs.dev(lens), gs.dev(r_k), gs.dev(r_v))
 
 
-@pytest.mark.parametrize("G", [64, 128])
+@pytest.mark.parametrize("G,sb", [(64, 16), (128, 16), (64, 8)])
 @pytest.mark.parametrize("kind,dtype", [("identity", None), ("signed_perm", None), ("signed_perm", "f32")])
 @pytest.mark.parametrize("wname,lens", [("tiny", (1024,)), ("layer_small", (700, 333, 40))])
-def test_append_lower_metadata_bit_exact(G, kind, dtype, wname, lens):
+def test_append_lower_metadata_bit_exact(G, sb, kind, dtype, wname, lens):
     """Groups of 64 and 128 channels (one (s, z) per group: 80- and 72-byte head
-    records) with exactly representable rotations: every byte equals the oracle's."""
-    w = workloads.custom(wname, group_size=G)
+    records; 72 bytes with E4M3 (s, z) at G = 64) with exactly representable
+    rotations: every byte equals the oracle's."""
+    w = workloads.custom(wname, group_size=G, scale_bits=sb)
     r_k, r_v = gs.exact_rotations(kind, w.num_kv_heads)
     out = _run_append(w, lens, r_k, r_v, dtype=dtype)
     lay_o = out["lay_o"]
-    assert lay_o.head_record_bytes == {64: 80, 128: 72}[G]
+    assert lay_o.head_record_bytes == {(64, 16): 80, (128, 16): 72, (64, 8): 72}[(G, sb)]
     opool = cache.new_pool(lay_o)
     cache.append(opool, lay_o, out["k"], out["v"], out["req"], out["pos"], out["slots"],
                  np.asarray(lens), r_k, r_v)
@@ -197,9 +198,9 @@ def test_append_lower_metadata_bit_exact(G, kind, dtype, wname, lens):
     assert np.array_equal(recent, opool.recent)
 
 
-@pytest.mark.parametrize("G", [64, 128])
-def test_append_lower_metadata_oscar_rotation_matches_where_unique(G):
-    w = workloads.custom("layer_small", group_size=G)
+@pytest.mark.parametrize("G,sb", [(64, 16), (128, 16), (64, 8)])
+def test_append_lower_metadata_oscar_rotation_matches_where_unique(G, sb):
+    w = workloads.custom("layer_small", group_size=G, scale_bits=sb)
     r_k, r_v = gs.product_rotations(w)
     out = _run_append(w, (2413,), r_k, r_v)
     lay_o = out["lay_o"]

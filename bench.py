@@ -349,15 +349,16 @@ def run_extend(args, torch, B, workloads):
                 output_finite=bool(torch.isfinite(out.float()).all().item()))
 
 
-def run_lower_metadata(args, torch, B, workloads, group_size):
+def run_lower_metadata(args, torch, B, workloads, group_size, scale_bits=16):
     """The decode step of the decode workload with one (s, z) per group_size
-    channels (80- or 72-byte head records): append one token per request, then
-    decode.  Fewer steps than the headline run (a comparison line)."""
-    w = workloads.custom(args.workload, group_size=group_size)
+    channels (80- or 72-byte head records; 72 with E4M3 (s, z) at 64): append
+    one token per request, then decode.  Fewer steps than the headline run (a
+    comparison line)."""
+    w = workloads.custom(args.workload, group_size=group_size, scale_bits=scale_bits)
     lens = np.asarray(w.seq_lens, np.int32)
     bsz, hkv = w.batch, w.num_kv_heads
     lay = B.Layout(128, group_size, hkv, w.num_q_heads, w.sink, w.recent, num_slots=w.num_slots,
-                   max_requests=bsz)
+                   max_requests=bsz, scale_bits=scale_bits)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
     rk, rv = build_rotations(B, w)
     rk_d, rv_d = dev(rk), dev(rv)
@@ -404,9 +405,9 @@ def run_lower_metadata(args, torch, B, workloads, group_size):
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
     kern_ms = float(np.mean([a_.elapsed_time(b_) for a_, b_ in evs]))
-    head_rec = 64 + 8 * (128 // group_size)
+    head_rec = 64 + 4 * (scale_bits // 8) * (128 // group_size)
     kbytes = decode_kernel_bytes(lens.tolist(), hkv, w.sink, w.recent, head_record=head_rec)
-    return dict(group_size=group_size, head_record_bytes=head_rec, steps=steps, ms_per_step=ms,
+    return dict(group_size=group_size, scale_bits=scale_bits, head_record_bytes=head_rec, steps=steps, ms_per_step=ms,
                 kernel_ms=kern_ms, kv_tokens_per_s=int(lens.sum()) / (ms * 1e-3), algorithmic_bytes=kbytes,
                 gb_per_s=kbytes / (kern_ms * 1e-3) / 1e9, frac_hbm=kbytes / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                 output_finite=bool(torch.isfinite(out.float()).all().item()))
@@ -529,10 +530,10 @@ def main():
             f"{bf['int2_speedup_step']:.2f}x (step)")
     lowmeta = None
     if not args.no_lower_metadata:
-        lowmeta = [run_lower_metadata(args, torch, B, workloads, g) for g in (64, 128)]
+        lowmeta = [run_lower_metadata(args, torch, B, workloads, g, sb) for g, sb in ((64, 16), (128, 16), (64, 8))]
         for lm in lowmeta:
-            log(f"[bench] G={lm['group_size']} step {lm['ms_per_step']:.3f} ms, history kernels "
-                f"{lm['kernel_ms']:.3f} ms, {lm['gb_per_s']:.0f} GB/s")
+            log(f"[bench] G={lm['group_size']} ({lm['scale_bits']}-bit s, z) step {lm['ms_per_step']:.3f} ms, "
+                f"split-K kernels {lm['kernel_ms']:.3f} ms, {lm['gb_per_s']:.0f} GB/s")
     ext = None if args.no_extend else run_extend(args, torch, B, workloads)
     if ext:
         log(f"[bench] extend {ext['ms']:.2f} ms ({ext['new_tokens']} new tokens over {ext['prefix_len']}), "

@@ -36,7 +36,6 @@ __device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-}  // namespace oscar
 
 // E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; the all-ones
 // exponent still holds numbers, largest finite 448): the 8-bit scale/zero
@@ -64,3 +63,17 @@ __device__ __forceinline__ uint32_t e4m3_code_rn(float x) {
     }
     return mag | (__builtin_signbitf(x) ? 0x80u : 0u);
 }
+
+// Two E4M3 codes (bytes 0 and 1 of w) as an fp16 pair (low half = byte 0),
+// exact: the code's exponent and mantissa fields moved into the fp16 fields
+// give the value times 2^-8 (fp16's exponent bias is 15, E4M3's 7; code
+// exponent 0 lands on fp16 subnormals the same way), and one fp16 multiply
+// by 2^8 restores it.
+__device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t w) {
+    const uint32_t x = __builtin_amdgcn_perm(0u, w, 0x0C010C00u);      // byte 0 -> bits 0..7, byte 1 -> 16..23
+    const uint32_t h = ((x << 7) & 0x3F803F80u) | ((x << 8) & 0x80008000u);
+    const f16x2 v = __builtin_bit_cast(f16x2, h) * f16x2{_Float16(256.0f), _Float16(256.0f)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+}  // namespace oscar

@@ -595,8 +595,8 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
                 const uint32_t k4 = lds_ld<uint32_t>(szk_at + ho), v4 = lds_ld<uint32_t>(szv_at + ho);
 #pragma unroll
                 for (int g = 0; g < 2; ++g) {
-                    szk[g] = pk_rn(e4m3_to_f32((k4 >> (16 * g)) & 0xFFu), e4m3_to_f32((k4 >> (16 * g + 8)) & 0xFFu));
-                    szv[hf][g] = pk_rn(e4m3_to_f32((v4 >> (16 * g)) & 0xFFu), e4m3_to_f32((v4 >> (16 * g + 8)) & 0xFFu));
+                    szk[g] = e4m3x2_to_f16x2(k4 >> (16 * g));
+                    szv[hf][g] = e4m3x2_to_f16x2(v4 >> (16 * g));
                 }
             } else if constexpr (NG == 2) {
                 const u32x2 k2 = lds_ld<u32x2>(szk_at + ho), v2 = lds_ld<u32x2>(szv_at + ho);
@@ -1062,8 +1062,9 @@ __global__ __launch_bounds__(64 * kPartialWaves) void hist_lowmeta_kernel(Decode
             } else {                                        // E4M3 codes, s first
                 const uint32_t kw = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(base + 2 * kCodeBytes) + gi);
                 const uint32_t vw = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(base + 2 * kCodeBytes + 2 * NG) + gi);
-                ksz[gi] = pk_rn(e4m3_to_f32(kw & 0xFFu), e4m3_to_f32(kw >> 8));
-                vsz[lane][gi] = make_float2(e4m3_to_f32(vw & 0xFFu), e4m3_to_f32(vw >> 8));
+                ksz[gi] = e4m3x2_to_f16x2(kw);
+                const uint32_t vh = e4m3x2_to_f16x2(vw);
+                vsz[lane][gi] = make_float2(half_lo_f(vh), half_hi_f(vh));
             }
         }
 #pragma unroll

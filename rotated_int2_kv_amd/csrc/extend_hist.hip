@@ -224,8 +224,8 @@ __global__ __launch_bounds__(kThreads, 4) void extend_hist_kernel(ExtendHistArgs
             const uint32_t w = *reinterpret_cast<const uint32_t *>(p);
             return make_float2(sz_s(w) * kDqScale, sz_z(w) * kDqScale);
         } else {
-            const uint32_t w = *reinterpret_cast<const uint16_t *>(p);
-            return make_float2(e4m3_to_f32(w & 0xFFu) * kDqScale, e4m3_to_f32(w >> 8) * kDqScale);
+            const uint32_t w = e4m3x2_to_f16x2(*reinterpret_cast<const uint16_t *>(p));
+            return make_float2(sz_s(w) * kDqScale, sz_z(w) * kDqScale);
         }
     };
     constexpr int kUnit = kRec % 16 == 0 ? 16 : 8;

@@ -223,7 +223,7 @@ __device__ __forceinline__ f16x8 u4_as_h8(uint32_t a, uint32_t b, uint32_t c, ui
 // denormal of value c 2^(e_j - 24).
 __host__ __device__ constexpr int pair_exp(int j) { return j <= 4 ? 2 * j : 2 * j - 6; }
 
-__device__ __forceinline__ uint32_t code_bits(uint32_t w, uint32_t w_sh6, int j) {
+[[maybe_unused]] __device__ __forceinline__ uint32_t code_bits(uint32_t w, uint32_t w_sh6, int j) {
     return j <= 4 ? (w & (0x00030003u << (2 * j))) : (w_sh6 & (0x00030003u << (2 * j - 6)));
 }
 
@@ -232,7 +232,7 @@ template <int K>
 __device__ __forceinline__ float row_ror(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x120 + K, 0xF, 0xF, false));
 }
-__device__ __forceinline__ float row16_max(float v) {
+[[maybe_unused]] __device__ __forceinline__ float row16_max(float v) {
     v = fmaxf(v, row_ror<1>(v));
     v = fmaxf(v, row_ror<2>(v));
     v = fmaxf(v, row_ror<4>(v));
@@ -244,8 +244,8 @@ __device__ __forceinline__ float row16_sum(float v) {
     v += row_ror<4>(v);
     return v + row_ror<8>(v);
 }
-__device__ __forceinline__ float half_lo(uint32_t w) { return __half2float(__ushort_as_half(uint16_t(w))); }
-__device__ __forceinline__ float half_hi(uint32_t w) { return __half2float(__ushort_as_half(uint16_t(w >> 16))); }
+[[maybe_unused]] __device__ __forceinline__ float half_lo(uint32_t w) { return __half2float(__ushort_as_half(uint16_t(w))); }
+[[maybe_unused]] __device__ __forceinline__ float half_hi(uint32_t w) { return __half2float(__ushort_as_half(uint16_t(w >> 16))); }
 
 // History item on the matrix cores.  GQ = query heads per KV head, handled in
 // sets of 4.  A workgroup holds four waves, one per KV head of the head chunk
@@ -291,7 +291,6 @@ constexpr int kStage = kTileTokens * kTokBytes;        // 12 KiB per tile
 constexpr int kStages = 4;                             // three tiles in flight while one is computed
 constexpr int kRingBytes = kTileTokens * 4;            // slot ids of one tile
 constexpr int kRing = 4;                               // slot-id ring of the workgroup
-constexpr int kHalfTok = 16 * kTokBytes;               // token 16 + t of a stage is this far after token t
 __host__ __device__ constexpr int int2_lds_bytes() { return kStages * kStage + kRing * kRingBytes; }
 
 // The same pipeline for the lower-metadata records: 80 bytes (G = 64, two
@@ -309,10 +308,11 @@ __host__ __device__ constexpr int int2_lds_bytes_lowmeta() { return int2_lds_byt
 
 // XOR applied to the unit index (within its 128-byte line) of token t: bits
 // 0 and 1 of t % 8 swapped, bit 1 flipped for t % 16 >= 8.  Tokens t and
-// t + 16 share it (token 16 + t is kHalfTok after token t).  It makes the
+// t + 16 share it (token 16 + t is 16 x 384 bytes after token t).  It makes the
 // units read by any 8 consecutive tokens distinct, the (line parity, unit)
 // pairs of tokens 0..15 distinct, and the V-code units of tokens t, t + 1
-// (and t + 4, t + 5) read by one PV load distinct.
+// (and t + 4, t + 5) read by one PV load distinct.  (Token 16 + t of a stage
+// is 16 kTokBytes after token t.)
 __host__ __device__ constexpr int tok_swizzle(int t) {
     return (((t & 1) << 1) | ((t >> 1) & 1) | (t & 4)) ^ (2 * ((t >> 3) & 1));
 }
@@ -323,7 +323,7 @@ __device__ __forceinline__ int unit_addr(int t, int q) {
 }
 
 // Byte offset inside a stage of physical unit u (0..3) of row r (0..15) of
-// wave w's PV weight plane 0 (hi parts); plane 1 (lo parts) is kHalfTok
+// wave w's PV weight plane 0 (hi parts); plane 1 (lo parts) is 16 x 384 bytes
 // further.  Row r's units go to K-code or (s, z) unit {0, 1, 4, 5}[r / 4] of
 // w's head record, of the one token among 0..15 that puts the unit in bank
 // group (4 r + (u ^ 2 ((r / 2) % 2))) % 16 (16-byte groups of a 256-byte

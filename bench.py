@@ -413,6 +413,35 @@ def run_lower_metadata(args, torch, B, workloads, group_size, scale_bits=16):
                 output_finite=bool(torch.isfinite(out.float()).all().item()))
 
 
+def run_copy_reference(torch, record_bytes: int, n_records: int):
+    """Reference rates of plain device copies on the same GPU: a 2 GiB
+    contiguous copy, and a gather of n_records rows of record_bytes each at
+    random row indices (torch index_select), the access pattern of the INT2
+    history stream.  Bytes counted: read + written (+ 8 B of index per row)."""
+    def timed(fn, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(reps):
+            fn()
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / reps
+    src = torch.empty(1 << 31, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    copy_ms = timed(lambda: dst.copy_(src))
+    del src, dst
+    rows = torch.empty((n_records, record_bytes), dtype=torch.uint8, device="cuda")
+    idx = torch.randperm(n_records, device="cuda")
+    out = torch.empty_like(rows)
+    gather_ms = timed(lambda: torch.index_select(rows, 0, idx, out=out))
+    del rows, idx, out
+    return dict(plain_copy_gb_per_s=2 * (1 << 31) / (copy_ms * 1e-3) / 1e9,
+                record_gather_gb_per_s=n_records * (2 * record_bytes + 8) / (gather_ms * 1e-3) / 1e9,
+                record_bytes=record_bytes, records=n_records)
+
+
 def run_covariance(args, torch, B, workloads):
     """Calibration statistics: C_Q Gram sums of 131,072 captured query tokens of
     a 32 q / 8 KV head layer (bf16), one oscar_covariance_accumulate call."""
@@ -486,6 +515,8 @@ def main():
     ap.add_argument("--no-lower-metadata", action="store_true")
     ap.add_argument("--only-extend", action="store_true",
                     help="run only the extend call (prints its own JSON object; for profiling)")
+    ap.add_argument("--no-copy-reference", action="store_true",
+                    help="skip the plain-copy and record-gather reference rates")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -518,6 +549,14 @@ def main():
     kv_tokens = int(d["lens"].sum())
     achieved = d["kbytes"] / (d["kern_ms"] * 1e-3) / 1e9
     log(f"[bench] step {ms:.3f} ms, split-K kernel {d['kern_ms']:.3f} ms, {achieved:.0f} GB/s")
+    # (not with --copy-calibration: the counter runs calibrate on their one 1 GiB copy)
+    ref = None if (args.no_copy_reference or args.copy_calibration) else \
+        run_copy_reference(torch, 8 * 96, int(d["lens"].sum()))
+    if ref:
+        ref["decode_frac_of_plain_copy"] = achieved / ref["plain_copy_gb_per_s"]
+        log(f"[bench] reference rates: copy {ref['plain_copy_gb_per_s']:.0f} GB/s, 768-byte random-row gather "
+            f"{ref['record_gather_gb_per_s']:.0f} GB/s; decode at {100 * ref['decode_frac_of_plain_copy']:.0f}% "
+            f"of the plain copy")
     app = None if args.no_append else run_append(args, torch, B, workloads)
     if app:
         log(f"[bench] append {app['ms']:.3f} ms, {app['tokens_per_s']:.3e} tok/s, {app['gb_per_s']:.0f} GB/s")
@@ -568,6 +607,7 @@ def main():
                      "kernel": "partial_kernel (split-K)", "kernel_ms": d["kern_ms"],
                      "algorithmic_bytes": d["kbytes"]},
         "decode_steps_per_s": 1e3 / ms,
+        "copy_reference": ref,
         "quant_append": app,
         "bf16_baseline": bf,
         "lower_metadata": lowmeta,

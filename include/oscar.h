@@ -26,7 +26,8 @@
  *   - Calls are re-entrant.  The only global state is a thread-local error
  *     message (oscar_last_error).  Two calls that write the same pool bytes
  *     concurrently race; serialise them on one stream.
- *   - Supported shapes: head_dim 128, group_size 32, 64 or 128,
+ *   - Supported shapes: head_dim 128, group_size 32, 64 or 128 with fp16
+ *     scale/zero, or 64 with E4M3 scale/zero (scale_bits = 8),
  *     1 <= num_kv_heads <= 16, num_q_heads = g * num_kv_heads with
  *     1 <= g <= 8.  Other shapes return OSCAR_ERR_UNSUPPORTED.
  */

@@ -14,10 +14,15 @@ import gpu_setup as gs
 pytestmark = pytest.mark.gpu
 
 
-def test_decode_step_graph_replays_match_eager():
+@pytest.mark.parametrize("G,sb", [(32, 16), (64, 16), (128, 16), (64, 8)])
+def test_decode_step_graph_replays_match_eager(G, sb):
+    """Every head-record layout: 96-, 80- and 72-byte records with fp16 (s, z),
+    72-byte records with E4M3 (s, z)."""
     torch = gs.torch_gpu()
     from rotated_int2_kv_amd import binding as B
-    w = workloads.custom("decode_small", batch=4, seq_lens=(1500, 777, 3001, 321))
+    w = workloads.custom("decode_small", batch=4, seq_lens=(1500, 777, 3001, 321), group_size=G,
+                         scale_bits=sb)
+    gs.say(f"graph step G={G} sz{sb}")
     lens = np.asarray(w.seq_lens, np.int32)
     total = int(lens.sum())
     lay, _ = gs.layouts(w, total + 16, len(lens))

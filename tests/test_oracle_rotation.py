@@ -186,3 +186,37 @@ def test_key_error_identity():
     assert abs(lhs - rhs) <= 1e-12 * lhs
     assert lhs > 0
     _ = rng
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_composite_rotation_factor_order(seed):
+    """R_K = U_Q H P_br in that order (OSCAR page, "What OSCAR does differently":
+    the eigenbasis first, then the Hadamard step that spreads importance evenly
+    over the channels, then the group-tier permutation).
+
+    For a covariance C with a generic eigenbasis U:
+      * R^T C R = P^T H^T diag(lambda) H P has the constant diagonal tr C / d
+        (every entry of H is +-1/sqrt d), which is what "equalises channel
+        importance" means; an order such as H U P leaves it uneven;
+      * R (H P)^T = U diagonalises C with eigenvalues in descending order.
+    """
+    rng = np.random.default_rng(100 + seed)
+    d = 128
+    a = rng.standard_normal((d, d))
+    w = np.exp(-np.arange(d) / 12.0) * (1.0 + rng.random(d))       # distinct, spread spectrum
+    q, _ = np.linalg.qr(a)
+    c = (q * w[None, :]) @ q.T
+    c = 0.5 * (c + c.T)
+    r = rotation.composite_rotation(c, rotation.ROT_OSCAR)
+    diag = np.diag(r.T @ c @ r)
+    assert np.abs(diag - np.trace(c) / d).max() <= 1e-12 * np.trace(c)
+    hp = rotation.hadamard(d) @ rotation.bit_reversal_matrix(d)
+    u = r @ hp.T
+    lam = u.T @ c @ u
+    off = lam - np.diag(np.diag(lam))
+    assert np.abs(off).max() <= 1e-12 * np.abs(c).max()
+    assert np.all(np.diff(np.diag(lam)) < 0)
+    assert np.allclose(np.diag(lam), np.sort(w)[::-1], rtol=1e-10)
+    # the swapped order fails the first property: the check can tell them apart
+    wrong = rotation.hadamard(d) @ rotation.eigenbasis(c)[1] @ rotation.bit_reversal_matrix(d)
+    assert np.abs(np.diag(wrong.T @ c @ wrong) - np.trace(c) / d).max() > 1e-3 * np.trace(c) / d

@@ -33,7 +33,7 @@
 #include <type_traits>
 #include <vector>
 
-#include "common.cuh"
+#include "common.h"
 #include "internal.h"
 
 namespace oscar {
@@ -1190,7 +1190,10 @@ __global__ __launch_bounds__(512) void merge_kernel(DecodeArgs a) {
     item_range(a, L, 1, p0, p1);
     const bool recent_ok = p0 < p1;
     const int hist = max(0, max(a.sink_tokens, L - a.recent_tokens) - a.sink_tokens);
-    const int n_hist_items = a.num_slots > 0 ? 2 + (hist + a.chunk - 1) / a.chunk : 2;
+    // capped at the planned items: a device length longer than the host copy
+    // the plan was made from must not read partials past this request's rows
+    const int item_cap = a.extra_item >= 0 ? a.extra_item : a.items;
+    const int n_hist_items = a.num_slots > 0 ? min(item_cap, 2 + (hist + a.chunk - 1) / a.chunk) : 2;
     // the extend's new-token item is the last one and always holds a partial;
     // items between the request's chunks and it hold none
     const int n_items = a.extra_item >= 0 ? a.extra_item + 1 : n_hist_items;

@@ -269,3 +269,24 @@ def test_decode_lower_metadata_gqa_and_bad_slots(G, sb):
             o_rot = attention.attention(qrot, kv[keep, hk, 0], kv[keep, hk, 1], 128 ** -0.5)
             o_ref[b, 6 * hk:6 * hk + 6] = o_rot @ r_v[hk].astype(np.float64).T
     _compare(o_gpu, o_ref, f"G={G} bad slots")
+
+
+def test_decode_device_lengths_longer_than_host_lengths():
+    """seq_lens on the device longer than the host copy the plan is made from:
+    the call succeeds, stays inside the planned work items and the workspace,
+    and writes finite values (the output itself is undefined by the contract)."""
+    torch = gs.torch_gpu()
+    w = workloads.custom("decode_small", batch=2, seq_lens=(1500, 3001))
+    lens = np.asarray(w.seq_lens, np.int32)
+    lay_b, lay_o, opool, table, r_k, r_v = _oracle_pool_case(w, lens, seed=8)
+    host_lens = np.array([700, 900], np.int32)
+    qh, qd = _queries(w, 2, 4, "bf16")
+    from rotated_int2_kv_amd import binding as B
+    ws = torch.empty(B.oscar_decode_workspace_size(lay_b, host_lens), dtype=torch.uint8, device="cuda")
+    out = torch.empty((2, lay_b.num_q_heads, lay_b.head_dim), dtype=torch.float32, device="cuda")
+    gs.say("decode with device lengths (1500, 3001) over a plan for (700, 900)")
+    B.oscar_decode_attn(lay_b, gs.upload_oracle_pool(opool), qd, gs.dev(np.arange(2, dtype=np.int32)),
+                        gs.dev(lens), host_lens, gs.dev(table), gs.dev(r_k), gs.dev(r_v),
+                        lay_b.head_dim ** -0.5, out, ws)
+    torch.cuda.synchronize()
+    assert np.all(np.isfinite(out.cpu().numpy()))

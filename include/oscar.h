@@ -52,7 +52,17 @@ typedef enum {
     OSCAR_ERR_NUMERIC = 5       /* eigensolver did not converge */
 } oscar_status;
 
-typedef enum { OSCAR_F32 = 0, OSCAR_BF16 = 1, OSCAR_F16 = 2 } oscar_dtype;
+typedef enum {
+    OSCAR_F32 = 0,
+    OSCAR_BF16 = 1,
+    OSCAR_F16 = 2,
+    /* Not formats.  They make every int32 value a value of this type, so that
+       an out-of-range argument from a C caller is a defined value that the
+       library rejects with OSCAR_ERR_INVALID_ARG (in C++ an enum's values are
+       otherwise only those its enumerators' bits can hold). */
+    OSCAR_DTYPE_RANGE_MIN_ = INT32_MIN,
+    OSCAR_DTYPE_RANGE_MAX_ = INT32_MAX
+} oscar_dtype;
 
 /* Shape of one attention layer's cache. */
 typedef struct {

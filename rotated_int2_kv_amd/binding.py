@@ -16,7 +16,9 @@ from typing import Optional, Tuple
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "liboscar.so")
+# OSCAR_LIB_PATH selects another build of the same library (the host-only
+# sanitizer build of the host-side tests); by default the in-tree build
+LIB_PATH = os.environ.get("OSCAR_LIB_PATH") or os.path.join(_PKG, "liboscar.so")
 
 OSCAR_OK = 0
 OSCAR_ERR_INVALID_ARG = 1

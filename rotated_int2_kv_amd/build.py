@@ -1,6 +1,14 @@
 """Build liboscar.so (HIP kernels for gfx950 + the C ABI) in-tree with hipcc.
 
     python -m rotated_int2_kv_amd.build          # or __graft_entry__.build()
+    python -m rotated_int2_kv_amd.build --host-sanitized
+
+build() also links a second copy, _build/hostsan/liboscar_hostsan.so, whose
+host code carries AddressSanitizer and UndefinedBehaviorSanitizer (device code
+as in the product build), for the host-side tests: argument validation, the
+split-K planner and the Jacobi rotation builder run under both sanitizers
+(load it with the compiler's ASan runtime preloaded and OSCAR_LIB_PATH
+pointing at it).  `--host-sanitized` builds only that copy.
 """
 
 from __future__ import annotations
@@ -34,8 +42,18 @@ COMMON_FLAGS = [
     # assume finite values); without it every fmax first quiets NaNs, which
     # also keeps DPP lane moves from fusing into the max
     "-fno-honor-nans",
-    "-Wall", "-Wextra", "-Wno-unused-parameter",
+    "-Wall", "-Wextra", "-Werror", "-Wno-unused-parameter",
     "-I", os.path.join(ROOT, "include"),
+]
+
+# sanitizer copy: the product flags (device code unchanged) plus host-only
+# instrumentation; every -fsanitize= applies to the host pass alone
+SAN_DIR = os.path.join(OUT_DIR, "hostsan")
+SAN_LIB = os.path.join(SAN_DIR, "liboscar_hostsan.so")
+SAN_FLAGS = COMMON_FLAGS + [
+    "-Xarch_host", "-g",
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
 ]
 
 
@@ -46,9 +64,24 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm toolchain required to build liboscar)")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, "-c", os.path.join(SRC, src), "-o", obj]
+def asan_runtime() -> str:
+    """The compiler's shared ASan runtime (to preload into a process that loads
+    the sanitized library)."""
+    out = subprocess.run([hipcc(), "--print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True,
+                         text=True)
+    path = out.stdout.strip()
+    if out.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        import glob
+        found = sorted(glob.glob("/opt/rocm/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+        if not found:
+            raise RuntimeError("the compiler's ASan runtime was not found")
+        path = found[-1]
+    return path
+
+
+def _compile_into(src: str, out_dir: str, flags) -> str:
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *flags, "-c", os.path.join(SRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                      if "packed-fp32-ops" not in l)
@@ -59,21 +92,48 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link liboscar.so; returns the library path."""
-    os.makedirs(OUT_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs]
+def _link(objs, lib: str, extra=()) -> None:
+    tmp = lib + ".tmp"
+    cmd = [hipcc(), "-shared", f"--offload-arch={ARCH}", *extra, "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"linking liboscar failed:\n{' '.join(cmd)}\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"linking {os.path.basename(lib)} failed:\n{' '.join(cmd)}\n{r.stdout}{r.stderr}")
+    os.replace(tmp, lib)
+
+
+SAN_LINK = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-shared-libsan"]
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """Only the sanitizer copy of the library; returns its path."""
+    os.makedirs(SAN_DIR, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(lambda s: _compile_into(s, SAN_DIR, SAN_FLAGS), SOURCES))
+    _link(objs, SAN_LIB, SAN_LINK)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {SAN_LIB}")
+    return SAN_LIB
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link liboscar.so (and the sanitizer copy);
+    returns the product library's path."""
+    os.makedirs(OUT_DIR, exist_ok=True)
+    os.makedirs(SAN_DIR, exist_ok=True)
+    jobs = [(s, OUT_DIR, COMMON_FLAGS) for s in SOURCES] + [(s, SAN_DIR, SAN_FLAGS) for s in SOURCES]
+    # the longest compiles first
+    jobs.sort(key=lambda j: (j[0] != "decode_attn.hip", j[1] != OUT_DIR))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(lambda j: (j[1], _compile_into(*j)), jobs))
+    _link([o for d, o in objs if d == OUT_DIR], LIB)
+    _link([o for d, o in objs if d == SAN_DIR], SAN_LIB, SAN_LINK)
+    if verbose:
+        print(f"built {LIB} and {SAN_LIB}")
     return LIB
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--host-sanitized" in sys.argv[1:]:
+        build_host_sanitized(verbose=True)
+    else:
+        build(verbose=True)

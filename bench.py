@@ -51,11 +51,11 @@ BF16_BYTES_PER_TOKEN_HEAD = 512        # K and V, 128 bf16 each
 # (FETCH_SIZE and WRITE_SIZE, scaled by a plain-copy calibration); valid only
 # while the kernel's sources hash to the value recorded with them
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "partial_kernel_decode_b32_hbm_bytes.md")
-KERNEL_SOURCES = ("rotated_int2_kv_amd/csrc/decode_attn.hip", "rotated_int2_kv_amd/csrc/common.cuh",
+KERNEL_SOURCES = ("rotated_int2_kv_amd/csrc/decode_attn.hip", "rotated_int2_kv_amd/csrc/common.h",
                   "rotated_int2_kv_amd/csrc/internal.h", "rotated_int2_kv_amd/build.py")
 # the same for the BF16 baseline's split-K kernel
 BF16_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bf16_partial_kernel_decode_b32_hbm_bytes.md")
-BF16_KERNEL_SOURCES = ("rotated_int2_kv_amd/csrc/bf16_decode.hip", "rotated_int2_kv_amd/csrc/common.cuh",
+BF16_KERNEL_SOURCES = ("rotated_int2_kv_amd/csrc/bf16_decode.hip", "rotated_int2_kv_amd/csrc/common.h",
                        "rotated_int2_kv_amd/csrc/internal.h", "rotated_int2_kv_amd/build.py")
 CPU_BASELINE_SECONDS = 10.0
 

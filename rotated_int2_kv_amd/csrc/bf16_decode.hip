@@ -27,7 +27,7 @@
 #include <cmath>
 #include <string>
 
-#include "common.cuh"
+#include "common.h"
 #include "internal.h"
 
 namespace oscar {

@@ -18,7 +18,7 @@
 #include <algorithm>
 #include <string>
 
-#include "common.cuh"
+#include "common.h"
 #include "internal.h"
 
 namespace oscar {

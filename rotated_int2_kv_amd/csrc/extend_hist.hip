@@ -26,7 +26,7 @@
 #include <cmath>
 #include <type_traits>
 
-#include "common.cuh"
+#include "common.h"
 #include "internal.h"
 
 namespace oscar {

@@ -18,7 +18,7 @@
 
 #include <algorithm>
 
-#include "common.cuh"
+#include "common.h"
 #include "internal.h"
 
 namespace oscar {

@@ -661,8 +661,16 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
                 const float p = __builtin_amdgcn_exp2f(fmaf(lg[hs][hf], qout[hs], -m_ref));   // 0 for masked tokens
                 pw[hs][hf] = p;
                 l_lane[hs] += p;
+                // tokens 16..31 enter the PV products as -p s_g against 3 - c (see
+                // below); their zero-point term carries the difference, z + 3 s
+                if (hf == 0) {
 #pragma unroll
-                for (int g = 0; g < NG; ++g) zl[hs][g] = fmaf(p, half_hi(szv[hf][g]), zl[hs][g]);
+                    for (int g = 0; g < NG; ++g) zl[hs][g] = fmaf(p, half_hi(szv[hf][g]), zl[hs][g]);
+                } else {
+#pragma unroll
+                    for (int g = 0; g < NG; ++g)
+                        zl[hs][g] = fmaf(p, fmaf(3.0f, half_lo(szv[hf][g]), half_hi(szv[hf][g])), zl[hs][g]);
+                }
             }
         }
         // ---- PV: A rows (g, h) = weights of K-slots 8 kb .. 8 kb + 7; B = V
@@ -673,7 +681,8 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
             u16x2 pr;
             pr.x = lds_ld<uint16_t>(pv_at[2 * pp] + so);
             pr.y = lds_ld<uint16_t>(pv_at[2 * pp + 1] + so);
-            xw[pp] = __builtin_bit_cast(uint32_t, pr);
+            // tokens 16..31 (pp = 2, 3) as 3 - c: every 2-bit code inverted
+            xw[pp] = pp >= 2 ? ~__builtin_bit_cast(uint32_t, pr) : __builtin_bit_cast(uint32_t, pr);
             xs[pp] = xw[pp] >> 6;
         }
 #pragma unroll
@@ -682,7 +691,14 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
             // They overwrite this head's K codes and (s, z) of the stage, read above.
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
-                const float p = pw[hs][hf];
+                // sign balance: the matrix core sums its 32 products after
+                // aligning them to the largest and truncating the low bits toward
+                // zero, so products of one sign (p s c >= 0) would lose a little
+                // in the same direction on every tile.  Tokens 16..31 enter as
+                // (-p s)(3 - c) = p s c - 3 p s, the -3 p s is returned through
+                // the zero-point sum, and the truncation errors cancel; the running
+                // sums also stay near the output instead of growing to ~1.5 s l.
+                const float p = hf ? -pw[hs][hf] : pw[hs][hf];
                 constexpr int kPairs = (NG + 1) / 2;
                 uint32_t hw[kPairs], lw[kPairs];
 #pragma unroll

@@ -57,7 +57,8 @@ KERNEL_SOURCES = ("rotated_int2_kv_amd/csrc/decode_attn.hip", "rotated_int2_kv_a
 BF16_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bf16_partial_kernel_decode_b32_hbm_bytes.md")
 BF16_KERNEL_SOURCES = ("rotated_int2_kv_amd/csrc/bf16_decode.hip", "rotated_int2_kv_amd/csrc/common.h",
                        "rotated_int2_kv_amd/csrc/internal.h", "rotated_int2_kv_amd/build.py")
-CPU_BASELINE_SECONDS = 10.0
+# worker threads of the CPU oracle baseline: the host's share of cores on the GPU machine
+CPU_BASELINE_THREADS = 16
 
 
 def log(*a):
@@ -115,8 +116,14 @@ def build_rotations(B, w):
     return rk.astype(np.float32), rv.astype(np.float32)
 
 
-def run_decode(args, torch, B, workloads):
-    w = workloads.workload(args.workload)
+def run_decode(args, torch, B, workloads, name=None, steps=None, warmup=None):
+    """Fill the cache of a decode workload (positions 0 .. L-2 of every request)
+    and time `steps` serving steps (append of position L-1, then decode) after
+    `warmup` untimed ones.  Returns per-step, per-decode-call and split-K kernel
+    times (mean and median) from HIP events on the launch stream."""
+    w = workloads.workload(name or args.workload)
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
     lens = np.asarray(w.seq_lens, np.int32)
     bsz, hkv = w.batch, w.num_kv_heads
     lay = B.Layout(128, 32, hkv, w.num_q_heads, w.sink, w.recent, num_slots=w.num_slots,
@@ -143,7 +150,7 @@ def run_decode(args, torch, B, workloads):
                                  after, rk_d, rv_d)
             del k, v
     torch.cuda.synchronize()
-    log(f"[bench] cache filled: {bsz} x {int(lens.max())} tokens in {time.time() - t0:.1f}s")
+    log(f"[bench] {w.name}: cache filled, {bsz} requests, {int(lens.sum())} tokens in {time.time() - t0:.1f}s")
 
     # step inputs
     q = dev(workloads.queries(w, n_rows=bsz, stream=7)).to(torch.bfloat16)
@@ -161,33 +168,60 @@ def run_decode(args, torch, B, workloads):
     def step(ev=None):
         B.oscar_quant_append(lay, pool, kn, vn, req_ids, pos, new_slots, lens_d, rk_d, rv_d,
                              stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
         B.oscar_decode_attn(lay, pool, q, req_ids, lens_d, lens, table, rk_d, rv_d, 128 ** -0.5,
                             out, ws, stream=stream, kernel_begin=None if ev is None else ev[0],
                             kernel_end=None if ev is None else ev[1],
                             history_chunk=args.history_chunk)
+        if ev is not None:
+            ev[3].record(stream)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     evs = []
-    for _ in range(args.steps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)   # create the underlying HIP events
-        b.record(stream)
-        evs.append((a, b))
+    for _ in range(steps):
+        e = tuple(torch.cuda.Event(enable_timing=True) for _ in range(4))
+        for x in e:
+            x.record(stream)   # create the underlying HIP events
+        evs.append(e)
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         step(evs[i])
     end.record(stream)
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
-    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ms = start.elapsed_time(end) / steps
+    kern = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    call = np.array([e[2].elapsed_time(e[3]) for e in evs])
     chunk_sz, items = B.oscar_decode_plan(lay, lens, args.history_chunk)
     kbytes = decode_kernel_bytes(lens.tolist(), hkv, w.sink, w.recent)
-    return dict(w=w, lens=lens, ms=ms, kern_ms=kern_ms, kbytes=kbytes, chunk=chunk_sz, items=items,
+    # the whole call also reads q, the two rotations and writes o (and the
+    # split-K partials, which are not the method's traffic)
+    call_bytes = kbytes + bsz * w.num_q_heads * 128 * 2 * 2 + 2 * hkv * 128 * 128 * 4
+    hist_items = items - 2
+    return dict(w=w, lens=lens, ms=ms, kern_ms=float(kern.mean()), kern_ms_median=float(np.median(kern)),
+                kern_ms_min=float(kern.min()), kern_ms_max=float(kern.max()),
+                call_ms=float(call.mean()), call_ms_median=float(np.median(call)),
+                kbytes=kbytes, call_bytes=call_bytes, chunk=chunk_sz, items=items,
+                workgroups=int(hist_items * bsz * ((hkv + 3) // 4)), per_launch_kernel_ms=kern.tolist(),
                 o_finite=bool(torch.isfinite(out.float()).all().item()))
+
+
+def decode_leg(d, label):
+    """Summary of a non-headline decode workload for the JSON line."""
+    kb = d["kbytes"]
+    return dict(workload=d["w"].name, label=label, batch=d["w"].batch, kv_tokens=int(d["lens"].sum()),
+                min_len=int(d["lens"].min()), max_len=int(d["lens"].max()), q_heads=d["w"].num_q_heads,
+                kv_heads=d["w"].num_kv_heads, steps=len(d["per_launch_kernel_ms"]), ms_per_step=d["ms"],
+                call_ms=d["call_ms"], kernel_ms=d["kern_ms"], kernel_ms_median=d["kern_ms_median"],
+                kv_tokens_per_s=int(d["lens"].sum()) / (d["call_ms"] * 1e-3), algorithmic_bytes=kb,
+                gb_per_s=kb / (d["kern_ms"] * 1e-3) / 1e9, frac_hbm=kb / (d["kern_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                frac_hbm_call=d["call_bytes"] / (d["call_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                history_chunk=d["chunk"], items_per_request=d["items"], history_workgroups=d["workgroups"],
+                output_finite=d["o_finite"])
 
 
 def run_append(args, torch, B, workloads):
@@ -470,34 +504,80 @@ def run_covariance(args, torch, B, workloads):
 
 
 def cpu_baseline(workloads):
-    """The oracle, as it stands, on one request of the decode workload."""
+    """The oracle as it stands (fp64 NumPy), on every host core: one full
+    decode step of the decode workload's shape and one full append of the
+    append workload, with worker threads over requests (decode) and over
+    token ranges (append).  NumPy releases the GIL inside its array
+    operations, so the threads run in parallel; BLAS is held to one thread
+    per worker."""
+    from concurrent.futures import ThreadPoolExecutor
+
     from threadpoolctl import threadpool_limits
 
     from oracle import attention, cache, quant, rotation
+    threads = max(1, min(CPU_BASELINE_THREADS, os.cpu_count() or 1))
     w = workloads.workload("decode_b32")
-    L = w.seq_lens[0]
-    with threadpool_limits(limits=1):
+    L, bsz, hkv = w.seq_lens[0], w.batch, w.num_kv_heads
+    cov = workloads.covariances(w)
+    rk = np.stack([rotation.composite_rotation(cov.sigma_q[h]) for h in range(hkv)]).astype(np.float32)
+    rv = np.stack([rotation.composite_rotation(cov.sigma_s[h]) for h in range(hkv)]).astype(np.float32)
+    with threadpool_limits(limits=1), ThreadPoolExecutor(threads) as ex:
+        # untimed set-up: the oracle writes one 100,000-token context, which
+        # all 32 requests of the step read (one row of the index table each)
         k, v = workloads.raw_kv_host(w, L)
         k, v = quant.bf16_round(k), quant.bf16_round(v)
-        cov = workloads.covariances(w)
-        rk = np.stack([rotation.composite_rotation(cov.sigma_q[h]) for h in range(w.num_kv_heads)])
-        rv = np.stack([rotation.composite_rotation(cov.sigma_s[h]) for h in range(w.num_kv_heads)])
-        rk, rv = rk.astype(np.float32), rv.astype(np.float32)
-        lay = cache.Layout(128, 32, w.num_kv_heads, w.num_q_heads, w.sink, w.recent, L, 1)
+        lay = cache.Layout(128, 32, hkv, w.num_q_heads, w.sink, w.recent, L, bsz)
         pool = cache.new_pool(lay)
-        slots = np.arange(L)
-        cache.append(pool, lay, k, v, np.zeros(L, int), np.arange(L), slots, [L], rk, rv)
+        cuts = np.linspace(0, L, threads + 1).astype(int)
+        list(ex.map(lambda i: cache.append(pool, lay, k[cuts[i]:cuts[i + 1]], v[cuts[i]:cuts[i + 1]],
+                                           np.zeros(cuts[i + 1] - cuts[i], int), np.arange(cuts[i], cuts[i + 1]),
+                                           np.arange(cuts[i], cuts[i + 1]), [L] * bsz, rk, rv),
+                    range(threads)))
+        for b in range(1, bsz):                 # the same context in every request's windows
+            pool.sink[b], pool.recent[b] = pool.sink[0], pool.recent[0]
         del k, v
-        q = quant.bf16_round(workloads.queries(w, n_rows=1, stream=7))
-        reps = 0
+        table = np.tile(np.arange(L), (bsz, 1))
+        q = quant.bf16_round(workloads.queries(w, n_rows=bsz, stream=7))
+
+        def decode_one(b):
+            return attention.decode(pool, lay, q, np.arange(bsz), [L] * bsz, table, rk, rv, 128 ** -0.5,
+                                    requests=[b])
+
+        decode_one(0)                           # warm-up
         t0 = time.perf_counter()
-        while reps < 1 or time.perf_counter() - t0 < CPU_BASELINE_SECONDS:
-            attention.decode(pool, lay, q, [0], [L], slots[None, :], rk, rv, 128 ** -0.5)
-            reps += 1
-        dt = time.perf_counter() - t0
-    return {"value": reps * L / dt, "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} decode steps of one request of the decode_b32 workload (L = {L}, "
-                      f"32 q / 8 KV heads, all heads), fp64 NumPy oracle, 1 thread, {dt:.1f} s"}
+        list(ex.map(decode_one, range(bsz)))
+        t_dec = time.perf_counter() - t0
+
+        # the append workload: 131,072 tokens x 8 KV heads of one request
+        wa = workloads.workload("append_131k")
+        n = wa.seq_lens[0]
+        ka, va = workloads.raw_kv_host(wa, n)
+        ka, va = quant.bf16_round(ka), quant.bf16_round(va)
+        cova = workloads.covariances(wa)
+        rka = np.stack([rotation.composite_rotation(cova.sigma_q[h]) for h in range(wa.num_kv_heads)]).astype(np.float32)
+        rva = np.stack([rotation.composite_rotation(cova.sigma_s[h]) for h in range(wa.num_kv_heads)]).astype(np.float32)
+        laya = cache.Layout(128, 32, wa.num_kv_heads, wa.num_q_heads, wa.sink, wa.recent, wa.num_slots, 1)
+        poola = cache.new_pool(laya)
+        slots = workloads.slot_table(wa)[0]
+        cuts = np.linspace(0, n, threads + 1).astype(int)
+
+        def append_part(i):
+            a, b = cuts[i], cuts[i + 1]
+            cache.append(poola, laya, ka[a:b], va[a:b], np.zeros(b - a, int), np.arange(a, b), slots[a:b], [n],
+                         rka, rva)
+
+        append_part(0)                          # warm-up (rewrites the same bytes)
+        t0 = time.perf_counter()
+        list(ex.map(append_part, range(threads)))
+        t_app = time.perf_counter() - t0
+    return {"value": bsz * L / t_dec, "unit": "KV tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"one full decode step of the decode_b32 shape ({bsz} requests x {L} tokens, "
+                      f"{w.num_q_heads} q / {hkv} KV heads; the requests read one oracle-written context) "
+                      f"in {t_dec:.2f} s, and the full append_131k append ({n} tokens x {wa.num_kv_heads} "
+                      f"KV heads) in {t_app:.2f} s; fp64 NumPy oracle, {threads} worker threads, one BLAS "
+                      f"thread each",
+            "decode_step_s": t_dec, "append_s": t_app, "append_tokens_per_s": n / t_app,
+            "append_head_vectors_per_s": n * wa.num_kv_heads * 2 / t_app}
 
 
 def main():
@@ -513,6 +593,8 @@ def main():
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-covariance", action="store_true")
     ap.add_argument("--no-lower-metadata", action="store_true")
+    ap.add_argument("--no-extra-decode", action="store_true",
+                    help="skip the mixed-batch and 32K-layer decode legs")
     ap.add_argument("--only-extend", action="store_true",
                     help="run only the extend call (prints its own JSON object; for profiling)")
     ap.add_argument("--no-copy-reference", action="store_true",
@@ -548,7 +630,19 @@ def main():
     ms = d["ms"]
     kv_tokens = int(d["lens"].sum())
     achieved = d["kbytes"] / (d["kern_ms"] * 1e-3) / 1e9
-    log(f"[bench] step {ms:.3f} ms, split-K kernel {d['kern_ms']:.3f} ms, {achieved:.0f} GB/s")
+    log(f"[bench] step {ms:.3f} ms, decode call {d['call_ms']:.3f} ms (median {d['call_ms_median']:.3f}), "
+        f"split-K kernel {d['kern_ms']:.3f} ms (median {d['kern_ms_median']:.3f}, first {d['per_launch_kernel_ms'][0]:.3f}, "
+        f"last {d['per_launch_kernel_ms'][-1]:.3f}), {achieved:.0f} GB/s")
+    legs = []
+    if not args.no_extra_decode:
+        leg_steps, leg_warm = min(args.steps, 200), min(args.warmup, 50)
+        for name, label in (("mixed_b64", "ragged 4,096..131,072-token batch, fragmented slots (split-K balance)"),
+                            ("layer_32k", "one 32,768-token request: 27 MB of records, resident in the 256 MB "
+                                          "last-level cache between steps (cache-resident, not an HBM figure)")):
+            leg = decode_leg(run_decode(args, torch, B, workloads, name, leg_steps, leg_warm), label)
+            legs.append(leg)
+            log(f"[bench] {name}: decode call {leg['call_ms']:.3f} ms, split-K kernel {leg['kernel_ms']:.3f} ms, "
+                f"{leg['gb_per_s']:.0f} GB/s ({100 * leg['frac_hbm']:.1f}% of HBM peak)")
     # (not with --copy-calibration: the counter runs calibrate on their one 1 GiB copy)
     ref = None if (args.no_copy_reference or args.copy_calibration) else \
         run_copy_reference(torch, 8 * 96, int(d["lens"].sum()))
@@ -605,8 +699,17 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": "partial_kernel (split-K)", "kernel_ms": d["kern_ms"],
-                     "algorithmic_bytes": d["kbytes"]},
+                     "kernel_ms_median": d["kern_ms_median"], "kernel_ms_first": d["per_launch_kernel_ms"][0],
+                     "kernel_ms_last": d["per_launch_kernel_ms"][-1],
+                     "frac_median": d["kbytes"] / (d["kern_ms_median"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "algorithmic_bytes": d["kbytes"],
+                     "call": "oscar_decode_attn (query rotation + split-K + merge and un-rotation)",
+                     "call_ms": d["call_ms"], "call_ms_median": d["call_ms_median"], "call_bytes": d["call_bytes"],
+                     "frac_call": d["call_bytes"] / (d["call_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "frac_call_median": d["call_bytes"] / (d["call_ms_median"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "decode_steps_per_s": 1e3 / ms,
+        "decode_calls_per_s": 1e3 / d["call_ms"],
+        "decode_workloads": legs or None,
         "copy_reference": ref,
         "quant_append": app,
         "bf16_baseline": bf,

@@ -232,6 +232,33 @@ oscar_status oscar_decode_attn(hipStream_t stream, const oscar_layout *layout,
                                void *out, oscar_dtype out_dtype, void *workspace,
                                size_t workspace_bytes, const oscar_launch_opts *opts);
 
+/*
+ * oscar_decode_attn_noalloc: the same decode step for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Arguments, computation and results are
+ * those of oscar_decode_attn (bit for bit: the same kernels and plan); the
+ * workspace is instead a device array inside the library, one per GPU, of
+ * OSCAR_NOALLOC_SCRATCH_BYTES (32 MiB; the 32 x 100K-token batch of
+ * 32 q / 8 KV heads needs about 19 MB, oscar_decode_workspace_size tells any
+ * other), held by each GPU the library runs on until the process ends.
+ * A batch whose workspace would exceed it returns OSCAR_ERR_WORKSPACE and
+ * launches nothing.  The call makes no allocation (no hipMalloc, hipFree or
+ * allocating library routine); its first use on a device looks up that
+ * device's array address (hipGetSymbolAddress) once.  Every call on one GPU
+ * shares its array, so calls that overlap on one GPU (different streams, or
+ * threads without ordering) race and may return wrong results; serialise
+ * them, e.g. on one stream.
+ */
+#define OSCAR_NOALLOC_SCRATCH_BYTES (32u << 20)
+oscar_status oscar_decode_attn_noalloc(hipStream_t stream, const oscar_layout *layout,
+                                       const oscar_pool *pool, const void *q, oscar_dtype q_dtype,
+                                       int32_t batch, const int32_t *req_ids,
+                                       const int32_t *seq_lens, const int32_t *seq_lens_host,
+                                       const int32_t *req_to_slot, int64_t req_to_slot_stride,
+                                       const float *R_K, const float *R_V, float sm_scale,
+                                       void *out, oscar_dtype out_dtype,
+                                       const oscar_launch_opts *opts);
+
 /* Split-K plan that oscar_decode_attn uses: history tokens per work item and
    work items per request (sink + recent + history chunks). */
 oscar_status oscar_decode_plan(const oscar_layout *layout, int32_t batch,

@@ -32,7 +32,7 @@ OSCAR_ROT_EIG, OSCAR_ROT_HAD, OSCAR_ROT_PBR, OSCAR_ROT_OSCAR = 1, 2, 4, 7
 
 EXPORTED = (
     "oscar_layout_check", "oscar_pool_bytes", "oscar_build_rotation", "oscar_quant_append",
-    "oscar_decode_workspace_size", "oscar_decode_attn", "oscar_decode_plan",
+    "oscar_decode_workspace_size", "oscar_decode_attn", "oscar_decode_attn_noalloc", "oscar_decode_plan",
     "oscar_extend_workspace_size", "oscar_extend_attn", "oscar_bf16_pool_bytes", "oscar_bf16_append",
     "oscar_bf16_decode_workspace_size", "oscar_bf16_decode_attn", "oscar_covariance_workspace_size",
     "oscar_covariance_accumulate", "oscar_last_error", "oscar_version",
@@ -84,6 +84,7 @@ def _load() -> ctypes.CDLL:
         "oscar_decode_workspace_size": (I32, [LP, I32, P, OP, ctypes.POINTER(SZ)]),
         "oscar_decode_attn": (I32, [P, LP, PP, P, I32, I32, P, P, P, P, I64, P, P, F32, P, I32,
                                     P, SZ, OP]),
+        "oscar_decode_attn_noalloc": (I32, [P, LP, PP, P, I32, I32, P, P, P, P, I64, P, P, F32, P, I32, OP]),
         "oscar_decode_plan": (I32, [LP, I32, P, OP, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
         "oscar_extend_workspace_size": (I32, [LP, I32, I32, OP, ctypes.POINTER(SZ)]),
         "oscar_extend_attn": (I32, [P, LP, PP, P, I32, P, P, I32, I32, I32, I32, P, I64, P, P, F32,
@@ -255,6 +256,21 @@ def oscar_decode_attn(layout: Layout, pool: Pool, q, req_ids, seq_lens, seq_lens
         _ptr(req_to_slot), int(req_to_slot.shape[-1]), _ptr(R_K), _ptr(R_V), float(sm_scale),
         _ptr(out), _dtype_code(out), _ptr(workspace), int(workspace.numel() * workspace.element_size()),
         _opts(kernel_begin, kernel_end, history_chunk)))
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def oscar_decode_attn_noalloc(layout: Layout, pool: Pool, q, req_ids, seq_lens, seq_lens_host,
+                              req_to_slot, R_K, R_V, sm_scale: float, out, stream=None,
+                              kernel_begin=None, kernel_end=None, history_chunk: int = 0) -> None:
+    _dev(q, req_ids, seq_lens, req_to_slot, R_K, R_V, out)
+    lens = np.ascontiguousarray(seq_lens_host, dtype=np.int32)
+    _check(_lib.oscar_decode_attn_noalloc(
+        _stream(stream), ctypes.byref(layout.c()), ctypes.byref(pool.c()), _ptr(q),
+        _dtype_code(q), int(q.shape[0]), _ptr(req_ids), _ptr(seq_lens), lens.ctypes.data,
+        _ptr(req_to_slot), int(req_to_slot.shape[-1]), _ptr(R_K), _ptr(R_V), float(sm_scale),
+        _ptr(out), _dtype_code(out), _opts(kernel_begin, kernel_end, history_chunk)))
 
 
 def oscar_extend_workspace_size(layout: Layout, n_new: int, prefix_len: int,

@@ -29,6 +29,7 @@
 #include <hip/hip_fp16.h>
 
 #include <cmath>
+#include <mutex>
 #include <string>
 #include <type_traits>
 #include <vector>
@@ -1496,6 +1497,72 @@ oscar_status launch_decode(const DecodeArgs &a, const DecodePlan &plan, hipStrea
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// Decode that allocates nothing: the workspace is a file-scope device array.
+// Each GPU holds its own copy at its own address, found once per device with
+// hipGetSymbolAddress; host code uses only that address, never the array's
+// name (which on the host is a stand-in, not a device address).
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[OSCAR_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_at[kMaxScratchDevices] = {};
+
+// address of the current device's copy of `scratch` (set up on first use)
+oscar_status scratch_address(void **at) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(OSCAR_ERR_HIP, "hipGetDevice failed");
+    if (dev < 0 || dev >= kMaxScratchDevices) return fail(OSCAR_ERR_UNSUPPORTED, "device index beyond 64");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_at[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(OSCAR_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+        g_scratch_at[dev] = p;
+    }
+    *at = g_scratch_at[dev];
+    return OSCAR_OK;
+}
+
+}  // namespace
+
+extern "C" oscar_status oscar_decode_attn_noalloc(hipStream_t stream, const oscar_layout *layout,
+                                                  const oscar_pool *pool, const void *q, oscar_dtype q_dtype,
+                                                  int32_t batch, const int32_t *req_ids,
+                                                  const int32_t *seq_lens, const int32_t *seq_lens_host,
+                                                  const int32_t *req_to_slot, int64_t req_to_slot_stride,
+                                                  const float *R_K, const float *R_V, float sm_scale,
+                                                  void *out, oscar_dtype out_dtype,
+                                                  const oscar_launch_opts *opts) {
+    oscar_status st = check_decode_common(layout, pool, q, q_dtype, req_to_slot, R_K, R_V, sm_scale, out,
+                                          out_dtype);
+    if (st != OSCAR_OK) return st;
+    if (!req_ids || !seq_lens) return fail(OSCAR_ERR_INVALID_ARG, "a required pointer is null");
+    DecodePlan plan;
+    st = make_decode_plan(*layout, batch, seq_lens_host, opts, &plan);
+    if (st != OSCAR_OK) return st;
+    if (plan.ws_bytes > OSCAR_NOALLOC_SCRATCH_BYTES)
+        return fail(OSCAR_ERR_WORKSPACE, "this batch needs " + std::to_string(plan.ws_bytes) +
+                                             " bytes of workspace, more than the " +
+                                             std::to_string(size_t(OSCAR_NOALLOC_SCRATCH_BYTES)) +
+                                             " bytes of the library's scratch array (use oscar_decode_attn "
+                                             "with a workspace)");
+    void *ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != OSCAR_OK) return st;
+    st = check_workspace(plan, req_to_slot_stride, ws, OSCAR_NOALLOC_SCRATCH_BYTES);
+    if (st != OSCAR_OK) return st;
+    DecodeArgs a = make_args(layout, pool, q, q_dtype, batch, req_to_slot, req_to_slot_stride, R_K, R_V,
+                             sm_scale, out, out_dtype, ws, plan);
+    a.req_ids = req_ids;
+    a.seq_lens = seq_lens;
+    return launch_decode(a, plan, stream, opts);
+}
 
 extern "C" oscar_status oscar_decode_attn(hipStream_t stream, const oscar_layout *layout,
                                           const oscar_pool *pool, const void *q, oscar_dtype q_dtype,

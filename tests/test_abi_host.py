@@ -382,3 +382,18 @@ def test_eight_bit_scale_zero_layouts():
         with pytest.raises(B.OscarError) as ei:
             B.oscar_layout_check(L(**bad))
         assert ei.value.status == st
+
+
+def test_noalloc_decode_rejects_a_batch_beyond_its_scratch_before_launch():
+    """A batch whose workspace exceeds the library's scratch array is refused
+    with OSCAR_ERR_WORKSPACE before any HIP call (no device needed)."""
+    lay = L(num_slots=10 ** 7, max_requests=512)
+    lens = np.full(512, 100_000, np.int32)
+    need = B.oscar_decode_workspace_size(lay, lens)
+    assert need > B.NOALLOC_SCRATCH_BYTES
+    st = B._lib.oscar_decode_attn_noalloc(
+        None, ctypes.byref(lay.c()), ctypes.byref(B.CPool(FAKE.value, FAKE.value, FAKE.value)), FAKE,
+        B.OSCAR_BF16, len(lens), FAKE, FAKE, lens.ctypes.data, FAKE, 100_000, FAKE, FAKE, 0.088, FAKE,
+        B.OSCAR_F32, None)
+    assert st == B.OSCAR_ERR_WORKSPACE
+    assert "scratch" in B.oscar_last_error()

@@ -142,19 +142,28 @@ def append(pool: Pool, lay: Layout, k, v, req_ids, positions, slots, seq_len_aft
     """
     k = np.asarray(k, dtype=np.float32)
     v = np.asarray(v, dtype=np.float32)
-    n = k.shape[0]
-    req_ids = np.asarray(req_ids, dtype=np.int64)
-    positions = np.asarray(positions, dtype=np.int64)
-    slots = np.asarray(slots, dtype=np.int64)
-    lens = np.asarray(seq_len_after, dtype=np.int64)
     rot = {}
     for t, (x, r) in enumerate(((k, r_k), (v, r_v))):
         xr = np.empty_like(x)
         for h in range(lay.num_kv_heads):
             xr[:, h, :] = quant.rotate(x[:, h, :], np.asarray(r, np.float32)[h])
         rot["kv"[t]] = xr
+    store_rotated(pool, lay, rot["k"], rot["v"], req_ids, positions, slots, seq_len_after, alpha)
+    return rot
+
+
+def store_rotated(pool: Pool, lay: Layout, xr_k, xr_v, req_ids, positions, slots, seq_len_after,
+                  alpha: float = 1.0) -> None:
+    """Route and quantise n tokens whose rotated fp32 values are given
+    (xr_k, xr_v [n, Hkv, d]): the steps of ``append`` after the rotation."""
+    rot = {"k": np.asarray(xr_k, dtype=np.float32), "v": np.asarray(xr_v, dtype=np.float32)}
+    n = rot["k"].shape[0]
+    req_ids = np.asarray(req_ids, dtype=np.int64)
+    positions = np.asarray(positions, dtype=np.int64)
+    slots = np.asarray(slots, dtype=np.int64)
+    lens = np.asarray(seq_len_after, dtype=np.int64)
     if n == 0:
-        return rot
+        return
     in_sink = positions < lay.sink
     in_pool = ~in_sink
     in_ring = in_pool & (positions >= lens[req_ids] - lay.recent)
@@ -175,7 +184,6 @@ def append(pool: Pool, lay: Layout, k, v, req_ids, positions, slots, seq_len_aft
                 pool.records[slots[in_pool], a:b] = packed[:, h, :]
                 a, b = off["ksz" if t == 0 else "vsz"]
                 pool.records[slots[in_pool], a:b] = szb[:, h, :]
-    return rot
 
 
 def read_record(pool: Pool, lay: Layout, slots):

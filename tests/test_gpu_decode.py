@@ -145,8 +145,16 @@ def test_decode_is_deterministic():
     ("mixed_small", workloads.workload("mixed_small").seq_lens),
 ])
 def test_end_to_end_against_full_oracle(wname, lens):
-    """GPU append (library rotations) + GPU decode vs the oracle's own rotations,
-    quantisation and attention on the same seeded inputs."""
+    """The whole path on the GPU (the library's rotation builder, append and
+    decode) against the oracle (its own rotations, quantiser and attention).
+
+    Codes are decisions taken from fp32 rotated values: a value within rounding
+    of a threshold has two valid codes, and one such flip on a heavily attended
+    token moves the output past any fixed bar.  So the decisions are taken in
+    the kernel's precision: the GPU's rotated values are checked against the
+    exact product (the 1e-5 rotated-value bar), the oracle routes and quantises
+    those values and its pool must equal the GPU's byte for byte, and the GPU's
+    decode must match the oracle's decode of that pool (2e-3)."""
     torch = gs.torch_gpu()
     from rotated_int2_kv_amd import binding as B
     w = workloads.custom(wname, batch=len(lens), seq_lens=tuple(lens))
@@ -157,14 +165,24 @@ def test_end_to_end_against_full_oracle(wname, lens):
     kh, vh, kd, vd = gs.kv_values(w, total, stream=4)
     r_k, r_v = gs.product_rotations(w)
     pool = B.new_pool(lay_b)
+    rot = torch.zeros((total, w.num_kv_heads, 2, w.head_dim), dtype=torch.float32, device="cuda")
     gs.say(f"end-to-end {wname}")
     B.oscar_quant_append(lay_b, pool, kd, vd, gs.dev(req), gs.dev(pos), gs.dev(slots),
-                         gs.dev(np.asarray(lens, np.int32)), gs.dev(r_k), gs.dev(r_v))
+                         gs.dev(np.asarray(lens, np.int32)), gs.dev(r_k), gs.dev(r_v), 1.0, rot)
     qh, qd = _queries(w, len(lens), 2, w.q_dtype)
     o_gpu = _gpu_decode(lay_b, pool, qd, lens, table, r_k, r_v)
+    x_gpu = rot.cpu().numpy()
     ork, orv = gs.oracle_rotations(w)
+    for t, (x, rr) in enumerate(((kh, ork), (vh, orv))):
+        for h in range(w.num_kv_heads):
+            exact = x[:, h, :].astype(np.float64) @ rr[h].astype(np.float64)
+            assert pt.normwise_rel(x_gpu[:, h, t, :], exact).max() <= 1e-5
     opool = cache.new_pool(lay_o)
-    cache.append(opool, lay_o, kh, vh, req, pos, slots, np.asarray(lens), ork, orv)
+    cache.store_rotated(opool, lay_o, x_gpu[:, :, 0, :], x_gpu[:, :, 1, :], req, pos, slots, np.asarray(lens))
+    rec, sink, recent = gs.pool_host(pool, lay_o)
+    assert np.array_equal(rec, opool.records)
+    assert np.array_equal(sink, opool.sink)
+    assert np.array_equal(recent, opool.recent)
     o_ref = attention.decode(opool, lay_o, qh, np.arange(len(lens)), lens, table, ork, orv,
                              128 ** -0.5)
     _compare(o_gpu, o_ref, f"end-to-end {wname}")

@@ -118,7 +118,7 @@ typedef struct {
     /* Decode only: history tokens per split-K work item (multiple of 32,
        32..65536); 0 = chosen from the sequence lengths. */
     int32_t history_chunk;
-    /* Append only: tokens per workgroup (multiple of 16); 0 = automatic. */
+    /* Append only: tokens per workgroup (multiple of 32); 0 = automatic. */
     int32_t append_chunk;
 } oscar_launch_opts;
 

@@ -7,11 +7,15 @@
 // transposed rotation columns of its group in registers as MFMA A operands:
 // the fp32 rotation is split exactly into three bf16 terms r1 + r2 + r3, so
 // with bf16 inputs the product x R is formed without approximation and
-// accumulated in fp32 on the matrix cores.  Tiles of 16 tokens are staged
-// through LDS as the B operand (x^T), and each lane ends up with 8 contiguous
-// rotated channels of one token, which it quantises, packs into 16 bits and
-// stores.  Group min/max need two cross-lane steps (the 4 lanes of a token);
-// with groups of 64 or 128 channels (NGW = 2 or 4 waves per group) the waves
+// accumulated in fp32 on the matrix cores (v_mfma_f32_32x32x16_bf16: 32
+// output channels x 32 tokens per product, 16 input channels deep).  Tiles
+// of 32 tokens are staged through LDS as the B operand (x^T).  The rows of A
+// are ordered so that each lane ends up with 16 contiguous rotated channels
+// of one token: the two lanes l and l + 32 hold the two halves of a token's
+// group, so the group's statistics, scale, zero and code thresholds are
+// formed by two lanes (each lane forms two of the thresholds and swaps them
+// with its partner), and each lane writes its 16 codes as one 32-bit word.
+// With groups of 64 or 128 channels (NGW = 2 or 4 waves per group) the waves
 // of a group also exchange their minima and maxima through LDS.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
@@ -24,11 +28,17 @@
 namespace oscar {
 namespace {
 
-constexpr int kTile = 16;             // tokens per MFMA tile
+constexpr int kTile = 32;             // tokens per MFMA tile
 constexpr int kWaves = 4;             // one per output group
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowBytes = 2 * kHeadDim + 16;   // padded LDS row of one token (bf16 plane)
 constexpr int kPlaneBytes = kTile * kRowBytes;
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma32_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
 
 struct AppendArgs {
     const void *k;
@@ -95,102 +105,111 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(AppendArgs a) {
     const int tid = threadIdx.x;
     const int w = tid >> 6;          // output group
     const int lane = tid & 63;
-    const int n = lane & 15;
-    const int kb = lane >> 4;
+    const int tt = lane & 31;        // token of the tile (MFMA column)
+    const int hh = lane >> 5;        // half of the group: channels 16 hh .. 16 hh + 15
 
     // A operands: transposed rotation rows of this wave's 32 output channels.
-    // Row r of M-tile mt is output channel 32 w + 8 (r / 4) + 4 mt + r % 4, so
-    // that output lane (n, kb) receives channels 32 w + 8 kb + 0..7.
+    // Output element 4 j + i of lane (tt, hh) is row 8 j + 4 hh + i; that row
+    // holds output channel 32 w + 16 hh + 4 j + i, so the lane's 16 elements
+    // are the channels 32 w + 16 hh + 0..15 in order.
     const float *R = (t == 0 ? a.r_k : a.r_v) + size_t(h) * kHeadDim * kHeadDim;
-    bf16x8 rf[2][4][3];
+    bf16x8 rf[8][3];
+    {
+        const int r = lane & 31;
+        const int oc = 32 * w + 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-        const int oc = 32 * w + 8 * (n >> 2) + 4 * mt + (n & 3);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+        for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const int ic = 32 * ks + 8 * kb + j;
+                const int ic = 16 * ks + 8 * hh + j;
                 uint16_t x0, x1, x2;
                 split3(R[size_t(ic) * kHeadDim + oc], x0, x1, x2);
-                rf[mt][ks][0][j] = bits_to_bf16(x0);
-                rf[mt][ks][1][j] = bits_to_bf16(x1);
-                rf[mt][ks][2][j] = bits_to_bf16(x2);
+                rf[ks][0][j] = bits_to_bf16(x0);
+                rf[ks][1][j] = bits_to_bf16(x1);
+                rf[ks][2][j] = bits_to_bf16(x2);
             }
         }
     }
 
-    // staging: thread -> (token row, 8-channel chunk)
-    const int st_row = tid >> 4;
-    const int st_col = tid & 15;
+    // staging: a tile is 32 token rows x 16 units of 8 channels; thread tid
+    // stages units tid and tid + 256 (row u / 16, channels 8 (u % 16) ..)
     const void *X = (t == 0 ? a.k : a.v);
-
-    auto load_tile = [&](int tb, u32x4 &r0, u32x4 &r1) {
-        const int tok = tb + st_row;
-        r0 = u32x4{0, 0, 0, 0};
-        r1 = u32x4{0, 0, 0, 0};
-        if (tok < tok_end) {
-            const size_t elem = (size_t(tok) * a.hkv + h) * kHeadDim + 8 * st_col;
-            if (a.in_dtype == OSCAR_F32) {
-                const u32x4 *p = reinterpret_cast<const u32x4 *>(static_cast<const float *>(X) + elem);
-                r0 = __builtin_nontemporal_load(p);        // input read once
-                r1 = __builtin_nontemporal_load(p + 1);
-            } else {
-                r0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(X) + elem));
+    auto load_tile = [&](int tb, u32x4 (&r)[2][2]) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int u = tid + 256 * q;
+            const int tok = tb + (u >> 4);
+            r[q][0] = u32x4{0, 0, 0, 0};
+            r[q][1] = u32x4{0, 0, 0, 0};
+            if (tok < tok_end) {
+                const size_t elem = (size_t(tok) * a.hkv + h) * kHeadDim + 8 * (u & 15);
+                if (a.in_dtype == OSCAR_F32) {
+                    const u32x4 *p = reinterpret_cast<const u32x4 *>(static_cast<const float *>(X) + elem);
+                    r[q][0] = __builtin_nontemporal_load(p);        // input read once
+                    r[q][1] = __builtin_nontemporal_load(p + 1);
+                } else {
+                    r[q][0] = __builtin_nontemporal_load(
+                        reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(X) + elem));
+                }
             }
         }
     };
-    auto store_tile = [&](uint8_t *lds, const u32x4 &r0, const u32x4 &r1) {
-        uint8_t *dst = lds + st_row * kRowBytes + 16 * st_col;
-        if constexpr (XT == 1) {
-            *reinterpret_cast<u32x4 *>(dst) = r0;
-        } else {
-            float f[8];
-            if (a.in_dtype == OSCAR_F32) {
+    auto store_tile = [&](uint8_t *lds, const u32x4 (&r)[2][2]) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int u = tid + 256 * q;
+            uint8_t *dst = lds + (u >> 4) * kRowBytes + 16 * (u & 15);
+            if constexpr (XT == 1) {
+                *reinterpret_cast<u32x4 *>(dst) = r[q][0];
+            } else {
+                float f[8];
+                if (a.in_dtype == OSCAR_F32) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        f[j] = __uint_as_float(r[q][0][j]);
+                        f[4 + j] = __uint_as_float(r[q][1][j]);
+                    }
+                } else {  // fp16 input, converted exactly to fp32
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        f[2 * j] = __half2float(__ushort_as_half(uint16_t(r[q][0][j] & 0xFFFFu)));
+                        f[2 * j + 1] = __half2float(__ushort_as_half(uint16_t(r[q][0][j] >> 16)));
+                    }
+                }
+                uint16_t p0[8], p1[8], p2[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) split3(f[j], p0[j], p1[j], p2[j]);
+                u32x4 w0, w1, w2;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    f[j] = __uint_as_float(r0[j]);
-                    f[4 + j] = __uint_as_float(r1[j]);
+                    w0[j] = uint32_t(p0[2 * j]) | (uint32_t(p0[2 * j + 1]) << 16);
+                    w1[j] = uint32_t(p1[2 * j]) | (uint32_t(p1[2 * j + 1]) << 16);
+                    w2[j] = uint32_t(p2[2 * j]) | (uint32_t(p2[2 * j + 1]) << 16);
                 }
-            } else {  // fp16 input, converted exactly to fp32
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    f[2 * j] = __half2float(__ushort_as_half(uint16_t(r0[j] & 0xFFFFu)));
-                    f[2 * j + 1] = __half2float(__ushort_as_half(uint16_t(r0[j] >> 16)));
-                }
+                *reinterpret_cast<u32x4 *>(dst) = w0;
+                *reinterpret_cast<u32x4 *>(dst + kPlaneBytes) = w1;
+                *reinterpret_cast<u32x4 *>(dst + 2 * kPlaneBytes) = w2;
             }
-            uint16_t p0[8], p1[8], p2[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) split3(f[j], p0[j], p1[j], p2[j]);
-            u32x4 w0, w1, w2;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                w0[j] = uint32_t(p0[2 * j]) | (uint32_t(p0[2 * j + 1]) << 16);
-                w1[j] = uint32_t(p1[2 * j]) | (uint32_t(p1[2 * j + 1]) << 16);
-                w2[j] = uint32_t(p2[2 * j]) | (uint32_t(p2[2 * j + 1]) << 16);
-            }
-            *reinterpret_cast<u32x4 *>(dst) = w0;
-            *reinterpret_cast<u32x4 *>(dst + kPlaneBytes) = w1;
-            *reinterpret_cast<u32x4 *>(dst + 2 * kPlaneBytes) = w2;
         }
     };
 
     constexpr int kHeadRec = 2 * kCodeBytes + 2 * SZB * (kWaves / NGW);   // head record of this layout
     constexpr int kSzTensor = SZB * (kWaves / NGW);                        // (s, z) bytes per tensor
     const int64_t rec_bytes = int64_t(a.hkv) * kHeadRec;
-    // kDepth tiles of input in flight in registers (the waits are the
-    // compiler's); the LDS tile is double-buffered, so one barrier per tile
-    // both publishes the new tile and retires the buffer it overwrites next
-    constexpr int kDepth = 2;
-    u32x4 pr0[kDepth], pr1[kDepth];
+    // the next tile of input in flight in registers (the waits are the
+    // compiler's; a second tile would take the registers of a third wave per
+    // SIMD); the LDS tile is double-buffered, so one barrier per tile both
+    // publishes the new tile and retires the buffer it overwrites next
+    constexpr int kDepth = 1;
+    u32x4 pr[kDepth][2][2];
 #pragma unroll
-    for (int d = 0; d < kDepth; ++d) load_tile(tok_begin + d * kTile, pr0[d], pr1[d]);
+    for (int d = 0; d < kDepth; ++d) load_tile(tok_begin + d * kTile, pr[d]);
 
-    // per-token routing data of this lane's token (tb + n), fetched ahead:
+    // per-token routing data of this lane's token (tb + tt), fetched ahead:
     // request, position and slot two tiles early, the request's length one
     // tile early, so that no tile waits on a dependent global load
     auto load_meta = [&](int tb, int &req, int &pos, int &slot) {
-        const int tok = tb + n;
+        const int tok = tb + tt;
         const int tc = tok < tok_end ? tok : tok_begin;
         req = a.req_ids[tc];
         pos = a.positions[tc];
@@ -209,61 +228,50 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(AppendArgs a) {
     for (int d = 0; d < kDepth; ++d) {
         const int tb = tb0 + d * kTile;
         if (tb >= tok_end) break;
-        uint8_t *lds = lds_buf[d & 1];
-        store_tile(lds, pr0[d], pr1[d]);
+        uint8_t *lds = lds_buf[((tb - tok_begin) / kTile) & 1];
+        store_tile(lds, pr[d]);
         __syncthreads();
-        load_tile(tb + kDepth * kTile, pr0[d], pr1[d]);
+        load_tile(tb + kDepth * kTile, pr[d]);
         int req2, pos2, slot2;
         load_meta(tb + 2 * kTile, req2, pos2, slot2);
         const int len1 = load_len(req1);
 
-        // x'^T (16 out channels x 16 tokens) per M-tile
-        f32x4 acc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+        // x'^T: 32 output channels x 32 tokens, 16 input channels per step
+        f32x16 acc = {};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+        for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
             for (int xa = 0; xa < XT; ++xa) {
                 const bf16x8 b = *reinterpret_cast<const bf16x8 *>(
-                    lds + xa * kPlaneBytes + n * kRowBytes + ks * 64 + kb * 16);
+                    lds + xa * kPlaneBytes + tt * kRowBytes + ks * 32 + hh * 16);
 #pragma unroll
-                for (int tr = 0; tr + xa < 3; ++tr) {
-                    acc[0] = mfma_bf16(rf[0][ks][tr], b, acc[0]);
-                    acc[1] = mfma_bf16(rf[1][ks][tr], b, acc[1]);
-                }
+                for (int tr = 0; tr + xa < 3; ++tr) acc = mfma32_bf16(rf[ks][tr], b, acc);
             }
         }
 
-        // lane (n, kb): token tb + n, rotated channels 32 w + 8 kb + j
-        float vals[8];
+        // lane (tt, hh): token tb + tt, rotated channels 32 w + 16 hh + 0..15
+        float lo = fminf(acc[0], acc[1]), hi = fmaxf(acc[0], acc[1]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            vals[i] = acc[0][i];
-            vals[4 + i] = acc[1][i];
+        for (int j = 2; j < 16; ++j) {
+            lo = fminf(lo, acc[j]);
+            hi = fmaxf(hi, acc[j]);
         }
-        float lo = vals[0], hi = vals[0];
-#pragma unroll
-        for (int j = 1; j < 8; ++j) {
-            lo = fminf(lo, vals[j]);
-            hi = fmaxf(hi, vals[j]);
-        }
-        lo = fminf(lo, __shfl_xor(lo, 16));
-        hi = fmaxf(hi, __shfl_xor(hi, 16));
         lo = fminf(lo, __shfl_xor(lo, 32));
         hi = fmaxf(hi, __shfl_xor(hi, 32));
         if constexpr (NGW > 1) {
             // the other waves of this group: every wave passes here (no lane has
             // left the iteration yet)
-            if (kb == 0) grp_stat[w][n] = make_float2(lo, hi);
+            if (hh == 0) grp_stat[w][tt] = make_float2(lo, hi);
             __syncthreads();
 #pragma unroll
             for (int o = 1; o < NGW; ++o) {
-                const float2 st = grp_stat[(w & ~(NGW - 1)) | ((w + o) & (NGW - 1))][n];
+                const float2 st = grp_stat[(w & ~(NGW - 1)) | ((w + o) & (NGW - 1))][tt];
                 lo = fminf(lo, st.x);
                 hi = fmaxf(hi, st.y);
             }
         }
 
-        const int tok = tb + n;
+        const int tok = tb + tt;
         const int req = req0, pos = pos0, slot = slot0, L = len0;
         // the next tile's routing data moves up (every lane, before any early exit)
         req0 = req1; pos0 = pos1; slot0 = slot1; len0 = len1;
@@ -273,20 +281,24 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(AppendArgs a) {
         const bool to_sink = pos < a.sink_tokens;
         if (!to_sink && (slot < 0 || int64_t(slot) >= a.num_slots)) continue;
 
-        const int c0 = 32 * w + 8 * kb;
+        const int c0 = 32 * w + 16 * hh;
         if (a.rotated_out) {
             float *ro = a.rotated_out + ((size_t(tok) * a.hkv + h) * 2 + t) * kHeadDim + c0;
-            *reinterpret_cast<f32x4 *>(ro) = f32x4{vals[0], vals[1], vals[2], vals[3]};
-            *reinterpret_cast<f32x4 *>(ro + 4) = f32x4{vals[4], vals[5], vals[6], vals[7]};
-        }
-        u32x4 bf;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            bf[j] = uint32_t(bf16_bits_rn(vals[2 * j])) | (uint32_t(bf16_bits_rn(vals[2 * j + 1])) << 16);
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<f32x4 *>(ro + 4 * q) = f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+        }
+        // BF16 copy of the rotated values: only the sink and recent windows keep one
+        auto store_bf16 = [&](uint16_t *dst) {
+            u32x4 bf[2];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                bf[j >> 2][j & 3] = uint32_t(bf16_bits_rn(acc[2 * j])) | (uint32_t(bf16_bits_rn(acc[2 * j + 1])) << 16);
+            reinterpret_cast<u32x4 *>(dst)[0] = bf[0];
+            reinterpret_cast<u32x4 *>(dst)[1] = bf[1];
+        };
         if (to_sink) {
-            uint16_t *dst = a.sink + ((size_t(req) * a.sink_tokens + pos) * a.hkv + h) * 2 * kHeadDim +
-                            t * kHeadDim + c0;
-            *reinterpret_cast<u32x4 *>(dst) = bf;
+            store_bf16(a.sink + ((size_t(req) * a.sink_tokens + pos) * a.hkv + h) * 2 * kHeadDim + t * kHeadDim + c0);
             continue;
         }
 
@@ -315,36 +327,39 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(AppendArgs a) {
         }
         // thresholds z + (k + 1/2) s: exact in fp64 (fp16 operands, sums below
         // 2^19 on a 2^-25 grid), rounded up to fp32 so that "x >= T" is exact
-        // for fp32 x; a scale of zero gives +inf thresholds (codes 0)
+        // for fp32 x; a scale of zero gives +inf thresholds (codes 0).  The two
+        // lanes of a token's group share the work: each forms T1, lane hh = 0
+        // forms T0 and lane hh = 1 forms T2, and they swap those (both lanes of
+        // a token are active or inactive together: they share the routing data
+        // above, so the swap reads an active lane)
         const bool zero_scale = sd == 0.0;
-        const float u0 = zero_scale ? INFINITY : round_up_f32(zd + 0.5 * sd);
+        const float ua = zero_scale ? INFINITY : round_up_f32(zd + (hh ? 2.5 : 0.5) * sd);
         const float u1 = zero_scale ? INFINITY : round_up_f32(zd + 1.5 * sd);
-        const float u2 = zero_scale ? INFINITY : round_up_f32(zd + 2.5 * sd);
+        const float pa = __shfl_xor(ua, 32);
+        const float u0 = hh ? pa : ua;
+        const float u2 = hh ? ua : pa;
         // code = number of thresholds at or below x (u0 <= u1 <= u2): one
         // comparison picks the upper or lower pair, a second settles it
         uint32_t packed = 0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float xc = __builtin_amdgcn_fmed3f(vals[j], lo_c, hi_c);   // lo_c <= hi_c
+        for (int j = 0; j < 16; ++j) {
+            const float xc = __builtin_amdgcn_fmed3f(acc[j], lo_c, hi_c);   // lo_c <= hi_c
             const bool upper = xc >= u1;
             const uint32_t c = (upper ? 2u : 0u) + uint32_t(xc >= (upper ? u2 : u0));
             packed |= c << (2 * j);
         }
         uint8_t *rec = a.records + int64_t(slot) * rec_bytes + h * kHeadRec;
-        *reinterpret_cast<uint16_t *>(rec + t * kCodeBytes + 8 * w + 2 * kb) = uint16_t(packed);
-        if (kb == 0 && (w & (NGW - 1)) == 0) {            // one writer per group
+        *reinterpret_cast<uint32_t *>(rec + t * kCodeBytes + 8 * w + 4 * hh) = packed;
+        if (hh == 0 && (w & (NGW - 1)) == 0) {            // one writer per group
             uint8_t *dst = rec + 2 * kCodeBytes + t * kSzTensor + SZB * (w / NGW);
             if constexpr (SZB == 4)
                 *reinterpret_cast<uint32_t *>(dst) = sz_word;
             else
                 *reinterpret_cast<uint16_t *>(dst) = uint16_t(sz_word);
         }
-        if (pos >= L - a.recent_tokens) {
-            uint16_t *dst = a.recent +
-                            ((size_t(req) * a.recent_tokens + pos % a.recent_tokens) * a.hkv + h) * 2 * kHeadDim +
-                            t * kHeadDim + c0;
-            *reinterpret_cast<u32x4 *>(dst) = bf;
-        }
+        if (pos >= L - a.recent_tokens)
+            store_bf16(a.recent + ((size_t(req) * a.recent_tokens + pos % a.recent_tokens) * a.hkv + h) * 2 * kHeadDim +
+                       t * kHeadDim + c0);
     }
     }
 }
@@ -393,8 +408,8 @@ extern "C" oscar_status oscar_quant_append(hipStream_t stream, const oscar_layou
     int chunk = 0;
     if (opts && opts->append_chunk) {
         chunk = opts->append_chunk;
-        if (chunk < 16 || chunk % 16)
-            return fail(OSCAR_ERR_INVALID_ARG, "append_chunk must be a positive multiple of 16");
+        if (chunk < kTile || chunk % kTile)
+            return fail(OSCAR_ERR_INVALID_ARG, "append_chunk must be a positive multiple of 32");
     } else {
         // one round of workgroups that are all resident at once: compute
         // units x workgroups per compute unit (from the kernel's registers)
@@ -408,7 +423,7 @@ extern "C" oscar_status oscar_quant_append(hipStream_t stream, const oscar_layou
         const int slots = std::max(1, cus * std::max(1, per_cu));
         const int per = std::max(1, slots / (2 * layout->num_kv_heads));
         chunk = (n_tokens + per - 1) / per;
-        chunk = std::max(16, (chunk + 15) / 16 * 16);
+        chunk = std::max(kTile, (chunk + kTile - 1) / kTile * kTile);
     }
     const int n_chunks = (n_tokens + chunk - 1) / chunk;
 

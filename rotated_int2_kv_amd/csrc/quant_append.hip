@@ -338,15 +338,22 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(AppendArgs a) {
         const float pa = __shfl_xor(ua, 32);
         const float u0 = hh ? pa : ua;
         const float u2 = hh ? ua : pa;
-        // code = number of thresholds at or below x (u0 <= u1 <= u2): one
-        // comparison picks the upper or lower pair, a second settles it
+        // code = number of thresholds at or below the clipped value.  With
+        // alpha = 1 the clip bounds are the group's own min and max, so every
+        // value is inside them and the clip is skipped (uniform branch).
         uint32_t packed = 0;
+        if (a.alpha == 1.0f) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const float xc = __builtin_amdgcn_fmed3f(acc[j], lo_c, hi_c);   // lo_c <= hi_c
-            const bool upper = xc >= u1;
-            const uint32_t c = (upper ? 2u : 0u) + uint32_t(xc >= (upper ? u2 : u0));
-            packed |= c << (2 * j);
+            for (int j = 0; j < 16; ++j) {
+                const float x = acc[j];
+                packed |= (uint32_t(x >= u0) + uint32_t(x >= u1) + uint32_t(x >= u2)) << (2 * j);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const float x = __builtin_amdgcn_fmed3f(acc[j], lo_c, hi_c);   // lo_c <= hi_c
+                packed |= (uint32_t(x >= u0) + uint32_t(x >= u1) + uint32_t(x >= u2)) << (2 * j);
+            }
         }
         uint8_t *rec = a.records + int64_t(slot) * rec_bytes + h * kHeadRec;
         *reinterpret_cast<uint32_t *>(rec + t * kCodeBytes + 8 * w + 4 * hh) = packed;

@@ -228,6 +228,16 @@ __host__ __device__ constexpr int pair_exp(int j) { return j <= 4 ? 2 * j : 2 * 
     return j <= 4 ? (w & (0x00030003u << (2 * j))) : (w_sh6 & (0x00030003u << (2 * j - 6)));
 }
 
+// The matrix-core products below span the channels of at most two groups each:
+// channel halves 0..63 and 64..127 (P = 0, 1), and within a half the 16-channel
+// quarter k = 0..3 lies in group (64 P + 16 k) / G.  The group's index within
+// its half ("pair-local", 0 or 1) picks the A rows that carry it; with G >= 64
+// a half holds one group.
+template <int NG>
+__host__ __device__ constexpr int pair_local_group(int quarter) { return NG == 4 ? quarter >> 1 : 0; }
+template <int NG>
+__host__ __device__ constexpr int half_group(int P, int gl) { return NG == 4 ? 2 * P + gl : NG == 2 ? P : 0; }
+
 // reductions over the 16 lanes of a DPP row (every lane of the row gets the result)
 template <int K>
 __device__ __forceinline__ float row_ror(float v) {
@@ -264,29 +274,38 @@ __device__ __forceinline__ float row16_sum(float v) {
 // a fourth is computed; one workgroup barrier per tile publishes a landed
 // tile and retires the stage that the next loads overwrite.  The slot ids of
 // a tile go to a ring shared by the workgroup (each wave fetches 8 of them)
-// two tiles before its records.  Tokens past the item or with an
-// out-of-range slot read a zero record, so they arrive as s = z = 0 and
-// codes 0, and are masked out of the softmax.
+// two tiles before its records.  Tokens past the item read the record of
+// the item's first position and tokens with an out-of-range slot id that of
+// the last slot; both are masked out of the softmax (p = 0), and tiles with
+// every token usable skip the mask.
 //
-// QK (per half of 16 tokens): B = the tokens' K codes as exact fp16 denormals
-// (one AND per pair, no scale); A = q' (hi and lo fp16 parts, times
-// 2^(K - e)) in rows (h, g) that are block-diagonal over the K blocks, so
-// that output row (h, g) holds the dot product of group g only.  Lane
-// (token n, head h) thereby receives its four group sums and applies s and z
-// in fp32: one logit per lane, nothing repeated.
+// Every matrix-core product spans the channels of two groups at most (the
+// halves 0..63 and 64..127 with G = 32), so that its A rows can carry two
+// parts of one quantity instead of one row per group.
+// QK (per half of 16 tokens): lane group kb holds K-code words P = 0, 1
+// (channels 64 P + 16 kb .. + 15: group 2 P + kb / 2); B = a word's codes as
+// exact fp16 denormals (one AND per pair, no scale); A = q' (hi and lo fp16
+// parts in two products that share an output, times 2^(K - e)) in rows
+// (h, x), x = the pair-local group, nonzero where it matches the lane group's.
+// Lane (token n, head h) thereby receives its four group sums and applies s
+// and z in fp32: one logit per lane, nothing repeated.
 // PV: the lane of (token, head) forms p s_g (hi and lo fp16 parts) for the
 // four groups and accumulates p z_g itself; the weights go through the
-// wave's LDS into rows (g, h) of A, B holds the V codes of 8 tokens per lane
-// as exact denormals, and the output of column (channel) c is read from the
-// row whose group is c's group.  K-slot 8 kb + i of the PV products is token
-// 2 (i % 2) + 8 (i / 2) + (kb % 2) + 4 (kb / 2): the four lane groups read V
-// codes of tokens t, t + 1, t + 4, t + 5 at once, which the token swizzle
-// puts in disjoint LDS banks.  Weight rows hold 4 units of 16 bytes (8
-// K-slots each), the physical unit of logical unit v in row (g, h) being
-// v ^ g.  The rows live in the stage itself: once a wave has read its K codes
-// and both (s, z) of the tile into registers, those 128 units of its head are
-// dead, and each weight unit takes a dead unit in a bank group chosen so that
-// the 16-bit weight writes and the 128-bit operand reads hit distinct banks.
+// wave's LDS into rows 4 q + h of two weight planes (plane = channel half,
+// q = (pair-local group, part)), so that one product carries both parts.  B
+// holds the V codes of 8 tokens per lane as exact denormals: column n of
+// plane c is channel 64 c + 4 n + j, byte n % 4 of a V-code dword picked by
+// one v_perm_b32 per token pair.  The hi and lo rows of a column's group are
+// summed once, when the partial is written.  K-slot 8 kb + i of the PV
+// products is token 2 (i % 2) + 8 (i / 2) + (kb % 2) + 4 (kb / 2): the four
+// lane groups read V codes of tokens t, t + 1, t + 4, t + 5 at once, which the
+// token swizzle puts in disjoint LDS banks.  Weight rows hold 4 units of 16
+// bytes (8 K-slots each), the physical unit of logical unit v in row 4 q + h
+// being v ^ q.  The rows live in the stage itself: once a wave has read its K
+// codes and both (s, z) of the tile into registers, those 128 units of its
+// head are dead, and each weight unit takes a dead unit in a bank group chosen
+// so that the 16-bit weight writes and the 128-bit operand reads hit distinct
+// banks.
 constexpr int kTokBytes = 4 * kHeadRecord;             // 384: one token of a head chunk
 constexpr int kStage = kTileTokens * kTokBytes;        // 12 KiB per tile
 constexpr int kStages = 4;                             // three tiles in flight while one is computed
@@ -299,10 +318,11 @@ __host__ __device__ constexpr int int2_lds_bytes() { return kStages * kStage + k
 // (G = 128, one group).  A token of a 4-head chunk is 320 or 288 bytes (20 or
 // 18 units), stored in token order without a swizzle; a tile takes 640 or 576
 // of the stage's 768 unit positions, the rest receive zero-record loads so
-// that every lane still issues three.  The A rows (h, g) of the QK products
-// are block-diagonal over the two groups, or a single group.  The PV weights
+// that every lane still issues three.  With G >= 64 a channel half holds one
+// group, so the A rows x = 1 of the QK products are zero and the PV weights use
+// rows q = part only (G = 128: one plane serves both halves).  The PV weights
 // get their own LDS area (a head has too few dead units per token): per wave
-// two planes (hi, lo) of up to 8 rows (g, h) x 32 K-slots of fp16.
+// two planes (channel halves) of 8 rows 4 q + h x 32 K-slots of fp16.
 constexpr int kWeightPlane = 8 * kTileTokens * 2;      // 512 bytes
 constexpr int kWeightWave = 2 * kWeightPlane;          // 1 KiB
 __host__ __device__ constexpr int int2_lds_bytes_lowmeta() { return int2_lds_bytes() + 4 * kWeightWave; }
@@ -317,6 +337,14 @@ __host__ __device__ constexpr int int2_lds_bytes_lowmeta() { return int2_lds_byt
 __host__ __device__ constexpr int tok_swizzle(int t) {
     return (((t & 1) << 1) | ((t >> 1) & 1) | (t & 4)) ^ (2 * ((t >> 3) & 1));
 }
+// Bit 0 of the swizzle is bit 1 of the token: it orders the two units of an
+// even/odd pair (K codes 0, 1 and V codes 2, 3 of a head record) in the line.
+constexpr bool swizzle_bit0_is_token_bit1() {
+    for (int t = 0; t < 32; ++t)
+        if ((tok_swizzle(t) & 1) != ((t >> 1) & 1)) return false;
+    return true;
+}
+static_assert(swizzle_bit0_is_token_bit1(), "unit pair order");
 
 // byte offset of 16-byte unit q (0..23) of token t inside a stage
 __device__ __forceinline__ int unit_addr(int t, int q) {
@@ -402,7 +430,10 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
     const size_t head0 = size_t(b) * a.hq + size_t(active ? hk : 0) * GQ;
 
     // ---- per-item operands
-    f16x8 qA[HS][4][2];   // QK A: row n = (h = n / 4, g = n % 4), nonzero in K block g
+    // QK A of word P (K codes 64 P + 16 kb .. + 15 in lane group kb), half sh
+    // (pairs 4 sh .. 4 sh + 3): row n = (h = n / 4, x = n % 4) with x = (pair-local
+    // group, part); nonzero where the row's group is the lane group's
+    f16x8 qA[HS][2][2];
     float qz[HS][4];      // Qbar[head kb][g] 2^(K - 24): zero-point term in the MFMA's units
     float qout[HS];       // 2^(24 - K) of head kb: MFMA units -> logit units (log2)
 #pragma unroll
@@ -412,23 +443,25 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
             const bool hv = h < GQ && active;
             const float *qr = a.qrot + (head0 + (hv ? h : 0)) * kHeadDim;
             const float k2 = a.qsum[(head0 + (hv ? h : 0)) * 8 + 4];
-            const bool nz = hv && (n & 3) == (kb * NG) / 4;   // row group = group of K block kb
+            const bool nz = hv && ((n & 3) >> 1) == pair_local_group<NG>(kb);
+            const bool lo_row = (n & 1) != 0;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                uint32_t whi[4], wlo[4];
+            for (int P = 0; P < 2; ++P) {
 #pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const int jj = 4 * (r & 1) + p;
-                    const int c0 = 32 * kb + 16 * (r >> 1) + jj;
-                    const float sc = k2 * __builtin_ldexpf(1.0f, -pair_exp(jj));
-                    const float x0 = nz ? qr[c0] * sc : 0.0f;
-                    const float x1 = nz ? qr[c0 + 8] * sc : 0.0f;
-                    const HiLo2 hl = split_hilo(x0, x1);
-                    whi[p] = hl.hi;
-                    wlo[p] = hl.lo;
+                for (int sh = 0; sh < 2; ++sh) {
+                    uint32_t wv[4];
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        const int jj = 4 * sh + p;
+                        const int c0 = 64 * P + 16 * kb + jj;
+                        const float sc = k2 * __builtin_ldexpf(1.0f, -pair_exp(jj));
+                        const float x0 = nz ? qr[c0] * sc : 0.0f;
+                        const float x1 = nz ? qr[c0 + 8] * sc : 0.0f;
+                        const HiLo2 hl = split_hilo(x0, x1);
+                        wv[p] = lo_row ? hl.lo : hl.hi;
+                    }
+                    qA[hs][P][sh] = u4_as_h8(wv[0], wv[1], wv[2], wv[3]);
                 }
-                qA[hs][r][0] = u4_as_h8(whi[0], whi[1], whi[2], whi[3]);
-                qA[hs][r][1] = u4_as_h8(wlo[0], wlo[1], wlo[2], wlo[3]);
             }
         }
         {
@@ -487,27 +520,41 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
     for (int u = 0; u < 3; ++u) slot_at[u] = lds_pin(ring + 4 * tq[u]);
     const uint32_t slot_own = lds_pin(ring + 4 * (lane & 31));
     // record addresses of tile T (slot ids in ring slot rs) and its usable
-    // tokens (bit t); out-of-range slot ids read the zero record
+    // tokens (bit t).  History items run only with num_slots >= 1.
+    const uint32_t slot_max = uint32_t(a.num_slots - 1);
     struct Fetch {
         const uint8_t *src[3];
         uint32_t valid;
     };
-    auto prep = [&](int T, int rs) -> Fetch {
-        Fetch f;
+    // the slot ids of a tile in ring slot rs: this lane's three record tokens
+    // and its own token
+    struct SlotIds {
         int slot[3];
+        int own;
+    };
+    auto read_ids = [&](int rs) -> SlotIds {
+        SlotIds ids;
 #pragma unroll
-        for (int u = 0; u < 3; ++u) slot[u] = lds_ld<int>(slot_at[u] + rs * kRingBytes);
-        const int s_own = lds_ld<int>(slot_own + rs * kRingBytes);
+        for (int u = 0; u < 3; ++u) ids.slot[u] = lds_ld<int>(slot_at[u] + rs * kRingBytes);
+        ids.own = lds_ld<int>(slot_own + rs * kRingBytes);
+        return ids;
+    };
+    auto form = [&](int T, const SlotIds &ids) -> Fetch {
+        Fetch f;
+        // out-of-range slot ids read the last slot's record: their tokens are
+        // masked (p = 0), so what they hold does not enter the result
 #pragma unroll
         for (int u = 0; u < 3; ++u) {
-            const bool ok = uint32_t(slot[u]) < uint32_t(a.num_slots) && in_tile[u];
-            f.src[u] = ok ? src_base[u] + uint64_t(uint32_t(slot[u])) * rec_bytes : a.zero_rec;
+            const uint32_t sl = min(uint32_t(ids.slot[u]), slot_max);
+            const uint8_t *rec = src_base[u] + uint64_t(sl) * rec_bytes;
+            f.src[u] = NG == 4 || in_tile[u] ? rec : a.zero_rec;
         }
         const uint32_t left = span - uint32_t(T * kTileTokens);   // positions left in the item (may wrap: none)
         const uint32_t n_ok = uint32_t(T * kTileTokens) < span ? left : 0u;
-        f.valid = uint32_t(__ballot((uint32_t(lane & 31) < n_ok) & (uint32_t(s_own) < uint32_t(a.num_slots))));
+        f.valid = uint32_t(__ballot((uint32_t(lane & 31) < n_ok) & (uint32_t(ids.own) < uint32_t(a.num_slots))));
         return f;
     };
+    auto prep = [&](int T, int rs) -> Fetch { return form(T, read_ids(rs)); };
     auto issue = [&](const Fetch &f, int k) {
 #pragma unroll
         for (int u = 0; u < 3; ++u)
@@ -521,11 +568,14 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
     };
 
     // running state, per lane = (token n, head kb of each set)
-    float m_run[HS], l_lane[HS], zl[HS][NG];
-    f32x4 oacc[HS][8];    // PV output: lane (n, kb) rows (g = kb, h = i), channel 8 n + jj
+    // m_ref = m_run 2^(24 - K) in log2 units, or 0 (a finite stand-in) while
+    // every token so far is masked; it changes only when the running max grows
+    float m_run[HS], m_ref[HS], l_lane[HS], zl[HS][NG];
+    f32x4 oacc[HS][8];    // PV output: lane (n, kb) rows 4 q + h = (kb, i), channels 64 c + 4 n + j
 #pragma unroll
     for (int hs = 0; hs < HS; ++hs) {
         m_run[hs] = -INFINITY;
+        m_ref[hs] = 0.0f;
         l_lane[hs] = 0.0f;
 #pragma unroll
         for (int g = 0; g < NG; ++g) zl[hs][g] = 0.0f;
@@ -539,50 +589,84 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
     // byte b of head w's record of token t in stage 0 (80-byte layout)
     auto rec_at = [&](int t, int byte) { return st0 + t * kTokB + kRecH * w + byte; };
     const int kb_tok = (kb & 1) + 4 * (kb >> 1);
-    uint32_t qk_at, szk_at, szv_at, a_at;
-    constexpr uint32_t wlo_off = NG == 4 ? kHalfTok : kWeightPlane;   // lo plane of the PV weights
-    uint32_t pv_at[8];    // V codes (channels 8 n .. 8 n + 7) of the tokens of K-slots 8 kb + i
-    uint32_t w_at[NG];    // PV weight of token t of this lane's row (g, kb); token 16 + t 8 bytes further
+    // K codes: word P of the lane = bytes 16 P + 4 kb .. + 3 (channels 64 P + 16 kb .. + 15)
+    uint32_t qk_at[2], szk_at, szv_at, a_at;
+    // second plane of the PV weights (channels 64..127)
+    constexpr uint32_t wpl_off = NG == 4 ? kHalfTok : kWeightPlane;
+    // V codes of the token of K-slot 8 kb + i: byte n (channels 4 n .. 4 n + 3)
+    // is byte n % 4 of the dword at pv_at[i] + pv_off(0, i), byte 16 + n that of
+    // the dword at pv_at[i] + pv_off(1, i)
+    uint32_t pv_at[8];
+    // v_perm_b32 selector: bytes (n % 4 of the first token, 0, n % 4 of the second, 0)
+    const uint32_t pv_sel = lds_pin(0x0c040c00u | uint32_t(n & 3) * 0x00010001u);
+    // PV weight of token t in row 4 q + kb (q = 0 .. NQ - 1); token 16 + t 8 bytes further
+    constexpr int NQ = NG == 4 ? 4 : 2;
+    uint32_t w_at[NQ];
     const int w_unit = (n & 1) + 2 * ((n >> 2) & 1);            // K-slot / 8 of token n
     const int w_i = ((n >> 1) & 1) + 2 * (n >> 3);              // K-slot % 8
     if constexpr (NG == 4) {
-        qk_at = lds_pin(st0 + unit_addr(n, 6 * w + (kb >> 1)) + 8 * (kb & 1));   // K codes
+#pragma unroll
+        for (int P = 0; P < 2; ++P) qk_at[P] = lds_pin(st0 + unit_addr(n, 6 * w + P) + 4 * kb);
         szk_at = lds_pin(st0 + unit_addr(n, 6 * w + 4));
         szv_at = lds_pin(st0 + unit_addr(n, 6 * w + 5));
+        // V-code units 2 and 3 of the head record sit side by side, in the
+        // order given by bit 0 of the token's swizzle, which is bit 1 of the
+        // token, i.e. i % 2: the lower of the two is the base
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            pv_at[i] = lds_pin(st0 + unit_addr(2 * (i & 1) + 8 * (i >> 1) + kb_tok, 6 * w + 2 + (n >> 3)) + ((2 * n) & 15));
-        // K-slot 8 unit + i of the row, unit XOR-permuted by g
+            pv_at[i] = lds_pin(st0 + unit_addr(2 * (i & 1) + 8 * (i >> 1) + kb_tok, 6 * w + 2 + (i & 1)) + (n & ~3));
+        // K-slot 8 unit + i of the row, unit XOR-permuted by q
 #pragma unroll
-        for (int g = 0; g < 4; ++g) w_at[g] = lds_pin(st0 + wunit_addr(w, 4 * g + kb, w_unit ^ g) + 2 * w_i);
+        for (int q = 0; q < 4; ++q) w_at[q] = lds_pin(st0 + wunit_addr(w, 4 * q + kb, w_unit ^ q) + 2 * w_i);
         // A-operand read of row n, K-slots 8 kb .. 8 kb + 7
         a_at = lds_pin(st0 + wunit_addr(w, n, kb ^ (n >> 2)));
     } else {
-        qk_at = lds_pin(rec_at(n, 8 * kb));
+        qk_at[0] = lds_pin(rec_at(n, 4 * kb));
+        qk_at[1] = qk_at[0] + 16;
         szk_at = lds_pin(rec_at(n, 2 * kCodeBytes));
         szv_at = lds_pin(rec_at(n, 2 * kCodeBytes + SZB * NG));
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pv_at[i] = lds_pin(rec_at(2 * (i & 1) + 8 * (i >> 1) + kb_tok, kCodeBytes + 2 * n));
+        for (int i = 0; i < 8; ++i) pv_at[i] = lds_pin(rec_at(2 * (i & 1) + 8 * (i >> 1) + kb_tok, kCodeBytes + (n & ~3)));
         const uint32_t wb = st0 + int2_lds_bytes() + w * kWeightWave;   // after the stages and the ring
 #pragma unroll
-        for (int g = 0; g < NG; ++g) w_at[g] = lds_pin(wb + (4 * g + kb) * 64 + 16 * w_unit + 2 * w_i);
-        // rows of absent groups repeat written rows; their outputs are never read
-        a_at = lds_pin(wb + (n & (4 * NG - 1)) * 64 + 16 * kb);
+        for (int q = 0; q < 2; ++q) w_at[q] = lds_pin(wb + (4 * q + kb) * 64 + 16 * w_unit + 2 * w_i);
+        a_at = lds_pin(wb + (n & 7) * 64 + 16 * kb);
     }
+    // byte offset of V-code byte 16 c + n from pv_at[i]
+    auto pv_off = [](int c, int i) -> uint32_t { return NG == 4 ? 16u * uint32_t(c ^ (i & 1)) : 16u * uint32_t(c); };
     // the weight area of the 80-byte layout does not move with the stage
     constexpr bool kWeightsInStage = NG == 4;
 
     // one tile: QK, online softmax, PV (LDS stage K)
     auto compute = [&](auto K, uint32_t valid) {
         constexpr uint32_t so = decltype(K)::value * kStage;   // stage offset
+        // ---- V codes for the PV products, read first so that their LDS latency
+        // overlaps the QK products and the softmax.  Plane c (channels 64 c .. 64 c + 63) has A
+        // rows 4 q + h, q = (pair-local group, part): the hi and lo fp16 parts
+        // of the weights p s_g of the half's groups for K-slots 8 kb .. 8 kb + 7,
+        // so that one product carries both parts.  B of plane c, pair j = the V
+        // codes of channel 64 c + 4 n + j for the same tokens, two tokens per
+        // 32-bit word.
+        uint32_t xw[2][4];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) {
+                const uint32_t lo = lds_ld<uint32_t>(pv_at[2 * pp] + pv_off(c, 2 * pp) + so);
+                const uint32_t hi = lds_ld<uint32_t>(pv_at[2 * pp + 1] + pv_off(c, 2 * pp + 1) + so);
+                const uint32_t pr = __builtin_amdgcn_perm(hi, lo, pv_sel);
+                // tokens 16..31 (pp = 2, 3) as 3 - c: every 2-bit code inverted
+                // (the bits above the codes are never read)
+                xw[c][pp] = pp >= 2 ? ~pr : pr;
+            }
+        }
         // ---- QK: logit of (token 16 hf + n, head 4 hs + kb)
         float lg[HS][2];
         uint32_t szv[2][NG];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-            const int tk = 16 * hf + n;
             const uint32_t ho = so + hf * kHalfTok;
-            const u32x2 kc = lds_ld<u32x2>(qk_at + ho);
+            const uint32_t kc[2] = {lds_ld<uint32_t>(qk_at[0] + ho), lds_ld<uint32_t>(qk_at[1] + ho)};
             uint32_t szk[NG];
             if constexpr (NG == 4) {
                 const u32x4 k4 = lds_ld<u32x4>(szk_at + ho), v4 = lds_ld<u32x4>(szv_at + ho);
@@ -610,33 +694,49 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
                 szk[0] = lds_ld<uint32_t>(szk_at + ho);
                 szv[hf][0] = lds_ld<uint32_t>(szv_at + ho);
             }
-            const uint32_t d0s = kc[0] >> 6, d1s = kc[1] >> 6;
-            f16x8 B[4];
+            // B of word P, half sh: pairs 4 sh .. 4 sh + 3 of the word as exact denormals
+            f16x8 B[2][2];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const uint32_t d = r < 2 ? kc[0] : kc[1];
-                const uint32_t ds = r < 2 ? d0s : d1s;
-                B[r] = u4_as_h8(code_bits(d, ds, 4 * (r & 1) + 0), code_bits(d, ds, 4 * (r & 1) + 1),
-                                code_bits(d, ds, 4 * (r & 1) + 2), code_bits(d, ds, 4 * (r & 1) + 3));
+            for (int P = 0; P < 2; ++P) {
+                const uint32_t ds = kc[P] >> 6;
+#pragma unroll
+                for (int sh = 0; sh < 2; ++sh)
+                    B[P][sh] = u4_as_h8(code_bits(kc[P], ds, 4 * sh + 0), code_bits(kc[P], ds, 4 * sh + 1),
+                                        code_bits(kc[P], ds, 4 * sh + 2), code_bits(kc[P], ds, 4 * sh + 3));
             }
-            const bool live = (valid >> tk) & 1u;
 #pragma unroll
             for (int hs = 0; hs < HS; ++hs) {
-                f32x4 acc = f32x4{0, 0, 0, 0};
+                // acc[P] element x = (pair-local group x / 2, part x % 2) of
+                // group half_group(P, x / 2): its hi or lo dot product
+                f32x4 acc[2];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    acc = mfma_f16(qA[hs][r][0], B[r], acc);
-                    acc = mfma_f16(qA[hs][r][1], B[r], acc);
+                for (int P = 0; P < 2; ++P) {
+                    acc[P] = mfma_f16(qA[hs][P][0], B[P][0], f32x4{0, 0, 0, 0});
+                    acc[P] = mfma_f16(qA[hs][P][1], B[P][1], acc[P]);
                 }
-                // acc[g] = group g's dot product; s_g, z_g are halves of szk[g].
-                // The logit stays in the MFMA's units (a factor 2^(K - 24) of the
-                // log2 logit, K fixed per head); masked tokens start from -inf.
-                float x = live ? 0.0f : -INFINITY;
+                // s_g, z_g are halves of szk[g].  The logit stays in the MFMA's
+                // units (a factor 2^(K - 24) of the log2 logit, K fixed per head).
+                float x = 0.0f;
 #pragma unroll
                 for (int g = 0; g < NG; ++g) x = fmaf(half_hi(szk[g]), qz[hs][g], x);
 #pragma unroll
-                for (int g = 0; g < NG; ++g) x = fmaf(acc[g], half_lo(szk[g]), x);
+                for (int P = 0; P < 2; ++P) {
+#pragma unroll
+                    for (int gl = 0; gl < (NG == 4 ? 2 : 1); ++gl) {
+                        const float sg = half_lo(szk[half_group<NG>(P, gl)]);
+                        x = fmaf(acc[P][2 * gl], sg, x);
+                        x = fmaf(acc[P][2 * gl + 1], sg, x);
+                    }
+                }
                 lg[hs][hf] = x;
+            }
+        }
+        // masked tokens (only in tiles that are not full) get -inf
+        if (__builtin_expect(valid != 0xffffffffu, 0)) {
+#pragma unroll
+            for (int hs = 0; hs < HS; ++hs) {
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) lg[hs][hf] = ((valid >> (16 * hf + n)) & 1u) ? lg[hs][hf] : -INFINITY;
             }
         }
         // ---- online softmax
@@ -653,13 +753,11 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
 #pragma unroll
                 for (int g = 0; g < NG; ++g) zl[hs][g] *= alpha[hs];
                 m_run[hs] = m_new;
+                m_ref[hs] = m_new == -INFINITY ? 0.0f : m_new * qout[hs];
             }
-            // exponent reference in log2 units: a finite stand-in while every
-            // token so far is masked
-            const float m_ref = m_run[hs] == -INFINITY ? 0.0f : m_run[hs] * qout[hs];
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(lg[hs][hf], qout[hs], -m_ref));   // 0 for masked tokens
+                const float p = __builtin_amdgcn_exp2f(fmaf(lg[hs][hf], qout[hs], -m_ref[hs]));   // 0 for masked tokens
                 pw[hs][hf] = p;
                 l_lane[hs] += p;
                 // tokens 16..31 enter the PV products as -p s_g against 3 - c (see
@@ -674,18 +772,7 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
                 }
             }
         }
-        // ---- PV: A rows (g, h) = weights of K-slots 8 kb .. 8 kb + 7; B = V
-        // codes of channel 8 n + jj for the same tokens, two per 32-bit word
-        uint32_t xw[4], xs[4];
-#pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
-            u16x2 pr;
-            pr.x = lds_ld<uint16_t>(pv_at[2 * pp] + so);
-            pr.y = lds_ld<uint16_t>(pv_at[2 * pp + 1] + so);
-            // tokens 16..31 (pp = 2, 3) as 3 - c: every 2-bit code inverted
-            xw[pp] = pp >= 2 ? ~__builtin_bit_cast(uint32_t, pr) : __builtin_bit_cast(uint32_t, pr);
-            xs[pp] = xw[pp] >> 6;
-        }
+        // ---- PV
 #pragma unroll
         for (int hs = 0; hs < HS; ++hs) {
             // w_g = p s_g as hi + lo fp16 parts, both rounded to nearest; lo = w_g - hi.
@@ -700,26 +787,28 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
                 // the zero-point sum, and the truncation errors cancel; the running
                 // sums also stay near the output instead of growing to ~1.5 s l.
                 const float p = hf ? -pw[hs][hf] : pw[hs][hf];
+                constexpr uint32_t wso = kWeightsInStage ? so : 0u;
                 constexpr int kPairs = (NG + 1) / 2;
-                uint32_t hw[kPairs], lw[kPairs];
+                HiLo2 hl[kPairs];
 #pragma unroll
                 for (int q2 = 0; q2 < kPairs; ++q2) {
                     const float s0 = half_lo(szv[hf][2 * q2]);
                     const float s1 = NG > 1 ? half_lo(szv[hf][(2 * q2 + 1) % NG]) : 0.0f;
-                    hw[q2] = pk_rn(fmaf(p, s0, 0.0f), fmaf(p, s1, 0.0f));
-                    lw[q2] = pk_rn(fmaf(p, s0, -half_lo(hw[q2])), fmaf(p, s1, -half_hi(hw[q2])));
+                    hl[q2].hi = pk_rn(fmaf(p, s0, 0.0f), fmaf(p, s1, 0.0f));
+                    hl[q2].lo = pk_rn(fmaf(p, s0, -half_lo(hl[q2].hi)), fmaf(p, s1, -half_hi(hl[q2].hi)));
                 }
-                constexpr uint32_t wso = kWeightsInStage ? so : 0u;
 #pragma unroll
                 for (int g = 0; g < NG; ++g) {
                     const int sh = 16 * (g & 1);
-                    lds_st<uint16_t>(w_at[g] + wso + 8 * hf, uint16_t(hw[g >> 1] >> sh));
-                    lds_st<uint16_t>(w_at[g] + wso + 8 * hf + wlo_off, uint16_t(lw[g >> 1] >> sh));
+                    const int gl = NG == 4 ? (g & 1) : 0;
+                    const uint32_t pl = NG == 4 ? uint32_t(g >> 1) * wpl_off : NG == 2 ? uint32_t(g) * wpl_off : 0u;
+                    lds_st<uint16_t>(w_at[2 * gl] + pl + wso + 8 * hf, uint16_t(hl[g >> 1].hi >> sh));
+                    lds_st<uint16_t>(w_at[2 * gl + 1] + pl + wso + 8 * hf, uint16_t(hl[g >> 1].lo >> sh));
                 }
             }
             lds_order();
             // rescale the output rows of heads whose running max grew; PV output
-            // row (g, h) = (kb, i): the factor of head i lives in row i of lanes
+            // row 4 q + h = (kb, i): the factor of head i lives in row i of lanes
             if (__builtin_expect(grow[hs], 0)) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -730,14 +819,18 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
                 }
             }
             constexpr uint32_t aso = kWeightsInStage ? so : 0u;
-            const f16x8 ahi = lds_ld<f16x8>(a_at + aso);
-            const f16x8 alo = lds_ld<f16x8>(a_at + aso + wlo_off);
+            f16x8 A[2];
+            A[0] = lds_ld<f16x8>(a_at + aso);
+            // with one group, both halves use its weights
+            A[1] = NG == 1 ? A[0] : lds_ld<f16x8>(a_at + aso + wpl_off);
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                const f16x8 Bj = u4_as_h8(code_bits(xw[0], xs[0], jj), code_bits(xw[1], xs[1], jj),
-                                          code_bits(xw[2], xs[2], jj), code_bits(xw[3], xs[3], jj));
-                oacc[hs][jj] = mfma_f16(ahi, Bj, oacc[hs][jj]);
-                oacc[hs][jj] = mfma_f16(alo, Bj, oacc[hs][jj]);
+            for (int c = 0; c < 2; ++c) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t m = 0x00030003u << (2 * j);
+                    const f16x8 Bj = u4_as_h8(xw[c][0] & m, xw[c][1] & m, xw[c][2] & m, xw[c][3] & m);
+                    oacc[hs][4 * c + j] = mfma_f16(A[c], Bj, oacc[hs][4 * c + j]);
+                }
             }
             // the next set's weights go to the same units: the reads above come first
             lds_order();
@@ -784,8 +877,11 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
         sync();
         slot_load(t + 6, (k + 2) & 3);
         issue(f, (k + 3) & 3);                            // R(t + 3)
+        // the slot ids of tile t + 4 are read before the compute, so that their
+        // LDS latency overlaps it; its record addresses are formed after
+        const SlotIds ids = read_ids(k);
         if (run_compute && vq0 != 0u) compute(K, vq0);
-        f = prep(t + 4, k);
+        f = form(t + 4, ids);
         vq0 = vq1;
         vq1 = vq2;
         vq2 = vq3;
@@ -803,7 +899,15 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
 
     // ---- write the partial (m, l, o') of the GQ heads
     const size_t row0 = (size_t(b) * a.items + j) * a.hq + hk * GQ;
-    const int cg = (8 * n) / (kHeadDim / NG);   // group of output channels 8 n .. 8 n + 7
+    // lane (n, kb) holds rows 4 kb + i = (q = kb, h = i) of column n: channel
+    // 64 c + 4 n + j in oacc[hs][4 c + j].  That channel's group is
+    // half_group(c, gl) with gl = pair_local_group(n / 4); its hi and lo rows
+    // (q = 2 gl, 2 gl + 1) are in lanes kb = 2 gl and 2 gl + 1, 16 lanes apart
+    const int gl_o = pair_local_group<NG>(n >> 2);
+    const bool writer = kb == 2 * gl_o;
+    auto swap16 = [](float v) {   // the value of lane l ^ 16
+        return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+    };
 #pragma unroll
     for (int hs = 0; hs < HS; ++hs) {
         const float l_row = row16_sum(l_lane[hs]);
@@ -814,26 +918,30 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
             a.part_ml[(row0 + 4 * hs + kb) * 2 + 0] = m_run[hs] * qout[hs];   // log2 units
             a.part_ml[(row0 + 4 * hs + kb) * 2 + 1] = l_row;
         }
-        // lane (n, kb) holds rows (g = kb, h = i); the row whose group matches
-        // channel 8 n + jj (group n / 4) carries the result
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if (4 * hs + i >= GQ) break;
-            // p z summed over the item for head i, group cg (held by row i of lanes)
-            float z = 0.0f;
+            // p z summed over the item for head i and each group (held by row i of lanes)
+            float zg[NG];
 #pragma unroll
-            for (int g = 0; g < NG; ++g) {
-                const float zi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, zt[g]), 16 * i));
-                z = g == cg ? zi : z;
+            for (int g = 0; g < NG; ++g)
+                zg[g] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, zt[g]), 16 * i));
+            float o[8];
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                float z = 0.0f;
+#pragma unroll
+                for (int gl = 0; gl < (NG == 4 ? 2 : 1); ++gl) z = gl == gl_o ? zg[half_group<NG>(c, gl)] : z;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const float v = oacc[hs][4 * c + jj][i];
+                    o[4 * c + jj] = (v + swap16(v)) * __builtin_ldexpf(1.0f, 24 - pair_exp(jj)) + z;
+                }
             }
-            if (kb == cg) {
-                float o[8];
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj)
-                    o[jj] = oacc[hs][jj][i] * __builtin_ldexpf(1.0f, 24 - pair_exp(jj)) + z;
-                float *dst = a.part_o + (row0 + 4 * hs + i) * kHeadDim + 8 * n;
+            if (writer) {
+                float *dst = a.part_o + (row0 + 4 * hs + i) * kHeadDim + 4 * n;
                 *reinterpret_cast<f32x4 *>(dst) = f32x4{o[0], o[1], o[2], o[3]};
-                *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
+                *reinterpret_cast<f32x4 *>(dst + 64) = f32x4{o[4], o[5], o[6], o[7]};
             }
         }
     }

@@ -345,6 +345,13 @@ constexpr bool swizzle_bit0_is_token_bit1() {
     return true;
 }
 static_assert(swizzle_bit0_is_token_bit1(), "unit pair order");
+// Tokens t and t + 2 with bit 1 of t clear differ in bit 0 of the swizzle only.
+constexpr bool swizzle_of_t_plus_2() {
+    for (int t = 0; t < 32; ++t)
+        if ((t & 2) == 0 && tok_swizzle(t + 2) != (tok_swizzle(t) ^ 1)) return false;
+    return true;
+}
+static_assert(swizzle_of_t_plus_2(), "V-code unit pairs of tokens t, t + 2");
 
 // byte offset of 16-byte unit q (0..23) of token t inside a stage
 __device__ __forceinline__ int unit_addr(int t, int q) {
@@ -595,7 +602,12 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
     constexpr uint32_t wpl_off = NG == 4 ? kHalfTok : kWeightPlane;
     // V codes of the token of K-slot 8 kb + i: byte n (channels 4 n .. 4 n + 3)
     // is byte n % 4 of the dword at pv_at[i] + pv_off(0, i), byte 16 + n that of
-    // the dword at pv_at[i] + pv_off(1, i)
+    // the dword at pv_at[i] + pv_off(1, i).  With G = 32, the tokens of K-slots
+    // 2 pp and 2 pp + 1 are t and t + 2, 768 bytes apart, and the swizzle puts
+    // each V unit of token t + 2 at the line position of the other V unit of
+    // token t: pv_at[2 pp] (+ 768) reads V-code unit 2 of t and unit 3 of t + 2,
+    // pv_at[2 pp + 1] (+ 768) unit 3 of t and unit 2 of t + 2, each pair in one
+    // ds_read2st64_b32 whose offsets also take the stage.
     uint32_t pv_at[8];
     // v_perm_b32 selector: bytes (n % 4 of the first token, 0, n % 4 of the second, 0)
     const uint32_t pv_sel = lds_pin(0x0c040c00u | uint32_t(n & 3) * 0x00010001u);
@@ -610,11 +622,13 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
         szk_at = lds_pin(st0 + unit_addr(n, 6 * w + 4));
         szv_at = lds_pin(st0 + unit_addr(n, 6 * w + 5));
         // V-code units 2 and 3 of the head record sit side by side, in the
-        // order given by bit 0 of the token's swizzle, which is bit 1 of the
-        // token, i.e. i % 2: the lower of the two is the base
+        // order given by bit 0 of the token's swizzle (bit 1 of the token): for
+        // token t = 8 pp + kb_tok (bit 1 clear) unit 2 is the lower one
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            pv_at[i] = lds_pin(st0 + unit_addr(2 * (i & 1) + 8 * (i >> 1) + kb_tok, 6 * w + 2 + (i & 1)) + (n & ~3));
+        for (int pp = 0; pp < 4; ++pp) {
+            pv_at[2 * pp] = lds_pin(st0 + unit_addr(8 * pp + kb_tok, 6 * w + 2) + (n & ~3));
+            pv_at[2 * pp + 1] = lds_pin(st0 + unit_addr(8 * pp + kb_tok, 6 * w + 3) + (n & ~3));
+        }
         // K-slot 8 unit + i of the row, unit XOR-permuted by q
 #pragma unroll
         for (int q = 0; q < 4; ++q) w_at[q] = lds_pin(st0 + wunit_addr(w, 4 * q + kb, w_unit ^ q) + 2 * w_i);
@@ -632,8 +646,8 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
         for (int q = 0; q < 2; ++q) w_at[q] = lds_pin(wb + (4 * q + kb) * 64 + 16 * w_unit + 2 * w_i);
         a_at = lds_pin(wb + (n & 7) * 64 + 16 * kb);
     }
-    // byte offset of V-code byte 16 c + n from pv_at[i]
-    auto pv_off = [](int c, int i) -> uint32_t { return NG == 4 ? 16u * uint32_t(c ^ (i & 1)) : 16u * uint32_t(c); };
+    // byte offset of V-code byte 16 c + n from pv_at[i] (80- and 72-byte layouts)
+    auto pv_off = [](int c) -> uint32_t { return 16u * uint32_t(c); };
     // the weight area of the 80-byte layout does not move with the stage
     constexpr bool kWeightsInStage = NG == 4;
 
@@ -649,12 +663,23 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
         // 32-bit word.
         uint32_t xw[2][4];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int pp = 0; pp < 4; ++pp) {
+            uint32_t lo[2], hi[2];   // plane c dword of the first and the second token
+            if constexpr (NG == 4) {
+                lo[0] = lds_ld<uint32_t>(pv_at[2 * pp] + so);
+                hi[1] = lds_ld<uint32_t>(pv_at[2 * pp] + so + 2 * kTokBytes);
+                lo[1] = lds_ld<uint32_t>(pv_at[2 * pp + 1] + so);
+                hi[0] = lds_ld<uint32_t>(pv_at[2 * pp + 1] + so + 2 * kTokBytes);
+            } else {
 #pragma unroll
-            for (int pp = 0; pp < 4; ++pp) {
-                const uint32_t lo = lds_ld<uint32_t>(pv_at[2 * pp] + pv_off(c, 2 * pp) + so);
-                const uint32_t hi = lds_ld<uint32_t>(pv_at[2 * pp + 1] + pv_off(c, 2 * pp + 1) + so);
-                const uint32_t pr = __builtin_amdgcn_perm(hi, lo, pv_sel);
+                for (int c = 0; c < 2; ++c) {
+                    lo[c] = lds_ld<uint32_t>(pv_at[2 * pp] + pv_off(c) + so);
+                    hi[c] = lds_ld<uint32_t>(pv_at[2 * pp + 1] + pv_off(c) + so);
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const uint32_t pr = __builtin_amdgcn_perm(hi[c], lo[c], pv_sel);
                 // tokens 16..31 (pp = 2, 3) as 3 - c: every 2-bit code inverted
                 // (the bits above the codes are never read)
                 xw[c][pp] = pp >= 2 ? ~pr : pr;

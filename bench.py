@@ -177,17 +177,21 @@ def run_decode(args, torch, B, workloads, name=None, steps=None, warmup=None):
         if ev is not None:
             ev[3].record(stream)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    # the timing events exist before the warm-up steps, so that the timed steps
+    # follow the warm-up without an idle gap (an idle GPU lowers its clock)
     evs = []
     for _ in range(steps):
         e = tuple(torch.cuda.Event(enable_timing=True) for _ in range(4))
         for x in e:
             x.record(stream)   # create the underlying HIP events
         evs.append(e)
-    torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
     start.record(stream)
     for i in range(steps):
         step(evs[i])
@@ -701,6 +705,11 @@ def main():
                      "kernel": "partial_kernel (split-K)", "kernel_ms": d["kern_ms"],
                      "kernel_ms_median": d["kern_ms_median"], "kernel_ms_first": d["per_launch_kernel_ms"][0],
                      "kernel_ms_last": d["per_launch_kernel_ms"][-1],
+                     "kernel_ms_min": d["kern_ms_min"], "kernel_ms_max": d["kern_ms_max"],
+                     # every timed launch in order, for short runs (the clock and
+                     # power state of the first milliseconds shows in them)
+                     "kernel_ms_per_launch": [round(x, 4) for x in d["per_launch_kernel_ms"]]
+                     if len(d["per_launch_kernel_ms"]) <= 100 else None,
                      "frac_median": d["kbytes"] / (d["kern_ms_median"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "algorithmic_bytes": d["kbytes"],
                      "call": "oscar_decode_attn (query rotation + split-K + merge and un-rotation)",

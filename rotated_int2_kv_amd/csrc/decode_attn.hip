@@ -1754,7 +1754,8 @@ extern "C" oscar_status oscar_extend_attn(hipStream_t stream, const oscar_layout
     a.fixed_req = req_id;
     a.fixed_len = prefix_len;
 
-    // work items on the matrix cores, 128 / g new tokens per workgroup
+    // work items on the matrix cores: 256 / g new tokens per history
+    // workgroup, 128 / g per workgroup of the BF16 items
     ExtendHistArgs xh;
     xh.records = pool->records;
     xh.slot_row = req_to_slot + size_t(req_id) * req_to_slot_stride;
@@ -1775,6 +1776,8 @@ extern "C" oscar_status oscar_extend_attn(hipStream_t stream, const oscar_layout
     xh.n_new = n_new;
     xh.tok_per_block = 128 / a.g;
     xh.row_blocks = (n_new + xh.tok_per_block - 1) / xh.tok_per_block;
+    xh.hist_tok_per_block = 256 / a.g;
+    xh.hist_row_blocks = (n_new + xh.hist_tok_per_block - 1) / xh.hist_tok_per_block;
     xh.hist_items = plan.extra_item - 2;
     xh.sink_store = pool->sink;
     xh.recent_store = pool->recent;

@@ -3,8 +3,8 @@
 //
 // The decode kernel's history path is shaped for one query row per KV head
 // and reads every history tile once per row; a prefill chunk has thousands of
-// rows over the same prefix.  Here one workgroup takes 128 query rows of one
-// KV head (128 / g new tokens x g heads) and one history work item, and for
+// rows over the same prefix.  Here one workgroup takes 256 query rows of one
+// KV head (256 / g new tokens x g heads) and one history work item, and for
 // every 32-token tile of the item:
 //   1. the tile's 96-byte head records (K, V codes and (s, z)) are staged in
 //      LDS; records of the next tile are in flight meanwhile;
@@ -33,7 +33,8 @@ namespace oscar {
 namespace {
 
 constexpr int kTile = 32;                    // history tokens per tile
-constexpr int kThreads = 512;                // 8 waves x 16 query rows per workgroup
+constexpr int kThreads = 512;                // 8 waves x 16 query rows per workgroup (BF16 items)
+constexpr int kHistThreads = 1024;           // 16 waves x 16 query rows per workgroup (history items)
 constexpr int kKdStride = kHeadDim + 8;      // halves per K row (272 bytes: conflict-free 16-byte reads)
 constexpr int kVtStride = kTile + 4;         // halves per V^T row (72 bytes: conflict-free 8-byte reads)
 constexpr float kDqScale = 0.125f;           // dequantised values are stored times 1/8
@@ -66,12 +67,13 @@ struct Rows {
     bool row_ok;
 };
 
-__device__ __forceinline__ void load_rows(const ExtendHistArgs &a, int rb, int hk, int w, int col, int kq, Rows &r) {
+__device__ __forceinline__ void load_rows(const ExtendHistArgs &a, int tpb, int rb, int hk, int w, int col, int kq,
+                                          Rows &r) {
     const int rho = 16 * w + col;
     const int tl = rho / a.g;
     const int head = rho - tl * a.g;
-    r.tok = rb * a.tok_per_block + tl;
-    r.row_ok = tl < a.tok_per_block && r.tok < a.n_new;
+    r.tok = rb * tpb + tl;
+    r.row_ok = tl < tpb && r.tok < a.n_new;
     const size_t qrow = size_t(r.row_ok ? r.tok : 0) * a.hq + size_t(hk) * a.g + head;
     float qscale = 0.0f;
     r.unscale = 1.0f;                                       // rows past the block: q = 0, S = 0
@@ -100,7 +102,7 @@ __device__ __forceinline__ void load_rows(const ExtendHistArgs &a, int rb, int h
 // Partials of work item j: (m, l) of row 16 w + col from the lanes of kq 0;
 // o rows 16 w + 4 kq + i, channels 16 n + col (stored times 8, undoing the
 // 1/8 of the V tile).
-__device__ __forceinline__ void store_partials(const ExtendHistArgs &a, int rb, int hk, int j, int w, int col, int kq,
+__device__ __forceinline__ void store_partials(const ExtendHistArgs &a, int tpb, int rb, int hk, int j, int w, int col, int kq,
                                                const Rows &r, float m_run, float l_run, const f32x4 *o) {
     if (kq == 0 && r.row_ok) {
         const int rho = 16 * w + col;
@@ -114,8 +116,8 @@ __device__ __forceinline__ void store_partials(const ExtendHistArgs &a, int rb, 
         const int rr = 16 * w + 4 * kq + i;
         const int tli = rr / a.g;
         const int hi = rr - tli * a.g;
-        const int toki = rb * a.tok_per_block + tli;
-        if (tli < a.tok_per_block && toki < a.n_new) {
+        const int toki = rb * tpb + tli;
+        if (tli < tpb && toki < a.n_new) {
             float *dst = a.part_o + ((size_t(toki) * a.items + j) * a.hq + size_t(hk) * a.g + hi) * kHeadDim;
 #pragma unroll
             for (int n = 0; n < 8; ++n) dst[16 * n + col] = o[n][i] * (1.0f / kDqScale);
@@ -209,13 +211,14 @@ __device__ __forceinline__ void flash_step(const _Float16 (*kd)[kTile][kKdStride
     }
 }
 
-// At most 128 VGPRs (launch bound of 4 waves per SIMD): two workgroups per
-// compute unit overlap one another's dequantisation, barriers and MFMA work.
+// At most 128 VGPRs (launch bound of 4 waves per SIMD): one workgroup of 16
+// waves per compute unit, so that each tile's dequantisation (K by waves
+// 0-7, V by waves 8-15) serves 256 query rows.
 // NG = groups per head vector (4, 2, 1 for G = 32, 64, 128), SZB = bytes of
 // one group's (s, z) (4: fp16, 2: E4M3 codes): head records of 96, 80 or 72
 // bytes, staged in 16-byte units (8-byte units for 72).
 template <int NG, int SZB>
-__global__ __launch_bounds__(kThreads, 4) void extend_hist_kernel(ExtendHistArgs a) {
+__global__ __launch_bounds__(kHistThreads, 4) void extend_hist_kernel(ExtendHistArgs a) {
     constexpr int kRec = 2 * kCodeBytes + 2 * NG * SZB;
     // (s, z) stored at p, times 1/8 (exact); group g of tensor t (0 = K, 1 = V)
     // sits at byte 64 + (t NG + g) SZB of a head record
@@ -239,8 +242,8 @@ __global__ __launch_bounds__(kThreads, 4) void extend_hist_kernel(ExtendHistArgs
     __shared__ __attribute__((aligned(16))) _Float16 vt_all[2][1][kHeadDim][kVtStride];
 
     const int id = blockIdx.x;
-    const int rb = id % a.row_blocks;
-    const int rest = id / a.row_blocks;
+    const int rb = id % a.hist_row_blocks;
+    const int rest = id / a.hist_row_blocks;
     const int hk = rest % a.hkv;
     const int jj = rest / a.hkv;
     const int j = 2 + jj;                                   // work item index in the decode layout
@@ -256,7 +259,7 @@ __global__ __launch_bounds__(kThreads, 4) void extend_hist_kernel(ExtendHistArgs
     const int kq = lane >> 4;
 
     Rows r;
-    load_rows(a, rb, hk, w, col, kq, r);
+    load_rows(a, a.hist_tok_per_block, rb, hk, w, col, kq, r);
     float m_run = -INFINITY, l_run = 0.0f;
     f32x4 o[8];
 #pragma unroll
@@ -297,10 +300,11 @@ __global__ __launch_bounds__(kThreads, 4) void extend_hist_kernel(ExtendHistArgs
         const uint8_t *raw = raw_all[b];
         _Float16(*kd)[kTile][kKdStride] = kd_all[b];
         _Float16(*vt)[kHeadDim][kVtStride] = vt_all[b];
-        // ---- 2. dequantise.  K rows (token t, channels 8 part .. +7): the
-        // group's four levels (s c + z) / 8, c = 0..3, as fp16 hi and lo pairs,
-        // then one byte-select (v_perm) per two channels picks their levels
-        {
+        // ---- 2. dequantise.  K rows (token t, channels 8 part .. +7), by
+        // threads 0..511: the group's four levels (s c + z) / 8, c = 0..3, as
+        // fp16 hi and lo pairs, then one byte-select (v_perm) per two channels
+        // picks their levels
+        if (tid < 512) {
             const int t = tid >> 4, part = tid & 15;
             const uint32_t cw = *reinterpret_cast<const uint16_t *>(raw + t * kRec + 2 * part);
             const float2 sz = load_sz(raw + t * kRec + 2 * kCodeBytes + SZB * (part * NG / 16));
@@ -322,10 +326,11 @@ __global__ __launch_bounds__(kThreads, 4) void extend_hist_kernel(ExtendHistArgs
             *reinterpret_cast<u32x4 *>(&kd[0][t][8 * part]) = u32x4{hi[0], hi[1], hi[2], hi[3]};
             *reinterpret_cast<u32x4 *>(&kd[1][t][8 * part]) = u32x4{lo[0], lo[1], lo[2], lo[3]};
         }
-        // V^T rows (channels 2 cp, 2 cp + 1; tokens 4 tq .. 4 tq + 3), one fp16 per
-        // value; 8-byte row writes (at most 2 lanes of 16 per bank)
-        {
-            const int cp = tid & 63, tq = tid >> 6;
+        // V^T rows (channels 2 cp, 2 cp + 1; tokens 4 tq .. 4 tq + 3), by threads
+        // 512..1023, one fp16 per value; 8-byte row writes (at most 2 lanes of
+        // 16 per bank)
+        else {
+            const int cp = (tid - 512) & 63, tq = (tid - 512) >> 6;
             const int byte = 32 + (cp >> 1), sh = 4 * (cp & 1);
             const int sz_off = 2 * kCodeBytes + SZB * NG + SZB * (cp * NG / 64);
             float x0[4], x1[4];
@@ -373,7 +378,7 @@ __global__ __launch_bounds__(kThreads, 4) void extend_hist_kernel(ExtendHistArgs
         if (cb + kTile < p1) tile(std::integral_constant<int, 1>{}, cb + kTile);
     }
 
-    store_partials(a, rb, hk, j, w, col, kq, r, m_run, l_run, o);
+    store_partials(a, a.hist_tok_per_block, rb, hk, j, w, col, kq, r, m_run, l_run, o);
 }
 
 // BF16 items: kind 0 = sink window [0, min(S, P)), kind 1 = recent window
@@ -413,7 +418,7 @@ __global__ __launch_bounds__(kThreads, 4) void extend_bf16_kernel(ExtendHistArgs
     const int col = lane & 15;
     const int kq = lane >> 4;
     Rows r;
-    load_rows(a, rb, hk, w, col, kq, r);
+    load_rows(a, a.tok_per_block, rb, hk, w, col, kq, r);
     float m_run = -INFINITY, l_run = 0.0f;
     f32x4 o[8];
 #pragma unroll
@@ -477,7 +482,7 @@ __global__ __launch_bounds__(kThreads, 4) void extend_bf16_kernel(ExtendHistArgs
             }
         flash_step<false>(kd, vt, r.bq_hi, r.bq_lo, r.unscale, valid, m_run, l_run, o, col, kq);
     }
-    store_partials(a, rb, hk, j, w, col, kq, r, m_run, l_run, o);
+    store_partials(a, a.tok_per_block, rb, hk, j, w, col, kq, r, m_run, l_run, o);
 }
 
 // Merge of the work items and un-rotation, o = o' R_V^T, for 8 new tokens
@@ -575,20 +580,20 @@ hipError_t launch_extend_bf16(const ExtendHistArgs &a, hipStream_t stream) {
 }
 
 int64_t extend_history_blocks(const ExtendHistArgs &a) {
-    return int64_t(a.row_blocks) * a.hist_items * a.hkv;
+    return int64_t(a.hist_row_blocks) * a.hist_items * a.hkv;
 }
 
 hipError_t launch_extend_history(const ExtendHistArgs &a, hipStream_t stream) {
     const int64_t blocks = extend_history_blocks(a);
     if (blocks <= 0) return hipSuccess;
     if (a.scale_bits == 8) {
-        hipLaunchKernelGGL((extend_hist_kernel<2, 2>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((extend_hist_kernel<2, 2>), dim3(unsigned(blocks)), dim3(kHistThreads), 0, stream, a);
         return hipGetLastError();
     }
     switch (a.group_size) {
-        case 64: hipLaunchKernelGGL((extend_hist_kernel<2, 4>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a); break;
-        case 128: hipLaunchKernelGGL((extend_hist_kernel<1, 4>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a); break;
-        default: hipLaunchKernelGGL((extend_hist_kernel<4, 4>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a); break;
+        case 64: hipLaunchKernelGGL((extend_hist_kernel<2, 4>), dim3(unsigned(blocks)), dim3(kHistThreads), 0, stream, a); break;
+        case 128: hipLaunchKernelGGL((extend_hist_kernel<1, 4>), dim3(unsigned(blocks)), dim3(kHistThreads), 0, stream, a); break;
+        default: hipLaunchKernelGGL((extend_hist_kernel<4, 4>), dim3(unsigned(blocks)), dim3(kHistThreads), 0, stream, a); break;
     }
     return hipGetLastError();
 }

@@ -86,8 +86,10 @@ struct ExtendHistArgs {
     int32_t recent;
     int32_t prefix_len;
     int32_t n_new;
-    int32_t tok_per_block;        // new tokens per workgroup: 128 / g
+    int32_t tok_per_block;        // new tokens per workgroup of the BF16 items: 128 / g
     int32_t row_blocks;
+    int32_t hist_tok_per_block;   // new tokens per workgroup of the history items: 256 / g
+    int32_t hist_row_blocks;
     int32_t hist_items;
     // BF16 items (sink window, recent window, the new tokens themselves)
     const uint16_t *sink_store;   // [max_requests][S][Hkv][2][128]
@@ -102,7 +104,7 @@ struct ExtendHistArgs {
     int32_t group_size;
     int32_t scale_bits;           // 16 (fp16 s, z) or 8 (E4M3 s, z)
 };
-// Grid sizes of the two launches (row_blocks x items x hkv).
+// Grid sizes of the two launches (row blocks x items x hkv).
 int64_t extend_history_blocks(const ExtendHistArgs &a);
 int64_t extend_bf16_blocks(const ExtendHistArgs &a);
 hipError_t launch_extend_history(const ExtendHistArgs &a, hipStream_t stream);

@@ -76,12 +76,12 @@ oscar_status make_decode_plan(const oscar_layout &lay, int32_t batch,
         if (chunk < 32 || chunk > 65536 || chunk % 32)
             return fail(OSCAR_ERR_INVALID_ARG, "history_chunk must be a multiple of 32 in [32, 65536]");
     } else if (extend) {
-        // every row reads the same prefix and a workgroup serves 128 / g rows:
-        // about 4096 history workgroups (sixteen per compute unit) in total, so
-        // that few partials go through the merge
+        // every row reads the same prefix and a history workgroup serves
+        // 256 / g new tokens: about 2048 history workgroups (eight rounds of
+        // one per compute unit) in total, so that few partials go through the merge
         const int64_t g = lay.num_q_heads / lay.num_kv_heads;
-        const int64_t row_blocks = (batch + 128 / g - 1) / (128 / g);
-        const int64_t want = std::max<int64_t>(1, (4096 + row_blocks * lay.num_kv_heads - 1) /
+        const int64_t row_blocks = (batch + 256 / g - 1) / (256 / g);
+        const int64_t want = std::max<int64_t>(1, (2048 + row_blocks * lay.num_kv_heads - 1) /
                                                       (row_blocks * lay.num_kv_heads));
         chunk = (max_hist + want - 1) / want;
         chunk = std::max<int64_t>(256, (chunk + 31) / 32 * 32);

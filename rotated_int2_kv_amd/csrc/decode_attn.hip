@@ -297,9 +297,11 @@ __device__ __forceinline__ float row16_sum(float v) {
 // plane c is channel 64 c + 4 n + j, byte n % 4 of a V-code dword picked by
 // one v_perm_b32 per token pair.  The hi and lo rows of a column's group are
 // summed once, when the partial is written.  K-slot 8 kb + i of the PV
-// products is token 2 (i % 2) + 8 (i / 2) + (kb % 2) + 4 (kb / 2): the four
-// lane groups read V codes of tokens t, t + 1, t + 4, t + 5 at once, which the
-// token swizzle puts in disjoint LDS banks.  Weight rows hold 4 units of 16
+// products is token 16 (i % 2) + 2 ((i / 2) % 2) + 8 (i / 4) + (kb % 2) +
+// 4 (kb / 2): a lane's two tokens n and 16 + n take adjacent K-slots, so that
+// one 32-bit write stores both weights of a row, and the four lane groups read
+// V codes of tokens t, t + 1, t + 4, t + 5 at once, which the token swizzle
+// puts in disjoint LDS banks.  Weight rows hold 4 units of 16
 // bytes (8 K-slots each), the physical unit of logical unit v in row 4 q + h
 // being v ^ q.  The rows live in the stage itself: once a wave has read its K
 // codes and both (s, z) of the tile into registers, those 128 units of its
@@ -337,21 +339,13 @@ __host__ __device__ constexpr int int2_lds_bytes_lowmeta() { return int2_lds_byt
 __host__ __device__ constexpr int tok_swizzle(int t) {
     return (((t & 1) << 1) | ((t >> 1) & 1) | (t & 4)) ^ (2 * ((t >> 3) & 1));
 }
-// Bit 0 of the swizzle is bit 1 of the token: it orders the two units of an
-// even/odd pair (K codes 0, 1 and V codes 2, 3 of a head record) in the line.
-constexpr bool swizzle_bit0_is_token_bit1() {
-    for (int t = 0; t < 32; ++t)
-        if ((tok_swizzle(t) & 1) != ((t >> 1) & 1)) return false;
+// Tokens t and t + 16 share the swizzle (the PV reads take both in one instruction).
+constexpr bool swizzle_period_16() {
+    for (int t = 0; t < 16; ++t)
+        if (tok_swizzle(t + 16) != tok_swizzle(t)) return false;
     return true;
 }
-static_assert(swizzle_bit0_is_token_bit1(), "unit pair order");
-// Tokens t and t + 2 with bit 1 of t clear differ in bit 0 of the swizzle only.
-constexpr bool swizzle_of_t_plus_2() {
-    for (int t = 0; t < 32; ++t)
-        if ((t & 2) == 0 && tok_swizzle(t + 2) != (tok_swizzle(t) ^ 1)) return false;
-    return true;
-}
-static_assert(swizzle_of_t_plus_2(), "V-code unit pairs of tokens t, t + 2");
+static_assert(swizzle_period_16(), "V-code units of tokens t, t + 16");
 
 // byte offset of 16-byte unit q (0..23) of token t inside a stage
 __device__ __forceinline__ int unit_addr(int t, int q) {
@@ -600,18 +594,16 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
     uint32_t qk_at[2], szk_at, szv_at, a_at;
     // second plane of the PV weights (channels 64..127)
     constexpr uint32_t wpl_off = NG == 4 ? kHalfTok : kWeightPlane;
-    // V codes of the token of K-slot 8 kb + i: byte n (channels 4 n .. 4 n + 3)
-    // is byte n % 4 of the dword at pv_at[i] + pv_off(0, i), byte 16 + n that of
-    // the dword at pv_at[i] + pv_off(1, i).  With G = 32, the tokens of K-slots
-    // 2 pp and 2 pp + 1 are t and t + 2, 768 bytes apart, and the swizzle puts
-    // each V unit of token t + 2 at the line position of the other V unit of
-    // token t: pv_at[2 pp] (+ 768) reads V-code unit 2 of t and unit 3 of t + 2,
-    // pv_at[2 pp + 1] (+ 768) unit 3 of t and unit 2 of t + 2, each pair in one
-    // ds_read2st64_b32 whose offsets also take the stage.
-    uint32_t pv_at[8];
+    // V codes of the tokens t and t + 16 of K-slots 8 kb + 2 pp and 8 kb + 2 pp + 1
+    // (t = 8 (pp / 2) + 2 (pp % 2) + kb_tok): byte n (channels 4 n .. 4 n + 3) of
+    // plane c is byte n % 4 of the dword at pv_at[pp][c], token 16 + n 16 token
+    // strides further.  With G = 32 that stride is 6144 bytes and token t + 16
+    // has the swizzle of t, so each pair is one ds_read2st64_b32 whose offsets
+    // also take the stage.
+    uint32_t pv_at[4][2];
     // v_perm_b32 selector: bytes (n % 4 of the first token, 0, n % 4 of the second, 0)
     const uint32_t pv_sel = lds_pin(0x0c040c00u | uint32_t(n & 3) * 0x00010001u);
-    // PV weight of token t in row 4 q + kb (q = 0 .. NQ - 1); token 16 + t 8 bytes further
+    // PV weights of tokens n and 16 + n (one dword) in row 4 q + kb (q = 0 .. NQ - 1)
     constexpr int NQ = NG == 4 ? 4 : 2;
     uint32_t w_at[NQ];
     const int w_unit = (n & 1) + 2 * ((n >> 2) & 1);            // K-slot / 8 of token n
@@ -621,17 +613,15 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
         for (int P = 0; P < 2; ++P) qk_at[P] = lds_pin(st0 + unit_addr(n, 6 * w + P) + 4 * kb);
         szk_at = lds_pin(st0 + unit_addr(n, 6 * w + 4));
         szv_at = lds_pin(st0 + unit_addr(n, 6 * w + 5));
-        // V-code units 2 and 3 of the head record sit side by side, in the
-        // order given by bit 0 of the token's swizzle (bit 1 of the token): for
-        // token t = 8 pp + kb_tok (bit 1 clear) unit 2 is the lower one
+        // V-code units 2 and 3 of the head record (channels 0..63, 64..127)
 #pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
-            pv_at[2 * pp] = lds_pin(st0 + unit_addr(8 * pp + kb_tok, 6 * w + 2) + (n & ~3));
-            pv_at[2 * pp + 1] = lds_pin(st0 + unit_addr(8 * pp + kb_tok, 6 * w + 3) + (n & ~3));
-        }
-        // K-slot 8 unit + i of the row, unit XOR-permuted by q
+        for (int pp = 0; pp < 4; ++pp)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) w_at[q] = lds_pin(st0 + wunit_addr(w, 4 * q + kb, w_unit ^ q) + 2 * w_i);
+            for (int c = 0; c < 2; ++c)
+                pv_at[pp][c] = lds_pin(st0 + unit_addr(8 * (pp >> 1) + 2 * (pp & 1) + kb_tok, 6 * w + 2 + c) + (n & ~3));
+        // K-slots 8 unit + 2 w_i, + 1 of the row (tokens n, 16 + n), unit XOR-permuted by q
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w_at[q] = lds_pin(st0 + wunit_addr(w, 4 * q + kb, w_unit ^ q) + 4 * w_i);
         // A-operand read of row n, K-slots 8 kb .. 8 kb + 7
         a_at = lds_pin(st0 + wunit_addr(w, n, kb ^ (n >> 2)));
     } else {
@@ -640,14 +630,17 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
         szk_at = lds_pin(rec_at(n, 2 * kCodeBytes));
         szv_at = lds_pin(rec_at(n, 2 * kCodeBytes + SZB * NG));
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pv_at[i] = lds_pin(rec_at(2 * (i & 1) + 8 * (i >> 1) + kb_tok, kCodeBytes + (n & ~3)));
+        for (int pp = 0; pp < 4; ++pp)
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+                pv_at[pp][c] = lds_pin(rec_at(8 * (pp >> 1) + 2 * (pp & 1) + kb_tok, kCodeBytes + 16 * c + (n & ~3)));
         const uint32_t wb = st0 + int2_lds_bytes() + w * kWeightWave;   // after the stages and the ring
 #pragma unroll
-        for (int q = 0; q < 2; ++q) w_at[q] = lds_pin(wb + (4 * q + kb) * 64 + 16 * w_unit + 2 * w_i);
+        for (int q = 0; q < 2; ++q) w_at[q] = lds_pin(wb + (4 * q + kb) * 64 + 16 * w_unit + 4 * w_i);
         a_at = lds_pin(wb + (n & 7) * 64 + 16 * kb);
     }
-    // byte offset of V-code byte 16 c + n from pv_at[i] (80- and 72-byte layouts)
-    auto pv_off = [](int c) -> uint32_t { return 16u * uint32_t(c); };
+    // token 16 + t of a stage: 16 token strides after token t
+    constexpr uint32_t kHalfTokOff = 16 * kTokB;
     // the weight area of the 80-byte layout does not move with the stage
     constexpr bool kWeightsInStage = NG == 4;
 
@@ -659,30 +652,18 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
         // rows 4 q + h, q = (pair-local group, part): the hi and lo fp16 parts
         // of the weights p s_g of the half's groups for K-slots 8 kb .. 8 kb + 7,
         // so that one product carries both parts.  B of plane c, pair j = the V
-        // codes of channel 64 c + 4 n + j for the same tokens, two tokens per
-        // 32-bit word.
+        // codes of channel 64 c + 4 n + j for the same tokens, two tokens (t in
+        // the low half, t + 16 in the high half) per 32-bit word.
         uint32_t xw[2][4];
 #pragma unroll
         for (int pp = 0; pp < 4; ++pp) {
-            uint32_t lo[2], hi[2];   // plane c dword of the first and the second token
-            if constexpr (NG == 4) {
-                lo[0] = lds_ld<uint32_t>(pv_at[2 * pp] + so);
-                hi[1] = lds_ld<uint32_t>(pv_at[2 * pp] + so + 2 * kTokBytes);
-                lo[1] = lds_ld<uint32_t>(pv_at[2 * pp + 1] + so);
-                hi[0] = lds_ld<uint32_t>(pv_at[2 * pp + 1] + so + 2 * kTokBytes);
-            } else {
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    lo[c] = lds_ld<uint32_t>(pv_at[2 * pp] + pv_off(c) + so);
-                    hi[c] = lds_ld<uint32_t>(pv_at[2 * pp + 1] + pv_off(c) + so);
-                }
-            }
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
-                const uint32_t pr = __builtin_amdgcn_perm(hi[c], lo[c], pv_sel);
-                // tokens 16..31 (pp = 2, 3) as 3 - c: every 2-bit code inverted
-                // (the bits above the codes are never read)
-                xw[c][pp] = pp >= 2 ? ~pr : pr;
+                const uint32_t lo = lds_ld<uint32_t>(pv_at[pp][c] + so);
+                const uint32_t hi = lds_ld<uint32_t>(pv_at[pp][c] + so + kHalfTokOff);
+                // token t + 16 as 3 - c: its 2-bit codes inverted (the bits
+                // above the codes are never read)
+                xw[c][pp] = __builtin_amdgcn_perm(hi, lo, pv_sel) ^ 0xffff0000u;
             }
         }
         // ---- QK: logit of (token 16 hf + n, head 4 hs + kb)
@@ -802,34 +783,24 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
         for (int hs = 0; hs < HS; ++hs) {
             // w_g = p s_g as hi + lo fp16 parts, both rounded to nearest; lo = w_g - hi.
             // They overwrite this head's K codes and (s, z) of the stage, read above.
+            // Sign balance: the matrix core sums its 32 products after aligning
+            // them to the largest and truncating the low bits toward zero, so
+            // products of one sign (p s c >= 0) would lose a little in the same
+            // direction on every tile.  Tokens 16..31 enter as (-p s)(3 - c) =
+            // p s c - 3 p s, the -3 p s is returned through the zero-point sum,
+            // and the truncation errors cancel; the running sums also stay near
+            // the output instead of growing to ~1.5 s l.
+            const float p0 = pw[hs][0], p1 = -pw[hs][1];
+            constexpr uint32_t wso = kWeightsInStage ? so : 0u;
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                // sign balance: the matrix core sums its 32 products after
-                // aligning them to the largest and truncating the low bits toward
-                // zero, so products of one sign (p s c >= 0) would lose a little
-                // in the same direction on every tile.  Tokens 16..31 enter as
-                // (-p s)(3 - c) = p s c - 3 p s, the -3 p s is returned through
-                // the zero-point sum, and the truncation errors cancel; the running
-                // sums also stay near the output instead of growing to ~1.5 s l.
-                const float p = hf ? -pw[hs][hf] : pw[hs][hf];
-                constexpr uint32_t wso = kWeightsInStage ? so : 0u;
-                constexpr int kPairs = (NG + 1) / 2;
-                HiLo2 hl[kPairs];
-#pragma unroll
-                for (int q2 = 0; q2 < kPairs; ++q2) {
-                    const float s0 = half_lo(szv[hf][2 * q2]);
-                    const float s1 = NG > 1 ? half_lo(szv[hf][(2 * q2 + 1) % NG]) : 0.0f;
-                    hl[q2].hi = pk_rn(fmaf(p, s0, 0.0f), fmaf(p, s1, 0.0f));
-                    hl[q2].lo = pk_rn(fmaf(p, s0, -half_lo(hl[q2].hi)), fmaf(p, s1, -half_hi(hl[q2].hi)));
-                }
-#pragma unroll
-                for (int g = 0; g < NG; ++g) {
-                    const int sh = 16 * (g & 1);
-                    const int gl = NG == 4 ? (g & 1) : 0;
-                    const uint32_t pl = NG == 4 ? uint32_t(g >> 1) * wpl_off : NG == 2 ? uint32_t(g) * wpl_off : 0u;
-                    lds_st<uint16_t>(w_at[2 * gl] + pl + wso + 8 * hf, uint16_t(hl[g >> 1].hi >> sh));
-                    lds_st<uint16_t>(w_at[2 * gl + 1] + pl + wso + 8 * hf, uint16_t(hl[g >> 1].lo >> sh));
-                }
+            for (int g = 0; g < NG; ++g) {
+                const float s0 = half_lo(szv[0][g]), s1 = half_lo(szv[1][g]);
+                const uint32_t whi = pk_rn(p0 * s0, p1 * s1);   // tokens n, 16 + n
+                const uint32_t wlo = pk_rn(fmaf(p0, s0, -half_lo(whi)), fmaf(p1, s1, -half_hi(whi)));
+                const int gl = NG == 4 ? (g & 1) : 0;
+                const uint32_t pl = NG == 4 ? uint32_t(g >> 1) * wpl_off : NG == 2 ? uint32_t(g) * wpl_off : 0u;
+                lds_st<uint32_t>(w_at[2 * gl] + pl + wso, whi);
+                lds_st<uint32_t>(w_at[2 * gl + 1] + pl + wso, wlo);
             }
             lds_order();
             // rescale the output rows of heads whose running max grew; PV output

@@ -73,6 +73,44 @@ __device__ __forceinline__ float round_up_f32(double t) {
     return double(f) < t ? __int_as_float(__float_as_int(f) + (f >= 0.0f ? 1 : -1)) : f;
 }
 
+// Four 2-bit codes into a word, the code of x3 first: with thresholds
+// u0 <= u1 <= u2 the code (number of thresholds at or below x) has high bit
+// x >= u1 and low bit x >= u2 if that holds, else x >= u0.  Each code enters
+// as two doublings of the word with the bit as carry-in (v_addc_co_u32 takes
+// it straight from the compare's lane mask): 5 instructions per code.  Every
+// lane mask is read three or more instructions after the compare that writes
+// it, past the wait a VALU-written mask needs before a VALU reads it.
+__device__ __forceinline__ uint32_t codes4_into(uint32_t p, float x3, float x2, float x1, float x0, float u0,
+                                                float u1, float u2) {
+    uint64_t m3, m2, m1, m0, n3, n2, n1, n0, co;
+    float s3, s2, s1, s0;
+    asm("v_cmp_ge_f32_e64 %[m3], %[x3], %[u1]\n\t"
+        "v_cmp_ge_f32_e64 %[m2], %[x2], %[u1]\n\t"
+        "v_cmp_ge_f32_e64 %[m1], %[x1], %[u1]\n\t"
+        "v_cmp_ge_f32_e64 %[m0], %[x0], %[u1]\n\t"
+        "v_cndmask_b32_e64 %[s3], %[u0], %[u2], %[m3]\n\t"
+        "v_cndmask_b32_e64 %[s2], %[u0], %[u2], %[m2]\n\t"
+        "v_cndmask_b32_e64 %[s1], %[u0], %[u2], %[m1]\n\t"
+        "v_cndmask_b32_e64 %[s0], %[u0], %[u2], %[m0]\n\t"
+        "v_cmp_ge_f32_e64 %[n3], %[x3], %[s3]\n\t"
+        "v_cmp_ge_f32_e64 %[n2], %[x2], %[s2]\n\t"
+        "v_cmp_ge_f32_e64 %[n1], %[x1], %[s1]\n\t"
+        "v_cmp_ge_f32_e64 %[n0], %[x0], %[s0]\n\t"
+        "v_addc_co_u32_e64 %[p], %[co], %[p], %[p], %[m3]\n\t"
+        "v_addc_co_u32_e64 %[p], %[co], %[p], %[p], %[n3]\n\t"
+        "v_addc_co_u32_e64 %[p], %[co], %[p], %[p], %[m2]\n\t"
+        "v_addc_co_u32_e64 %[p], %[co], %[p], %[p], %[n2]\n\t"
+        "v_addc_co_u32_e64 %[p], %[co], %[p], %[p], %[m1]\n\t"
+        "v_addc_co_u32_e64 %[p], %[co], %[p], %[p], %[n1]\n\t"
+        "v_addc_co_u32_e64 %[p], %[co], %[p], %[p], %[m0]\n\t"
+        "v_addc_co_u32_e64 %[p], %[co], %[p], %[p], %[n0]"
+        : [p] "+v"(p), [m3] "=&s"(m3), [m2] "=&s"(m2), [m1] "=&s"(m1), [m0] "=&s"(m0), [n3] "=&s"(n3),
+          [n2] "=&s"(n2), [n1] "=&s"(n1), [n0] "=&s"(n0), [co] "=&s"(co), [s3] "=&v"(s3), [s2] "=&v"(s2),
+          [s1] "=&v"(s1), [s0] "=&v"(s0)
+        : [x3] "v"(x3), [x2] "v"(x2), [x1] "v"(x1), [x0] "v"(x0), [u0] "v"(u0), [u1] "v"(u1), [u2] "v"(u2));
+    return p;
+}
+
 // Split an fp32 value into three bf16 terms whose sum is the value.
 __device__ __forceinline__ void split3(float x, uint16_t &a, uint16_t &b, uint16_t &c) {
     a = bf16_bits_rn(x);
@@ -132,25 +170,24 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(AppendArgs a) {
     }
 
     // staging: a tile is 32 token rows x 16 units of 8 channels; thread tid
-    // stages units tid and tid + 256 (row u / 16, channels 8 (u % 16) ..)
-    const void *X = (t == 0 ? a.k : a.v);
+    // stages units tid and tid + 256 (row u / 16, channels 8 (u % 16) ..).
+    // Addresses: a per-thread base (head h, channels 8 (tid % 16) ..) plus
+    // token x the bytes of one token's heads (one 32 x 32 -> 64-bit multiply-add).
+    const bool f32_in = a.in_dtype == OSCAR_F32;
+    const uint32_t esz = f32_in ? 4u : 2u;
+    const uint32_t x_tok_bytes = uint32_t(a.hkv) * kHeadDim * esz;
+    const uint8_t *const x_base = static_cast<const uint8_t *>(t == 0 ? a.k : a.v) +
+                                  (uint32_t(h) * kHeadDim + 8u * uint32_t(tid & 15)) * esz;
     auto load_tile = [&](int tb, u32x4 (&r)[2][2]) {
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-            const int u = tid + 256 * q;
-            const int tok = tb + (u >> 4);
+            const int tok = tb + (tid >> 4) + 16 * q;
             r[q][0] = u32x4{0, 0, 0, 0};
             r[q][1] = u32x4{0, 0, 0, 0};
             if (tok < tok_end) {
-                const size_t elem = (size_t(tok) * a.hkv + h) * kHeadDim + 8 * (u & 15);
-                if (a.in_dtype == OSCAR_F32) {
-                    const u32x4 *p = reinterpret_cast<const u32x4 *>(static_cast<const float *>(X) + elem);
-                    r[q][0] = __builtin_nontemporal_load(p);        // input read once
-                    r[q][1] = __builtin_nontemporal_load(p + 1);
-                } else {
-                    r[q][0] = __builtin_nontemporal_load(
-                        reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(X) + elem));
-                }
+                const u32x4 *p = reinterpret_cast<const u32x4 *>(x_base + uint64_t(uint32_t(tok)) * x_tok_bytes);
+                r[q][0] = __builtin_nontemporal_load(p);            // input read once
+                if (f32_in) r[q][1] = __builtin_nontemporal_load(p + 1);
             }
         }
     };
@@ -195,7 +232,10 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(AppendArgs a) {
 
     constexpr int kHeadRec = 2 * kCodeBytes + 2 * SZB * (kWaves / NGW);   // head record of this layout
     constexpr int kSzTensor = SZB * (kWaves / NGW);                        // (s, z) bytes per tensor
-    const int64_t rec_bytes = int64_t(a.hkv) * kHeadRec;
+    const uint32_t rec_bytes = uint32_t(a.hkv) * kHeadRec;
+    // this lane's code word and its group's (s, z) in the record of slot 0
+    uint8_t *const code_base = a.records + (h * kHeadRec + t * kCodeBytes + 8 * w + 4 * hh);
+    uint8_t *const sz_base = a.records + (h * kHeadRec + 2 * kCodeBytes + t * kSzTensor + SZB * (w / NGW));
     // the next tile of input in flight in registers (the waits are the
     // compiler's; a second tile would take the registers of a third wave per
     // SIMD); the LDS tile is double-buffered, so one barrier per tile both
@@ -208,16 +248,18 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(AppendArgs a) {
     // per-token routing data of this lane's token (tb + tt), fetched ahead:
     // request, position and slot two tiles early, the request's length one
     // tile early, so that no tile waits on a dependent global load
+    // (32-bit byte offsets from the arrays' bases)
+    auto at = [](const int32_t *base, int i) {
+        return *reinterpret_cast<const int32_t *>(reinterpret_cast<const uint8_t *>(base) + 4u * uint32_t(i));
+    };
     auto load_meta = [&](int tb, int &req, int &pos, int &slot) {
         const int tok = tb + tt;
         const int tc = tok < tok_end ? tok : tok_begin;
-        req = a.req_ids[tc];
-        pos = a.positions[tc];
-        slot = a.slots[tc];
+        req = at(a.req_ids, tc);
+        pos = at(a.positions, tc);
+        slot = at(a.slots, tc);
     };
-    auto load_len = [&](int req) {
-        return a.seq_len_after[(req >= 0 && req < a.max_requests) ? req : 0];
-    };
+    auto load_len = [&](int req) { return at(a.seq_len_after, (req >= 0 && req < a.max_requests) ? req : 0); };
     int req0, pos0, slot0, req1, pos1, slot1;
     load_meta(tok_begin, req0, pos0, slot0);
     load_meta(tok_begin + kTile, req1, pos1, slot1);
@@ -333,32 +375,30 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(AppendArgs a) {
         // a token are active or inactive together: they share the routing data
         // above, so the swap reads an active lane)
         const bool zero_scale = sd == 0.0;
-        const float ua = zero_scale ? INFINITY : round_up_f32(zd + (hh ? 2.5 : 0.5) * sd);
-        const float u1 = zero_scale ? INFINITY : round_up_f32(zd + 1.5 * sd);
+        const float ua = zero_scale ? INFINITY : round_up_f32(fma(hh ? 2.5 : 0.5, sd, zd));
+        const float u1 = zero_scale ? INFINITY : round_up_f32(fma(1.5, sd, zd));
         const float pa = __shfl_xor(ua, 32);
         const float u0 = hh ? pa : ua;
         const float u2 = hh ? ua : pa;
-        // code = number of thresholds at or below the clipped value.  With
-        // alpha = 1 the clip bounds are the group's own min and max, so every
-        // value is inside them and the clip is skipped (uniform branch).
+        // code = number of thresholds at or below the clipped value, code j
+        // at bits 2 j, 2 j + 1.  With alpha = 1 the clip bounds are the group's
+        // own min and max, so every value is inside them and the clip is
+        // skipped (uniform branch).
         uint32_t packed = 0;
         if (a.alpha == 1.0f) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const float x = acc[j];
-                packed |= (uint32_t(x >= u0) + uint32_t(x >= u1) + uint32_t(x >= u2)) << (2 * j);
-            }
+            for (int j = 12; j >= 0; j -= 4)
+                packed = codes4_into(packed, acc[j + 3], acc[j + 2], acc[j + 1], acc[j], u0, u1, u2);
         } else {
+            auto clip = [&](float x) { return __builtin_amdgcn_fmed3f(x, lo_c, hi_c); };   // lo_c <= hi_c
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const float x = __builtin_amdgcn_fmed3f(acc[j], lo_c, hi_c);   // lo_c <= hi_c
-                packed |= (uint32_t(x >= u0) + uint32_t(x >= u1) + uint32_t(x >= u2)) << (2 * j);
-            }
+            for (int j = 12; j >= 0; j -= 4)
+                packed = codes4_into(packed, clip(acc[j + 3]), clip(acc[j + 2]), clip(acc[j + 1]), clip(acc[j]), u0, u1, u2);
         }
-        uint8_t *rec = a.records + int64_t(slot) * rec_bytes + h * kHeadRec;
-        *reinterpret_cast<uint32_t *>(rec + t * kCodeBytes + 8 * w + 4 * hh) = packed;
+        const uint64_t rec_off = uint64_t(uint32_t(slot)) * rec_bytes;     // slot >= 0 here
+        *reinterpret_cast<uint32_t *>(code_base + rec_off) = packed;
         if (hh == 0 && (w & (NGW - 1)) == 0) {            // one writer per group
-            uint8_t *dst = rec + 2 * kCodeBytes + t * kSzTensor + SZB * (w / NGW);
+            uint8_t *dst = sz_base + rec_off;
             if constexpr (SZB == 4)
                 *reinterpret_cast<uint32_t *>(dst) = sz_word;
             else

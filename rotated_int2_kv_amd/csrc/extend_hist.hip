@@ -125,6 +125,32 @@ __device__ __forceinline__ void store_partials(const ExtendHistArgs &a, int tpb,
     }
 }
 
+// o *= al (row 4 kq + i by al[i]) for two output blocks, skipped by a scalar
+// branch when `moved` (wave-uniform) is 0: a row's reference moves in few
+// tiles.  The branch sits inside the asm so that the compiler sees straight
+// code (an `if` around the products made it spill the accumulators).
+__device__ __forceinline__ void rescale_if(f32x4 &oa, f32x4 &ob, const float (&al)[4], int moved) {
+    float a0 = oa[0], a1 = oa[1], a2 = oa[2], a3 = oa[3], b0 = ob[0], b1 = ob[1], b2 = ob[2], b3 = ob[3];
+    asm volatile(
+        "s_cmp_eq_u32 %[mv], 0\n\t"
+        "s_cbranch_scc1 .Lrescale_skip_%=\n\t"
+        "v_mul_f32_e32 %[a0], %[a0], %[s0]\n\t"
+        "v_mul_f32_e32 %[a1], %[a1], %[s1]\n\t"
+        "v_mul_f32_e32 %[a2], %[a2], %[s2]\n\t"
+        "v_mul_f32_e32 %[a3], %[a3], %[s3]\n\t"
+        "v_mul_f32_e32 %[b0], %[b0], %[s0]\n\t"
+        "v_mul_f32_e32 %[b1], %[b1], %[s1]\n\t"
+        "v_mul_f32_e32 %[b2], %[b2], %[s2]\n\t"
+        "v_mul_f32_e32 %[b3], %[b3], %[s3]\n\t"
+        ".Lrescale_skip_%=:"
+        : [a0] "+v"(a0), [a1] "+v"(a1), [a2] "+v"(a2), [a3] "+v"(a3), [b0] "+v"(b0), [b1] "+v"(b1),
+          [b2] "+v"(b2), [b3] "+v"(b3)
+        : [s0] "v"(al[0]), [s1] "v"(al[1]), [s2] "v"(al[2]), [s3] "v"(al[3]), [mv] "s"(moved)
+        : "scc");
+    oa = f32x4{a0, a1, a2, a3};
+    ob = f32x4{b0, b1, b2, b3};
+}
+
 // One 32-token tile of flash attention for the wave's 16 query rows.
 // kd: K tile [hi, lo][token][channel]; vt: V tile [hi, lo][channel][token]
 // (fp16, times 1/8).  S^T = K q'^T leaves lane (col, kq) with tokens
@@ -196,10 +222,9 @@ __device__ __forceinline__ void flash_step(const _Float16 (*kd)[kTile][kKdStride
     float al[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * kq + i);        // alpha of output row 4 kq + i
+    const int moved = __builtin_amdgcn_readfirstlane(__any(move) ? 1 : 0);
 #pragma unroll
-    for (int n = 0; n < 8; ++n)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[n][i] *= al[i];
+    for (int n = 0; n < 8; n += 2) rescale_if(o[n], o[n + 1], al, moved);
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
         const int ch = 16 * n + col;

@@ -47,10 +47,16 @@ __device__ __forceinline__ uint32_t pk_f16(float x0, float x1) {
 __device__ __forceinline__ float f16_lo(uint32_t w) { return __half2float(__ushort_as_half(uint16_t(w))); }
 __device__ __forceinline__ float f16_hi(uint32_t w) { return __half2float(__ushort_as_half(uint16_t(w >> 16))); }
 
-// (x0, x1) ~ hi + lo, both fp16 pairs rounded to nearest
+// (x0, x1) ~ hi + lo, both fp16 pairs rounded to nearest.  x - hi is exact
+// in fp32, so one fused x * 1 - hi rounded to fp16 gives the same lo; the 1 is
+// kept opaque so that the compiler emits that (one mixed-precision fma per
+// half, reading hi's fp16 halves in place) instead of folding it to a
+// subtraction with separate conversions.
 __device__ __forceinline__ void split2(float x0, float x1, uint32_t &hi, uint32_t &lo) {
+    float one = 1.0f;
+    asm("" : "+s"(one));
     hi = pk_f16(x0, x1);
-    lo = pk_f16(x0 - f16_lo(hi), x1 - f16_hi(hi));
+    lo = pk_f16(fmaf(x0, one, -f16_lo(hi)), fmaf(x1, one, -f16_hi(hi)));
 }
 
 __device__ __forceinline__ float sz_s(uint32_t w) { return f16_lo(w); }
@@ -154,7 +160,9 @@ __device__ __forceinline__ void rescale_if(f32x4 &oa, f32x4 &ob, const float (&a
 // One 32-token tile of flash attention for the wave's 16 query rows.
 // kd: K tile [hi, lo][token][channel]; vt: V tile [hi, lo][channel][token]
 // (fp16, times 1/8).  S^T = K q'^T leaves lane (col, kq) with tokens
-// 16 u + 4 kq + i of row col; bit 4 u + i of `valid` keeps that token.  With
+// 16 u + 4 kq + i of row col; the products start from bias[u][i], 0 for a
+// usable token and -inf for one that is masked, so a masked logit is -inf
+// and its weight exp2(-inf) = 0 with no select.  With
 // kKLo false the K lo tile is zero (BF16 sources are exact in fp16) and its
 // products are skipped.  V is one fp16 per value: its rounding (relative
 // 2^-12, unbiased) enters the output as a weighted average, so it stays near
@@ -163,12 +171,12 @@ __device__ __forceinline__ void rescale_if(f32x4 &oa, f32x4 &ob, const float (&a
 template <bool kKLo>
 __device__ __forceinline__ void flash_step(const _Float16 (*kd)[kTile][kKdStride],
                                            const _Float16 (*vt)[kHeadDim][kVtStride], const f16x8 *bq_hi,
-                                           const f16x8 *bq_lo, float unscale, uint32_t valid, float &m_run,
+                                           const f16x8 *bq_lo, float unscale, const f32x4 *bias, float &m_run,
                                            float &l_run, f32x4 *o, int col, int kq) {
     f32x4 d[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        f32x4 acc = bias[u];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const f16x8 kh = *reinterpret_cast<const f16x8 *>(&kd[0][16 * u + col][32 * s + 8 * kq]);
@@ -182,11 +190,11 @@ __device__ __forceinline__ void flash_step(const _Float16 (*kd)[kTile][kKdStride
         d[u] = acc;
     }
     // row maximum of the tile in S^T units (unscale > 0 keeps the order)
-    float mt = -INFINITY;
+    float mt = fmaxf(d[0][0], d[0][1]);
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mt = fmaxf(mt, ((valid >> (4 * u + i)) & 1u) ? d[u][i] : -INFINITY);
+        for (int i = 2 * (u == 0); i < 4; ++i) mt = fmaxf(mt, d[u][i]);
     mt = fmaxf(mt, __shfl_xor(mt, 16));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     mt *= unscale;                                          // log2 units
@@ -196,14 +204,16 @@ __device__ __forceinline__ void flash_step(const _Float16 (*kd)[kTile][kKdStride
     const float m_new = move ? mt : m_run;
     const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
     m_run = m_new;
+    // while every token of the row so far is masked, m is -inf: a finite
+    // stand-in keeps exp2(-inf - m) from becoming NaN
+    const float m_ref = m_new == -INFINITY ? 0.0f : m_new;
     float p[2][4];
     float lsum = 0.0f;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float e = __builtin_amdgcn_exp2f(fmaf(d[u][i], unscale, -m_new));
-            p[u][i] = ((valid >> (4 * u + i)) & 1u) ? e : 0.0f;
+            p[u][i] = __builtin_amdgcn_exp2f(fmaf(d[u][i], unscale, -m_ref));
             lsum += p[u][i];
         }
     }
@@ -262,7 +272,7 @@ __global__ __launch_bounds__(kHistThreads, 4) void extend_hist_kernel(ExtendHist
     // two of everything: tile k is computed from one buffer while tile k + 1
     // is dequantised into the other, one workgroup barrier per tile
     __shared__ __attribute__((aligned(16))) uint8_t raw_all[2][kTile * kRec];
-    __shared__ __attribute__((aligned(16))) uint8_t flag_all[2][kTile];
+    __shared__ __attribute__((aligned(16))) float bias_all[2][kTile];
     __shared__ __attribute__((aligned(16))) _Float16 kd_all[2][2][kTile][kKdStride];
     __shared__ __attribute__((aligned(16))) _Float16 vt_all[2][1][kHeadDim][kVtStride];
 
@@ -313,7 +323,7 @@ __global__ __launch_bounds__(kHistThreads, 4) void extend_hist_kernel(ExtendHist
     auto stage = [&](int b, int cb) {
         if (producer) {
             *reinterpret_cast<Unit *>(raw_all[b] + pt * kRec + kUnit * pu) = rec;
-            if (pu == 0) flag_all[b][pt] = ok_cur ? 1 : 0;
+            if (pu == 0) bias_all[b][pt] = ok_cur ? 0.0f : -INFINITY;
         }
         if (cb + kTile < p1) {
             if (producer) rec = load_rec(slot_nxt);
@@ -382,20 +392,13 @@ __global__ __launch_bounds__(kHistThreads, 4) void extend_hist_kernel(ExtendHist
         constexpr int buf = decltype(bufc)::value;
         const bool more = cb + kTile < p1;
         if (more) stage(buf ^ 1, cb + kTile);
-        // usable-token flags of tile cb (read before the barrier: the staging of
-        // tile cb + 2 overwrites them once every wave has passed it)
-        const uint32_t fl0 = *reinterpret_cast<const uint32_t *>(&flag_all[buf][4 * kq]);
-        const uint32_t fl1 = *reinterpret_cast<const uint32_t *>(&flag_all[buf][16 + 4 * kq]);
+        // logit biases of tile cb, 0 or -inf for tokens that are not usable
+        // (past the item included); read before the barrier: the staging of
+        // tile cb + 2 overwrites them once every wave has passed it
+        const f32x4 bias[2] = {*reinterpret_cast<const f32x4 *>(&bias_all[buf][4 * kq]),
+                               *reinterpret_cast<const f32x4 *>(&bias_all[buf][16 + 4 * kq])};
         __syncthreads();
-        uint32_t valid = 0;
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool use = ((u ? fl1 : fl0) >> (8 * i)) & 1u;    // tokens past the item are unusable
-                valid |= uint32_t(use) << (4 * u + i);
-            }
-        flash_step<true>(kd_all[buf], vt_all[buf], r.bq_hi, r.bq_lo, r.unscale, valid, m_run, l_run, o, col, kq);
+        flash_step<true>(kd_all[buf], vt_all[buf], r.bq_hi, r.bq_lo, r.unscale, bias, m_run, l_run, o, col, kq);
         if (more) dequant(buf ^ 1);                         // overlaps the step's matrix-core work
     };
     for (int cb = p0; cb < p1; cb += 2 * kTile) {
@@ -496,16 +499,16 @@ __global__ __launch_bounds__(kThreads, 4) void extend_bf16_kernel(ExtendHistArgs
         }
         if (cb + kTile < p1) load_tile(cb + kTile);
         __syncthreads();
-        uint32_t valid = 0;
+        f32x4 bias[2];
         const int lim = kind == 2 ? r.tok : INT32_MAX;      // causal: key position <= row token
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int pos = cb + 16 * u + 4 * kq + i;
-                valid |= uint32_t(pos < p1 && pos <= lim) << (4 * u + i);
+                bias[u][i] = (pos < p1 && pos <= lim) ? 0.0f : -INFINITY;
             }
-        flash_step<false>(kd, vt, r.bq_hi, r.bq_lo, r.unscale, valid, m_run, l_run, o, col, kq);
+        flash_step<false>(kd, vt, r.bq_hi, r.bq_lo, r.unscale, bias, m_run, l_run, o, col, kq);
     }
     store_partials(a, a.tok_per_block, rb, hk, j, w, col, kq, r, m_run, l_run, o);
 }

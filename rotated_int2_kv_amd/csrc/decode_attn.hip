@@ -795,7 +795,8 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
                 const float s0 = half_lo(szv[0][g]), s1 = half_lo(szv[1][g]);
-                const uint32_t whi = pk_rn(p0 * s0, p1 * s1);   // tokens n, 16 + n
+                // (fmaf with a zero addend reads the fp16 s in place: one mixed-precision fma)
+                const uint32_t whi = pk_rn(fmaf(p0, s0, 0.0f), fmaf(p1, s1, 0.0f));   // tokens n, 16 + n
                 const uint32_t wlo = pk_rn(fmaf(p0, s0, -half_lo(whi)), fmaf(p1, s1, -half_hi(whi)));
                 const int gl = NG == 4 ? (g & 1) : 0;
                 const uint32_t pl = NG == 4 ? uint32_t(g >> 1) * wpl_off : NG == 2 ? uint32_t(g) * wpl_off : 0u;

@@ -271,7 +271,7 @@ __global__ __launch_bounds__(64 * kWaves) void bf16_partial_kernel(Bf16Args a) {
 }
 
 // One workgroup per (request, KV head); thread (h, c) merges channel c of
-// query head h over the request's items.
+// query head h over the request's items, 16 items' loads in flight at a time.
 __global__ __launch_bounds__(512) void bf16_merge_kernel(Bf16Args a) {
     const int b = blockIdx.x / a.hkv;
     const int hk = blockIdx.x % a.hkv;
@@ -282,9 +282,11 @@ __global__ __launch_bounds__(512) void bf16_merge_kernel(Bf16Args a) {
     for (int h = threadIdx.x >> 7; h < a.g; h += 4) {
         const size_t row_h = size_t(b) * a.items * a.hq + size_t(hk) * a.g + h;
         float M = -INFINITY;
+#pragma unroll 16
         for (int jj = 0; jj < n_items; ++jj) M = fmaxf(M, a.part_ml[(row_h + size_t(jj) * a.hq) * 2]);
         float l = 0.0f, acc = 0.0f;
         if (M != -INFINITY) {
+#pragma unroll 16
             for (int jj = 0; jj < n_items; ++jj) {
                 const size_t row = row_h + size_t(jj) * a.hq;
                 const float e = __builtin_amdgcn_exp2f(a.part_ml[row * 2] - M);

@@ -1292,10 +1292,12 @@ __global__ __launch_bounds__(64 * kPartialWaves) void hist_lowmeta_kernel(Decode
 // 3. merge + un-rotation
 // ---------------------------------------------------------------------------
 // One workgroup per (request, KV head).  Wave h first reduces the running
-// maxima and sums of query head h over the items; then thread (h, c)
-// accumulates channel c over the items with independent loads.
+// maxima and sums of query head h over the items in one pass (each lane keeps
+// a running (m, l) of its items); then thread (h, c) accumulates channel c
+// over the items, 16 items' loads in flight at a time.
 __global__ __launch_bounds__(512) void merge_kernel(DecodeArgs a) {
     __shared__ float ob[kMaxGroup][kHeadDim];
+    __shared__ float red[4][kMaxGroup][kHeadDim];
     __shared__ float m_head[kMaxGroup], l_head[kMaxGroup];
     const int b = blockIdx.x / a.hkv;
     const int hk = blockIdx.x % a.hkv;
@@ -1326,23 +1328,22 @@ __global__ __launch_bounds__(512) void merge_kernel(DecodeArgs a) {
 
     const int wv = t >> 6;
     if (wv < a.g) {
-        float mx = -INFINITY;
+        float mx = -INFINITY, l = 0.0f;          // this lane's items, l relative to mx
         for (int j = lane; j < n_items; j += 64) {
-            const float m = a.part_ml[(row_b + size_t(j) * a.hq + wv) * 2];
-            mx = item_ok(j) ? fmaxf(mx, m) : mx;
-        }
-        mx = wave_max(mx);
-        float l = 0.0f;
-        if (mx != -INFINITY) {
-            for (int j = lane; j < n_items; j += 64) {
-                const size_t row = row_b + size_t(j) * a.hq + wv;
-                const float e = __builtin_amdgcn_exp2f(a.part_ml[row * 2] - mx);
-                l = item_ok(j) ? fmaf(e, a.part_ml[row * 2 + 1], l) : l;
+            if (!item_ok(j)) continue;
+            const float2 ml = *reinterpret_cast<const float2 *>(a.part_ml + (row_b + size_t(j) * a.hq + wv) * 2);
+            if (ml.x == -INFINITY) continue;     // every token of the item masked: weight 0
+            if (ml.x > mx) {
+                l = fmaf(l, __builtin_amdgcn_exp2f(mx - ml.x), ml.y);
+                mx = ml.x;
+            } else {
+                l = fmaf(ml.y, __builtin_amdgcn_exp2f(ml.x - mx), l);
             }
         }
-        l = wave_sum(l);
+        const float M = wave_max(mx);
+        l = wave_sum(mx == -INFINITY ? 0.0f : l * __builtin_amdgcn_exp2f(mx - M));
         if (lane == 0) {
-            m_head[wv] = mx;
+            m_head[wv] = M;
             l_head[wv] = l;
         }
     }
@@ -1360,7 +1361,7 @@ __global__ __launch_bounds__(512) void merge_kernel(DecodeArgs a) {
                 const size_t row = row_h + a.hq;
                 acc = fmaf(__builtin_amdgcn_exp2f(a.part_ml[row * 2] - M), a.part_o[row * kHeadDim + c], acc);
             }
-#pragma unroll 8
+#pragma unroll 16
             for (int j = 2; j < n_hist_items; ++j) {
                 const size_t row = row_h + size_t(j) * a.hq;
                 acc = fmaf(__builtin_amdgcn_exp2f(a.part_ml[row * 2] - M), a.part_o[row * kHeadDim + c], acc);
@@ -1373,18 +1374,33 @@ __global__ __launch_bounds__(512) void merge_kernel(DecodeArgs a) {
         ob[h][c] = l > 0.0f ? acc / l : 0.0f;
     }
     __syncthreads();
-    // o[h][c] = sum_i o'[h][i] R_V[c][i]
-    const float *R = a.r_v + (size_t(hk) * kHeadDim + c) * kHeadDim;
-    for (int h = t >> 7; h < a.g; h += 4) {
-        float o = 0.0f;
-#pragma unroll 8
-        for (int i = 0; i < kHeadDim; i += 4) {
-            const f32x4 r = *reinterpret_cast<const f32x4 *>(R + i);
-            o = fmaf(ob[h][i], r[0], o);
-            o = fmaf(ob[h][i + 1], r[1], o);
-            o = fmaf(ob[h][i + 2], r[2], o);
-            o = fmaf(ob[h][i + 3], r[3], o);
+    // o[h][c] = sum_i o'[h][i] R_V[c][i]: thread (part, c) reads the quarter
+    // i = 32 part .. 32 part + 31 of row c of R_V once and forms that part of
+    // the sum for every query head; the four parts add up through LDS
+    {
+        const int part = t >> 7;
+        const float *R = a.r_v + (size_t(hk) * kHeadDim + c) * kHeadDim + 32 * part;
+        f32x4 r[8];
+#pragma unroll
+        for (int i4 = 0; i4 < 8; ++i4) r[i4] = *reinterpret_cast<const f32x4 *>(R + 4 * i4);
+#pragma unroll
+        for (int h = 0; h < kMaxGroup; ++h) {
+            if (h >= a.g) break;
+            const float *ov = ob[h] + 32 * part;
+            float o = 0.0f;
+#pragma unroll
+            for (int i4 = 0; i4 < 8; ++i4) {
+                o = fmaf(ov[4 * i4], r[i4][0], o);
+                o = fmaf(ov[4 * i4 + 1], r[i4][1], o);
+                o = fmaf(ov[4 * i4 + 2], r[i4][2], o);
+                o = fmaf(ov[4 * i4 + 3], r[i4][3], o);
+            }
+            red[part][h][c] = o;
         }
+    }
+    __syncthreads();
+    for (int h = t >> 7; h < a.g; h += 4) {
+        const float o = (red[0][h][c] + red[1][h][c]) + (red[2][h][c] + red[3][h][c]);
         const size_t idx = (size_t(b) * a.hq + hk * a.g + h) * kHeadDim + c;
         if (a.out_dtype == OSCAR_F32)
             static_cast<float *>(a.out)[idx] = o;

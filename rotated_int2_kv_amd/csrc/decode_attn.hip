@@ -318,13 +318,18 @@ __host__ __device__ constexpr int int2_lds_bytes() { return kStages * kStage + k
 // The same pipeline for the lower-metadata records: 80 bytes (G = 64, two
 // groups; the K and V (s, z) of a head share one 16-byte unit) and 72 bytes
 // (G = 128, one group).  A token of a 4-head chunk is 320 or 288 bytes (20 or
-// 18 units), stored in token order without a swizzle; a tile takes 640 or 576
-// of the stage's 768 unit positions, the rest receive zero-record loads so
-// that every lane still issues three.  With G >= 64 a channel half holds one
-// group, so the A rows x = 1 of the QK products are zero and the PV weights use
-// rows q = part only (G = 128: one plane serves both halves).  The PV weights
-// get their own LDS area (a head has too few dead units per token): per wave
-// two planes (channel halves) of 8 rows 4 q + h x 32 K-slots of fp16.
+// 18 units), stored in token order without a swizzle but with one padding
+// unit after each token: a token stride of 21 or 19 units (84 or 76 dwords)
+// puts the same word of tokens 0..15 in 16 distinct 4-bank groups, so the
+// K-code, (s, z) and V-code reads hit distinct banks.  A tile takes 672 or 608
+// of the stage's 768 unit positions; the padding units and the rest receive
+// zero-record loads so that every lane still issues three.  With G >= 64 a
+// channel half holds one group, so the A rows x = 1 of the QK products are
+// zero and the PV weights use rows q = part only (G = 128: one plane serves
+// both halves).  The PV weights get their own LDS area (a head has too few
+// dead units per token): per wave two planes (channel halves) of 8 rows
+// 4 q + h x 32 K-slots of fp16, the 16-byte units of rows 4..7 XOR-permuted by
+// 1 so that the operand reads of rows r and r + 4 hit distinct banks.
 constexpr int kWeightPlane = 8 * kTileTokens * 2;      // 512 bytes
 constexpr int kWeightWave = 2 * kWeightPlane;          // 1 KiB
 __host__ __device__ constexpr int int2_lds_bytes_lowmeta() { return int2_lds_bytes() + 4 * kWeightWave; }
@@ -414,8 +419,11 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
     constexpr int kRecH = 2 * kCodeBytes + 2 * NG * SZB;  // head record: 96, 80 or 72 bytes
     constexpr int kUnitsH = kRecH / 16;                   // whole units of a head record
     constexpr int kTokB = 4 * kRecH;                      // one token of the 4-head chunk
-    constexpr int kTokUnits = kTokB / 16;                 // 24, 20 or 18 units
-    constexpr int kTileUnits = kTileTokens * kTokUnits;   // 768, 640 or 576 units per tile
+    constexpr int kRecUnits = kTokB / 16;                 // 24, 20 or 18 units of records
+    constexpr int kTokUnits = NG == 4 ? 24 : kRecUnits + 1;   // LDS units per token (one padding unit)
+    constexpr int kTokL = 16 * kTokUnits;                 // LDS bytes per token
+    constexpr int kTileUnits = kTileTokens * kTokUnits;   // 768, 672 or 608 units per tile
+    static_assert(kTileUnits <= 768, "a tile fits the stage");
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform over the wave
     const int lane = threadIdx.x & 63;
     const int n = lane & 15;
@@ -484,11 +492,12 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
     // units of KV heads past the chunk (never read) repeat the chunk's first head
     int tq[3];
     const uint8_t *src_base[3];
-    bool in_tile[3];                          // false: a padding position of the 80-byte layout
+    bool in_tile[3];                          // false: a padding position of the 80- or 72-byte layout
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
         const int P = 64 * (3 * w + u) + lane;
-        in_tile[u] = NG == 4 || P < kTileUnits;      // the 96-byte layout fills the stage
+        // the 96-byte layout fills the stage; the others pad each token by one unit
+        in_tile[u] = NG == 4 || (P < kTileUnits && P % kTokUnits < kRecUnits);
         const int Pc = in_tile[u] ? P : 0;
         const int t = Pc / kTokUnits, U = Pc % kTokUnits;
         const int q = NG == 4 ? ((U & ~7) | ((U & 7) ^ tok_swizzle(t))) : U;
@@ -586,9 +595,9 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
 
     // this lane's LDS addresses in stage 0 (head w of token t); token 16 + t
     // of a stage is 6144 bytes after token t (same swizzle)
-    constexpr int kHalfTok = 16 * kTokB;
+    constexpr int kHalfTok = 16 * kTokL;
     // byte b of head w's record of token t in stage 0 (80-byte layout)
-    auto rec_at = [&](int t, int byte) { return st0 + t * kTokB + kRecH * w + byte; };
+    auto rec_at = [&](int t, int byte) { return st0 + t * kTokL + kRecH * w + byte; };
     const int kb_tok = (kb & 1) + 4 * (kb >> 1);
     // K codes: word P of the lane = bytes 16 P + 4 kb .. + 3 (channels 64 P + 16 kb .. + 15)
     uint32_t qk_at[2], szk_at, szv_at, a_at;
@@ -635,12 +644,13 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
             for (int c = 0; c < 2; ++c)
                 pv_at[pp][c] = lds_pin(rec_at(8 * (pp >> 1) + 2 * (pp & 1) + kb_tok, kCodeBytes + 16 * c + (n & ~3)));
         const uint32_t wb = st0 + int2_lds_bytes() + w * kWeightWave;   // after the stages and the ring
+        // row r's unit v at physical unit v ^ (r / 4)
 #pragma unroll
-        for (int q = 0; q < 2; ++q) w_at[q] = lds_pin(wb + (4 * q + kb) * 64 + 16 * w_unit + 4 * w_i);
-        a_at = lds_pin(wb + (n & 7) * 64 + 16 * kb);
+        for (int q = 0; q < 2; ++q) w_at[q] = lds_pin(wb + (4 * q + kb) * 64 + 16 * (w_unit ^ q) + 4 * w_i);
+        a_at = lds_pin(wb + (n & 7) * 64 + 16 * (kb ^ ((n >> 2) & 1)));
     }
     // token 16 + t of a stage: 16 token strides after token t
-    constexpr uint32_t kHalfTokOff = 16 * kTokB;
+    constexpr uint32_t kHalfTokOff = 16 * kTokL;
     // the weight area of the 80-byte layout does not move with the stage
     constexpr bool kWeightsInStage = NG == 4;
 

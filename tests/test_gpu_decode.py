@@ -308,3 +308,39 @@ def test_decode_device_lengths_longer_than_host_lengths():
                         lay_b.head_dim ** -0.5, out, ws)
     torch.cuda.synchronize()
     assert np.all(np.isfinite(out.cpu().numpy()))
+
+
+def test_decode_whole_items_of_unusable_slots():
+    """A history work item whose every slot id is out of range writes a partial
+    with m = -inf and l = 0, which the merge must leave out; so must it when that
+    item comes first among the request's items.  Request 0 loses its first
+    history item and a middle one (96-token items), request 1 the first two
+    tiles of its first item (rows that see only masked tokens at first)."""
+    w = workloads.custom("decode_small", batch=2, seq_lens=(1500, 777))
+    lens = w.seq_lens
+    chunk = 96
+    lay_b, lay_o, opool, table, r_k, r_v = _oracle_pool_case(w, lens, seed=8)
+    s0 = w.sink
+    bad = {0: list(range(s0, s0 + chunk)) + list(range(s0 + 3 * chunk, s0 + 4 * chunk)),
+           1: list(range(s0, s0 + 64))}
+    bad_table = table.copy()
+    for b, ps in bad.items():
+        for p in ps:
+            assert s0 <= p < lens[b] - w.recent
+            bad_table[b, p] = -1 if p % 2 else lay_b.num_slots
+    qh, qd = _queries(w, 2, 12, "bf16")
+    gs.say("decode with whole items of unusable slot ids")
+    o_gpu = _gpu_decode(lay_b, gs.upload_oracle_pool(opool), qd, lens, bad_table, r_k, r_v,
+                        history_chunk=chunk)
+    g = w.num_q_heads // w.num_kv_heads
+    o_ref = np.zeros_like(o_gpu, dtype=np.float64)
+    rk = r_k.astype(np.float64)
+    rv = r_v.astype(np.float64)
+    for b in range(2):
+        kv = cache.gather(opool, lay_o, b, lens[b], table[b])
+        keep = np.setdiff1d(np.arange(lens[b]), bad[b])
+        for hk in range(w.num_kv_heads):
+            qr = qh[b, hk * g:(hk + 1) * g, :].astype(np.float64) @ rk[hk]
+            o_rot = attention.attention(qr, kv[keep, hk, 0, :], kv[keep, hk, 1, :], w.head_dim ** -0.5)
+            o_ref[b, hk * g:(hk + 1) * g, :] = o_rot @ rv[hk].T
+    _compare(o_gpu, o_ref, "whole items of unusable slots")

@@ -149,3 +149,45 @@ def test_extend_lower_metadata(G, sb, wname, P, n):
     at G = 64)."""
     w = workloads.custom(wname, group_size=G, scale_bits=sb)
     _run(w, P, n, seed=P + n + G)
+
+
+@pytest.mark.parametrize("history_chunk", [0, 96])
+def test_extend_skips_unusable_slot_ids(history_chunk):
+    """History positions whose slot id is negative or >= num_slots are left out
+    of an extend's softmax: the first two tiles of the history (rows see only
+    masked tokens at first), a whole 96-token span and scattered positions."""
+    w = workloads.workload("layer_small")
+    P, n = 2413, 40
+    lay_b, lay_o, opool, table, r_k, r_v, qh, qd, kh, vh, kd, vd = _case(w, P, n, seed=21)
+    s0 = w.sink
+    bad = list(range(s0, s0 + 64)) + list(range(s0 + 288, s0 + 384)) + [700, 701, 1333]
+    bad_table = table.copy()
+    for i, p in enumerate(bad):
+        assert s0 <= p < P - w.recent
+        bad_table[1, p] = [-1, lay_b.num_slots, np.iinfo(np.int32).max][i % 3]
+    gs.say(f"extend with unusable slot ids, chunk={history_chunk}")
+    o_gpu = _gpu_extend(lay_b, gs.upload_oracle_pool(opool), qd, kd, vd, P, bad_table, r_k, r_v,
+                        history_chunk=history_chunk)
+    # reference: the oracle's attention over the prefix positions that remain and
+    # the chunk's own tokens (causal)
+    from oracle import quant
+    keep = np.setdiff1d(np.arange(P), bad)
+    prefix = cache.gather(opool, lay_o, 1, P, table[1])[keep]
+    g = w.num_q_heads // w.num_kv_heads
+    o_ref = np.zeros((n, w.num_q_heads, w.head_dim))
+    for hk in range(w.num_kv_heads):
+        rk = np.asarray(r_k[hk], np.float32)
+        rv = np.asarray(r_v[hk], np.float32)
+        kn = quant.bf16_round(quant.rotate(kh[:, hk, :], rk)).astype(np.float64)
+        vn = quant.bf16_round(quant.rotate(vh[:, hk, :], rv)).astype(np.float64)
+        keys = np.concatenate([prefix[:, hk, 0, :], kn])
+        vals = np.concatenate([prefix[:, hk, 1, :], vn])
+        for i in range(n):
+            qr = qh[i, hk * g:(hk + 1) * g, :].astype(np.float64) @ rk.astype(np.float64)
+            m = len(keep) + i + 1
+            o_rot = attention.attention(qr, keys[:m], vals[:m], w.head_dim ** -0.5)
+            o_ref[i, hk * g:(hk + 1) * g, :] = o_rot @ rv.astype(np.float64).T
+    assert np.all(np.isfinite(o_gpu))
+    err = pt.normwise_rel(o_gpu, o_ref)
+    gs.say(f"  max normwise rel err {err.max():.3e} (median {np.median(err):.3e})")
+    assert err.max() <= TOL

@@ -260,7 +260,10 @@ oscar_status oscar_decode_attn_noalloc(hipStream_t stream, const oscar_layout *l
                                        const oscar_launch_opts *opts);
 
 /* Split-K plan that oscar_decode_attn uses: history tokens per work item and
-   work items per request (sink + recent + history chunks). */
+   work items per request: ceil(sink_tokens / 64) items of the sink window (at
+   least one), ceil(recent_tokens / 64) of the recent window, then the history
+   chunks.  Items of 64 positions let one request's window attention run on
+   several compute units. */
 oscar_status oscar_decode_plan(const oscar_layout *layout, int32_t batch,
                                const int32_t *seq_lens_host,
                                const oscar_launch_opts *opts, int32_t *history_chunk,

@@ -75,6 +75,8 @@ struct DecodeArgs {
     int32_t max_requests;
     int32_t chunk;
     int32_t items;
+    int32_t sink_items;   // items [0, sink_items): the sink window, kWindowItemTokens positions each
+    int32_t win_items;    // items [sink_items, win_items): the recent window; then the history chunks
     int32_t waves;     // KV heads per workgroup
     int32_t head_chunks;
     int32_t group_size;
@@ -87,18 +89,24 @@ struct DecodeArgs {
     const uint16_t *newkv;    // [rows][Hkv][2][128] BF16 rotated K, V of the new tokens
 };
 
-// Position range [p0, p1) of work item j of a request of length L.
+// Position range [p0, p1) of work item j of a request of length L: the sink
+// window [0, min(S, L)) and the recent window [max(S, L - W), L) in items of
+// kWindowItemTokens positions (one item each when the plan has one), then the
+// history [S, L - W) in chunks.
 __device__ __forceinline__ void item_range(const DecodeArgs &a, int L, int j, int &p0, int &p1) {
     const int S = a.sink_tokens, W = a.recent_tokens;
     const int hist_end = max(S, L - W);
-    if (j == 0) {
-        p0 = 0;
-        p1 = min(S, L);
-    } else if (j == 1) {
-        p0 = L > S ? hist_end : L;
-        p1 = L;
+    if (j < a.sink_items) {
+        const int end = min(S, L);
+        p0 = a.sink_items == 1 ? 0 : min(end, j * kWindowItemTokens);
+        p1 = a.sink_items == 1 ? end : min(end, p0 + kWindowItemTokens);
+    } else if (j < a.win_items) {
+        const int start = L > S ? hist_end : L;
+        const int r = j - a.sink_items;
+        p0 = a.win_items - a.sink_items == 1 ? start : min(L, start + r * kWindowItemTokens);
+        p1 = a.win_items - a.sink_items == 1 ? L : min(L, p0 + kWindowItemTokens);
     } else {
-        p0 = S + (j - 2) * a.chunk;
+        p0 = S + (j - a.win_items) * a.chunk;
         p1 = min(p0 + a.chunk, hist_end);
     }
 }
@@ -972,7 +980,7 @@ __device__ __forceinline__ void bf16_item(const DecodeArgs &a, int b, int req, i
     for (int e = lane; e < g * kHeadDim; e += 64) qs[e] = qr[e];
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const bool is_sink = (j == 0);
+    const bool is_sink = j < a.sink_items;
     float m_run[kMaxGroup], l_lane[kMaxGroup], o0[kMaxGroup], o1[kMaxGroup];
 #pragma unroll
     for (int h = 0; h < kMaxGroup; ++h) {
@@ -1104,7 +1112,7 @@ __global__ __launch_bounds__(64 * kPartialWaves) void partial_kernel(DecodeArgs 
     const int w = threadIdx.x >> 6;
     const int hk = hc * kPartialWaves + w;
     const bool active = hk < a.hkv;
-    if (j < 2) {
+    if (j < a.win_items) {
         float *pbuf = reinterpret_cast<float *>(smem) + w * kBf16WaveFloats;
         bf16_item(a, b, req, j, active ? hk : 0, p0, p1, active, pbuf);
     } else if (a.num_slots > 0) {
@@ -1132,7 +1140,7 @@ __global__ __launch_bounds__(64 * kPartialWaves) void hist_lowmeta_kernel(Decode
     const int hc = id % a.head_chunks;
     const int rest = id / a.head_chunks;
     const int b = rest % a.batch;
-    const int j = 2 + rest / a.batch;
+    const int j = a.win_items + rest / a.batch;
     int req = 0;
     const int L = request_length(a, b, req);
     int p0, p1;
@@ -1316,24 +1324,29 @@ __global__ __launch_bounds__(512) void merge_kernel(DecodeArgs a) {
     const int c = t & (kHeadDim - 1);
     int req = 0;
     const int L = request_length(a, b, req);
-    // items that hold a partial: the two BF16 windows if non-empty, then every
-    // history chunk (written only when the INT2 pool exists)
-    int p0, p1;
-    item_range(a, L, 0, p0, p1);
-    const bool sink_ok = p0 < p1;
-    item_range(a, L, 1, p0, p1);
-    const bool recent_ok = p0 < p1;
-    const int hist = max(0, max(a.sink_tokens, L - a.recent_tokens) - a.sink_tokens);
+    // items that hold a partial: the window items that hold positions (item_range
+    // fills them from the start: the first n_sink of the sink's, the first
+    // n_recent of the recent window's), then every history chunk (written only
+    // when the INT2 pool exists)
+    const int hist_end = max(a.sink_tokens, L - a.recent_tokens);
+    const int sink_len = min(a.sink_tokens, L), recent_len = L > a.sink_tokens ? L - hist_end : 0;
+    const int recent_items = a.win_items - a.sink_items;
+    const int n_sink = a.sink_items == 1 ? int(sink_len > 0) : (sink_len + kWindowItemTokens - 1) / kWindowItemTokens;
+    const int n_recent =
+        recent_items == 1 ? int(recent_len > 0) : (recent_len + kWindowItemTokens - 1) / kWindowItemTokens;
+    const int hist = hist_end - a.sink_tokens;
     // capped at the planned items: a device length longer than the host copy
     // the plan was made from must not read partials past this request's rows
     const int item_cap = a.extra_item >= 0 ? a.extra_item : a.items;
-    const int n_hist_items = a.num_slots > 0 ? min(item_cap, 2 + (hist + a.chunk - 1) / a.chunk) : 2;
+    const int n_hist_items =
+        a.num_slots > 0 ? min(item_cap, a.win_items + (hist + a.chunk - 1) / a.chunk) : a.win_items;
     // the extend's new-token item is the last one and always holds a partial;
     // items between the request's chunks and it hold none
     const int n_items = a.extra_item >= 0 ? a.extra_item + 1 : n_hist_items;
     const size_t row_b = size_t(b) * a.items * a.hq + size_t(hk) * a.g;   // item 0, head 0
     auto item_ok = [&](int j) {
-        return j == a.extra_item || (j >= 2 && j < n_hist_items) || (j == 0 && sink_ok) || (j == 1 && recent_ok);
+        return j == a.extra_item || (j >= a.win_items && j < n_hist_items) || j < n_sink ||
+               (j >= a.sink_items && j < a.sink_items + n_recent);
     };
 
     const int wv = t >> 6;
@@ -1365,14 +1378,16 @@ __global__ __launch_bounds__(512) void merge_kernel(DecodeArgs a) {
             const size_t row_h = row_b + h;
             // every item that exists wrote finite (m, l, o'); a fully masked
             // one has m = -inf and weight exp2(-inf) = 0
-            if (sink_ok)
-                acc = fmaf(__builtin_amdgcn_exp2f(a.part_ml[row_h * 2] - M), a.part_o[row_h * kHeadDim + c], acc);
-            if (recent_ok) {
-                const size_t row = row_h + a.hq;
+            for (int j = 0; j < n_sink; ++j) {
+                const size_t row = row_h + size_t(j) * a.hq;
+                acc = fmaf(__builtin_amdgcn_exp2f(a.part_ml[row * 2] - M), a.part_o[row * kHeadDim + c], acc);
+            }
+            for (int j = a.sink_items; j < a.sink_items + n_recent; ++j) {
+                const size_t row = row_h + size_t(j) * a.hq;
                 acc = fmaf(__builtin_amdgcn_exp2f(a.part_ml[row * 2] - M), a.part_o[row * kHeadDim + c], acc);
             }
 #pragma unroll 16
-            for (int j = 2; j < n_hist_items; ++j) {
+            for (int j = a.win_items; j < n_hist_items; ++j) {
                 const size_t row = row_h + size_t(j) * a.hq;
                 acc = fmaf(__builtin_amdgcn_exp2f(a.part_ml[row * 2] - M), a.part_o[row * kHeadDim + c], acc);
             }
@@ -1543,6 +1558,8 @@ DecodeArgs make_args(const oscar_layout *layout, const oscar_pool *pool, const v
     a.max_requests = layout->max_requests;
     a.chunk = plan.chunk;
     a.items = plan.items;
+    a.sink_items = plan.sink_items;
+    a.win_items = plan.sink_items + plan.recent_items;
     a.waves = kPartialWaves;
     a.head_chunks = (a.hkv + kPartialWaves - 1) / kPartialWaves;
     a.group_size = layout->group_size;
@@ -1577,9 +1594,9 @@ oscar_status launch_decode(const DecodeArgs &a, const DecodePlan &plan, hipStrea
         if (e != hipSuccess) return fail(OSCAR_ERR_HIP, std::string("extend bf16 launch: ") + hipGetErrorString(e));
     } else if (head_record_bytes(a.group_size, a.scale_bits) % 16 != 0 && (a.hkv & 1)) {
         // 72-byte records and an odd number of KV heads (a 4-head chunk would
-        // end inside a 16-byte unit): the BF16 windows (items 0, 1) on
-        // partial_kernel, the history items on hist_lowmeta_kernel
-        const int bf_blocks = 2 * a.batch * a.head_chunks;
+        // end inside a 16-byte unit): the BF16 window items on partial_kernel,
+        // the history items on hist_lowmeta_kernel
+        const int bf_blocks = a.win_items * a.batch * a.head_chunks;
         switch (a.g) {
             case 1: e = launch_partial<1>(a, bf_blocks, stream); break;
             case 2: e = launch_partial<2>(a, bf_blocks, stream); break;
@@ -1591,7 +1608,7 @@ oscar_status launch_decode(const DecodeArgs &a, const DecodePlan &plan, hipStrea
             default: e = launch_partial<8>(a, bf_blocks, stream); break;
         }
         if (e != hipSuccess) return fail(OSCAR_ERR_HIP, std::string("partial launch: ") + hipGetErrorString(e));
-        const int h_blocks = (plan.items - 2) * a.batch * a.head_chunks;
+        const int h_blocks = (plan.items - a.win_items) * a.batch * a.head_chunks;
         if (h_blocks > 0 && a.num_slots > 0) {
             if (a.scale_bits == 8)
                 hipLaunchKernelGGL((hist_lowmeta_kernel<2, 2>), dim3(h_blocks), dim3(64 * kPartialWaves), 0, stream, a);

@@ -41,10 +41,16 @@ inline int64_t record_bytes(const oscar_layout &lay) {
     return static_cast<int64_t>(lay.num_kv_heads) * head_record_bytes(lay.group_size, scale_bits(lay));
 }
 
+// Decode splits the sink and recent windows into work items of this many
+// positions, so that a request's window work runs on several compute units.
+constexpr int kWindowItemTokens = 64;
+
 // Split-K plan of one decode call (pure function of the host lengths).
 struct DecodePlan {
     int32_t chunk = 0;           // history tokens per work item
     int32_t items = 0;           // work items per request: sink, recent, chunks
+    int32_t sink_items = 1;      // items 0 .. sink_items-1 cover the sink window
+    int32_t recent_items = 1;    // the next recent_items cover the recent window
     int32_t max_len = 0;
     size_t ws_qrot = 0;          // byte offsets into the workspace
     size_t ws_qsum = 0;

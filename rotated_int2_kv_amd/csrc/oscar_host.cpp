@@ -93,11 +93,16 @@ oscar_status make_decode_plan(const oscar_layout &lay, int32_t batch,
         chunk = (chunk + 31) / 32 * 32;
         chunk = std::min<int64_t>(8192, std::max<int64_t>(256, chunk));
     }
-    const int64_t items = 2 + (max_hist + chunk - 1) / chunk + (extend ? 1 : 0);
+    // decode: windows in items of kWindowItemTokens positions; extend: one item each
+    const int64_t sink_items = extend ? 1 : std::max<int64_t>(1, (S + kWindowItemTokens - 1) / kWindowItemTokens);
+    const int64_t recent_items = extend ? 1 : (W + kWindowItemTokens - 1) / kWindowItemTokens;
+    const int64_t items = sink_items + recent_items + (max_hist + chunk - 1) / chunk + (extend ? 1 : 0);
     const int64_t hq = lay.num_q_heads;
     auto align = [](size_t x) { return (x + 255) / 256 * 256; };
     plan->chunk = static_cast<int32_t>(chunk);
     plan->items = static_cast<int32_t>(items);
+    plan->sink_items = static_cast<int32_t>(sink_items);
+    plan->recent_items = static_cast<int32_t>(recent_items);
     plan->max_len = static_cast<int32_t>(max_len);
     size_t off = 0;
     plan->ws_qrot = off;

@@ -200,14 +200,15 @@ def test_decode_plan_and_workspace():
     hist = 100000 - 64 - 256
     assert chunk % 32 == 0 and 256 <= chunk <= 8192
     assert chunk == -(-(-(-32 * hist // 1024)) // 32) * 32
-    assert items == 2 + -(-hist // chunk)
+    # the sink (64) and recent (256) windows in work items of 64 positions
+    assert items == 1 + 4 + -(-hist // chunk)
     ws = B.oscar_decode_workspace_size(lay, lens)
     # rotated q, per-head group sums + operand scales (8 floats), partial o', (m, l), zero record
     need = (32 * 32 * 128 * 4 + 32 * 32 * 8 * 4 + 32 * items * 32 * 128 * 4 + 32 * items * 32 * 8
             + 256)
     assert need <= ws <= need + 5 * 256
     c2, it2 = B.oscar_decode_plan(lay, [300], history_chunk=64)
-    assert (c2, it2) == (64, 2)
+    assert (c2, it2) == (64, 5)
     with pytest.raises(B.OscarError):
         B.oscar_decode_plan(lay, [300], history_chunk=48)
 

@@ -208,12 +208,15 @@ def run_decode(args, torch, B, workloads, name=None, steps=None, warmup=None):
     # the whole call also reads q, the two rotations and writes o (and the
     # split-K partials, which are not the method's traffic)
     call_bytes = kbytes + bsz * w.num_q_heads * 128 * 2 * 2 + 2 * hkv * 128 * 128 * 4
-    hist_items = items - 2
+    # the sink and recent windows go to work items of 64 positions each
+    win_items = max(1, -(-w.sink // 64)) + -(-w.recent // 64)
+    hist_items = items - win_items
     return dict(w=w, lens=lens, ms=ms, kern_ms=float(kern.mean()), kern_ms_median=float(np.median(kern)),
                 kern_ms_min=float(kern.min()), kern_ms_max=float(kern.max()),
                 call_ms=float(call.mean()), call_ms_median=float(np.median(call)),
                 kbytes=kbytes, call_bytes=call_bytes, chunk=chunk_sz, items=items,
-                workgroups=int(hist_items * bsz * ((hkv + 3) // 4)), per_launch_kernel_ms=kern.tolist(),
+                workgroups=int(hist_items * bsz * ((hkv + 3) // 4)),
+                window_workgroups=int(win_items * bsz * ((hkv + 3) // 4)), per_launch_kernel_ms=kern.tolist(),
                 o_finite=bool(torch.isfinite(out.float()).all().item()))
 
 

@@ -251,7 +251,7 @@ template <int K>
 __device__ __forceinline__ float row_ror(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x120 + K, 0xF, 0xF, false));
 }
-[[maybe_unused]] __device__ __forceinline__ float row16_max(float v) {
+__device__ __forceinline__ float row16_max(float v) {
     v = fmaxf(v, row_ror<1>(v));
     v = fmaxf(v, row_ror<2>(v));
     v = fmaxf(v, row_ror<4>(v));
@@ -962,133 +962,161 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
     }
 }
 
-// BF16 window item on fp32 VALU (the sink and recent windows: a few hundred
-// tokens per request).  Chunks of 64 tokens; every load of a chunk is issued
-// before its data is used, so a chunk costs a few memory latencies, not one
-// per token.  QK: lane = token, its K row (16 x 16 bytes) against q' staged
-// in this wave's LDS.  PV: lane = channel pair, V rows of 16 tokens at a time.
-// `pbuf` is this wave's LDS scratch: q' [kMaxGroup][128] then p [kMaxGroup][64].
+// BF16 window item on fp32 VALU: at most kWindowItemTokens = 64 positions of
+// the sink or recent window, one wave per KV head.  Two memory round trips:
+// QK with lane = position (its K row, 16 x 16 bytes, against q' staged in
+// this wave's LDS), then PV with lane = channel pair and the V rows of all the
+// item's positions in flight at once, each row's offset broadcast from the
+// lane that computed it.  The softmax runs while the V rows arrive.
+// `pbuf` is this wave's LDS scratch: q' [kMaxGroup][128] then p [64][kMaxGroup].
+static_assert(kWindowItemTokens == kBf16Chunk, "a window item is one chunk of 64 positions");
 constexpr int kBf16WaveFloats = kMaxGroup * kHeadDim + kMaxGroup * kBf16Chunk;
 
+// Ends a block of PV products: the accumulators pass through an empty asm
+// statement with a memory clobber, so the next block's LDS reads cannot be
+// hoisted above this block's products (held all at once they would need 256
+// registers).
+template <int NH>
+__device__ __forceinline__ void pv_block_end(float (&o0)[NH], float (&o1)[NH]) {
+    if constexpr (NH == 4)
+        asm volatile("" : "+v"(o0[0]), "+v"(o0[1]), "+v"(o0[2]), "+v"(o0[3]), "+v"(o1[0]), "+v"(o1[1]),
+                     "+v"(o1[2]), "+v"(o1[3])::"memory");
+    else
+        asm volatile("" : "+v"(o0[0]), "+v"(o0[1]), "+v"(o0[2]), "+v"(o0[3]), "+v"(o0[4]), "+v"(o0[5]),
+                     "+v"(o0[6]), "+v"(o0[7]), "+v"(o1[0]), "+v"(o1[1]), "+v"(o1[2]), "+v"(o1[3]),
+                     "+v"(o1[4]), "+v"(o1[5]), "+v"(o1[6]), "+v"(o1[7])::"memory");
+}
+
+// o[h] += p[t][h] v_t over the 64 positions for NH heads (the group padded to
+// 4 or 8; the padding heads' weights are zero), lane = channel pair, in blocks
+// of 4 positions whose weights are read while the previous block's products
+// run.  Positions past the item's end have p = 0 and the first position's V row.
+template <int NH>
+__device__ __forceinline__ void bf16_pv(const uint32_t (&vw)[kBf16Chunk], const float *ps, float (&o0)[NH],
+                                        float (&o1)[NH]) {
+    constexpr int kBlk = 4, kQ = NH / 4;
+    f32x4 pw[2][kBlk][kQ];
+#pragma unroll
+    for (int u = 0; u < kBlk; ++u)
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) pw[0][u][q] = *reinterpret_cast<const f32x4 *>(ps + u * kMaxGroup + 4 * q);
+#pragma unroll
+    for (int blk = 0; blk < kBf16Chunk / kBlk; ++blk) {
+        if (blk + 1 < kBf16Chunk / kBlk) {
+#pragma unroll
+            for (int u = 0; u < kBlk; ++u)
+#pragma unroll
+                for (int q = 0; q < kQ; ++q)
+                    pw[(blk + 1) & 1][u][q] =
+                        *reinterpret_cast<const f32x4 *>(ps + ((blk + 1) * kBlk + u) * kMaxGroup + 4 * q);
+        }
+#pragma unroll
+        for (int u = 0; u < kBlk; ++u) {
+            const uint32_t v = vw[blk * kBlk + u];
+            const float v0 = bf16_bits_to_f32(v & 0xFFFFu), v1 = bf16_bits_to_f32(v >> 16);
+#pragma unroll
+            for (int q = 0; q < kQ; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    o0[4 * q + e] = fmaf(pw[blk & 1][u][q][e], v0, o0[4 * q + e]);
+                    o1[4 * q + e] = fmaf(pw[blk & 1][u][q][e], v1, o1[4 * q + e]);
+                }
+        }
+        pv_block_end<NH>(o0, o1);
+    }
+}
+
+template <int NH>
 __device__ __forceinline__ void bf16_item(const DecodeArgs &a, int b, int req, int j, int hk, int p0, int p1,
-                          bool active, float *pbuf) {
+                                          bool active, float *pbuf) {
     const int lane = threadIdx.x & 63;
     const int g = a.g;
     float *qs = pbuf;
     float *ps = pbuf + kMaxGroup * kHeadDim;
     const float *qr = a.qrot + (size_t(b) * a.hq + hk * g) * kHeadDim;
-    for (int e = lane; e < g * kHeadDim; e += 64) qs[e] = qr[e];
+    for (int e = lane; e < NH * kHeadDim; e += 64) qs[e] = e < g * kHeadDim ? qr[e] : 0.0f;   // padding: q' = 0
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // row of window position pos: base + ring index x row_elems (K at +0, V at
+    // +128); windows of at most 4096 rows and 16 KV heads keep it below 2^24
     const bool is_sink = j < a.sink_items;
-    float m_run[kMaxGroup], l_lane[kMaxGroup], o0[kMaxGroup], o1[kMaxGroup];
+    const uint32_t ring = uint32_t(is_sink ? a.sink_tokens : a.recent_tokens);
+    const uint16_t *base = (is_sink ? a.sink : a.recent) + (size_t(req) * ring * a.hkv + hk) * 2 * kHeadDim;
+    const uint32_t row_elems = uint32_t(a.hkv) * 2 * kHeadDim;
+    const int cnt = p1 - p0;                             // 1 .. 64
+    const bool ok = active && lane < cnt;
+    const uint32_t pos = uint32_t(p0 + (lane < cnt ? lane : 0));   // past the end: the first position
+    const uint32_t roff = (is_sink ? pos : pos % ring) * row_elems;
+    // ---- QK: the whole K row of this lane's position in flight at once
+    u32x4 kw[kHeadDim / 8];
 #pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h) {
-        m_run[h] = -INFINITY;
-        l_lane[h] = 0.0f;
+    for (int i = 0; i < kHeadDim / 8; ++i) kw[i] = *reinterpret_cast<const u32x4 *>(base + roff + 8 * i);
+    float acc[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) acc[h] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kHeadDim / 8; ++i) {
+        float kf[8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            kf[2 * u] = bf16_bits_to_f32(kw[i][u] & 0xFFFFu);
+            kf[2 * u + 1] = bf16_bits_to_f32(kw[i][u] >> 16);
+        }
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            const f32x4 qa = *reinterpret_cast<const f32x4 *>(qs + h * kHeadDim + 8 * i);
+            const f32x4 qb = *reinterpret_cast<const f32x4 *>(qs + h * kHeadDim + 8 * i + 4);
+            acc[h] = fmaf(qa[0], kf[0], acc[h]);
+            acc[h] = fmaf(qa[1], kf[1], acc[h]);
+            acc[h] = fmaf(qa[2], kf[2], acc[h]);
+            acc[h] = fmaf(qa[3], kf[3], acc[h]);
+            acc[h] = fmaf(qb[0], kf[4], acc[h]);
+            acc[h] = fmaf(qb[1], kf[5], acc[h]);
+            acc[h] = fmaf(qb[2], kf[6], acc[h]);
+            acc[h] = fmaf(qb[3], kf[7], acc[h]);
+        }
+    }
+    // ---- V rows of every position, in flight during the softmax
+    uint32_t vw[kBf16Chunk];
+#pragma unroll
+    for (int t = 0; t < kBf16Chunk; ++t) {
+        const uint32_t ro = uint32_t(__builtin_amdgcn_readlane(int(roff), t));
+        vw[t] = *reinterpret_cast<const uint32_t *>(base + ro + kHeadDim + 2 * lane);
+    }
+    // ---- softmax over the item's positions (log2 units), p token-major in LDS
+    float m[NH], l[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        const float x = ok ? acc[h] : -INFINITY;
+        float mx = row16_max(x);                         // DPP within rows, then across the 4 rows
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float p = ok ? __builtin_amdgcn_exp2f(x - mx) : 0.0f;
+        m[h] = mx;
+        l[h] = p;
+        ps[lane * kMaxGroup + h] = h < g ? p : 0.0f;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // ---- PV
+    float o0[NH], o1[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
         o0[h] = 0.0f;
         o1[h] = 0.0f;
     }
-    auto row_ptr = [&](int pos, int t) -> const uint16_t * {
-        if (is_sink)
-            return a.sink + ((size_t(req) * a.sink_tokens + pos) * a.hkv + hk) * 2 * kHeadDim + t * kHeadDim;
-        return a.recent + ((size_t(req) * a.recent_tokens + pos % a.recent_tokens) * a.hkv + hk) * 2 * kHeadDim +
-               t * kHeadDim;
-    };
-    for (int cb = p0; cb < p1; cb += kBf16Chunk) {
-        const int cnt = min(kBf16Chunk, p1 - cb);
-        const bool ok = active && lane < cnt;
-        // ---- QK: the whole K row of this lane's token in flight at once
-        const uint16_t *kr = row_ptr(cb + (lane < cnt ? lane : 0), 0);
-        u32x4 kw[kHeadDim / 8];
-#pragma unroll
-        for (int i = 0; i < kHeadDim / 8; ++i) kw[i] = *reinterpret_cast<const u32x4 *>(kr + 8 * i);
-        float acc[kMaxGroup];
-#pragma unroll
-        for (int h = 0; h < kMaxGroup; ++h) acc[h] = 0.0f;
-#pragma unroll
-        for (int i = 0; i < kHeadDim / 8; ++i) {
-            float kf[8];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                kf[2 * u] = bf16_bits_to_f32(kw[i][u] & 0xFFFFu);
-                kf[2 * u + 1] = bf16_bits_to_f32(kw[i][u] >> 16);
-            }
-#pragma unroll
-            for (int h = 0; h < kMaxGroup; ++h) {
-                if (h < g) {
-                    const f32x4 qa = *reinterpret_cast<const f32x4 *>(qs + h * kHeadDim + 8 * i);
-                    const f32x4 qb = *reinterpret_cast<const f32x4 *>(qs + h * kHeadDim + 8 * i + 4);
-                    acc[h] = fmaf(qa[0], kf[0], acc[h]);
-                    acc[h] = fmaf(qa[1], kf[1], acc[h]);
-                    acc[h] = fmaf(qa[2], kf[2], acc[h]);
-                    acc[h] = fmaf(qa[3], kf[3], acc[h]);
-                    acc[h] = fmaf(qb[0], kf[4], acc[h]);
-                    acc[h] = fmaf(qb[1], kf[5], acc[h]);
-                    acc[h] = fmaf(qb[2], kf[6], acc[h]);
-                    acc[h] = fmaf(qb[3], kf[7], acc[h]);
-                }
-            }
-        }
-        float alpha[kMaxGroup];
-#pragma unroll
-        for (int h = 0; h < kMaxGroup; ++h) {
-            const float x = ok ? acc[h] : -INFINITY;
-            float mx = x;
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-            const float m_new = fmaxf(m_run[h], mx);
-            alpha[h] = (m_new > m_run[h]) ? __builtin_amdgcn_exp2f(m_run[h] - m_new) : 1.0f;
-            m_run[h] = m_new;
-            const float p = (x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x - m_new);
-            l_lane[h] = l_lane[h] * alpha[h] + p;
-            if (h < g) ps[h * kBf16Chunk + lane] = p;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // ---- PV: lane holds channels 2 lane, 2 lane + 1; 16 V rows in flight
-#pragma unroll
-        for (int h = 0; h < kMaxGroup; ++h) {
-            o0[h] *= alpha[h];
-            o1[h] *= alpha[h];
-        }
-        if (active) {
-            for (int t0 = 0; t0 < cnt; t0 += 16) {
-                uint32_t vw[16];
-#pragma unroll
-                for (int u = 0; u < 16; ++u) {
-                    const int tt = min(t0 + u, cnt - 1);   // past the chunk: p = 0 below
-                    vw[u] = *reinterpret_cast<const uint32_t *>(row_ptr(cb + tt, 1) + 2 * lane);
-                }
-#pragma unroll
-                for (int u = 0; u < 16; ++u) {
-                    const float v0 = bf16_bits_to_f32(vw[u] & 0xFFFFu), v1 = bf16_bits_to_f32(vw[u] >> 16);
-                    const int tt = min(t0 + u, kBf16Chunk - 1);
-#pragma unroll
-                    for (int h = 0; h < kMaxGroup; ++h) {
-                        if (h < g) {
-                            const float p = t0 + u < cnt ? ps[h * kBf16Chunk + tt] : 0.0f;
-                            o0[h] = fmaf(p, v0, o0[h]);
-                            o1[h] = fmaf(p, v1, o1[h]);
-                        }
-                    }
-                }
-            }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
+    bf16_pv<NH>(vw, ps, o0, o1);
     if (!active) return;
     const size_t row0 = (size_t(b) * a.items + j) * a.hq + hk * g;
 #pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h) {
+    for (int h = 0; h < NH; ++h) {
         if (h >= g) break;
-        float l = l_lane[h];
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
+        float lsum = row16_sum(l[h]);
+        lsum += __shfl_xor(lsum, 16);
+        lsum += __shfl_xor(lsum, 32);
         if (lane == 0) {
-            a.part_ml[(row0 + h) * 2 + 0] = m_run[h];
-            a.part_ml[(row0 + h) * 2 + 1] = l;
+            a.part_ml[(row0 + h) * 2 + 0] = m[h];
+            a.part_ml[(row0 + h) * 2 + 1] = lsum;
         }
         float *dst = a.part_o + (row0 + h) * kHeadDim + 2 * lane;
         dst[0] = o0[h];
@@ -1114,7 +1142,10 @@ __global__ __launch_bounds__(64 * kPartialWaves) void partial_kernel(DecodeArgs 
     const bool active = hk < a.hkv;
     if (j < a.win_items) {
         float *pbuf = reinterpret_cast<float *>(smem) + w * kBf16WaveFloats;
-        bf16_item(a, b, req, j, active ? hk : 0, p0, p1, active, pbuf);
+        if (a.g <= 4)                               // the group padded to 4 or 8 heads
+            bf16_item<4>(a, b, req, j, active ? hk : 0, p0, p1, active, pbuf);
+        else
+            bf16_item<8>(a, b, req, j, active ? hk : 0, p0, p1, active, pbuf);
     } else if (a.num_slots > 0) {
         int2_item<GQ, NG, SZB>(a, b, req, j, hc, p0, p1, smem);   // every wave: the loads are shared
     }

@@ -1402,32 +1402,47 @@ __global__ __launch_bounds__(512) void merge_kernel(DecodeArgs a) {
         }
     }
     __syncthreads();
-    for (int h = t >> 7; h < a.g; h += 4) {
-        const float M = m_head[h], l = l_head[h];
-        float acc = 0.0f;
-        if (M != -INFINITY && l > 0.0f) {
+    // o'[h] = sum over items of 2^(m_j - M) o'_j / l.  The items that hold a
+    // partial, numbered k = 0 .. n_part-1, are split among `splits` threads per
+    // (head, 4 channels), so that a long request's items are read with several
+    // times the loads in flight; the splits add up through LDS in a fixed order.
+    {
+        const int n_hist = n_hist_items - a.win_items;
+        const int n_part = n_sink + n_recent + n_hist + (a.extra_item >= 0 ? 1 : 0);
+        const int units = a.g * (kHeadDim / 4);                 // (head, 4 channels)
+        const int splits = 512 / units;                         // 2 .. 16
+        const int u = t % units, sp = t / units;
+        const int h = u / (kHeadDim / 4), c4 = 4 * (u % (kHeadDim / 4));
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (sp < splits) {
+            const float M = m_head[h];
             const size_t row_h = row_b + h;
-            // every item that exists wrote finite (m, l, o'); a fully masked
-            // one has m = -inf and weight exp2(-inf) = 0
-            for (int j = 0; j < n_sink; ++j) {
+#pragma unroll 8
+            for (int k = sp; k < n_part; k += splits) {
+                // k -> item: the sink's, the recent window's, the history chunks, the new tokens
+                int j = k < n_sink ? k : k - n_sink + a.sink_items;
+                j = k < n_sink + n_recent ? j : k - n_sink - n_recent + a.win_items;
+                j = k < n_sink + n_recent + n_hist ? j : a.extra_item;
                 const size_t row = row_h + size_t(j) * a.hq;
-                acc = fmaf(__builtin_amdgcn_exp2f(a.part_ml[row * 2] - M), a.part_o[row * kHeadDim + c], acc);
+                // every item that exists wrote finite (m, l, o'); a fully masked
+                // one has m = -inf and weight exp2(-inf) = 0
+                const float e = __builtin_amdgcn_exp2f(a.part_ml[row * 2] - M);
+                const f32x4 o = *reinterpret_cast<const f32x4 *>(a.part_o + row * kHeadDim + c4);
+                acc[0] = fmaf(e, o[0], acc[0]);
+                acc[1] = fmaf(e, o[1], acc[1]);
+                acc[2] = fmaf(e, o[2], acc[2]);
+                acc[3] = fmaf(e, o[3], acc[3]);
             }
-            for (int j = a.sink_items; j < a.sink_items + n_recent; ++j) {
-                const size_t row = row_h + size_t(j) * a.hq;
-                acc = fmaf(__builtin_amdgcn_exp2f(a.part_ml[row * 2] - M), a.part_o[row * kHeadDim + c], acc);
-            }
-#pragma unroll 16
-            for (int j = a.win_items; j < n_hist_items; ++j) {
-                const size_t row = row_h + size_t(j) * a.hq;
-                acc = fmaf(__builtin_amdgcn_exp2f(a.part_ml[row * 2] - M), a.part_o[row * kHeadDim + c], acc);
-            }
-            if (a.extra_item >= 0) {
-                const size_t row = row_h + size_t(a.extra_item) * a.hq;
-                acc = fmaf(__builtin_amdgcn_exp2f(a.part_ml[row * 2] - M), a.part_o[row * kHeadDim + c], acc);
-            }
+            *reinterpret_cast<f32x4 *>(&red[0][0][0] + (sp * units + u) * 4) = acc;
         }
-        ob[h][c] = l > 0.0f ? acc / l : 0.0f;
+        __syncthreads();
+        for (int e = t; e < a.g * kHeadDim; e += 512) {
+            const int hh = e / kHeadDim, cc = e % kHeadDim;
+            const float M = m_head[hh], l = l_head[hh];
+            float sum = 0.0f;
+            for (int q = 0; q < splits; ++q) sum += (&red[0][0][0])[(q * units + hh * (kHeadDim / 4) + cc / 4) * 4 + cc % 4];
+            ob[hh][cc] = (M != -INFINITY && l > 0.0f) ? sum / l : 0.0f;
+        }
     }
     __syncthreads();
     // o[h][c] = sum_i o'[h][i] R_V[c][i]: thread (part, c) reads the quarter

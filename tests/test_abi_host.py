@@ -286,6 +286,18 @@ def test_extend_rejects_before_launch(over, status):
     assert _extend(L(), 37, 5000, **over) == status
 
 
+@pytest.mark.parametrize("S,W", [(0, 256), (100, 150), (64, 1), (4096, 4096)])
+def test_decode_plan_window_items(S, W):
+    """Decode puts the sink and recent windows in items of 64 positions (at least
+    one sink item, even an empty one), ahead of the history chunks."""
+    lay = L(sink_tokens=S, recent_tokens=W)
+    lens = [S + W + 1000, 7]
+    chunk, items = B.oscar_decode_plan(lay, lens, history_chunk=256)
+    assert chunk == 256
+    win = max(1, -(-S // 64)) + -(-W // 64)
+    assert items == win + -(-1000 // 256)
+
+
 def test_extend_workspace_size():
     lay = L()
     for n, P in ((37, 100000), (8192, 122880), (5, 300)):

@@ -1,7 +1,7 @@
 """GPU parity at the edges of the supported layouts: the most KV heads (16),
 KV-head counts that do not fill a 4-head workgroup, no sink window, a one-token
-recent window, the largest windows, and every group size, for append, decode,
-extend and the BF16 baseline.  Oracle-written pools, same bars as the main
+recent window, the largest windows, windows that are not whole decode items,
+and every group size, for append, decode, extend and the BF16 baseline.  Oracle-written pools, same bars as the main
 suites (codes bit-exact with exact rotations, attention 2e-3)."""
 
 import numpy as np
@@ -24,6 +24,9 @@ CASES = [
     ("recent1", 2, 4, 64, 1, 32, (900, 64, 65, 66)),
     ("big_windows", 2, 4, 1024, 2048, 32, (3000, 3100, 4000)),
     ("hkv5_G128_no_sink", 5, 3, 0, 128, 128, (800, 129)),
+    # windows that are not whole 64-position decode items (sink 64 + 36, recent
+    # 64 + 64 + 22), lengths ending inside each of them, g = 6 (group padded to 8)
+    ("ragged_windows", 2, 6, 100, 150, 32, (5000, 1, 37, 64, 65, 101, 170, 250, 251)),
 ]
 
 

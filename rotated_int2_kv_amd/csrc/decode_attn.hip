@@ -77,6 +77,7 @@ struct DecodeArgs {
     int32_t items;
     int32_t sink_items;   // items [0, sink_items): the sink window, kWindowItemTokens positions each
     int32_t win_items;    // items [sink_items, win_items): the recent window; then the history chunks
+    int32_t win_last;     // partial_kernel's grid takes the history items first, the window items last
     int32_t waves;     // KV heads per workgroup
     int32_t head_chunks;
     int32_t group_size;
@@ -1131,7 +1132,10 @@ __global__ __launch_bounds__(64 * kPartialWaves) void partial_kernel(DecodeArgs 
     const int hc = id % a.head_chunks;
     const int rest = id / a.head_chunks;
     const int b = rest % a.batch;
-    const int j = rest / a.batch;
+    // grid order: the long history items first, so that the short window items
+    // fill the compute units that the last history items leave idle
+    const int jg = rest / a.batch, n_hist = a.items - a.win_items;
+    const int j = !a.win_last ? jg : jg < n_hist ? a.win_items + jg : jg - n_hist;
     int req = 0;
     const int L = request_length(a, b, req);
     int p0, p1;
@@ -1606,6 +1610,7 @@ DecodeArgs make_args(const oscar_layout *layout, const oscar_pool *pool, const v
     a.items = plan.items;
     a.sink_items = plan.sink_items;
     a.win_items = plan.sink_items + plan.recent_items;
+    a.win_last = 1;
     a.waves = kPartialWaves;
     a.head_chunks = (a.hkv + kPartialWaves - 1) / kPartialWaves;
     a.group_size = layout->group_size;
@@ -1643,15 +1648,17 @@ oscar_status launch_decode(const DecodeArgs &a, const DecodePlan &plan, hipStrea
         // end inside a 16-byte unit): the BF16 window items on partial_kernel,
         // the history items on hist_lowmeta_kernel
         const int bf_blocks = a.win_items * a.batch * a.head_chunks;
+        DecodeArgs aw = a;
+        aw.win_last = 0;                            // this grid holds the window items alone
         switch (a.g) {
-            case 1: e = launch_partial<1>(a, bf_blocks, stream); break;
-            case 2: e = launch_partial<2>(a, bf_blocks, stream); break;
-            case 3: e = launch_partial<3>(a, bf_blocks, stream); break;
-            case 4: e = launch_partial<4>(a, bf_blocks, stream); break;
-            case 5: e = launch_partial<5>(a, bf_blocks, stream); break;
-            case 6: e = launch_partial<6>(a, bf_blocks, stream); break;
-            case 7: e = launch_partial<7>(a, bf_blocks, stream); break;
-            default: e = launch_partial<8>(a, bf_blocks, stream); break;
+            case 1: e = launch_partial<1>(aw, bf_blocks, stream); break;
+            case 2: e = launch_partial<2>(aw, bf_blocks, stream); break;
+            case 3: e = launch_partial<3>(aw, bf_blocks, stream); break;
+            case 4: e = launch_partial<4>(aw, bf_blocks, stream); break;
+            case 5: e = launch_partial<5>(aw, bf_blocks, stream); break;
+            case 6: e = launch_partial<6>(aw, bf_blocks, stream); break;
+            case 7: e = launch_partial<7>(aw, bf_blocks, stream); break;
+            default: e = launch_partial<8>(aw, bf_blocks, stream); break;
         }
         if (e != hipSuccess) return fail(OSCAR_ERR_HIP, std::string("partial launch: ") + hipGetErrorString(e));
         const int h_blocks = (plan.items - a.win_items) * a.batch * a.head_chunks;

@@ -1131,10 +1131,16 @@ __global__ __launch_bounds__(64 * kPartialWaves) void partial_kernel(DecodeArgs 
     const int id = blockIdx.x;
     const int hc = id % a.head_chunks;
     const int rest = id / a.head_chunks;
-    const int b = rest % a.batch;
+    // grid row jg holds one item of every request, request b at column
+    // (b + jg) mod batch: the XCDs take workgroups round-robin by index, so
+    // rotating the columns spreads each request's items over the XCDs (with a
+    // multiple of 8 columns a request would otherwise stay on one XCD, and a
+    // ragged batch would load the XCDs unevenly)
+    const int jg = rest / a.batch;
+    const int b = (rest % a.batch + a.batch - jg % a.batch) % a.batch;
     // grid order: the long history items first, so that the short window items
     // fill the compute units that the last history items leave idle
-    const int jg = rest / a.batch, n_hist = a.items - a.win_items;
+    const int n_hist = a.items - a.win_items;
     const int j = !a.win_last ? jg : jg < n_hist ? a.win_items + jg : jg - n_hist;
     int req = 0;
     const int L = request_length(a, b, req);
@@ -1174,8 +1180,9 @@ __global__ __launch_bounds__(64 * kPartialWaves) void hist_lowmeta_kernel(Decode
     const int id = blockIdx.x;
     const int hc = id % a.head_chunks;
     const int rest = id / a.head_chunks;
-    const int b = rest % a.batch;
-    const int j = a.win_items + rest / a.batch;
+    const int jg = rest / a.batch;
+    const int b = (rest % a.batch + a.batch - jg % a.batch) % a.batch;   // rotated columns, as partial_kernel
+    const int j = a.win_items + jg;
     int req = 0;
     const int L = request_length(a, b, req);
     int p0, p1;

@@ -45,6 +45,13 @@ inline int64_t record_bytes(const oscar_layout &lay) {
 // positions, so that a request's window work runs on several compute units.
 constexpr int kWindowItemTokens = 64;
 
+// Decode planning: compute units of the device (MI355X) and split-K workgroups
+// that one compute unit holds at once (the history kernel takes 156 registers
+// per lane with up to 4 query heads per KV head, three workgroups of 4 waves
+// per CU, and over 200 with 5 to 8, two).
+constexpr int kDeviceCUs = 256;
+inline int decode_workgroups_per_cu(int group) { return group <= 4 ? 3 : 2; }
+
 // Split-K plan of one decode call (pure function of the host lengths).
 struct DecodePlan {
     int32_t chunk = 0;           // history tokens per work item

@@ -60,13 +60,12 @@ oscar_status make_decode_plan(const oscar_layout &lay, int32_t batch,
     if (batch < 1) return fail(OSCAR_ERR_INVALID_ARG, "batch must be >= 1");
     if (!seq_lens_host) return fail(OSCAR_ERR_INVALID_ARG, "seq_lens_host is null");
     const int64_t S = lay.sink_tokens, W = lay.recent_tokens;
-    int64_t total_hist = 0, max_hist = 0, max_len = 0;
+    int64_t max_hist = 0, max_len = 0;
     for (int32_t b = 0; b < batch; ++b) {
         const int64_t L = seq_lens_host[b];
         if (L < (extend ? 0 : 1))
             return fail(OSCAR_ERR_INVALID_ARG, extend ? "prefix_len must be >= 0" : "every sequence length must be >= 1");
         const int64_t hist = std::max<int64_t>(0, std::max(S, L - W) - S);
-        total_hist += hist;
         max_hist = std::max(max_hist, hist);
         max_len = std::max(max_len, L);
     }
@@ -86,12 +85,53 @@ oscar_status make_decode_plan(const oscar_layout &lay, int32_t batch,
         chunk = (max_hist + want - 1) / want;
         chunk = std::max<int64_t>(256, (chunk + 31) / 32 * 32);
     } else {
-        // about 1024 history work items over the batch (four per compute
-        // unit of a 256-CU device, where three run at once), each at least
-        // 256 and at most 8192 tokens
-        chunk = (total_hist + 1023) / 1024;
-        chunk = (chunk + 31) / 32 * 32;
-        chunk = std::min<int64_t>(8192, std::max<int64_t>(256, chunk));
+        // Rounds of the workgroups the device holds at once.  When every
+        // request has the same number of nearly full history items (a uniform
+        // batch), one round: its items start and end together, and the short
+        // window items, last in the grid, fill the compute units the history
+        // items leave idle.  Otherwise four rounds, so that the partial last
+        // items of ragged requests leave small gaps.  Each case takes the
+        // smallest chunk (a multiple of 32, at least 256) whose items fit.
+        const int64_t head_chunks = (lay.num_kv_heads + 3) / 4;
+        const int64_t g = lay.num_q_heads / lay.num_kv_heads;
+        const int64_t resident =
+            std::max<int64_t>(1, int64_t(kDeviceCUs) * decode_workgroups_per_cu(int(g)) / head_chunks);
+        auto items_for = [&](int64_t c) {
+            int64_t n = 0;
+            for (int32_t b = 0; b < batch; ++b) {
+                const int64_t hist = std::max<int64_t>(0, std::max(S, int64_t(seq_lens_host[b]) - W) - S);
+                n += (hist + c - 1) / c;
+            }
+            return n;
+        };
+        const int64_t c_max = std::max<int64_t>(256, (max_hist + 31) / 32 * 32);
+        // the fewest rounds any chunk allows (more than one only when the batch
+        // has more requests than the device holds workgroups)
+        const int64_t rounds = std::max<int64_t>(1, (items_for(c_max) + resident - 1) / resident);
+        auto chunk_for = [&](int64_t n_rounds) {   // smallest chunk whose items fit n_rounds
+            int64_t lo = 256 / 32, hi = c_max / 32;   // in units of 32 positions
+            while (lo < hi) {
+                const int64_t mid = (lo + hi) / 2;
+                if (items_for(32 * mid) <= n_rounds * resident)
+                    hi = mid;
+                else
+                    lo = mid + 1;
+            }
+            return 32 * lo;
+        };
+        chunk = chunk_for(rounds);
+        int64_t per_request = -1, hist_sum = 0, n_items = 0;
+        bool uniform = true;
+        for (int32_t b = 0; b < batch; ++b) {
+            const int64_t hist = std::max<int64_t>(0, std::max(S, int64_t(seq_lens_host[b]) - W) - S);
+            if (hist == 0) continue;
+            const int64_t k = (hist + chunk - 1) / chunk;
+            uniform = uniform && (per_request < 0 || k == per_request);
+            per_request = k;
+            hist_sum += hist;
+            n_items += k;
+        }
+        if (!uniform || 10 * hist_sum < 9 * n_items * chunk) chunk = chunk_for(4 * rounds);
     }
     // decode: windows in items of kWindowItemTokens positions; extend: one item each
     const int64_t sink_items = extend ? 1 : std::max<int64_t>(1, (S + kWindowItemTokens - 1) / kWindowItemTokens);

@@ -198,8 +198,10 @@ def test_decode_plan_and_workspace():
     lens = [100000] * 32
     chunk, items = B.oscar_decode_plan(lay, lens)
     hist = 100000 - 64 - 256
-    assert chunk % 32 == 0 and 256 <= chunk <= 8192
-    assert chunk == -(-(-(-32 * hist // 1024)) // 32) * 32
+    # the history items of 32 requests x 2 four-head chunks in one round of the
+    # 256 x 3 workgroups the device holds: the smallest multiple of 32 with at
+    # most 384 items per head chunk
+    assert chunk == min(c for c in range(256, hist + 32, 32) if 32 * -(-hist // c) <= 384) == 8320
     # the sink (64) and recent (256) windows in work items of 64 positions
     assert items == 1 + 4 + -(-hist // chunk)
     ws = B.oscar_decode_workspace_size(lay, lens)
@@ -284,6 +286,38 @@ def _extend(lay, n_new, prefix, **over):
 ])
 def test_extend_rejects_before_launch(over, status):
     assert _extend(L(), 37, 5000, **over) == status
+
+
+@pytest.mark.parametrize("hkv,g,lens,want", [
+    (8, 4, [32768], 256),                                    # one request: the smallest chunk
+    (8, 4, [100000] * 32, 8320),                             # uniform: one round
+    (8, 4, [100000 + 37 * i for i in range(32)], None),      # nearly uniform: still one round
+    (4, 6, [4096 + 7919 * i % 127000 for i in range(64)], None),   # ragged: four rounds
+    (8, 4, [50000] * 1000, 49696),                           # more requests than one round holds
+    (8, 4, [300, 7], 256),                                   # no history
+])
+def test_decode_plan_rounds(hkv, g, lens, want):
+    """The default history chunk is the smallest multiple of 32 (at least 256)
+    whose items fit R rounds of the workgroups the device holds at once (256
+    compute units x 3 workgroups with g <= 4, x 2 above, per 4-head chunk): R
+    the fewest any chunk allows when every request gets the same number of
+    items, at least 90% full; four times that otherwise."""
+    lay = L(num_kv_heads=hkv, num_q_heads=g * hkv, max_requests=len(lens))
+    chunk, items = B.oscar_decode_plan(lay, lens)
+    hists = [h for h in (max(0, max(64, n - 256) - 64) for n in lens)]
+    resident = 256 * (3 if g <= 4 else 2) // -(-hkv // 4)
+    n_items = lambda c: sum(-(-h // c) for h in hists)   # noqa: E731
+    top = max(256, -(-max(hists) // 32) * 32)
+    fewest = max(1, -(-n_items(top) // resident))
+    smallest = lambda r: min(c for c in range(256, top + 32, 32) if n_items(c) <= r * resident)   # noqa: E731
+    c1 = smallest(fewest)
+    counts = {-(-h // c1) for h in hists if h}
+    full = sum(hists) >= 0.9 * n_items(c1) * c1
+    expect = c1 if len(counts) <= 1 and full else smallest(4 * fewest)
+    assert chunk == expect
+    if want is not None:
+        assert chunk == want
+    assert items == 1 + 4 + max(-(-h // chunk) for h in hists)
 
 
 @pytest.mark.parametrize("S,W", [(0, 256), (100, 150), (64, 1), (4096, 4096)])

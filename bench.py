@@ -22,10 +22,10 @@ append on the host's cores.
 The default run times 2,000 steps after 500 warm-up steps: under this load the
 part runs at its board power limit, and its clocks take a few hundred
 milliseconds of sustained work to settle.  Short runs read that settling: on
-one MI355X, the split-K kernel takes 0.490-0.501 ms per launch (62-64% of the
-8 TB/s roofline) in the steady state and 0.592-0.603 ms on average (0.531-0.714
-ms per launch, 52-53%) over the 20 timed steps of --steps 20 --warmup 5 in a
-fresh process.  The JSON line carries every launch of runs up to 100 steps.
+one MI355X, the split-K kernel takes 0.483-0.485 ms per launch (65% of the
+8 TB/s roofline) in the steady state and 0.599 ms on average (0.544-0.691 ms
+per launch, 52%) over the 20 timed steps of --steps 20 --warmup 5 in a fresh
+process.  The JSON line carries every launch of runs up to 100 steps.
 """
 
 from __future__ import annotations

@@ -184,7 +184,7 @@ __global__ __launch_bounds__(512) void prep_kernel(DecodeArgs a) {
     __syncthreads();
     if (t < a.g) {
         // power-of-two operand scale 2^K with max|q'| 2^K < 2^15, so that
-        // q' 2^(K - e) (e = 0..8) fits fp16 and its low part stays normal
+        // q' 2^(K - e) (e = 0..8) fits fp16
         const int h = t;
         const float mx = fmaxf(half_max[h][0], half_max[h][1]);
         int e = 0;
@@ -236,6 +236,16 @@ __host__ __device__ constexpr int pair_exp(int j) { return j <= 4 ? 2 * j : 2 * 
 [[maybe_unused]] __device__ __forceinline__ uint32_t code_bits(uint32_t w, uint32_t w_sh6, int j) {
     return j <= 4 ? (w & (0x00030003u << (2 * j))) : (w_sh6 & (0x00030003u << (2 * j - 6)));
 }
+// Bit position of V code j (channel 4 n + j) in each 16-bit half of a PV
+// B-operand dword.  The matrix core aligns the products of one instruction by
+// their exponent fields, and every denormal carries the smallest exponent, so
+// a code low in its mantissa loses as many bits of the alignment window as it
+// has leading zeros: with the codes at bits 0, 2, 4, 6 the products of code 0
+// kept about 15 bits, and the output of 131K-token requests drifted by up to
+// 1.2e-3 of its scale.  Codes 0 and 1 are therefore taken after a left shift
+// by 4 (bits 4 and 6), codes 2 and 3 in place.  (The QK products showed no
+// such drift with their codes at bits 0..8.)
+__host__ __device__ constexpr int pv_code_exp(int j) { return j <= 1 ? 2 * j + 4 : 2 * j; }
 
 // The matrix-core products below span the channels of at most two groups each:
 // channel halves 0..63 and 64..127 (P = 0, 1), and within a half the 16-channel
@@ -680,9 +690,9 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
             for (int c = 0; c < 2; ++c) {
                 const uint32_t lo = lds_ld<uint32_t>(pv_at[pp][c] + so);
                 const uint32_t hi = lds_ld<uint32_t>(pv_at[pp][c] + so + kHalfTokOff);
-                // token t + 16 as 3 - c: its 2-bit codes inverted (the bits
-                // above the codes are never read)
-                xw[c][pp] = __builtin_amdgcn_perm(hi, lo, pv_sel) ^ 0xffff0000u;
+                // token t + 16 enters as 3 - c: its 2-bit codes are inverted
+                // where B is formed (the bits above the codes are never read)
+                xw[c][pp] = __builtin_amdgcn_perm(hi, lo, pv_sel);
             }
         }
         // ---- QK: logit of (token 16 hf + n, head 4 hs + kb)
@@ -843,8 +853,13 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
             for (int c = 0; c < 2; ++c) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const uint32_t m = 0x00030003u << (2 * j);
-                    const f16x8 Bj = u4_as_h8(xw[c][0] & m, xw[c][1] & m, xw[c][2] & m, xw[c][3] & m);
+                    // (x ^ inv) & m: one three-input bit operation per dword
+                    const uint32_t m = 0x00030003u << pv_code_exp(j);
+                    const uint32_t inv = j <= 1 ? 0xfff00000u : 0xffff0000u;
+                    uint32_t x[4];
+#pragma unroll
+                    for (int pp = 0; pp < 4; ++pp) x[pp] = ((j <= 1 ? xw[c][pp] << 4 : xw[c][pp]) ^ inv) & m;
+                    const f16x8 Bj = u4_as_h8(x[0], x[1], x[2], x[3]);
                     oacc[hs][4 * c + j] = mfma_f16(A[c], Bj, oacc[hs][4 * c + j]);
                 }
             }
@@ -951,7 +966,7 @@ __device__ __forceinline__ void int2_item(const DecodeArgs &a, int b, int req, i
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const float v = oacc[hs][4 * c + jj][i];
-                    o[4 * c + jj] = (v + swap16(v)) * __builtin_ldexpf(1.0f, 24 - pair_exp(jj)) + z;
+                    o[4 * c + jj] = (v + swap16(v)) * __builtin_ldexpf(1.0f, 24 - pv_code_exp(jj)) + z;
                 }
             }
             if (writer) {

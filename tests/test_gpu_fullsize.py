@@ -187,6 +187,13 @@ def _fill_all_oracle(w, q_stream):
     return pt.normwise_rel(o_gpu, o_ref)
 
 
+# Regression guard below the bar: the split-K products keep about 19.6 bits of
+# their largest product (V codes at bit 4 or above of their fp16 halves); with
+# codes at bit 0 the 131K-token requests of the mixed batch drifted to 1.2e-3,
+# and the every-request maxima are now 4.9e-5 and 7.4e-5.
+GUARD = 5e-4
+
+
 def _check_all(err, label):
     """Every (request, q head) of the batch within the bar; report the margin."""
     worst = np.unravel_index(int(err.argmax()), err.shape)
@@ -194,6 +201,7 @@ def _check_all(err, label):
            f"q head) {tuple(int(i) for i in worst)}, median {np.median(err):.3e}, 99th percentile "
            f"{np.percentile(err, 99):.3e}; bar {TOL:.0e} ({100 * err.max() / TOL:.0f}% of it used)")
     assert err.max() <= TOL
+    assert err.max() <= GUARD, f"{label}: within the bar but above the accumulation guard {GUARD:.0e}"
 
 
 def _check(errs, label):

@@ -235,6 +235,23 @@ def test_mixed_b64_full_size_every_request():
     _check_all(_fill_all_oracle(w, q_stream=5), "mixed_b64")
 
 
+@pytest.mark.timeout(900)
+def test_long_context_524k():
+    """One request of 524,288 tokens (4x the longest of the mixed batch), 24 q /
+    4 KV heads, page_size-1 slots in random order: every query head against the
+    oracle.  The split-K sums run over 16,000 tiles here, so a one-sided
+    rounding drift in the products grows with the context; the bar and the
+    guard below it hold at this length too."""
+    w = workloads.custom("mixed_b64", name="long_524k", batch=1, seq_lens=(524288,), pool_slack=1.0)
+    gs.say("long context: 1 x 524,288 tokens")
+    errs = _fill_and_sample(w, sampled={0}, q_stream=5)
+    e = errs[0]
+    gs.say(f"  long_524k: max normwise rel err {e.max():.3e} (median {np.median(e):.3e}); "
+           f"bar {TOL:.0e}, guard {GUARD:.0e}")
+    assert e.max() <= TOL
+    assert e.max() <= GUARD
+
+
 def test_append_131k_full_size_sampled():
     """One call appends 131,072 tokens x 8 KV heads; a seeded sample is checked."""
     torch = gs.torch_gpu()

@@ -220,6 +220,22 @@ def run_decode(args, torch, B, workloads, name=None, steps=None, warmup=None):
                 o_finite=bool(torch.isfinite(out.float()).all().item()))
 
 
+def split_k_spread(lens, sink, recent, chunk, hkv):
+    """Work per history item of a split-K plan: how evenly the ragged batch
+    fills its items (positions per non-empty item, items per request)."""
+    hist = [max(0, int(L) - min(int(L), sink + recent)) for L in lens]
+    per_req = [-(-h // chunk) for h in hist]
+    sizes = []
+    for h in hist:
+        sizes += [chunk] * (h // chunk) + ([h % chunk] if h % chunk else [])
+    sizes = np.asarray(sizes if sizes else [0])
+    head_chunks = (hkv + 3) // 4
+    return dict(history_items=int(sum(per_req)) * head_chunks, items_per_request_min=int(min(per_req)),
+                items_per_request_max=int(max(per_req)), item_positions_min=int(sizes.min()),
+                item_positions_median=float(np.median(sizes)), item_positions_max=int(sizes.max()),
+                fill=float(sizes.sum() / (len(sizes) * chunk)) if sizes.sum() else 0.0)
+
+
 def decode_leg(d, label):
     """Summary of a non-headline decode workload for the JSON line."""
     kb = d["kbytes"]
@@ -231,6 +247,7 @@ def decode_leg(d, label):
                 gb_per_s=kb / (d["kern_ms"] * 1e-3) / 1e9, frac_hbm=kb / (d["kern_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                 frac_hbm_call=d["call_bytes"] / (d["call_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                 history_chunk=d["chunk"], items_per_request=d["items"], history_workgroups=d["workgroups"],
+                split_k=split_k_spread(d["lens"], d["w"].sink, d["w"].recent, d["chunk"], d["w"].num_kv_heads),
                 output_finite=d["o_finite"])
 
 

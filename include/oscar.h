@@ -239,10 +239,12 @@ oscar_status oscar_decode_attn(hipStream_t stream, const oscar_layout *layout,
  * those of oscar_decode_attn (bit for bit: the same kernels and plan); the
  * workspace is instead a device array inside the library, one per GPU, of
  * OSCAR_NOALLOC_SCRATCH_BYTES (32 MiB; the 32 x 100K-token batch of
- * 32 q / 8 KV heads needs about 19 MB, oscar_decode_workspace_size tells any
+ * 32 q / 8 KV heads needs about 9.6 MB, oscar_decode_workspace_size tells any
  * other), held by each GPU the library runs on until the process ends.
  * A batch whose workspace would exceed it returns OSCAR_ERR_WORKSPACE and
- * launches nothing.  The call makes no allocation (no hipMalloc, hipFree or
+ * launches nothing; a larger history_chunk in opts makes fewer work items and
+ * a smaller workspace (a ragged batch of 64 requests up to 131K tokens, 24 q /
+ * 4 KV heads, needs 52 MB with the default plan and fits with 8192).  The call makes no allocation (no hipMalloc, hipFree or
  * allocating library routine); its first use on a device looks up that
  * device's array address (hipGetSymbolAddress) once.  Every call on one GPU
  * shares its array, so calls that overlap on one GPU (different streams, or

@@ -498,7 +498,7 @@ def run_lower_metadata(args, torch, B, workloads, group_size, scale_bits=16):
                 output_finite=bool(torch.isfinite(out.float()).all().item()))
 
 
-def run_copy_reference(torch, record_bytes: int, n_records: int):
+def run_copy_reference(torch, record_bytes: int, n_records: int, B=None):
     """Reference rates of plain device copies on the same GPU: a 2 GiB
     contiguous copy, and a gather of n_records rows of record_bytes each at
     random row indices (torch index_select), the access pattern of the INT2
@@ -521,10 +521,20 @@ def run_copy_reference(torch, record_bytes: int, n_records: int):
     idx = torch.randperm(n_records, device="cuda")
     out = torch.empty_like(rows)
     gather_ms = timed(lambda: torch.index_select(rows, 0, idx, out=out))
-    del rows, idx, out
+    del out
+    # the same rows read without a copy (the library's read-only gather
+    # reference: the decode's history access pattern with no arithmetic)
+    read_gbs = None
+    if B is not None and record_bytes == 768:
+        idx32 = idx.to(torch.int32)
+        sink = torch.empty(B.OSCAR_GATHER_REF_SINK_WORDS, dtype=torch.int32, device="cuda")
+        read_ms = timed(lambda: B.oscar_gather_read_reference(rows, idx32, sink), reps=20)
+        read_gbs = n_records * (record_bytes + 4) / (read_ms * 1e-3) / 1e9
+        del idx32, sink
+    del rows, idx
     return dict(plain_copy_gb_per_s=2 * (1 << 31) / (copy_ms * 1e-3) / 1e9,
                 record_gather_gb_per_s=n_records * (2 * record_bytes + 8) / (gather_ms * 1e-3) / 1e9,
-                record_bytes=record_bytes, records=n_records)
+                record_read_gb_per_s=read_gbs, record_bytes=record_bytes, records=n_records)
 
 
 def run_covariance(args, torch, B, workloads):
@@ -703,11 +713,14 @@ def main():
                 f"{leg['gb_per_s']:.0f} GB/s ({100 * leg['frac_hbm']:.1f}% of HBM peak)")
     # (not with --copy-calibration: the counter runs calibrate on their one 1 GiB copy)
     ref = None if (args.no_copy_reference or args.copy_calibration) else \
-        run_copy_reference(torch, 8 * 96, int(d["lens"].sum()))
+        run_copy_reference(torch, 8 * 96, int(d["lens"].sum()), B)
     if ref:
         ref["decode_frac_of_plain_copy"] = achieved / ref["plain_copy_gb_per_s"]
+        if ref["record_read_gb_per_s"]:
+            ref["decode_frac_of_record_read"] = achieved / ref["record_read_gb_per_s"]
         log(f"[bench] reference rates: copy {ref['plain_copy_gb_per_s']:.0f} GB/s, 768-byte random-row gather "
-            f"{ref['record_gather_gb_per_s']:.0f} GB/s; decode at {100 * ref['decode_frac_of_plain_copy']:.0f}% "
+            f"{ref['record_gather_gb_per_s']:.0f} GB/s, read-only gather of the same rows "
+            f"{ref['record_read_gb_per_s'] or 0:.0f} GB/s; decode at {100 * ref['decode_frac_of_plain_copy']:.0f}% "
             f"of the plain copy")
     app = None if args.no_append else run_append(args, torch, B, workloads)
     if app:

@@ -379,6 +379,25 @@ oscar_status oscar_covariance_accumulate(hipStream_t stream, const oscar_layout 
                                          oscar_dtype dtype, int64_t n_rows, double *acc, void *workspace,
                                          size_t workspace_bytes);
 
+/*
+ * oscar_gather_read_reference: a measurement reference, not a step of the
+ * method.  Reads whole rows of `rows` ([num_rows][row_bytes], device, 16-byte
+ * aligned; row_bytes = 768, the slot-major record of 8 KV heads of 96-byte
+ * head records) at the row indices idx[0..n-1] (device int32; an index
+ * outside 0..num_rows-1 reads the last row), 16 bytes per load with the
+ * non-temporal policy, and writes one XOR of what it read per thread to
+ * `sink` (device, OSCAR_GATHER_REF_SINK_WORDS uint32).  It is the access
+ * pattern of the INT2 history stream of oscar_decode_attn (OSCAR page,
+ * "Serving system": a token-granular pool read through the request's index
+ * table) with no arithmetic, so its rate bounds what that stream can reach on
+ * the device.  Asynchronous on `stream`; invalid arguments return a status
+ * and launch nothing.
+ */
+#define OSCAR_GATHER_REF_SINK_WORDS (2048 * 256)
+oscar_status oscar_gather_read_reference(hipStream_t stream, const void *rows, int64_t row_bytes,
+                                         int64_t num_rows, const int32_t *idx, int64_t n, uint32_t *sink,
+                                         int64_t sink_words);
+
 /* Thread-local message of the last non-OK status of this thread. */
 const char *oscar_last_error(void);
 

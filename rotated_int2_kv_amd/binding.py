@@ -35,7 +35,7 @@ EXPORTED = (
     "oscar_decode_workspace_size", "oscar_decode_attn", "oscar_decode_attn_noalloc", "oscar_decode_plan",
     "oscar_extend_workspace_size", "oscar_extend_attn", "oscar_bf16_pool_bytes", "oscar_bf16_append",
     "oscar_bf16_decode_workspace_size", "oscar_bf16_decode_attn", "oscar_covariance_workspace_size",
-    "oscar_covariance_accumulate", "oscar_last_error", "oscar_version",
+    "oscar_covariance_accumulate", "oscar_gather_read_reference", "oscar_last_error", "oscar_version",
 )
 
 
@@ -96,6 +96,7 @@ def _load() -> ctypes.CDLL:
                                          OP]),
         "oscar_covariance_workspace_size": (I32, [LP, I64, ctypes.POINTER(SZ)]),
         "oscar_covariance_accumulate": (I32, [P, LP, P, I32, I64, P, P, SZ]),
+        "oscar_gather_read_reference": (I32, [P, P, I64, I64, P, I64, P, I64]),
         "oscar_last_error": (ctypes.c_char_p, []),
         "oscar_version": (ctypes.c_char_p, []),
     }
@@ -340,6 +341,18 @@ def oscar_covariance_workspace_size(layout: Layout, n_rows: int) -> int:
     out = ctypes.c_size_t(0)
     _check(_lib.oscar_covariance_workspace_size(ctypes.byref(layout.c()), int(n_rows), ctypes.byref(out)))
     return int(out.value)
+
+
+OSCAR_GATHER_REF_SINK_WORDS = 2048 * 256
+
+
+def oscar_gather_read_reference(rows, idx, sink, stream=None) -> None:
+    """Read rows [num_rows, 768] uint8 (device) at idx [n] int32 (device);
+    sink [OSCAR_GATHER_REF_SINK_WORDS] int32/uint32 (device) receives one word per thread."""
+    _dev(rows, idx, sink)
+    _check(_lib.oscar_gather_read_reference(
+        _stream(stream), _ptr(rows), int(rows.shape[1] * rows.element_size()), int(rows.shape[0]), _ptr(idx),
+        int(idx.numel()), _ptr(sink), int(sink.numel())))
 
 
 def oscar_covariance_accumulate(layout: Layout, x, acc, workspace, stream=None) -> None:

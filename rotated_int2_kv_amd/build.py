@@ -26,7 +26,8 @@ OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liboscar.so")
 ARCH = "gfx950"
 
-SOURCES = ["oscar_host.cpp", "quant_append.hip", "decode_attn.hip", "bf16_decode.hip", "extend_hist.hip", "calib.hip"]
+SOURCES = ["oscar_host.cpp", "quant_append.hip", "decode_attn.hip", "bf16_decode.hip", "extend_hist.hip", "calib.hip",
+           "gather_ref.hip"]
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -444,3 +444,18 @@ def test_noalloc_decode_rejects_a_batch_beyond_its_scratch_before_launch():
         B.OSCAR_F32, None)
     assert st == B.OSCAR_ERR_WORKSPACE
     assert "scratch" in B.oscar_last_error()
+
+
+def test_gather_read_reference_rejects_before_launch():
+    """The read-only gather reference validates its arguments on the host and
+    launches nothing when they are wrong (fake, never dereferenced pointers)."""
+    f = B._lib.oscar_gather_read_reference
+    ok_ptr = 0x10000
+    words = B.OSCAR_GATHER_REF_SINK_WORDS
+    assert f(None, None, 768, 10, ok_ptr, 10, ok_ptr, words) == B.OSCAR_ERR_INVALID_ARG
+    assert f(None, ok_ptr, 384, 10, ok_ptr, 10, ok_ptr, words) == B.OSCAR_ERR_UNSUPPORTED
+    assert f(None, ok_ptr, 768, 0, ok_ptr, 10, ok_ptr, words) == B.OSCAR_ERR_INVALID_ARG
+    assert f(None, ok_ptr, 768, 10, ok_ptr, -1, ok_ptr, words) == B.OSCAR_ERR_INVALID_ARG
+    assert f(None, ok_ptr + 8, 768, 10, ok_ptr, 10, ok_ptr, words) == B.OSCAR_ERR_INVALID_ARG   # misaligned
+    assert f(None, ok_ptr, 768, 10, ok_ptr, 10, ok_ptr, words - 1) == B.OSCAR_ERR_INVALID_ARG    # small sink
+    assert f(None, ok_ptr, 768, 10, ok_ptr, 0, ok_ptr, words) == B.OSCAR_OK                      # n = 0: no-op

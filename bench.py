@@ -60,7 +60,7 @@ KERNEL_SOURCES = ("rotated_int2_kv_amd/csrc/decode_attn.hip", "rotated_int2_kv_a
 BF16_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bf16_partial_kernel_decode_b32_hbm_bytes.md")
 BF16_KERNEL_SOURCES = ("rotated_int2_kv_amd/csrc/bf16_decode.hip", "rotated_int2_kv_amd/csrc/common.h",
                        "rotated_int2_kv_amd/csrc/internal.h", "rotated_int2_kv_amd/build.py")
-# worker threads of the CPU oracle baseline: the host's share of cores on the GPU machine
+# worker threads of the CPU oracle baseline: the host cores one GPU's share of a node gets
 CPU_BASELINE_THREADS = 16
 
 
@@ -665,8 +665,8 @@ def main():
                     help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU: the hot path (per-request, per-KV-head "
-                                   "decode and append) is measured on one MI355X; --gpus must be 1"}))
+        print(json.dumps({"error": "the decode and append path runs on one GPU (requests and KV heads are "
+                                   "independent; sharding is not implemented); --gpus must be 1"}))
         sys.exit(2)
 
     import torch
